@@ -1,0 +1,355 @@
+"""Benchmark of the cross-tier KV transfer on one MI355X.
+
+One step = one pass of the hot path over a 32K-token prefix of an MLA-latent KV
+pool (78 layers x 576 bf16 = 1152-byte rows, page size 64): a D2H write-back of
+the prefix from contiguous device pages into the pinned host pool, then an H2D
+load of it (per-layer kernels and per-layer events) into another 512 device
+pages. Inputs are resident (device pool in HBM, host pool pinned) before the
+timed region. Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout layer_first]
+                    [--path auto|kernel|kernel_lds|dma] [--no-matrix] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV transfer GB/s H2D & D2H (32K-token prefix) as % of host-link peak"
+PCIE_GEN5_X16_GBPS = 64.0   # PCIe 5.0 x16, per direction, 32 GT/s x 16 lanes (raw)
+HBM_PEAK_GBPS = 8000.0
+LAYOUTS = {"layer_first": 0, "page_first": 1, "page_first_direct": 2}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--layout", default="layer_first", choices=sorted(LAYOUTS))
+    p.add_argument("--path", default="auto", choices=["auto", "kernel", "kernel_lds", "dma"])
+    p.add_argument("--no-matrix", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--matrix-reps", type=int, default=5)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this transfer path has no multi-GPU part "
+              "(each GPU moves its own KV over its own host link); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import hierarchical_kv_cache_backup_amd as kvt
+    from hierarchical_kv_cache_backup_amd import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    shape = workloads.mla32k()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S_dev, S_host = shape.device_slots, shape.host_slots
+    n = shape.extra["tokens"]
+    layout = LAYOUTS[args.layout]
+    path = {"auto": kvt.PATH_AUTO, "kernel": kvt.PATH_KERNEL, "kernel_lds": kvt.PATH_KERNEL_LDS,
+            "dma": kvt.PATH_DMA}[args.path]
+
+    # ---- resident inputs: device pool (seeded bf16 N(0,1)), host pool, index sets
+    t_setup = time.perf_counter()
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S_dev * R, dtype=torch.uint8, device=dev)
+            workloads.fill_device_buffer(b, shape, 3, l, c, torch)
+            bufs.append(b)
+    pages_total = S_dev // ps
+    npages = n // ps
+    first = workloads.contiguous_pages_at_offset(3, pages_total, npages)
+    dev_b = workloads.page_indices(first, ps)
+    second = (first + npages) % pages_total                  # the other 512 pages
+    dev_l = workloads.page_indices(second, ps)
+    host_idx = np.arange(n, dtype=np.int64)
+    geom = kvt.geometry(L, C, R, S_dev, S_host, ps, layout)
+    t0 = time.perf_counter()
+    pool = kvt.KvPool(geom, bufs, device=0)
+    t_pool = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    log("setup %.1fs (pool create %.2fs, host pool %.2f GB)" %
+        (time.perf_counter() - t_setup, t_pool, pool.host_array().nbytes / 1e9))
+    s = torch.cuda.Stream()
+    bytes_dir = n * L * C * R
+
+    def timed(fn, reps, warm=2):
+        """Median device time (s) of fn() on stream s, by events recorded on s."""
+        for _ in range(warm):
+            fn()
+        s.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) / 1e3)
+        return statistics.median(ts), ts
+
+    # ---- measured host-link peak: contiguous 1 GiB copy-engine copies, both ways
+    GiB = 1 << 30
+    dbuf = torch.empty(GiB, dtype=torch.uint8, device=dev)
+    hbuf = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    with torch.cuda.stream(s):
+        t_h2d, _ = timed(lambda: dbuf.copy_(hbuf, non_blocking=True), 10)
+        t_d2h, _ = timed(lambda: hbuf.copy_(dbuf, non_blocking=True), 10)
+    memcpy_peak = {"h2d": GiB / t_h2d / 1e9, "d2h": GiB / t_d2h / 1e9}
+    del dbuf, hbuf
+    log("copy-engine 1 GiB contiguous: H2D %.2f GB/s, D2H %.2f GB/s" %
+        (memcpy_peak["h2d"], memcpy_peak["d2h"]))
+
+    # ---- per-path measurements on the workload (calibrates the selector)
+    def run(direction, p, lay_pool):
+        lay_pool.set_path(p)
+        if direction == kvt.BACKUP:
+            return timed(lambda: lay_pool.backup(dev_b, host_idx, 0, L, s), args.matrix_reps)[0]
+        return timed(lambda: lay_pool.load(dev_l, host_idx, 0, L, s), args.matrix_reps)[0]
+
+    calib = pool.calibration()
+    meas = {}
+    for d in (kvt.BACKUP, kvt.LOAD):
+        for p in (kvt.PATH_KERNEL, kvt.PATH_DMA):
+            meas[(d, p)] = run(d, p, pool)
+            log("%s %s: %.2f GB/s" % ("D2H" if d == 0 else "H2D", kvt.PATH_NAMES[p],
+                                      bytes_dir / meas[(d, p)] / 1e9))
+        calib.kernel_gbps[d] = bytes_dir / meas[(d, kvt.PATH_KERNEL)] / 1e9
+        calib.dma_gbps[d] = bytes_dir / meas[(d, kvt.PATH_DMA)] / 1e9
+    pool.set_calibration(calib)
+    pool.set_path(path)
+    link_peak = {"h2d": max(memcpy_peak["h2d"], calib.kernel_gbps[1], calib.dma_gbps[1]),
+                 "d2h": max(memcpy_peak["d2h"], calib.kernel_gbps[0], calib.dma_gbps[0])}
+
+    # ---- the timed steps
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(s)
+        pool.backup(dev_b, host_idx, 0, L, s)
+        if ev is not None:
+            ev[1].record(s)
+        pool.load(dev_l, host_idx, 0, L, s)
+        if ev is not None:
+            ev[2].record(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    d2h_t = [e[0].elapsed_time(e[1]) / 1e3 for e in evs]
+    h2d_t = [e[1].elapsed_time(e[2]) / 1e3 for e in evs]
+    d2h_gbps = bytes_dir / statistics.median(d2h_t) / 1e9
+    h2d_gbps = bytes_dir / statistics.median(h2d_t) / 1e9
+    value = 2 * bytes_dir * args.steps / wall / 1e9
+    chosen = {"d2h": kvt.PATH_NAMES[pool.last_path(kvt.BACKUP)],
+              "h2d": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)]}
+    stats = pool.stats()
+    log("steps: %.2f GB/s aggregate; D2H %.2f GB/s (%s), H2D %.2f GB/s (%s)" %
+        (value, d2h_gbps, chosen["d2h"], h2d_gbps, chosen["h2d"]))
+
+    # ---- roofline of the dominant kernel (host link bound), measured live
+    roof = kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, args)
+
+    # ---- layout x path matrix at the same geometry
+    matrix = []
+    if not args.no_matrix:
+        matrix = layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args)
+
+    pool.close()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic (seeded bf16 N(0,1) KV bytes, contiguous pages at a seeded offset)",
+        "config": {"workload": "mla-latent KV, 78 layers x 576 bf16 (1152 B rows), page 64, "
+                               "32768-token prefix: D2H write-back then per-layer H2D load",
+                   "layers": L, "components": C, "row_bytes": R, "tokens": n, "page_size": ps,
+                   "device_slots": S_dev, "host_slots": S_host, "host_layout": args.layout,
+                   "path": args.path, "bytes_per_direction": bytes_dir},
+        "h2d_gbps": round(h2d_gbps, 3),
+        "d2h_gbps": round(d2h_gbps, 3),
+        "path_chosen": chosen,
+        "link_peak_measured_gbps": {k: round(v, 3) for k, v in link_peak.items()},
+        "copy_engine_1GiB_gbps": {k: round(v, 3) for k, v in memcpy_peak.items()},
+        "pct_of_measured_peak": {"h2d": round(100 * h2d_gbps / link_peak["h2d"], 1),
+                                 "d2h": round(100 * d2h_gbps / link_peak["d2h"], 1)},
+        "pct_of_pcie_gen5_x16": {"h2d": round(100 * h2d_gbps / PCIE_GEN5_X16_GBPS, 1),
+                                 "d2h": round(100 * d2h_gbps / PCIE_GEN5_X16_GBPS, 1)},
+        "submit_us_per_call": {"d2h": round(stats.submit_us[0] / max(1, stats.calls[0]), 1),
+                               "h2d": round(stats.submit_us[1] / max(1, stats.calls[1]), 1)},
+        "pool_create_s": round(t_pool, 3),
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "matrix": matrix,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "xfer_walk.hpp"):
+        with open(os.path.join(ROOT, "hierarchical_kv_cache_backup_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel_name, src_hash):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = d.get(kernel_name)
+    if not rec or rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, args):
+    """Achieved host-link GB/s of the H2D gather kernel (the one the per-layer load
+    launches, one launch per layer): algorithmic bytes per launch / mean launch
+    time, the launch time taken from events recorded on the launch stream."""
+    pool.set_path(kvt.PATH_KERNEL)
+    per_launch = n * C * R
+    for _ in range(2):
+        pool.load(dev_l, host_idx, 0, L, s)
+    s.synchronize()
+    durs = []
+    for _ in range(max(3, args.steps)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        pool.load(dev_l, host_idx, 0, L, s)
+        e1.record(s)
+        e1.synchronize()
+        durs.append(e0.elapsed_time(e1) / 1e3 / L)          # L launches per call
+    mean = statistics.mean(durs)
+    achieved = per_launch / mean / 1e9
+    src_hash = kernel_source_hash()
+    return {"kernel": "kvt::xfer_rows<false> (H2D gather, one launch per layer)",
+            "bound": "host_link",
+            "achieved": round(achieved, 3),
+            "peak": PCIE_GEN5_X16_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PCIE_GEN5_X16_GBPS, 4),
+            "traffic": counter_traffic("xfer_rows_h2d", src_hash),
+            "algorithmic_bytes_per_launch": per_launch,
+            "mean_launch_us": round(mean * 1e6, 2),
+            "launches_timed": len(durs) * L,
+            "hbm_secondary": {"peak": HBM_PEAK_GBPS, "frac": round(achieved / HBM_PEAK_GBPS, 5)},
+            "kernel_source_hash": src_hash}
+
+
+def layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args):
+    rows = []
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    n = host_idx.size
+    bytes_dir = n * L * C * R
+    for lname, lay in LAYOUTS.items():
+        geom = kvt.geometry(L, C, R, shape.device_slots, shape.host_slots, ps, lay)
+        with kvt.KvPool(geom, bufs) as pool:
+            for dname, d in (("d2h", kvt.BACKUP), ("h2d", kvt.LOAD)):
+                rc, copies = kvt.kv_count_dma_copies(geom, dev_b, host_idx, 0, L)
+                rc2, segs = kvt.kv_count_segments(geom, dev_b, host_idx, 0, L)
+                cell = {"layout": lname, "dir": dname, "segments": segs, "dma_copies": copies}
+                for pname, p in (("kernel", kvt.PATH_KERNEL), ("kernel_lds", kvt.PATH_KERNEL_LDS),
+                                 ("dma", kvt.PATH_DMA)):
+                    pool.set_path(p)
+                    fn = ((lambda: pool.backup(dev_b, host_idx, 0, L, s)) if d == kvt.BACKUP
+                          else (lambda: pool.load(dev_l, host_idx, 0, L, s)))
+                    t0 = time.perf_counter()
+                    fn()
+                    s.synchronize()
+                    first = time.perf_counter() - t0
+                    if first > 3.0:
+                        cell[pname] = {"gbps": round(bytes_dir / first / 1e9, 3), "reps": 1}
+                        continue
+                    ts = []
+                    for _ in range(args.matrix_reps):
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(s)
+                        fn()
+                        e1.record(s)
+                        e1.synchronize()
+                        ts.append(e0.elapsed_time(e1) / 1e3)
+                    g = bytes_dir / statistics.median(ts) / 1e9
+                    cell[pname] = {"gbps": round(g, 3),
+                                   "pct_of_measured_peak": round(100 * g / link_peak[dname], 1)}
+                log("matrix %s" % json.dumps(cell))
+                rows.append(cell)
+    return rows
+
+
+def cpu_baseline(shape):
+    """The oracle (single thread, as it stands) on host mirrors: backup + load of a
+    4096-token prefix of the same 78-layer geometry, repeated for ~10 s."""
+    import oracle
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    n = 4096
+    g = oracle.Geometry(L, C, R, 2 * n, n, ps, 0)
+    rng = np.random.default_rng(3)
+    dev = [rng.integers(0, 256, size=g.S_dev * R, dtype=np.uint8) for _ in range(L * C)]
+    host = np.zeros(g.host_bytes(), np.uint8)
+    d1 = np.arange(n, dtype=np.int64)
+    d2 = np.arange(n, 2 * n, dtype=np.int64)
+    h = np.arange(n, dtype=np.int64)
+    bytes_step = 2 * n * L * C * R
+    reps = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 10.0 or reps < 2:
+        assert oracle.backup(g, dev, host, d1, h) == 0
+        assert oracle.load(g, dev, host, d2, h) == 0
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_step * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "%d x (backup + load) of a 4096-token prefix, 78 layers x 1152 B rows, "
+                      "layer_first, host mirrors, one thread (%.1f s)" % (reps, dt)}
+
+
+if __name__ == "__main__":
+    main()

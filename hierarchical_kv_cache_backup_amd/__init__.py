@@ -1,0 +1,312 @@
+"""Cross-tier KV transfer between a device KV pool and a pinned host KV pool.
+
+Thin ctypes binding of libkvtier.so (C ABI declared in include/kvtier.h): the
+functions below carry the C names and only marshal arguments; every step of a
+transfer runs inside the library (host-side planning in C++, data movement in
+gfx950 kernels or on the copy engines). PyTorch supplies device memory and
+streams only.
+
+The library must be built (``__graft_entry__.build()`` or
+``python hierarchical_kv_cache_backup_amd/_build.py``); importing the binding
+without it raises, there is no fallback.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvtier.so")
+
+OK, EINVAL, ERANGE, EDUP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
+ERROR_NAMES = {EINVAL: "KV_EINVAL", ERANGE: "KV_ERANGE", EDUP: "KV_EDUP",
+               ENOMEM: "KV_ENOMEM", EHIP: "KV_EHIP"}
+LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT = 0, 1, 2
+PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA = 0, 1, 2, 3
+PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel_lds",
+              PATH_DMA: "dma", -1: "none"}
+F_CHECK_UNIQUE, F_HOST_NONCOHERENT = 0x1, 0x2
+BACKUP, LOAD = 0, 1
+
+
+class kv_geometry_t(ctypes.Structure):
+    _fields_ = [("num_layers", ctypes.c_int32), ("num_components", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int64), ("device_slots", ctypes.c_int64),
+                ("host_slots", ctypes.c_int64), ("page_size", ctypes.c_int32),
+                ("host_layout", ctypes.c_int32)]
+
+
+class kv_pool_desc_t(ctypes.Structure):
+    _fields_ = [("geom", kv_geometry_t), ("device_buffers", ctypes.POINTER(ctypes.c_void_p)),
+                ("device", ctypes.c_int32), ("numa_node", ctypes.c_int32),
+                ("flags", ctypes.c_uint32)]
+
+
+class kv_calib_t(ctypes.Structure):
+    _fields_ = [("kernel_launch_us", ctypes.c_double * 2), ("kernel_gbps", ctypes.c_double * 2),
+                ("dma_copy_us", ctypes.c_double * 2), ("dma_gbps", ctypes.c_double * 2),
+                ("load_split_min_bytes", ctypes.c_double)]
+
+
+class kv_stats_t(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2),
+                ("kernel_launches", ctypes.c_int64 * 2), ("dma_copies", ctypes.c_int64 * 2),
+                ("submit_us", ctypes.c_double * 2)]
+
+
+# Every symbol include/kvtier.h declares, with its ctypes signature.
+_P64 = ctypes.POINTER(ctypes.c_int64)
+_VP = ctypes.c_void_p
+_I32, _I64 = ctypes.c_int32, ctypes.c_int64
+_GEOM = ctypes.POINTER(kv_geometry_t)
+SIGNATURES = {
+    "kv_geometry_check": (_I32, [_GEOM]),
+    "kv_host_row": (_I64, [_GEOM, _I32, _I32, _I64]),
+    "kv_validate": (_I32, [_GEOM, _I32, _P64, _P64, _I64, _I32, _I32, _I32]),
+    "kv_count_segments": (_I32, [_GEOM, _P64, _P64, _I64, _I32, _I32, _P64]),
+    "kv_count_dma_copies": (_I32, [_GEOM, _P64, _P64, _I64, _I32, _I32, _P64]),
+    "kv_pool_create": (_I32, [ctypes.POINTER(kv_pool_desc_t), ctypes.POINTER(_VP)]),
+    "kv_pool_destroy": (_I32, [_VP]),
+    "kv_pool_host_ptr": (_VP, [_VP]),
+    "kv_pool_host_bytes": (_I64, [_VP]),
+    "kv_backup": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
+    "kv_load": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
+    "kv_load_layer": (_I32, [_VP, _I32, _VP]),
+    "kv_set_path": (_I32, [_VP, _I32]),
+    "kv_last_path": (_I32, [_VP, _I32]),
+    "kv_set_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
+    "kv_get_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
+    "kv_get_stats": (_I32, [_VP, ctypes.POINTER(kv_stats_t)]),
+    "kv_last_error": (ctypes.c_char_p, []),
+}
+
+
+def _load():
+    # One HIP runtime per process: torch ships its own libamdhip64 (same SONAME,
+    # different file name). Loading torch first makes libkvtier.so bind to that
+    # already-loaded runtime, so both share one device context; loading the
+    # system copy first would leave two runtimes fighting over the GPU.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libkvtier.so is not built (%s). Build it with __graft_entry__.build() or "
+            "`python hierarchical_kv_cache_backup_amd/_build.py`; there is no fallback path."
+            % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library():
+    return _lib
+
+
+class KvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (ERROR_NAMES.get(code, "?"), code, msg))
+        self.code = code
+
+
+def _check(rc):
+    if rc < 0:
+        raise KvError(rc, kv_last_error())
+    return rc
+
+
+def _idx(a):
+    """int64 contiguous numpy copy of an index sequence and its pointer (kept alive by caller)."""
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    return a, a.ctypes.data_as(_P64)
+
+
+def _stream_handle(stream):
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream
+
+
+def geometry(L, C, R, S_dev, S_host, ps, layout):
+    return kv_geometry_t(L, C, R, S_dev, S_host, ps, layout)
+
+
+# ---- same-name wrappers: return the C status, no exceptions ----------------
+
+def kv_last_error():
+    return (_lib.kv_last_error() or b"").decode()
+
+
+def kv_geometry_check(geom):
+    return _lib.kv_geometry_check(ctypes.byref(geom))
+
+
+def kv_host_row(geom, layer, comp, host_slot):
+    return _lib.kv_host_row(ctypes.byref(geom), layer, comp, host_slot)
+
+
+def kv_validate(geom, direction, dev_idx, host_idx, layer_begin, layer_end, check_unique=True,
+                n=None):
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    n = len(d) if n is None else n
+    return _lib.kv_validate(ctypes.byref(geom), direction, dp, hp, n, layer_begin, layer_end,
+                            int(check_unique))
+
+
+def kv_count_segments(geom, dev_idx, host_idx, layer_begin, layer_end):
+    """Returns (status, count)."""
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    out = ctypes.c_int64(-1)
+    rc = _lib.kv_count_segments(ctypes.byref(geom), dp, hp, len(d), layer_begin, layer_end,
+                                ctypes.byref(out))
+    return rc, out.value
+
+
+def kv_count_dma_copies(geom, dev_idx, host_idx, layer_begin, layer_end):
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    out = ctypes.c_int64(-1)
+    rc = _lib.kv_count_dma_copies(ctypes.byref(geom), dp, hp, len(d), layer_begin, layer_end,
+                                  ctypes.byref(out))
+    return rc, out.value
+
+
+def kv_pool_create(geom, device_buffer_ptrs, device=0, numa_node=-1, flags=F_CHECK_UNIQUE):
+    """Returns (status, handle)."""
+    arr = (ctypes.c_void_p * len(device_buffer_ptrs))(*device_buffer_ptrs)
+    desc = kv_pool_desc_t(geom, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), device,
+                          numa_node, flags)
+    h = ctypes.c_void_p()
+    rc = _lib.kv_pool_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h.value
+
+
+def kv_pool_destroy(pool):
+    return _lib.kv_pool_destroy(pool)
+
+
+def kv_pool_host_ptr(pool):
+    return _lib.kv_pool_host_ptr(pool)
+
+
+def kv_pool_host_bytes(pool):
+    return _lib.kv_pool_host_bytes(pool)
+
+
+def kv_backup(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    n = len(d) if n is None else n
+    return _lib.kv_backup(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
+
+
+def kv_load(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    n = len(d) if n is None else n
+    return _lib.kv_load(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
+
+
+def kv_load_layer(pool, layer, compute_stream=None):
+    return _lib.kv_load_layer(pool, layer, _stream_handle(compute_stream))
+
+
+def kv_set_path(pool, path):
+    return _lib.kv_set_path(pool, path)
+
+
+def kv_last_path(pool, direction):
+    return _lib.kv_last_path(pool, direction)
+
+
+def kv_set_calibration(pool, calib):
+    return _lib.kv_set_calibration(pool, ctypes.byref(calib))
+
+
+def kv_get_calibration(pool):
+    c = kv_calib_t()
+    rc = _lib.kv_get_calibration(pool, ctypes.byref(c))
+    return rc, c
+
+
+def kv_get_stats(pool):
+    s = kv_stats_t()
+    rc = _lib.kv_get_stats(pool, ctypes.byref(s))
+    return rc, s
+
+
+# ---- convenience object over torch device buffers ------------------------------
+
+class KvPool:
+    """Owns a library pool over L*C torch uint8 device tensors (borrowed: kept
+    referenced here so they outlive the pool). Methods raise KvError on failure."""
+
+    def __init__(self, geom, device_tensors, device=0, numa_node=-1, flags=F_CHECK_UNIQUE):
+        self.geom = geom
+        self.tensors = list(device_tensors)
+        assert len(self.tensors) == geom.num_layers * geom.num_components
+        ptrs = [t.data_ptr() for t in self.tensors]
+        rc, h = kv_pool_create(geom, ptrs, device, numa_node, flags)
+        _check(rc)
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            _check(kv_pool_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def host_array(self):
+        """numpy uint8 view of the host pool (CPU address; valid until close)."""
+        n = kv_pool_host_bytes(self.handle)
+        buf = (ctypes.c_uint8 * n).from_address(kv_pool_host_ptr(self.handle))
+        return np.frombuffer(buf, dtype=np.uint8)
+
+    def backup(self, dev_idx, host_idx, layer_begin=0, layer_end=None, stream=None):
+        le = self.geom.num_layers if layer_end is None else layer_end
+        _check(kv_backup(self.handle, dev_idx, host_idx, layer_begin, le, stream))
+
+    def load(self, dev_idx, host_idx, layer_begin=0, layer_end=None, stream=None):
+        le = self.geom.num_layers if layer_end is None else layer_end
+        _check(kv_load(self.handle, dev_idx, host_idx, layer_begin, le, stream))
+
+    def load_layer(self, layer, compute_stream=None):
+        _check(kv_load_layer(self.handle, layer, compute_stream))
+
+    def set_path(self, path):
+        _check(kv_set_path(self.handle, path))
+
+    def last_path(self, direction):
+        return kv_last_path(self.handle, direction)
+
+    def calibration(self):
+        rc, c = kv_get_calibration(self.handle)
+        _check(rc)
+        return c
+
+    def set_calibration(self, c):
+        _check(kv_set_calibration(self.handle, c))
+
+    def stats(self):
+        rc, s = kv_get_stats(self.handle)
+        _check(rc)
+        return s

@@ -1,0 +1,140 @@
+// kernels.hip — gfx950 kernels of the cross-tier KV transfer.
+//
+// Zero-copy gather/scatter between the device KV buffers (HBM) and the pinned,
+// device-mapped host pool: the GPU itself loads and stores host memory over
+// the host link (the "GPU-assisted I/O kernels" / "UVA copy" of the HiCache
+// system design page, section "data transfer optimisation", and of the Baidu
+// KV cache page, "optimisation techniques"), instead of one copy-engine
+// descriptor per contiguous segment.
+//
+// The work is pure data movement: no arithmetic on values, no MFMA. Each lane
+// moves 16-byte chunks, so one wave instruction covers 1 KiB of consecutive
+// chunks; rows are >= 16 B and 16-B aligned on both sides, and every row is
+// contiguous on both sides, so the layout transpose is row-granular and the
+// accesses stay fully coalesced on both sides. Loads and stores are
+// non-temporal: nothing is re-read, so nothing should stay in the caches.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace kvt {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+__device__ __forceinline__ uint8_t *dev_row(const XferArgs &a, uint32_t i, uint32_t lc) {
+  return a.dev_tab[a.lc0 + lc] + a.tok[2 * i] * a.R;
+}
+
+__device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint32_t lc) {
+  return a.host + ((int64_t)(a.lc0 + lc) * a.lc_stride + a.tok[2 * i + 1]) * a.R;
+}
+
+}  // namespace
+
+// Direct path: workgroup b moves rows [b*rows_per_block, ...) of the
+// host-order walk; lanes take consecutive 16-byte chunks of those rows.
+template <bool kToHost>
+__global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
+  const uint32_t row0 = blockIdx.x * a.rows_per_block;
+  const uint32_t nrows = min(a.rows_per_block, a.total_rows - row0);
+  const uint32_t nchunks = nrows * a.cpr;
+  for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
+    u32x4 v[kXferUnroll];
+    u32x4 *dst[kXferUnroll];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) {
+      const uint32_t f = base + u * kXferThreads + threadIdx.x;
+      dst[u] = nullptr;
+      if (f < nchunks) {
+        const uint32_t rr = f / a.cpr;
+        const uint32_t k = f - rr * a.cpr;
+        uint32_t i, lc;
+        walk_row(a, row0 + rr, i, lc);
+        u32x4 *d = reinterpret_cast<u32x4 *>(dev_row(a, i, lc)) + k;
+        u32x4 *h = reinterpret_cast<u32x4 *>(host_row(a, i, lc)) + k;
+        const u32x4 *src = kToHost ? d : h;
+        dst[u] = kToHost ? h : d;
+        v[u] = __builtin_nontemporal_load(src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++)
+      if (dst[u]) __builtin_nontemporal_store(v[u], dst[u]);
+  }
+}
+
+// LDS-staged path: a workgroup owns a tile of nt positions x nl pairs. It reads
+// the tile in source-address order into LDS (slot (pair, position)), then
+// writes it out in destination-address order. Device order is pair-major;
+// host order is position-major for page_first and pair-major otherwise.
+template <bool kToHost>
+__global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileArgs ta) {
+  extern __shared__ u32x4 lds[];
+  const Tile t = tile_of(a, ta, blockIdx.x);
+  const uint32_t cpr = a.cpr;
+  const uint32_t nchunks = t.nt * t.nl * cpr;
+  const bool host_pos_major = ta.token_major != 0;
+
+  // phase 1: source -> LDS, in source order
+  const bool src_pos_major = kToHost ? false : host_pos_major;
+  for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
+    u32x4 v[kXferUnroll];
+    uint32_t slot[kXferUnroll];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) {
+      const uint32_t f = base + u * kXferThreads + threadIdx.x;
+      slot[u] = 0xffffffffu;
+      if (f < nchunks) {
+        uint32_t lc_t, p_t, k;
+        tile_walk(t, cpr, src_pos_major, f, lc_t, p_t, k);
+        const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(kToHost ? dev_row(a, i, lc)
+                                                                    : host_row(a, i, lc)) + k;
+        v[u] = __builtin_nontemporal_load(src);
+        slot[u] = tile_slot(t, cpr, lc_t, p_t, k);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++)
+      if (slot[u] != 0xffffffffu) lds[slot[u]] = v[u];
+  }
+  __syncthreads();
+
+  // phase 2: LDS -> destination, in destination order
+  const bool dst_pos_major = kToHost ? host_pos_major : false;
+  for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) {
+      const uint32_t f = base + u * kXferThreads + threadIdx.x;
+      if (f < nchunks) {
+        uint32_t lc_t, p_t, k;
+        tile_walk(t, cpr, dst_pos_major, f, lc_t, p_t, k);
+        const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
+        u32x4 *dst = reinterpret_cast<u32x4 *>(kToHost ? host_row(a, i, lc) : dev_row(a, i, lc)) + k;
+        __builtin_nontemporal_store(lds[tile_slot(t, cpr, lc_t, p_t, k)], dst);
+      }
+    }
+  }
+}
+
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
+  if (to_host)
+    hipLaunchKernelGGL(xfer_rows<true>, dim3(blocks), dim3(kXferThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(xfer_rows<false>, dim3(blocks), dim3(kXferThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, bool to_host, hipStream_t s) {
+  const size_t lds = (size_t)t.tile_t * t.tile_lc * a.R;
+  const uint32_t blocks = t.tiles_t * t.tiles_lc;
+  if (to_host)
+    hipLaunchKernelGGL(xfer_tiles_lds<true>, dim3(blocks), dim3(kXferThreads), lds, s, a, t);
+  else
+    hipLaunchKernelGGL(xfer_tiles_lds<false>, dim3(blocks), dim3(kXferThreads), lds, s, a, t);
+  return hipGetLastError();
+}
+
+}  // namespace kvt

@@ -1,0 +1,13 @@
+// kernels.hpp — launch interface of the gfx950 transfer kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "xfer_walk.hpp"
+
+namespace kvt {
+
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s);
+hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, bool to_host, hipStream_t s);
+
+}  // namespace kvt

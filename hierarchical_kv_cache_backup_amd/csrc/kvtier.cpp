@@ -1,0 +1,578 @@
+// kvtier.cpp — C ABI of the cross-tier KV transfer: pool lifetime, request
+// intake, path selection, the kernel and copy-engine executors, per-layer load
+// events, statistics and error reporting.
+//
+// Submission model (Kunlunxin tuning page, section 2.2; Baidu KV cache page,
+// "bidirectional async transfer"): a call validates, plans and ENQUEUES on the
+// caller's stream, then returns; backup and load have separate state and locks
+// so one thread per direction can submit concurrently on private streams.
+#include <hip/hip_runtime.h>
+#include <sys/syscall.h>
+#include <unistd.h>
+
+#include <atomic>
+#include <chrono>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "kvtier.h"
+#include "plan.hpp"
+
+namespace kvt {
+
+thread_local std::string g_err;
+void set_error(const std::string &msg) { g_err = msg; }
+
+namespace {
+
+constexpr int kStagingSlots = 4;  // index-staging buffers in flight per direction
+constexpr int64_t kMaxRowsPerLaunch = (int64_t)1 << 31;
+
+int fail(int code, const std::string &msg) {
+  set_error(msg);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(KV_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+struct DeviceGuard {
+  int prev = -1;
+  bool changed = false;
+  hipError_t err = hipSuccess;
+  explicit DeviceGuard(int dev) {
+    err = hipGetDevice(&prev);
+    if (err == hipSuccess && prev != dev) {
+      err = hipSetDevice(dev);
+      changed = err == hipSuccess;
+    }
+  }
+  ~DeviceGuard() {
+    if (changed) (void)hipSetDevice(prev);
+  }
+};
+
+// Pinned host + device copy of the per-position {device slot, host key} pairs.
+struct Staging {
+  int64_t *pinned = nullptr;
+  int64_t *dev = nullptr;
+  int64_t cap = 0;  // positions
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+
+struct DirState {
+  std::mutex mu;
+  UniqueScratch uniq;
+  std::vector<Run> runs;
+  std::vector<Copy> copies;
+  Staging slots[kStagingSlots];
+  int next = 0;
+  hipEvent_t done = nullptr;  // recorded at the end of every call of this direction
+  bool done_pending = false;
+  std::atomic<int32_t> last_path{-1};
+  int64_t calls = 0, bytes = 0, launches = 0, dma = 0;
+  double submit_us = 0;
+};
+
+}  // namespace
+}  // namespace kvt
+
+using namespace kvt;
+
+struct kv_pool {
+  Geom g;
+  int device = 0;
+  uint32_t flags = 0;
+  int32_t numa = -1;
+  std::vector<uint8_t *> bufs;      // L*C device buffer bases
+  uint8_t **dev_tab = nullptr;      // device copy of bufs
+  uint8_t *host = nullptr;          // host pool, CPU address
+  uint8_t *host_dev = nullptr;      // host pool, device-visible address
+  int64_t host_bytes = 0;
+  std::vector<hipEvent_t> layer_ev; // per-layer "landed" events of kv_load
+  std::vector<std::atomic<uint8_t>> layer_ev_set;
+  DirState dir[2];
+  std::atomic<int32_t> path{KV_PATH_AUTO};
+  std::mutex calib_mu;
+  kv_calib_t calib{};
+  explicit kv_pool(int L) : layer_ev_set(L) {}
+};
+
+namespace kvt {
+namespace {
+
+void default_calibration(kv_calib_t *c) {
+  for (int d = 0; d < 2; d++) {
+    c->kernel_launch_us[d] = 8.0;
+    c->kernel_gbps[d] = 50.0;
+    c->dma_copy_us[d] = 4.0;
+    c->dma_gbps[d] = 55.0;
+  }
+  c->load_split_min_bytes = 4.0 * 1024 * 1024;
+}
+
+// Sets the calling thread's memory policy to bind to `node` (Linux mbind
+// semantics through set_mempolicy), returning the previous policy in
+// *old_mode / old_mask so it can be restored.
+constexpr int kMpolDefault = 0, kMpolBind = 2;
+bool bind_thread_to_node(int node, int *old_mode, unsigned long *old_mask) {
+  *old_mode = kMpolDefault;
+  *old_mask = 0;
+  if (syscall(SYS_get_mempolicy, old_mode, old_mask, 8 * sizeof(unsigned long), nullptr, 0) != 0)
+    return false;
+  unsigned long mask = 1ul << node;
+  return syscall(SYS_set_mempolicy, kMpolBind, &mask, 8 * sizeof(unsigned long)) == 0;
+}
+
+void restore_thread_policy(int mode, unsigned long mask) {
+  syscall(SYS_set_mempolicy, mode, mode == kMpolDefault ? nullptr : &mask,
+          8 * sizeof(unsigned long));
+}
+
+bool numa_node_exists(int node) {
+  char path[96];
+  std::snprintf(path, sizeof path, "/sys/devices/system/node/node%d", node);
+  return access(path, F_OK) == 0;
+}
+
+void free_staging(Staging &s) {
+  if (s.pinned) (void)hipHostFree(s.pinned);
+  if (s.dev) (void)hipFree(s.dev);
+  s.pinned = nullptr;
+  s.dev = nullptr;
+  s.cap = 0;
+}
+
+// Waits for every enqueued use of the direction's staging buffers.
+hipError_t drain_direction(DirState &d) {
+  hipError_t first = hipSuccess;
+  for (Staging &s : d.slots) {
+    if (s.pending) {
+      hipError_t e = hipEventSynchronize(s.ev);
+      if (e != hipSuccess && first == hipSuccess) first = e;
+      s.pending = false;
+    }
+  }
+  if (d.done_pending) {
+    hipError_t e = hipEventSynchronize(d.done);
+    if (e != hipSuccess && first == hipSuccess) first = e;
+    d.done_pending = false;
+  }
+  return first;
+}
+
+// Next staging slot with room for n positions. Blocks only when all slots
+// still carry work in flight (back-pressure after kStagingSlots calls).
+int acquire_staging(DirState &d, int64_t n, Staging **out) {
+  Staging &s = d.slots[d.next];
+  d.next = (d.next + 1) % kStagingSlots;
+  if (s.pending) {
+    hipError_t e = hipEventSynchronize(s.ev);
+    s.pending = false;
+    if (e != hipSuccess) return hip_fail(e, "waiting for an index staging buffer");
+  }
+  if (s.cap < n) {
+    free_staging(s);
+    int64_t cap = 1024;
+    while (cap < n) cap *= 2;
+    hipError_t e = hipHostMalloc((void **)&s.pinned, (size_t)cap * 16, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      s.pinned = nullptr;
+      return fail(KV_ENOMEM, "hipHostMalloc of index staging failed");
+    }
+    e = hipMalloc((void **)&s.dev, (size_t)cap * 16);
+    if (e != hipSuccess) {
+      s.dev = nullptr;
+      free_staging(s);
+      return fail(KV_ENOMEM, "hipMalloc of index staging failed");
+    }
+    s.cap = cap;
+  }
+  *out = &s;
+  return KV_OK;
+}
+
+double now_us() {
+  return std::chrono::duration<double, std::micro>(
+             std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
+// ---- copy-engine executor ------------------------------------------------
+
+hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_t s) {
+  const Geom &g = p->g;
+  uint8_t *dev = p->bufs[lc] + c.dev0 * g.R;
+  uint8_t *host = p->host + ((int64_t)lc * g.lc_stride + c.key0) * g.R;
+  const size_t width = (size_t)(c.len * g.R);
+  if (c.lines == 1) {
+    return dir == 0 ? hipMemcpyAsync(host, dev, width, hipMemcpyDeviceToHost, s)
+                    : hipMemcpyAsync(dev, host, width, hipMemcpyHostToDevice, s);
+  }
+  const size_t dpitch = (size_t)(c.dev_pitch * g.R), hpitch = (size_t)(c.key_pitch * g.R);
+  hipError_t e = dir == 0 ? hipMemcpy2DAsync(host, hpitch, dev, dpitch, width, (size_t)c.lines,
+                                             hipMemcpyDeviceToHost, s)
+                          : hipMemcpy2DAsync(dev, dpitch, host, hpitch, width, (size_t)c.lines,
+                                             hipMemcpyHostToDevice, s);
+  if (e == hipErrorInvalidValue || e == hipErrorInvalidPitchValue) {
+    // Shape the 2-D copy engine path refuses: fall back to one copy per line.
+    (void)hipGetLastError();
+    for (int64_t j = 0; j < c.lines; j++) {
+      Copy line{c.dev0 + j * c.dev_pitch, c.key0 + j * c.key_pitch, c.len, 1, 0, 0};
+      e = issue_copy(p, dir, lc, line, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  return e;
+}
+
+}  // namespace
+}  // namespace kvt
+
+// ---- transfers ----------------------------------------------------------------
+
+static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
+                    int64_t n, int32_t l0, int32_t l1, void *stream) {
+  const double t0 = now_us();
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  DirState &d = p->dir[dir];
+  std::lock_guard<std::mutex> lock(d.mu);
+  const Geom &g = p->g;
+  std::string why;
+  int rc = validate(g, dir, dev_idx, host_idx, n, l0, l1, (p->flags & KV_F_CHECK_UNIQUE) != 0,
+                    &d.uniq, &why);
+  if (rc) return fail(rc, why);
+  if (n == 0 || l0 == l1) return KV_OK;
+  const int64_t nlc_all = (int64_t)(l1 - l0) * g.C;
+  if (n * nlc_all >= kMaxRowsPerLaunch)
+    return fail(KV_EINVAL, "request has >= 2^31 rows; split it into several calls");
+
+  DeviceGuard dg(p->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t bytes = n * nlc_all * g.R;
+  const int64_t layer_bytes = n * g.C * g.R;
+  kv_calib_t c;
+  {
+    std::lock_guard<std::mutex> cl(p->calib_mu);
+    c = p->calib;
+  }
+  const bool per_layer = dir == 1 && (double)layer_bytes >= c.load_split_min_bytes && l1 - l0 > 1;
+
+  // ---- path selection
+  int32_t path = p->path.load();
+  bool planned = false;
+  if (path == KV_PATH_AUTO) {
+    build_runs(g, dev_idx, host_idx, n, &d.runs);
+    build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
+    planned = true;
+    const double launches = per_layer ? (double)(l1 - l0) : 1.0;
+    const double t_kernel = launches * c.kernel_launch_us[dir] + bytes / (c.kernel_gbps[dir] * 1e3);
+    const double copies = (double)d.copies.size() * (double)nlc_all;
+    const double t_dma = copies * c.dma_copy_us[dir] + bytes / (c.dma_gbps[dir] * 1e3);
+    path = t_dma < t_kernel ? KV_PATH_DMA : KV_PATH_KERNEL;
+  }
+  if (path == KV_PATH_KERNEL_LDS && g.R > kMaxLdsRowBytes) path = KV_PATH_KERNEL;
+
+  hipError_t e = hipSuccess;
+  if (path == KV_PATH_DMA) {
+    if (!planned) {
+      build_runs(g, dev_idx, host_idx, n, &d.runs);
+      build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
+    }
+    for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
+      for (int32_t c = 0; c < g.C && e == hipSuccess; c++)
+        for (const Copy &cp : d.copies) {
+          e = issue_copy(p, dir, l * g.C + c, cp, s);
+          if (e != hipSuccess) break;
+        }
+      if (e == hipSuccess && dir == 1) {
+        e = hipEventRecord(p->layer_ev[l], s);
+        p->layer_ev_set[l].store(1);
+      }
+    }
+    if (e != hipSuccess) return hip_fail(e, "enqueueing copy-engine transfers");
+    d.dma += (int64_t)d.copies.size() * nlc_all;
+  } else {
+    Staging *st = nullptr;
+    rc = acquire_staging(d, n, &st);
+    if (rc) return rc;
+    int64_t *tok = st->pinned;
+    for (int64_t i = 0; i < n; i++) {
+      tok[2 * i] = dev_idx[i];
+      tok[2 * i + 1] = host_key(g, host_idx[i]);
+    }
+    e = hipMemcpyAsync(st->dev, st->pinned, (size_t)n * 16, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "staging indices");
+
+    XferArgs a{};
+    a.tok = st->dev;
+    a.dev_tab = p->dev_tab;
+    a.host = p->host_dev;
+    a.R = g.R;
+    a.lc_stride = g.lc_stride;
+    a.n = (uint32_t)n;
+    auto launch = [&](int32_t la, int32_t lb) -> hipError_t {
+      XferArgs b = a;
+      b.lc0 = (uint32_t)(la * g.C);
+      b.nlc = (uint32_t)((lb - la) * g.C);
+      if (path == KV_PATH_KERNEL_LDS) {
+        plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
+        TileArgs t{};
+        plan_tiles(b, g.layout, &t);
+        d.launches++;
+        return launch_tiles_lds(b, t, dir == 0, s);
+      }
+      const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
+      d.launches++;
+      return launch_rows(b, blocks, dir == 0, s);
+    };
+    if (per_layer) {
+      for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
+        e = launch(l, l + 1);
+        if (e == hipSuccess) {
+          e = hipEventRecord(p->layer_ev[l], s);
+          p->layer_ev_set[l].store(1);
+        }
+      }
+    } else {
+      e = launch(l0, l1);
+      if (e == hipSuccess && dir == 1)
+        for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
+          e = hipEventRecord(p->layer_ev[l], s);
+          p->layer_ev_set[l].store(1);
+        }
+    }
+    if (e != hipSuccess) return hip_fail(e, "launching the transfer kernel");
+    e = hipEventRecord(st->ev, s);
+    if (e != hipSuccess) return hip_fail(e, "recording the staging event");
+    st->pending = true;
+  }
+  e = hipEventRecord(d.done, s);
+  if (e != hipSuccess) return hip_fail(e, "recording the completion event");
+  d.done_pending = true;
+  d.last_path.store(path);
+  d.calls++;
+  d.bytes += bytes;
+  d.submit_us += now_us() - t0;
+  return KV_OK;
+}
+
+// ---- C ABI ---------------------------------------------------------------------
+
+extern "C" {
+
+const char *kv_last_error(void) { return g_err.c_str(); }
+
+int kv_pool_destroy(kv_pool_t *p) {
+  if (!p) return KV_OK;
+  int rc = KV_OK;
+  {
+    DeviceGuard dg(p->device);
+    for (DirState &d : p->dir) {
+      std::lock_guard<std::mutex> lock(d.mu);
+      hipError_t e = drain_direction(d);
+      if (e != hipSuccess && rc == KV_OK) rc = hip_fail(e, "pending transfer failed");
+      for (Staging &s : d.slots) {
+        free_staging(s);
+        if (s.ev) (void)hipEventDestroy(s.ev);
+      }
+      if (d.done) (void)hipEventDestroy(d.done);
+    }
+    for (hipEvent_t ev : p->layer_ev)
+      if (ev) (void)hipEventDestroy(ev);
+    if (p->dev_tab) (void)hipFree(p->dev_tab);
+    if (p->host) (void)hipHostFree(p->host);
+  }
+  delete p;
+  return rc;
+}
+
+int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
+  if (!desc || !out) return fail(KV_EINVAL, "desc and out must be non-null");
+  *out = nullptr;
+  Geom g;
+  std::string why;
+  int rc = make_geom(&desc->geom, &g, &why);
+  if (rc) return fail(rc, why);
+  if (!desc->device_buffers) return fail(KV_EINVAL, "device_buffers is null");
+  if (desc->numa_node >= 0 && !numa_node_exists(desc->numa_node))
+    return fail(KV_EINVAL, "numa_node " + std::to_string(desc->numa_node) + " does not exist");
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (desc->device < 0 || desc->device >= ndev)
+    return fail(KV_EINVAL, "device " + std::to_string(desc->device) + " does not exist");
+  DeviceGuard dg(desc->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+
+  const int64_t nbuf = (int64_t)g.L * g.C;
+  const int64_t buf_bytes = g.S_dev * g.R;
+  kv_pool *p = new kv_pool(g.L);
+  p->g = g;
+  p->device = desc->device;
+  p->flags = desc->flags;
+  p->numa = desc->numa_node;
+  default_calibration(&p->calib);
+  p->bufs.resize(nbuf);
+  for (int64_t k = 0; k < nbuf; k++) {
+    uint8_t *b = static_cast<uint8_t *>(desc->device_buffers[k]);
+    if (!b || ((uintptr_t)b & 15u)) {
+      delete p;
+      return fail(KV_EINVAL, "device buffer " + std::to_string(k) + " is null or not 16-byte aligned");
+    }
+    // The buffer must be device memory of this device holding S_dev*R bytes.
+    hipPointerAttribute_t attr;
+    e = hipPointerGetAttributes(&attr, b);
+    if (e != hipSuccess || attr.type != hipMemoryTypeDevice || attr.device != desc->device) {
+      (void)hipGetLastError();
+      delete p;
+      return fail(KV_EINVAL, "device buffer " + std::to_string(k) +
+                                 " is not device memory of device " + std::to_string(desc->device));
+    }
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    e = hipMemGetAddressRange(&base, &size, b);
+    if (e != hipSuccess || (uint8_t *)b + buf_bytes > (uint8_t *)base + size) {
+      (void)hipGetLastError();
+      delete p;
+      return fail(KV_EINVAL, "device buffer " + std::to_string(k) + " is smaller than S_dev*R bytes");
+    }
+    p->bufs[k] = b;
+  }
+
+  // host pool: pinned and mapped for the device, optionally bound to a node
+  p->host_bytes = nbuf * g.S_host * g.R;
+  unsigned int hflags = hipHostMallocMapped | hipHostMallocPortable |
+                        ((desc->flags & KV_F_HOST_NONCOHERENT) ? hipHostMallocNonCoherent
+                                                               : hipHostMallocCoherent);
+  int old_mode = 0;
+  unsigned long old_mask = 0;
+  bool bound = false;
+  if (desc->numa_node >= 0) {
+    bound = bind_thread_to_node(desc->numa_node, &old_mode, &old_mask);
+    if (!bound) {
+      delete p;
+      return fail(KV_EINVAL, "set_mempolicy to node " + std::to_string(desc->numa_node) + " failed");
+    }
+    hflags |= hipHostMallocNumaUser;
+  }
+  e = hipHostMalloc((void **)&p->host, (size_t)p->host_bytes, hflags);
+  if (bound) restore_thread_policy(old_mode, old_mask);
+  if (e != hipSuccess) {
+    p->host = nullptr;
+    (void)hipGetLastError();
+    kv_pool_destroy(p);
+    return fail(KV_ENOMEM, "hipHostMalloc of " + std::to_string(p->host_bytes) +
+                               " bytes failed: " + hipGetErrorString(e));
+  }
+  void *hd = nullptr;
+  e = hipHostGetDevicePointer(&hd, p->host, 0);
+  if (e != hipSuccess) {
+    kv_pool_destroy(p);
+    return hip_fail(e, "hipHostGetDevicePointer");
+  }
+  p->host_dev = (uint8_t *)hd;
+
+  e = hipMalloc((void **)&p->dev_tab, (size_t)nbuf * sizeof(uint8_t *));
+  if (e == hipSuccess)
+    e = hipMemcpy(p->dev_tab, p->bufs.data(), (size_t)nbuf * sizeof(uint8_t *),
+                  hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    kv_pool_destroy(p);
+    return hip_fail(e, "device buffer table");
+  }
+  p->layer_ev.assign(g.L, nullptr);
+  for (int l = 0; l < g.L && e == hipSuccess; l++)
+    e = hipEventCreateWithFlags(&p->layer_ev[l], hipEventDisableTiming);
+  for (DirState &d : p->dir) {
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
+    for (Staging &s : d.slots)
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    kv_pool_destroy(p);
+    return hip_fail(e, "creating events");
+  }
+  *out = p;
+  return KV_OK;
+}
+
+void *kv_pool_host_ptr(const kv_pool_t *p) { return p ? p->host : nullptr; }
+int64_t kv_pool_host_bytes(const kv_pool_t *p) { return p ? p->host_bytes : 0; }
+
+int kv_backup(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+              int32_t layer_begin, int32_t layer_end, void *stream) {
+  return transfer(p, 0, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+}
+
+int kv_load(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+            int32_t layer_begin, int32_t layer_end, void *stream) {
+  return transfer(p, 1, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+}
+
+int kv_load_layer(kv_pool_t *p, int32_t layer, void *compute_stream) {
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (layer < 0 || layer >= p->g.L)
+    return fail(KV_EINVAL, "layer " + std::to_string(layer) + " is outside [0, L)");
+  if (!p->layer_ev_set[layer].load()) return KV_OK;
+  DeviceGuard dg(p->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, p->layer_ev[layer], 0);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  return KV_OK;
+}
+
+int kv_set_path(kv_pool_t *p, int32_t path) {
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (path < KV_PATH_AUTO || path > KV_PATH_DMA) return fail(KV_EINVAL, "unknown path");
+  p->path.store(path);
+  return KV_OK;
+}
+
+int32_t kv_last_path(const kv_pool_t *p, int32_t direction) {
+  if (!p || (direction != 0 && direction != 1)) return -1;
+  return p->dir[direction].last_path.load();
+}
+
+int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
+  if (!p || !c) return fail(KV_EINVAL, "pool and calibration must be non-null");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_gbps[d] > 0) || !(c->dma_gbps[d] > 0) || !(c->kernel_launch_us[d] >= 0) ||
+        !(c->dma_copy_us[d] >= 0))
+      return fail(KV_EINVAL, "calibration figures must be positive");
+  if (!(c->load_split_min_bytes >= 0)) return fail(KV_EINVAL, "load_split_min_bytes must be >= 0");
+  std::lock_guard<std::mutex> lock(p->calib_mu);
+  p->calib = *c;
+  return KV_OK;
+}
+
+int kv_get_calibration(const kv_pool_t *p, kv_calib_t *c) {
+  if (!p || !c) return fail(KV_EINVAL, "pool and calibration must be non-null");
+  std::lock_guard<std::mutex> lock(const_cast<kv_pool *>(p)->calib_mu);
+  *c = p->calib;
+  return KV_OK;
+}
+
+int kv_get_stats(const kv_pool_t *p, kv_stats_t *out) {
+  if (!p || !out) return fail(KV_EINVAL, "pool and out must be non-null");
+  for (int d = 0; d < 2; d++) {
+    DirState &s = const_cast<kv_pool *>(p)->dir[d];
+    std::lock_guard<std::mutex> lock(s.mu);
+    out->calls[d] = s.calls;
+    out->bytes[d] = s.bytes;
+    out->kernel_launches[d] = s.launches;
+    out->dma_copies[d] = s.dma;
+    out->submit_us[d] = s.submit_us;
+  }
+  return KV_OK;
+}
+
+}  // extern "C"

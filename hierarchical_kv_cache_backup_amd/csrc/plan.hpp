@@ -1,0 +1,88 @@
+// plan.hpp — host-side planner of the cross-tier KV transfer (no HIP).
+//
+// Every host layout's address map splits into a per-(layer, component) part
+// and a per-token part:
+//   host_row(l, c, h) = (l*C + c) * lc_stride + host_key(h)
+//   layer_first        lc_stride = S_host   host_key(h) = h
+//   page_first         lc_stride = 1        host_key(h) = h * L*C
+//   page_first_direct  lc_stride = ps       host_key(h) = (h / ps) * L*C*ps + h % ps
+// (dimension orders from "Tuning SGLang HiCache L2 on Kunlunxin P800/P900",
+// section 2.1, and "HiCache system design", section "data transfer
+// optimisation"; the component axis sits directly inside the layer axis).
+// Because of this split, whether two consecutive request positions are
+// contiguous on the host does not depend on (l, c), so the run structure of a
+// request is computed once per call, in O(n), and reused for every (l, c).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kvtier.h"
+
+namespace kvt {
+
+struct Geom {
+  int32_t L = 0, C = 0;
+  int64_t R = 0, S_dev = 0, S_host = 0;
+  int32_t ps = 1, layout = KV_LAYER_FIRST;
+  int64_t lc_stride = 0;  // host rows between (l,c) and the next (l,c)
+};
+
+// Checks the geometry and fills g (lc_stride included). On failure returns
+// KV_EINVAL and writes a reason to *why.
+int make_geom(const kv_geometry_t *in, Geom *g, std::string *why);
+
+inline int64_t host_key(const Geom &g, int64_t h) {
+  switch (g.layout) {
+    case KV_LAYER_FIRST:
+      return h;
+    case KV_PAGE_FIRST:
+      return h * (int64_t)g.L * g.C;
+    default: {
+      const int64_t q = h / g.ps;
+      return q * (int64_t)g.L * g.C * g.ps + (h - q * g.ps);
+    }
+  }
+}
+
+inline int64_t host_row(const Geom &g, int32_t l, int32_t c, int64_t h) {
+  return ((int64_t)l * g.C + c) * g.lc_stride + host_key(g, h);
+}
+
+// Reusable scratch for the O(n) destination-uniqueness check: one stamp per
+// slot and a generation counter, so no clearing between calls.
+struct UniqueScratch {
+  std::vector<uint32_t> stamp;
+  uint32_t gen = 0;
+};
+
+// Request validation (rules and their order are those documented for
+// kv_validate). `scratch` may be null when check_unique is false.
+int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t *host_idx,
+             int64_t n, int32_t l0, int32_t l1, bool check_unique, UniqueScratch *scratch,
+             std::string *why);
+
+// A maximal group of request positions [i0, i0+len) whose device slots and
+// host rows both advance by one row per position.
+struct Run {
+  int64_t i0, len;
+};
+
+// Runs of the request, in request order (identical for every (l, c)).
+void build_runs(const Geom &g, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+                std::vector<Run> *runs);
+
+// One copy-engine call, relative to (l, c): `lines` lines of `len` rows each;
+// line j starts at device slot dev0 + j*dev_pitch and host key key0 + j*key_pitch
+// (both in rows). lines == 1 means a plain 1-D copy.
+struct Copy {
+  int64_t dev0, key0, len, lines, dev_pitch, key_pitch;
+};
+
+// Merges consecutive runs of equal length at constant device and host pitch
+// (pitch >= len, so lines never overlap) into 2-D copies.
+void build_copies(const Geom &g, const std::vector<Run> &runs, const int64_t *dev_idx,
+                  const int64_t *host_idx, std::vector<Copy> *copies);
+
+}  // namespace kvt

@@ -1,0 +1,140 @@
+// xfer_walk.hpp — launch geometry and index walk of the transfer kernels.
+//
+// Plain C++ (no HIP types): the functions are constexpr, which clang's HIP
+// mode also compiles for the device, so the kernels and the host-side
+// checkers run the very same integer arithmetic.
+#pragma once
+
+#include <cstdint>
+
+namespace kvt {
+
+// One launch moves the rows (i, lc) for request positions i in [0, n) and
+// (layer, component) pairs lc0 + lc, lc in [0, nlc). Rows are enumerated in
+// host-address order: groups of G consecutive request positions, and inside a
+// group (lc, position) with the position fastest. G = n for layer_first,
+// 1 for page_first and page_size for page_first_direct, so consecutive rows of
+// the walk are consecutive host rows when the host slots are consecutive.
+struct XferArgs {
+  const int64_t *tok;       // device: 2 int64 per position, {device slot, host key}
+  uint8_t *const *dev_tab;  // device: L*C device buffer base pointers
+  uint8_t *host;            // device-visible base address of the host pool
+  int64_t R;                // row bytes (multiple of 16)
+  int64_t lc_stride;        // host rows between consecutive (layer, component) pairs
+  uint32_t n;               // request positions
+  uint32_t G;               // group size of the host-order walk
+  uint32_t nlc;             // (layer, component) pairs in this launch
+  uint32_t lc0;             // first pair = layer_begin * C
+  uint32_t cpr;             // 16-byte chunks per row
+  uint32_t rows_per_block;  // rows one workgroup moves
+  uint32_t rows_full;       // rows in complete groups (n / G * G * nlc)
+  uint32_t total_rows;      // n * nlc  (< 2^31)
+};
+
+// Tiling of the LDS-staged variant: a workgroup owns tile_t request positions x
+// tile_lc pairs (tile_t * tile_lc * R bytes of LDS).
+struct TileArgs {
+  uint32_t tile_t, tile_lc;
+  uint32_t tiles_t, tiles_lc;  // tile counts along positions and pairs
+  uint32_t token_major;        // host order is (position, pair): page_first
+};
+
+constexpr int kXferThreads = 256;
+constexpr int kXferUnroll = 8;                                    // chunks in flight per lane
+constexpr uint32_t kChunksPerBlock = kXferThreads * kXferUnroll;  // 32 KiB per workgroup
+constexpr uint32_t kLdsTileBytes = 32 * 1024;
+constexpr int64_t kMaxLdsRowBytes = 64 * 1024;
+constexpr int kLayoutLayerFirst = 0, kLayoutPageFirst = 1, kLayoutPageFirstDirect = 2;
+
+constexpr uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+constexpr uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// Fills the derived fields (G, cpr, rows_per_block, rows_full, total_rows)
+// from layout, n, nlc and R; returns the number of workgroups.
+constexpr uint32_t plan_rows(XferArgs *a, int32_t layout, int32_t page_size) {
+  a->G = layout == kLayoutLayerFirst ? a->n
+         : layout == kLayoutPageFirst ? 1u
+                                      : (uint32_t)page_size;
+  a->cpr = (uint32_t)(a->R / 16);
+  a->rows_per_block = a->cpr >= kChunksPerBlock ? 1u : kChunksPerBlock / a->cpr;
+  a->total_rows = a->n * a->nlc;
+  a->rows_full = (a->n / a->G) * a->G * a->nlc;
+  return (a->total_rows + a->rows_per_block - 1) / a->rows_per_block;
+}
+
+// Tile shape of the LDS variant (needs R <= kMaxLdsRowBytes); returns the
+// number of workgroups.
+constexpr uint32_t plan_tiles(const XferArgs &a, int32_t layout, TileArgs *t) {
+  const uint32_t rows_budget = a.R >= kLdsTileBytes ? 1u : (uint32_t)(kLdsTileBytes / a.R);
+  t->token_major = layout == kLayoutPageFirst ? 1u : 0u;
+  if (t->token_major) {
+    t->tile_lc = umin(a.nlc, umax(1u, rows_budget / 4));
+    t->tile_t = umin(a.n, umax(1u, rows_budget / t->tile_lc));
+  } else {
+    t->tile_lc = 1;
+    t->tile_t = umin(a.n, rows_budget);
+  }
+  t->tiles_t = (a.n + t->tile_t - 1) / t->tile_t;
+  t->tiles_lc = (a.nlc + t->tile_lc - 1) / t->tile_lc;
+  return t->tiles_t * t->tiles_lc;
+}
+
+// Request position i and pair lc of row r of the host-order walk.
+constexpr void walk_row(const XferArgs &a, uint32_t r, uint32_t &i, uint32_t &lc) {
+  if (r < a.rows_full) {
+    const uint32_t gsz = a.G * a.nlc;
+    const uint32_t grp = r / gsz;
+    const uint32_t rem = r - grp * gsz;
+    lc = rem / a.G;
+    i = grp * a.G + (rem - lc * a.G);
+  } else {  // ragged last group (page_first_direct with n % page_size != 0)
+    const uint32_t first = a.rows_full / a.nlc;
+    const uint32_t t = a.n - first;
+    const uint32_t rem = r - a.rows_full;
+    lc = rem / t;
+    i = first + (rem - lc * t);
+  }
+}
+
+// A tile of the LDS variant: positions [i0, i0+nt), pairs [lcf, lcf+nl).
+struct Tile {
+  uint32_t i0, lcf, nt, nl;
+};
+
+constexpr Tile tile_of(const XferArgs &a, const TileArgs &ta, uint32_t block) {
+  uint32_t bt = 0, bl = 0;
+  if (ta.token_major) {
+    bt = block / ta.tiles_lc;
+    bl = block - bt * ta.tiles_lc;
+  } else {
+    bl = block / ta.tiles_t;
+    bt = block - bl * ta.tiles_t;
+  }
+  Tile t{bt * ta.tile_t, bl * ta.tile_lc, 0, 0};
+  t.nt = umin(ta.tile_t, a.n - t.i0);
+  t.nl = umin(ta.tile_lc, a.nlc - t.lcf);
+  return t;
+}
+
+// Chunk f of a tile walk -> (pair, position, chunk in row), pair-major or
+// position-major.
+constexpr void tile_walk(const Tile &t, uint32_t cpr, bool pos_major, uint32_t f, uint32_t &lc_t,
+                         uint32_t &p_t, uint32_t &k) {
+  const uint32_t row = f / cpr;
+  k = f - row * cpr;
+  if (pos_major) {
+    p_t = row / t.nl;
+    lc_t = row - p_t * t.nl;
+  } else {
+    lc_t = row / t.nt;
+    p_t = row - lc_t * t.nt;
+  }
+}
+
+// LDS chunk slot of (pair, position, chunk) inside a tile: pair-major.
+constexpr uint32_t tile_slot(const Tile &t, uint32_t cpr, uint32_t lc_t, uint32_t p_t,
+                             uint32_t k) {
+  return (lc_t * t.nt + p_t) * cpr + k;
+}
+
+}  // namespace kvt

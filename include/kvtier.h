@@ -1,0 +1,270 @@
+/*
+ * kvtier.h — C ABI of the cross-tier KV transfer library (libkvtier.so).
+ *
+ * What it moves. A hierarchical prefix cache keeps KV in device HBM ("L1") and
+ * spills or restores it through a pinned host DRAM pool ("L2"). Write-back
+ * (device -> host, "D2H") and load (host -> device, "H2D") are indexed copies
+ * of whole KV rows between the two tiers (pages: "Tuning SGLang HiCache L2 on
+ * Kunlunxin P800/P900", sections 1.2 and 2.1; "HiCache system design",
+ * section "data transfer optimisation").
+ *
+ * Vocabulary used below.
+ *   L   layers, C components per layer (2 = K and V; 1 = an MLA latent).
+ *   R   row bytes: one token's K (or V, or latent) for one layer = H*D*elem.
+ *   S_dev  token slots in each device buffer; S_host token slots in the host pool.
+ *   ps  page size in tokens.
+ *   A "row" is R contiguous bytes. Values are moved as raw bytes, never
+ *   interpreted, so any element type (bf16, fp8 with NaN patterns, ...) is fine.
+ *
+ * Device pool (L1). Layer-first: L*C separate device buffers B[l][c], each
+ * S_dev*R bytes, row d at B[l][c] + d*R ("different layers are different
+ * buffers": Kunlunxin tuning page, section 2.1; "L1 is fixed layer-first":
+ * Baidu KV cache page, section "L2 layout choice"). The buffers are BORROWED:
+ * the caller (e.g. torch) owns them and keeps them alive until
+ * kv_pool_destroy().
+ *
+ * Host pool (L2). One byte array of L*C*S_host*R bytes, OWNED by the library,
+ * allocated pinned and mapped for the device. Host slot h of layer l,
+ * component c lives at row host_row(l,c,h), byte offset host_row*R:
+ *   KV_LAYER_FIRST        dims (layer, comp, slot, row):  (l*C + c)*S_host + h
+ *   KV_PAGE_FIRST         dims (slot, layer, comp, row):  (h*L + l)*C + c
+ *   KV_PAGE_FIRST_DIRECT  dims (page, layer, comp, offset-in-page, row):
+ *                         ((h/ps*L + l)*C + c)*ps + h%ps
+ * The layer_first and page_first_direct dimension orders are the ones the
+ * Kunlunxin tuning page gives in section 2.1 ("(layer, size, 1, kv_dim)" and
+ * "(page_num, layer_num, page_size, 1, kv_dim)"); page_first keeps a page
+ * contiguous and moves at one-token-per-layer granularity (HiCache system
+ * design page, section "data transfer optimisation"). Where the pages are
+ * silent we read: the component axis sits directly inside the layer axis in
+ * all three layouts, and page_first is token-outer, layer-inner.
+ *
+ * Asynchrony. kv_backup/kv_load return once the work is ENQUEUED on the given
+ * HIP stream; nothing blocks on the transfer ("start_writing()/start_loading()
+ * only enqueue; dedicated threads submit on private streams": Kunlunxin tuning
+ * page section 2.2; Baidu page "bidirectional async transfer"). Completion is
+ * observed through the stream or through kv_load_layer().
+ *
+ * Threads. One backup thread and one load thread may call concurrently on one
+ * pool (each direction has its own internal state and lock). Calls of the same
+ * direction from several threads are serialised by that lock.
+ *
+ * Errors. Every int-returning call returns KV_OK (0) or a negative KV_E* code;
+ * kv_last_error() gives a message for the calling thread. When validation
+ * fails nothing is enqueued and no byte of either pool is modified. A HIP
+ * failure of already-enqueued work surfaces at a later call or at destroy.
+ */
+#ifndef KVTIER_H
+#define KVTIER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define KV_OK       0
+#define KV_EINVAL  (-1) /* bad argument or precondition (null pointer, n<0, bad layer range, R%16, S_host%ps, ...) */
+#define KV_ERANGE  (-2) /* an index is outside [0, S_dev) or [0, S_host) */
+#define KV_EDUP    (-3) /* a destination slot appears twice in one call (only with KV_F_CHECK_UNIQUE) */
+#define KV_ENOMEM  (-4) /* host or device allocation failed */
+#define KV_EHIP    (-5) /* a HIP runtime call failed */
+
+/* ---- host layouts ------------------------------------------------------ */
+typedef enum {
+  KV_LAYER_FIRST = 0,
+  KV_PAGE_FIRST = 1,
+  KV_PAGE_FIRST_DIRECT = 2
+} kv_layout_t;
+
+/* ---- execution paths ---------------------------------------------------
+ * KV_PATH_AUTO        per call, pick the cheaper of KERNEL and DMA from the
+ *                     byte count and the number of DMA copies the request
+ *                     needs, using the pool's calibration (kv_calib_t).
+ * KV_PATH_KERNEL      zero-copy gather/scatter kernel: the GPU reads/writes the
+ *                     mapped host pool directly, 16 bytes per lane, rows taken
+ *                     in host-address order.
+ * KV_PATH_KERNEL_LDS  as KERNEL, but each workgroup stages a tile of rows in
+ *                     LDS: read in source order, written in destination order
+ *                     (the page_first <-> layer_first transpose).
+ * KV_PATH_DMA         coalesced copy-engine path: maximal contiguous runs,
+ *                     uniform-stride runs merged into 2-D copies, issued as
+ *                     hipMemcpyAsync / hipMemcpy2DAsync on the stream.      */
+typedef enum {
+  KV_PATH_AUTO = 0,
+  KV_PATH_KERNEL = 1,
+  KV_PATH_KERNEL_LDS = 2,
+  KV_PATH_DMA = 3
+} kv_path_t;
+
+/* ---- pool flags -------------------------------------------------------- */
+#define KV_F_CHECK_UNIQUE     0x1u /* reject duplicate destination slots (KV_EDUP) */
+#define KV_F_HOST_NONCOHERENT 0x2u /* allocate the host pool non-coherent (coarse-grained) instead of coherent */
+
+/* Geometry of one pool. Needs no GPU; the planner calls below take it alone. */
+typedef struct {
+  int32_t num_layers;     /* L  >= 1 */
+  int32_t num_components; /* C  >= 1 (2 = K,V; 1 = MLA latent) */
+  int64_t row_bytes;      /* R  >= 16, R % 16 == 0 */
+  int64_t device_slots;   /* S_dev >= 1 */
+  int64_t host_slots;     /* S_host >= 1, S_host % page_size == 0 */
+  int32_t page_size;      /* ps >= 1 */
+  int32_t host_layout;    /* kv_layout_t */
+} kv_geometry_t;
+
+typedef struct {
+  kv_geometry_t geom;
+  /* L*C device buffer base pointers, index l*C + c, each S_dev*R bytes and
+   * 16-byte aligned. The array itself is copied during kv_pool_create; the
+   * buffers it points to are borrowed. */
+  void *const *device_buffers;
+  int32_t device;    /* HIP device ordinal the buffers live on */
+  int32_t numa_node; /* -1: no binding; else the host pool's pages are bound to this node */
+  uint32_t flags;    /* KV_F_* */
+} kv_pool_desc_t;
+
+/* Selector calibration: modelled time of a call on each path.
+ *   t_kernel = launches * kernel_launch_us + bytes / kernel_gbps
+ *   t_dma    = copies * dma_copy_us + bytes / dma_gbps
+ * The four figures are measured per direction on the target machine.
+ * load_split_min_bytes: kv_load issues one kernel per layer (so each layer's
+ * event fires as soon as that layer has landed) when one layer of the request
+ * holds at least this many bytes; below it, one kernel covers all layers and
+ * every layer's event is recorded after it. */
+typedef struct {
+  double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
+  double kernel_gbps[2];
+  double dma_copy_us[2];
+  double dma_gbps[2];
+  double load_split_min_bytes;
+} kv_calib_t;
+
+typedef struct kv_pool kv_pool_t; /* opaque */
+
+/* ---- planner: pure host functions, no GPU needed ------------------------ */
+
+/* Checks a geometry: L,C,ps >= 1, R >= 16 and R % 16 == 0, S_dev,S_host >= 1,
+ * S_host % ps == 0, layout in range, and the pool sizes fit in int64.
+ * Returns KV_OK or KV_EINVAL. */
+int kv_geometry_check(const kv_geometry_t *geom);
+
+/* Host row index of (layer, comp, host slot) in the pool's layout (formulas
+ * above). Returns the row (>= 0) or KV_EINVAL / KV_ERANGE for a bad geometry
+ * or out-of-range argument. Byte offset = row * R. */
+int64_t kv_host_row(const kv_geometry_t *geom, int32_t layer, int32_t comp, int64_t host_slot);
+
+/* Validates one transfer exactly as kv_backup (direction 0) / kv_load
+ * (direction 1) do before enqueuing anything:
+ *   KV_EINVAL  null index pointer with n > 0, n < 0, or not
+ *              0 <= layer_begin <= layer_end <= L;
+ *   KV_ERANGE  some dev_idx[i] outside [0,S_dev) or host_idx[i] outside [0,S_host);
+ *   KV_EDUP    (check_unique != 0) a destination slot repeats: host_idx for
+ *              backup, dev_idx for load.
+ * The first failing rule in this order decides the code. n == 0 is KV_OK. */
+int kv_validate(const kv_geometry_t *geom, int32_t direction, const int64_t *dev_idx,
+                const int64_t *host_idx, int64_t n, int32_t layer_begin, int32_t layer_end,
+                int32_t check_unique);
+
+/* Number of contiguous copies ("DMA segments") the request needs: for each
+ * (l in [layer_begin,layer_end), c), the maximal runs of consecutive request
+ * positions whose device rows and host rows both advance by exactly one row.
+ * Runs never cross (l,c) buffers. This is the segment count of the Kunlunxin
+ * tuning page section 2.1: page_num*layer_num for page_first_direct against
+ * layer_num for layer_first at C = 1. Validates first (as kv_validate with
+ * check_unique = 0); *out is written only on KV_OK. */
+int kv_count_segments(const kv_geometry_t *geom, const int64_t *dev_idx, const int64_t *host_idx,
+                      int64_t n, int32_t layer_begin, int32_t layer_end, int64_t *out);
+
+/* Number of copy-engine calls the DMA path would issue for the request after
+ * merging equal-length runs at a uniform device and host stride into 2-D copies.
+ * Validates like kv_count_segments. */
+int kv_count_dma_copies(const kv_geometry_t *geom, const int64_t *dev_idx,
+                        const int64_t *host_idx, int64_t n, int32_t layer_begin,
+                        int32_t layer_end, int64_t *out);
+
+/* ---- pool lifetime (needs a GPU) ----------------------------------------- */
+
+/* Allocates the pinned, device-mapped host pool (L*C*S_host*R bytes, contents
+ * unspecified), copies the device-buffer table to the device, creates the
+ * per-layer load events and the per-direction index staging buffers.
+ * Not on the timed path. On success *out owns all of it. Errors: KV_EINVAL
+ * (bad desc / geometry / null buffer / misaligned buffer), KV_ENOMEM,
+ * KV_EHIP. */
+int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out);
+
+/* Waits for every transfer enqueued through the pool, then frees the host
+ * pool, events and staging. Returns the first HIP error seen while waiting,
+ * if any. NULL is a no-op returning KV_OK. */
+int kv_pool_destroy(kv_pool_t *pool);
+
+/* Host (CPU) address of the host pool and its size in bytes. The pointer stays
+ * valid until kv_pool_destroy. Reading it while a transfer that writes it is
+ * in flight gives unspecified bytes. */
+void *kv_pool_host_ptr(const kv_pool_t *pool);
+int64_t kv_pool_host_bytes(const kv_pool_t *pool);
+
+/* ---- transfers (the hot path) -------------------------------------------- */
+
+/* D2H write-back: for every i in [0,n), l in [layer_begin,layer_end), c in
+ * [0,C), copy the R bytes of device row dev_idx[i] of B[l][c] to host row
+ * host_row(l,c,host_idx[i]). Enqueued on `stream` (a hipStream_t; NULL = the
+ * null stream). dev_idx/host_idx are host arrays of n int64, read only during
+ * the call. The caller orders `stream` after the work that produced the KV and
+ * must not overwrite those device rows until the stream has passed this call.
+ * Returns after enqueue. n == 0 or an empty layer range: KV_OK, nothing
+ * enqueued. */
+int kv_backup(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+              int32_t layer_begin, int32_t layer_end, void *stream);
+
+/* H2D load: the reverse copy, host row host_row(l,c,host_idx[i]) -> device row
+ * dev_idx[i] of B[l][c]. Layers are issued in increasing order, and after the
+ * last byte of layer l is enqueued the pool's event for layer l is recorded
+ * on `stream`, so a consumer can start on layer l while later layers are
+ * still in flight (compute/transfer overlap: HiCache system design page,
+ * "data transfer optimisation"; "H2D stream -> KV_READY event -> compute
+ * stream": runtime-boundary page, "why compute, H2D and D2H should stay in one
+ * GPU execution domain"). The caller must not overwrite those host rows until
+ * the load has completed. */
+int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+            int32_t layer_begin, int32_t layer_end, void *stream);
+
+/* Makes `compute_stream` wait (on the device, the host does not block) until
+ * layer `layer` of the most recent kv_load that covered that layer on this
+ * pool has landed in device memory. Call it after that kv_load has returned.
+ * A layer no kv_load has covered yet: KV_OK, no wait. Errors: KV_EINVAL (layer
+ * out of [0,L)), KV_EHIP. */
+int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
+
+/* ---- path control, calibration and statistics -------------------------- */
+
+/* Forces a path (kv_path_t) for later calls on this pool; KV_PATH_AUTO
+ * restores the selector. */
+int kv_set_path(kv_pool_t *pool, int32_t path);
+
+/* Path the most recent call of `direction` (0 = backup, 1 = load) used: one of
+ * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA, or -1 if none yet. */
+int32_t kv_last_path(const kv_pool_t *pool, int32_t direction);
+
+/* Replaces / reads the selector calibration. */
+int kv_set_calibration(kv_pool_t *pool, const kv_calib_t *calib);
+int kv_get_calibration(const kv_pool_t *pool, kv_calib_t *calib);
+
+typedef struct {
+  int64_t calls[2];         /* per direction (0 backup, 1 load) */
+  int64_t bytes[2];         /* algorithmic bytes enqueued */
+  int64_t kernel_launches[2];
+  int64_t dma_copies[2];    /* copy-engine calls issued */
+  double submit_us[2];      /* host wall time spent inside the calls */
+} kv_stats_t;
+
+int kv_get_stats(const kv_pool_t *pool, kv_stats_t *out);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char *kv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVTIER_H */

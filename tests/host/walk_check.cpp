@@ -1,0 +1,314 @@
+// walk_check.cpp — CPU replay of the library's launch plans against the oracle.
+//
+// Built with the host compiler under AddressSanitizer/UBSan by
+// tests/test_host_planner.py. For random geometries and requests it replays,
+// on host mirrors of the device pool and of the host pool:
+//   * every workgroup/lane/unroll step of the direct kernel (xfer_rows), with
+//     the same constexpr walk the kernel runs (xfer_walk.hpp), for one launch
+//     over all layers and for per-layer launches;
+//   * every tile, phase and LDS slot of the LDS-staged kernel;
+//   * every copy of the copy-engine plan (runs merged into 2-D copies);
+// and checks that each 16-byte chunk of each row is moved exactly once, that
+// every address and LDS slot stays in bounds, and that the resulting bytes equal
+// the oracle's. It also checks the segment counter against the oracle's.
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "kvtier.h"
+#include "plan.hpp"
+#include "xfer_walk.hpp"
+
+extern "C" {
+int kvo_backup(int L, int C, int64_t R, int64_t S_dev, int64_t S_host, int ps, int layout,
+               uint8_t *const *dev_bufs, uint8_t *host, const int64_t *dev_idx,
+               const int64_t *host_idx, int64_t n, int l0, int l1, int check_unique);
+int kvo_load(int L, int C, int64_t R, int64_t S_dev, int64_t S_host, int ps, int layout,
+             uint8_t *const *dev_bufs, const uint8_t *host, const int64_t *dev_idx,
+             const int64_t *host_idx, int64_t n, int l0, int l1, int check_unique);
+int64_t kvo_count_segments(int L, int C, int64_t R, int64_t S_dev, int64_t S_host, int ps,
+                           int layout, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+                           int l0, int l1);
+}
+
+namespace kvt {
+void set_error(const std::string &) {}
+}
+
+using namespace kvt;
+
+static int failures = 0;
+#define CHECK(cond, ...)                                   \
+  do {                                                     \
+    if (!(cond)) {                                         \
+      if (failures < 20) {                                 \
+        std::fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__); \
+        std::fprintf(stderr, __VA_ARGS__);                 \
+        std::fprintf(stderr, "\n");                        \
+      }                                                    \
+      failures++;                                          \
+    }                                                      \
+  } while (0)
+
+struct Mirror {
+  Geom g;
+  std::vector<std::vector<uint8_t>> dev;  // L*C buffers
+  std::vector<uint8_t> host;
+  std::vector<uint8_t *> ptrs() {
+    std::vector<uint8_t *> p;
+    for (auto &b : dev) p.push_back(b.data());
+    return p;
+  }
+};
+
+// Replays one launch of xfer_rows on the mirrors. tok holds {dev slot, host key}.
+static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, int32_t la,
+                        int32_t lb, bool to_host, std::vector<uint8_t> &cover) {
+  const Geom &g = m.g;
+  XferArgs a{};
+  a.R = g.R;
+  a.lc_stride = g.lc_stride;
+  a.n = (uint32_t)n;
+  a.lc0 = (uint32_t)(la * g.C);
+  a.nlc = (uint32_t)((lb - la) * g.C);
+  const uint32_t blocks = plan_rows(&a, g.layout, g.ps);
+  CHECK((uint64_t)blocks * a.rows_per_block >= a.total_rows, "grid too small");
+  CHECK(blocks == 0 || (uint64_t)(blocks - 1) * a.rows_per_block < a.total_rows, "idle block");
+  for (uint32_t b = 0; b < blocks; b++) {
+    const uint32_t row0 = b * a.rows_per_block;
+    const uint32_t nrows = umin(a.rows_per_block, a.total_rows - row0);
+    const uint32_t nchunks = nrows * a.cpr;
+    for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock)
+      for (int u = 0; u < kXferUnroll; u++)
+        for (uint32_t tid = 0; tid < (uint32_t)kXferThreads; tid++) {
+          const uint32_t f = base + u * kXferThreads + tid;
+          if (f >= nchunks) continue;
+          const uint32_t rr = f / a.cpr, k = f - rr * a.cpr;
+          uint32_t i = 0, lc = 0;
+          walk_row(a, row0 + rr, i, lc);
+          CHECK(i < a.n && lc < a.nlc, "walk out of range i=%u lc=%u", i, lc);
+          if (!(i < a.n && lc < a.nlc)) return;
+          const int64_t dslot = tok[2 * i], key = tok[2 * i + 1];
+          const int64_t dev_off = dslot * g.R + 16 * (int64_t)k;
+          const int64_t host_off = ((int64_t)(a.lc0 + lc) * a.lc_stride + key) * g.R + 16 * (int64_t)k;
+          CHECK(dev_off >= 0 && dev_off + 16 <= g.S_dev * g.R, "device offset out of bounds");
+          CHECK(host_off >= 0 && host_off + 16 <= (int64_t)m.host.size(), "host offset out of bounds");
+          uint8_t *d = m.dev[a.lc0 + lc].data() + dev_off;
+          uint8_t *h = m.host.data() + host_off;
+          if (to_host)
+            std::memcpy(h, d, 16);
+          else
+            std::memcpy(d, h, 16);
+          const int64_t cell = ((int64_t)i * g.L * g.C + a.lc0 + lc) * a.cpr + k;
+          cover[cell]++;
+        }
+  }
+}
+
+// Replays one launch of xfer_tiles_lds.
+static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, int32_t la,
+                         int32_t lb, bool to_host, std::vector<uint8_t> &cover) {
+  const Geom &g = m.g;
+  XferArgs a{};
+  a.R = g.R;
+  a.lc_stride = g.lc_stride;
+  a.n = (uint32_t)n;
+  a.lc0 = (uint32_t)(la * g.C);
+  a.nlc = (uint32_t)((lb - la) * g.C);
+  plan_rows(&a, g.layout, g.ps);
+  TileArgs ta{};
+  const uint32_t blocks = plan_tiles(a, g.layout, &ta);
+  const size_t lds_bytes = (size_t)ta.tile_t * ta.tile_lc * g.R;
+  CHECK(lds_bytes <= 64 * 1024, "LDS tile of %zu bytes exceeds 64 KiB", lds_bytes);
+  std::vector<uint8_t> lds(lds_bytes);
+  for (uint32_t b = 0; b < blocks; b++) {
+    const Tile t = tile_of(a, ta, b);
+    CHECK(t.nt >= 1 && t.nl >= 1 && t.i0 + t.nt <= a.n && t.lcf + t.nl <= a.nlc, "bad tile");
+    const uint32_t nchunks = t.nt * t.nl * a.cpr;
+    const bool host_pm = ta.token_major != 0;
+    for (int phase = 0; phase < 2; phase++) {
+      const bool pos_major = phase == 0 ? (to_host ? false : host_pm) : (to_host ? host_pm : false);
+      for (uint32_t f = 0; f < nchunks; f++) {
+        uint32_t lc_t = 0, p_t = 0, k = 0;
+        tile_walk(t, a.cpr, pos_major, f, lc_t, p_t, k);
+        const uint32_t slot = tile_slot(t, a.cpr, lc_t, p_t, k);
+        CHECK((size_t)slot * 16 + 16 <= lds_bytes, "LDS slot out of bounds");
+        const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
+        const int64_t dev_off = tok[2 * i] * g.R + 16 * (int64_t)k;
+        const int64_t host_off =
+            ((int64_t)(a.lc0 + lc) * a.lc_stride + tok[2 * i + 1]) * g.R + 16 * (int64_t)k;
+        CHECK(host_off >= 0 && host_off + 16 <= (int64_t)m.host.size(), "host offset OOB");
+        uint8_t *d = m.dev[a.lc0 + lc].data() + dev_off;
+        uint8_t *h = m.host.data() + host_off;
+        uint8_t *s = lds.data() + (size_t)slot * 16;
+        if (phase == 0) {
+          std::memcpy(s, to_host ? d : h, 16);
+        } else {
+          std::memcpy(to_host ? h : d, s, 16);
+          cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * a.cpr + k]++;
+        }
+      }
+    }
+  }
+}
+
+// Executes the copy-engine plan with memcpy, line by line.
+static void replay_dma(Mirror &m, const int64_t *d, const int64_t *h, int64_t n, int32_t l0,
+                       int32_t l1, bool to_host, int64_t *copies_out) {
+  const Geom &g = m.g;
+  std::vector<Run> runs;
+  std::vector<Copy> copies;
+  build_runs(g, d, h, n, &runs);
+  build_copies(g, runs, d, h, &copies);
+  int64_t total = 0;
+  for (const Run &r : runs) total += r.len;
+  CHECK(total == n, "runs cover %lld of %lld positions", (long long)total, (long long)n);
+  for (int32_t l = l0; l < l1; l++)
+    for (int32_t c = 0; c < g.C; c++)
+      for (const Copy &cp : copies) {
+        CHECK(cp.lines == 1 || (cp.dev_pitch >= cp.len && cp.key_pitch >= cp.len), "bad pitch");
+        for (int64_t j = 0; j < cp.lines; j++) {
+          const int64_t dev_off = (cp.dev0 + j * cp.dev_pitch) * g.R;
+          const int64_t host_off = ((int64_t)(l * g.C + c) * g.lc_stride + cp.key0 + j * cp.key_pitch) * g.R;
+          const int64_t w = cp.len * g.R;
+          CHECK(dev_off >= 0 && dev_off + w <= g.S_dev * g.R, "DMA device range OOB");
+          CHECK(host_off >= 0 && host_off + w <= (int64_t)m.host.size(), "DMA host range OOB");
+          uint8_t *dp = m.dev[l * g.C + c].data() + dev_off;
+          uint8_t *hp = m.host.data() + host_off;
+          if (to_host)
+            std::memcpy(hp, dp, w);
+          else
+            std::memcpy(dp, hp, w);
+        }
+      }
+  *copies_out = (int64_t)copies.size() * (l1 - l0) * g.C;
+}
+
+int main(int argc, char **argv) {
+  const int cases = argc > 1 ? std::atoi(argv[1]) : 300;
+  std::mt19937_64 rng(12345);
+  auto uni = [&](int64_t lo, int64_t hi) {  // inclusive
+    return lo + (int64_t)(rng() % (uint64_t)(hi - lo + 1));
+  };
+  int64_t checked = 0;
+  for (int cs = 0; cs < cases; cs++) {
+    kv_geometry_t kg{};
+    kg.num_layers = (int32_t)uni(1, 5);
+    kg.num_components = (int32_t)uni(1, 2);
+    const int64_t rsel = uni(0, 5);
+    kg.row_bytes = rsel == 0 ? 16 : rsel == 1 ? 48 : rsel == 2 ? 272 : rsel == 3 ? 1152 : rsel == 4 ? 2048 : 36864;
+    kg.page_size = (int32_t)(std::vector<int>{1, 2, 3, 4, 16, 64})[uni(0, 5)];
+    kg.host_slots = kg.page_size * uni(1, 300 / kg.page_size + 1);
+    kg.device_slots = uni(1, 400);
+    kg.host_layout = (int32_t)uni(0, 2);
+    if (kg.row_bytes > 4096) {  // keep big-row cases small
+      kg.host_slots = kg.page_size * uni(1, 3);
+      kg.device_slots = uni(1, 8);
+    }
+    Geom g;
+    std::string why;
+    if (make_geom(&kg, &g, &why) != KV_OK) {
+      CHECK(false, "geometry rejected: %s", why.c_str());
+      continue;
+    }
+    const int64_t nmax = std::min(g.S_dev, g.S_host);
+    const int64_t n = uni(0, nmax);
+    // destinations unique for both directions: sample without replacement
+    std::vector<int64_t> dv(g.S_dev), hv(g.S_host);
+    for (int64_t i = 0; i < g.S_dev; i++) dv[i] = i;
+    for (int64_t i = 0; i < g.S_host; i++) hv[i] = i;
+    const int mode = (int)uni(0, 2);  // 0 random, 1 contiguous, 2 page-shuffled
+    if (mode == 0) {
+      std::shuffle(dv.begin(), dv.end(), rng);
+      std::shuffle(hv.begin(), hv.end(), rng);
+    } else if (mode == 1) {
+      std::rotate(dv.begin(), dv.begin() + uni(0, g.S_dev - n), dv.end());
+    } else {
+      std::shuffle(dv.begin(), dv.end(), rng);
+      std::sort(dv.begin(), dv.begin() + n);
+    }
+    std::vector<int64_t> d(dv.begin(), dv.begin() + n), h(hv.begin(), hv.begin() + n);
+    const int32_t l0 = (int32_t)uni(0, g.L), l1 = (int32_t)uni(l0, g.L);
+    const int64_t nlc = (int64_t)(l1 - l0) * g.C;
+
+    Mirror base;
+    base.g = g;
+    base.dev.resize((size_t)g.L * g.C);
+    for (auto &b : base.dev) {
+      b.resize((size_t)(g.S_dev * g.R));
+      for (auto &x : b) x = (uint8_t)rng();
+    }
+    base.host.resize((size_t)((int64_t)g.L * g.C * g.S_host * g.R));
+    for (auto &x : base.host) x = (uint8_t)rng();
+
+    // expected results from the oracle
+    Mirror want_b = base, want_l = base;
+    {
+      auto p = want_b.ptrs();
+      CHECK(kvo_backup(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, p.data(),
+                       want_b.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle backup");
+      auto q = want_l.ptrs();
+      CHECK(kvo_load(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, q.data(),
+                     want_l.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle load");
+    }
+    int64_t seg = -1;
+    CHECK(kv_count_segments(&kg, d.data(), h.data(), n, l0, l1, &seg) == KV_OK, "count");
+    CHECK(seg == kvo_count_segments(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, d.data(),
+                                    h.data(), n, l0, l1),
+          "segment count differs from the oracle");
+
+    std::vector<int64_t> tok(2 * (size_t)n);
+    for (int64_t i = 0; i < n; i++) {
+      tok[2 * i] = d[i];
+      tok[2 * i + 1] = host_key(g, h[i]);
+    }
+    const int64_t cells = n * g.L * g.C * (g.R / 16);
+    for (int dir = 0; dir < 2; dir++) {
+      const bool to_host = dir == 0;
+      const Mirror &want = to_host ? want_b : want_l;
+      for (int variant = 0; variant < 4; variant++) {
+        if (n == 0 || nlc == 0) break;
+        if (variant == 2 && g.R > kMaxLdsRowBytes) continue;
+        Mirror m = base;
+        std::vector<uint8_t> cover((size_t)cells, 0);
+        int64_t copies = 0;
+        if (variant == 0) {
+          replay_rows(m, tok, n, l0, l1, to_host, cover);
+        } else if (variant == 1) {
+          for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover);
+        } else if (variant == 2) {
+          replay_tiles(m, tok, n, l0, l1, to_host, cover);
+        } else {
+          replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
+          int64_t counted = -1;
+          CHECK(kv_count_dma_copies(&kg, d.data(), h.data(), n, l0, l1, &counted) == KV_OK &&
+                    counted == copies,
+                "dma copy count");
+          CHECK(copies <= seg, "more copies than segments");
+        }
+        if (variant != 3) {
+          for (int64_t i = 0; i < n; i++)
+            for (int32_t lc = 0; lc < g.L * g.C; lc++)
+              for (int64_t k = 0; k < g.R / 16; k++) {
+                const bool inside = lc >= l0 * g.C && lc < l1 * g.C;
+                const uint8_t cnt = cover[(size_t)((i * g.L * g.C + lc) * (g.R / 16) + k)];
+                CHECK(cnt == (inside ? 1 : 0), "chunk moved %d times (variant %d)", cnt, variant);
+              }
+        }
+        CHECK(m.host == want.host, "host pool differs from oracle (case %d dir %d variant %d)", cs,
+              dir, variant);
+        for (size_t b = 0; b < m.dev.size(); b++)
+          CHECK(m.dev[b] == want.dev[b], "device buffer %zu differs (case %d dir %d variant %d)", b,
+                cs, dir, variant);
+        checked++;
+      }
+    }
+  }
+  std::printf("walk_check: %lld replays, %d failures\n", (long long)checked, failures);
+  return failures == 0 ? 0 : 1;
+}

@@ -1,0 +1,236 @@
+"""GPU parity: the C-ABI transfers against the oracle, byte for byte.
+
+Small pools whose requests span many workgroups, LDS tiles and copy-engine
+copies, with ragged tails (request sizes that are not a multiple of the page
+size, row sizes that are not a power of two), every host layout, every path,
+both directions, partial layer ranges, and the edge cases (empty requests,
+empty layer ranges, one-token requests, 16-byte rows, rejected requests).
+"""
+import numpy as np
+import pytest
+
+import hierarchical_kv_cache_backup_amd as kvt
+from hierarchical_kv_cache_backup_amd import workloads
+import oracle
+from oracle import Geometry, LAYOUTS
+
+from gpu_util import (PATHS, SENTINEL, device_buffers, make_pool, mirrors,
+                      run_backup_and_compare, run_load_and_compare, kv_geom, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+@pytest.fixture
+def stream(torch):
+    return torch.cuda.Stream()
+
+
+# ---- config 1: tiny pool, round trip into fresh slots ------------------------------
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("path", PATHS)
+def test_tiny_round_trip(torch, stream, layout, path):
+    shape = workloads.tiny()
+    g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                 shape.host_slots, shape.page_size, layout)
+    dev_idx, host_idx, reload_idx = workloads.tiny_indices(shape)
+    src = device_buffers(g, seed=1)
+    pool = make_pool(g, src, path)
+    print("tiny layout=%d path=%d" % (layout, path), flush=True)
+    run_backup_and_compare(g, pool, src, dev_idx, host_idx, 0, g.L, stream)
+    # reload into a second, sentinel-filled device pool at an independent permutation
+    fresh = device_buffers(g, seed=2, fill=SENTINEL)
+    pool2 = make_pool(g, fresh, path, host_fill=None)
+    pool2.host_array()[:] = pool.host_array()
+    run_load_and_compare(g, pool2, fresh, reload_idx, host_idx, 0, g.L, stream)
+    # identity: fresh[reload[i]] == src[dev[i]] for every row
+    for k in range(g.L * g.C):
+        a = src[k].view(g.S_dev, g.R)[torch.from_numpy(dev_idx).cuda()]
+        b = fresh[k].view(g.S_dev, g.R)[torch.from_numpy(reload_idx).cuda()]
+        assert torch.equal(a, b)
+    pool.close()
+    pool2.close()
+
+
+# ---- random requests over several tiles with ragged tails ----------------------------
+
+GEOMS = [
+    # L, C, R, S_dev, S_host, ps
+    (3, 2, 272, 700, 640, 16),
+    (5, 1, 1152, 300, 256, 64),
+    (2, 2, 16, 2000, 2048, 4),
+    (4, 2, 2048, 200, 192, 64),
+]
+
+
+def _request(rng, g, kind):
+    n = int(min(g.S_dev, g.S_host) * 0.8) + 3
+    n = min(n, g.S_dev, g.S_host)
+    if kind == "random":
+        return (rng.choice(g.S_dev, n, replace=False).astype(np.int64),
+                rng.choice(g.S_host, n, replace=False).astype(np.int64))
+    if kind == "contiguous":
+        d0 = int(rng.integers(0, g.S_dev - n + 1))
+        return np.arange(d0, d0 + n, dtype=np.int64), np.arange(n, dtype=np.int64)
+    # whole device pages in random order, host slots in order
+    pages = rng.permutation(g.S_dev // g.ps)[: n // g.ps]
+    d = workloads.page_indices(pages, g.ps)
+    return d.astype(np.int64), np.arange(d.size, dtype=np.int64)
+
+
+@pytest.mark.parametrize("gi", range(len(GEOMS)))
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("path", PATHS)
+def test_random_requests_match_oracle(torch, stream, gi, layout, path):
+    L, C, R, S_dev, S_host, ps = GEOMS[gi]
+    g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+    rng = np.random.default_rng(100 * gi + 10 * layout + path)
+    bufs = device_buffers(g, seed=gi)
+    pool = make_pool(g, bufs, path)
+    for kind in ("random", "contiguous", "pages"):
+        d, h = _request(rng, g, kind)
+        for l0, l1 in ((0, L), (1, L), (0, 1)):
+            print("geom=%d layout=%d path=%d kind=%s layers=[%d,%d) n=%d" %
+                  (gi, layout, path, kind, l0, l1, d.size), flush=True)
+            run_backup_and_compare(g, pool, bufs, d, h, l0, l1, stream)
+            pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+            run_load_and_compare(g, pool, bufs, d, h, l0, l1, stream)
+            assert pool.last_path(kvt.LOAD) in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA)
+            if path != kvt.PATH_AUTO:
+                assert pool.last_path(kvt.BACKUP) == path
+    pool.close()
+
+
+# ---- edge cases --------------------------------------------------------------------
+
+def test_edge_cases(torch, stream):
+    g = Geometry(2, 2, 16, 64, 64, 8, oracle.PAGE_FIRST_DIRECT)
+    bufs = device_buffers(g, seed=5)
+    for path in PATHS:
+        pool = make_pool(g, bufs, path)
+        before = pool.host_array().copy()
+        # empty request / empty layer range: OK, nothing moves
+        pool.backup([], [], 0, 2, stream)
+        pool.backup([1, 2], [3, 4], 1, 1, stream)
+        stream.synchronize()
+        assert np.array_equal(pool.host_array(), before)
+        # one token, last slots
+        run_backup_and_compare(g, pool, bufs, [63], [63], 0, 2, stream)
+        run_load_and_compare(g, pool, bufs, [0], [63], 1, 2, stream)
+        # whole pool
+        run_backup_and_compare(g, pool, bufs, np.arange(64)[::-1], np.arange(64), 0, 2, stream)
+        # rejected requests change nothing
+        snap = pool.host_array().copy()
+        dev_snap = [b.clone() for b in bufs]
+        cases = [(kvt.EDUP, "backup", [1, 2], [5, 5], 0, 2),
+                 (kvt.ERANGE, "backup", [64], [0], 0, 2),
+                 (kvt.ERANGE, "load", [0], [-1], 0, 2),
+                 (kvt.EINVAL, "load", [0], [0], 0, 3),
+                 (kvt.EINVAL, "backup", [0], [0], 2, 1),
+                 (kvt.EDUP, "load", [7, 7], [1, 2], 0, 2)]
+        for code, op, d, h, l0, l1 in cases:
+            fn = kvt.kv_backup if op == "backup" else kvt.kv_load
+            rc = fn(pool.handle, d, h, l0, l1, stream)
+            assert rc == code, (op, d, h, l0, l1, rc, kvt.kv_last_error())
+            assert kvt.kv_last_error()
+        assert kvt.kv_backup(pool.handle, [1], [1], 0, 2, stream, n=-1) == kvt.EINVAL
+        stream.synchronize()
+        assert np.array_equal(pool.host_array(), snap)
+        for a, b in zip(bufs, dev_snap):
+            assert torch.equal(a, b)
+        assert kvt.kv_load_layer(pool.handle, 2, stream) == kvt.EINVAL
+        assert kvt.kv_load_layer(pool.handle, -1, stream) == kvt.EINVAL
+        assert kvt.kv_set_path(pool.handle, 7) == kvt.EINVAL
+        pool.close()
+    # duplicates are accepted when the pool does not check them (last writer unspecified,
+    # so only a non-overlapping request is compared)
+    pool = make_pool(g, bufs, kvt.PATH_KERNEL, flags=0)
+    assert kvt.kv_backup(pool.handle, [1, 2], [5, 5], 0, 2, stream) == kvt.OK
+    stream.synchronize()
+    pool.close()
+
+
+def test_pool_create_rejects_bad_buffers(torch):
+    g = Geometry(1, 2, 32, 16, 16, 4, 0)
+    good = device_buffers(g, seed=0)
+    kg = kv_geom(g)
+    # a buffer that runs 16 bytes past the end of its device allocation (torch's
+    # caching allocator sub-allocates, so find the end of the real segment)
+    holder = torch.zeros(4096, dtype=torch.uint8, device="cuda:0")
+    seg_end = None
+    for seg in torch.cuda.memory_snapshot():
+        if seg["address"] <= holder.data_ptr() < seg["address"] + seg["total_size"]:
+            seg_end = seg["address"] + seg["total_size"]
+    assert seg_end is not None
+    over = seg_end - g.S_dev * g.R + 16
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), over])
+    assert rc == kvt.EINVAL and h is None, kvt.kv_last_error()
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), over - 16])
+    assert rc == kvt.OK, kvt.kv_last_error()
+    assert kvt.kv_pool_destroy(h) == kvt.OK
+    big = torch.zeros(16 * 32 + 16, dtype=torch.uint8, device="cuda:0")
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), big.data_ptr() + 8])
+    assert rc == kvt.EINVAL
+    cpu = np.zeros(16 * 32, np.uint8)
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), cpu.ctypes.data])
+    assert rc == kvt.EINVAL
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), good[1].data_ptr()], device=99)
+    assert rc == kvt.EINVAL
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), good[1].data_ptr()], numa_node=4096)
+    assert rc == kvt.EINVAL
+    bad = kvt.geometry(1, 2, 24, 16, 16, 4, 0)
+    rc, h = kvt.kv_pool_create(bad, [good[0].data_ptr(), good[1].data_ptr()])
+    assert rc == kvt.EINVAL
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), good[1].data_ptr()], numa_node=0,
+                               flags=kvt.F_CHECK_UNIQUE | kvt.F_HOST_NONCOHERENT)
+    assert rc == kvt.OK, kvt.kv_last_error()
+    assert kvt.kv_pool_host_bytes(h) == 2 * 16 * 32
+    assert kvt.kv_pool_destroy(h) == kvt.OK
+    assert kvt.kv_pool_destroy(None) == kvt.OK
+
+
+def test_noncoherent_host_pool_parity(torch, stream):
+    g = Geometry(3, 2, 272, 700, 640, 16, oracle.PAGE_FIRST)
+    bufs = device_buffers(g, seed=9)
+    rng = np.random.default_rng(9)
+    for path in (kvt.PATH_KERNEL, kvt.PATH_DMA):
+        pool = make_pool(g, bufs, path, flags=kvt.F_CHECK_UNIQUE | kvt.F_HOST_NONCOHERENT)
+        d, h = _request(rng, g, "random")
+        run_backup_and_compare(g, pool, bufs, d, h, 0, 3, stream)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, 0, 3, stream)
+        pool.close()
+
+
+def test_stats_and_calibration(torch, stream):
+    g = Geometry(2, 1, 64, 32, 32, 8, 0)
+    bufs = device_buffers(g, seed=3)
+    pool = make_pool(g, bufs, kvt.PATH_AUTO)
+    c = pool.calibration()
+    assert c.kernel_gbps[0] > 0 and c.load_split_min_bytes >= 0
+    # a calibration that makes copies free selects the copy engines
+    c.dma_copy_us[0] = 0.0
+    c.dma_gbps[0] = 1e6
+    pool.set_calibration(c)
+    pool.backup(np.arange(8), np.arange(8), 0, 2, stream)
+    assert pool.last_path(kvt.BACKUP) == kvt.PATH_DMA
+    c.dma_copy_us[0] = 1e6
+    pool.set_calibration(c)
+    pool.backup(np.arange(8), np.arange(8), 0, 2, stream)
+    assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
+    stream.synchronize()
+    s = pool.stats()
+    assert s.calls[0] == 2 and s.bytes[0] == 2 * 8 * 2 * 64
+    assert s.kernel_launches[0] == 1 and s.dma_copies[0] == 2
+    c.kernel_gbps[0] = -1
+    with pytest.raises(kvt.KvError):
+        pool.set_calibration(c)
+    pool.close()

@@ -1,0 +1,156 @@
+"""Host-side checks of libkvtier.so that need no GPU.
+
+* the shared library loads and exports every function include/kvtier.h declares;
+* the planner's entry points (address map, validation, segment and copy counts)
+  agree with the oracle, element by element;
+* a host-compiled replay driver (tests/host/walk_check.cpp, AddressSanitizer +
+  UBSan) runs every launch plan of the kernels and of the copy-engine path on
+  CPU mirrors and compares the bytes with the oracle.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Geometry, LAYOUTS
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+HEADER = os.path.join(ROOT, "include", "kvtier.h")
+CSRC = os.path.join(ROOT, "hierarchical_kv_cache_backup_amd", "csrc")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kv_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def kvt():
+    import hierarchical_kv_cache_backup_amd as kvt
+    return kvt
+
+
+def test_library_exports_every_declared_symbol(kvt):
+    names = declared_functions()
+    assert len(names) >= 18
+    lib = kvt.library()
+    for name in names:
+        assert hasattr(lib, name), name
+        assert name in kvt.SIGNATURES, name
+    assert sorted(kvt.SIGNATURES) == names
+    out = subprocess.check_output(["nm", "-D", "--defined-only", kvt.LIB_PATH], text=True)
+    exported = set(re.findall(r" T (kv_\w+)", out))
+    assert set(names) <= exported
+
+
+def _geom(kvt, g):
+    return kvt.geometry(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout)
+
+
+def test_host_row_matches_oracle(kvt):
+    rng = np.random.default_rng(0)
+    for _ in range(60):
+        L, C = int(rng.integers(1, 80)), int(rng.integers(1, 3))
+        ps = int(rng.choice([1, 2, 16, 64]))
+        g = Geometry(L, C, 16 * int(rng.integers(1, 200)), 1000, ps * int(rng.integers(1, 600)),
+                     ps, int(rng.integers(0, 3)))
+        kg = _geom(kvt, g)
+        for _ in range(40):
+            l, c, h = int(rng.integers(0, L)), int(rng.integers(0, C)), int(rng.integers(0, g.S_host))
+            assert kvt.kv_host_row(kg, l, c, h) == oracle.host_row(g, l, c, h)
+        assert kvt.kv_host_row(kg, L, 0, 0) == kvt.ERANGE
+        assert kvt.kv_host_row(kg, 0, 0, g.S_host) == kvt.ERANGE
+
+
+def test_geometry_and_validation_codes_match_oracle(kvt):
+    base = Geometry(4, 2, 32, 10, 8, 4, 1)
+    bad = [base.replace(R=24), base.replace(R=0), base.replace(S_host=10), base.replace(ps=0),
+           base.replace(L=0), base.replace(C=0), base.replace(layout=3), base.replace(S_dev=0)]
+    for g in [base] + bad:
+        assert kvt.kv_geometry_check(_geom(kvt, g)) == oracle.check_geometry(g), g
+    cases = [([1, 2, 3], [0, 5, 7], 0, 4), ([], [], 0, 4), ([1, 2, 3], [0, 5, 7], 2, 2),
+             ([1, 2, 3], [0, 5, 7], -1, 2), ([1, 2, 3], [0, 5, 7], 3, 2),
+             ([1, 2, 3], [0, 5, 7], 0, 5), ([10, 1, 2], [0, 5, 7], 0, 4),
+             ([-1, 1, 2], [0, 5, 7], 0, 4), ([1, 2, 3], [0, 8, 1], 0, 4),
+             ([1, 1, 2], [0, 5, 7], 0, 4), ([1, 2, 3], [3, 4, 3], 0, 4),
+             ([1, 2, 3, 4], [3, 3, 1, 9], 0, 4), ([5, 5, 5], [1, 1, 1], 0, 1)]
+    kg = _geom(kvt, base)
+    for direction in (0, 1):
+        for uniq in (True, False):
+            for d, h, l0, l1 in cases:
+                want = oracle.validate(base, direction, d, h, l0, l1, uniq)
+                got = kvt.kv_validate(kg, direction, d, h, l0, l1, uniq)
+                assert got == want, (direction, uniq, d, h, l0, l1)
+    assert kvt.kv_validate(kg, 0, [1], [1], 0, 1, True, n=-1) == kvt.EINVAL
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        g = Geometry(int(rng.integers(1, 4)), int(rng.integers(1, 3)), 16, int(rng.integers(1, 9)),
+                     4 * int(rng.integers(1, 3)), 4, int(rng.integers(0, 3)))
+        n = int(rng.integers(0, 6))
+        d = rng.integers(-1, g.S_dev + 1, n)
+        h = rng.integers(-1, g.S_host + 1, n)
+        l0 = int(rng.integers(-1, g.L + 1))
+        l1 = int(rng.integers(-1, g.L + 2))
+        for direction in (0, 1):
+            assert (kvt.kv_validate(_geom(kvt, g), direction, d, h, l0, l1, True)
+                    == oracle.validate(g, direction, d, h, l0, l1, True))
+
+
+def test_segment_counts_match_oracle(kvt):
+    rng = np.random.default_rng(2)
+    for _ in range(150):
+        ps = int(rng.choice([1, 2, 4, 16]))
+        g = Geometry(int(rng.integers(1, 6)), int(rng.integers(1, 3)), 32, 300,
+                     ps * int(rng.integers(1, 20)), ps, int(rng.integers(0, 3)))
+        n = int(rng.integers(0, min(g.S_dev, g.S_host) + 1))
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            d = rng.choice(g.S_dev, n, replace=False)
+            h = rng.choice(g.S_host, n, replace=False)
+        elif kind == 1:
+            d0 = int(rng.integers(0, g.S_dev - n + 1))
+            d = np.arange(d0, d0 + n)
+            h = np.arange(n)
+        else:  # whole pages in random order on the device
+            d = np.arange(n)
+            h = np.arange(n)
+            pages = rng.permutation(max(1, n // ps))
+            d = np.concatenate([np.arange(p * ps, p * ps + ps) for p in pages])[:n] if n else d
+        l0 = int(rng.integers(0, g.L + 1))
+        l1 = int(rng.integers(l0, g.L + 1))
+        rc, cnt = kvt.kv_count_segments(_geom(kvt, g), d, h, l0, l1)
+        assert rc == 0 and cnt == oracle.count_segments(g, d, h, l0, l1)
+        rc2, copies = kvt.kv_count_dma_copies(_geom(kvt, g), d, h, l0, l1)
+        assert rc2 == 0 and copies <= cnt
+
+
+def test_pages_example_through_library(kvt):
+    """32K tokens, page 64, 78 layers: 39,936 segments page_first_direct, 78 layer_first;
+    the copy-engine plan merges page_first_direct's uniform-stride pages into one
+    2-D copy per layer."""
+    n = 32768
+    d = np.arange(n) + 8192
+    h = np.arange(n)
+    for layout, segs in ((2, 39936), (0, 78)):
+        kg = kvt.geometry(78, 1, 1152, 65536, n, 64, layout)
+        assert kvt.kv_count_segments(kg, d, h, 0, 78) == (0, segs)
+        assert kvt.kv_count_dma_copies(kg, d, h, 0, 78) == (0, 78)
+
+
+def test_replay_driver_under_sanitizers(tmp_path):
+    obj = tmp_path / "oracle.o"
+    exe = tmp_path / "walk_check"
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+    subprocess.check_call(["gcc", "-O1", "-g", "-c", os.path.join(ROOT, "oracle", "kv_oracle.c"),
+                           "-o", str(obj)] + san)
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-I" + os.path.join(ROOT, "include"),
+                           "-I" + CSRC, os.path.join(HERE, "host", "walk_check.cpp"),
+                           os.path.join(CSRC, "plan.cpp"), str(obj), "-o", str(exe)] + san)
+    res = subprocess.run([str(exe), "160"], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 failures" in res.stdout
