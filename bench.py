@@ -43,11 +43,19 @@ def parse():
     p.add_argument("--no-matrix", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--matrix-reps", type=int, default=5)
+    p.add_argument("--profile-counters", action="store_true",
+                   help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
+                        "into profiles/counters.json and exit")
     return p.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: this transfer path has no multi-GPU part "
@@ -93,6 +101,10 @@ def main():
         (time.perf_counter() - t_setup, t_pool, pool.host_array().nbytes / 1e9))
     s = torch.cuda.Stream()
     bytes_dir = n * L * C * R
+    if args.profile_counters:
+        profile_counters(torch, kvt, pool, s, dev_b, dev_l, host_idx, L)
+        pool.close()
+        return
 
     def timed(fn, reps, warm=2):
         """Median device time (s) of fn() on stream s, by events recorded on s."""
@@ -175,6 +187,20 @@ def main():
     log("steps: %.2f GB/s aggregate; D2H %.2f GB/s (%s), H2D %.2f GB/s (%s)" %
         (value, d2h_gbps, chosen["d2h"], h2d_gbps, chosen["h2d"]))
 
+    # ---- host time per call in isolation (no back-pressure): validation,
+    # planning, index staging and launch/enqueue
+    submit = {}
+    for dname, fn in (("d2h", lambda: pool.backup(dev_b, host_idx, 0, L, s)),
+                      ("h2d", lambda: pool.load(dev_l, host_idx, 0, L, s))):
+        ts = []
+        for _ in range(7):
+            s.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        submit[dname] = round(statistics.median(ts) * 1e6, 1)
+    s.synchronize()
+
     # ---- roofline of the dominant kernel (host link bound), measured live
     roof = kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, args)
 
@@ -215,8 +241,7 @@ def main():
                                  "d2h": round(100 * d2h_gbps / link_peak["d2h"], 1)},
         "pct_of_pcie_gen5_x16": {"h2d": round(100 * h2d_gbps / PCIE_GEN5_X16_GBPS, 1),
                                  "d2h": round(100 * d2h_gbps / PCIE_GEN5_X16_GBPS, 1)},
-        "submit_us_per_call": {"d2h": round(stats.submit_us[0] / max(1, stats.calls[0]), 1),
-                               "h2d": round(stats.submit_us[1] / max(1, stats.calls[1]), 1)},
+        "submit_us_per_call": submit,
         "pool_create_s": round(t_pool, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
@@ -249,38 +274,118 @@ def counter_traffic(kernel_name, src_hash):
 
 
 def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, args):
-    """Achieved host-link GB/s of the H2D gather kernel (the one the per-layer load
-    launches, one launch per layer): algorithmic bytes per launch / mean launch
-    time, the launch time taken from events recorded on the launch stream."""
+    """Achieved host-link GB/s of the transfer kernels: algorithmic bytes per
+    launch / mean launch time, the time taken from events recorded on the stream
+    the kernels are launched on. The headline is the D2H gather kernel (one
+    launch moves the whole 78-layer prefix); the H2D kernel (one launch per
+    layer) is reported beside it."""
     pool.set_path(kvt.PATH_KERNEL)
-    per_launch = n * C * R
-    for _ in range(2):
-        pool.load(dev_l, host_idx, 0, L, s)
-    s.synchronize()
-    durs = []
-    for _ in range(max(3, args.steps)):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(s)
-        pool.load(dev_l, host_idx, 0, L, s)
-        e1.record(s)
-        e1.synchronize()
-        durs.append(e0.elapsed_time(e1) / 1e3 / L)          # L launches per call
-    mean = statistics.mean(durs)
-    achieved = per_launch / mean / 1e9
     src_hash = kernel_source_hash()
-    return {"kernel": "kvt::xfer_rows<false> (H2D gather, one launch per layer)",
+
+    def measure(fn, launches_per_call):
+        for _ in range(2):
+            fn()
+        s.synchronize()
+        durs = []
+        for _ in range(max(3, args.steps)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            e1.synchronize()
+            durs.append(e0.elapsed_time(e1) / 1e3 / launches_per_call)
+        return statistics.mean(durs), len(durs) * launches_per_call
+
+    d2h_bytes = n * L * C * R
+    t_d2h, k_d2h = measure(lambda: pool.backup(dev_b, host_idx, 0, L, s), 1)
+    h2d_bytes = n * C * R
+    t_h2d, k_h2d = measure(lambda: pool.load(dev_l, host_idx, 0, L, s), L)
+    a_d2h = d2h_bytes / t_d2h / 1e9
+    a_h2d = h2d_bytes / t_h2d / 1e9
+    return {"kernel": "kvt::xfer_rows<true> (D2H gather, whole prefix in one launch)",
             "bound": "host_link",
-            "achieved": round(achieved, 3),
+            "achieved": round(a_d2h, 3),
             "peak": PCIE_GEN5_X16_GBPS,
             "unit": "GB/s",
-            "frac": round(achieved / PCIE_GEN5_X16_GBPS, 4),
-            "traffic": counter_traffic("xfer_rows_h2d", src_hash),
-            "algorithmic_bytes_per_launch": per_launch,
-            "mean_launch_us": round(mean * 1e6, 2),
-            "launches_timed": len(durs) * L,
-            "hbm_secondary": {"peak": HBM_PEAK_GBPS, "frac": round(achieved / HBM_PEAK_GBPS, 5)},
+            "frac": round(a_d2h / PCIE_GEN5_X16_GBPS, 4),
+            "traffic": counter_traffic("xfer_rows_d2h", src_hash),
+            "algorithmic_bytes_per_launch": d2h_bytes,
+            "mean_launch_us": round(t_d2h * 1e6, 2),
+            "launches_timed": k_d2h,
+            "h2d_kernel": {"kernel": "kvt::xfer_rows<false> (H2D scatter, one launch per layer)",
+                           "achieved": round(a_h2d, 3),
+                           "frac": round(a_h2d / PCIE_GEN5_X16_GBPS, 4),
+                           "algorithmic_bytes_per_launch": h2d_bytes,
+                           "mean_launch_us_incl_gap": round(t_h2d * 1e6, 2),
+                           "launches_timed": k_h2d,
+                           "traffic": counter_traffic("xfer_rows_h2d", src_hash)},
+            "hbm_secondary": {"peak": HBM_PEAK_GBPS, "frac": round(a_d2h / HBM_PEAK_GBPS, 5)},
             "kernel_source_hash": src_hash}
+
+
+def profile_counters(torch, kvt, pool, s, dev_b, dev_l, host_idx, L):
+    """Kernels for the rocprofv3 --pmc passes: a plain copy kernel of known size
+    (int32 -> float32 conversion, 256 MiB read + 256 MiB written) to scale the
+    counters, then two D2H and two H2D transfers on the kernel path."""
+    n_el = 64 << 20
+    a = torch.ones(n_el, dtype=torch.int32, device="cuda:0")
+    b = torch.empty(n_el, dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    pool.set_path(kvt.PATH_KERNEL)
+    for _ in range(2):
+        pool.backup(dev_b, host_idx, 0, L, s)
+        s.synchronize()
+    for _ in range(2):
+        pool.load(dev_l, host_idx, 0, L, s)
+        s.synchronize()
+    log("profile-counters: copy kernel %d bytes read + written; 2 D2H + 2 H2D transfers" %
+        (4 * n_el))
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize_counters(fetch_dir, write_dir):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the transfer kernels, scaled by
+    what the same counters read for the plain copy kernel of known size."""
+    known = 4 * (64 << 20)
+    out = {}
+    per = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        for r in _counter_rows(d):
+            if r.get("Counter_Name") != cname:
+                continue
+            k = r["Kernel_Name"]
+            key = ("copy" if "elementwise_kernel" in k and "copy" in k else
+                   "xfer_rows_d2h" if "xfer_rows<true>" in k else
+                   "xfer_rows_h2d" if "xfer_rows<false>" in k else None)
+            if key is None:
+                continue
+            per.setdefault((key, cname), []).append(float(r["Counter_Value"]) * 1024.0)
+    fetch_scale = known / statistics.median(per[("copy", "FETCH_SIZE")])
+    write_scale = known / statistics.median(per[("copy", "WRITE_SIZE")])
+    src_hash = kernel_source_hash()
+    for key in ("xfer_rows_d2h", "xfer_rows_h2d"):
+        f = statistics.median(per[(key, "FETCH_SIZE")]) * fetch_scale
+        w = statistics.median(per[(key, "WRITE_SIZE")]) * write_scale
+        out[key] = {"fetch_bytes_per_launch": round(f), "write_bytes_per_launch": round(w),
+                    "hbm_bytes_per_launch": round(f + w), "kernel_source_hash": src_hash}
+    out["scale"] = {"fetch": fetch_scale, "write": write_scale,
+                    "copy_kernel_bytes_each_way": known}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args):

@@ -51,7 +51,7 @@ class kv_calib_t(ctypes.Structure):
 class kv_stats_t(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2),
                 ("kernel_launches", ctypes.c_int64 * 2), ("dma_copies", ctypes.c_int64 * 2),
-                ("submit_us", ctypes.c_double * 2)]
+                ("submit_us", ctypes.c_double * 2), ("blocked_us", ctypes.c_double * 2)]
 
 
 # Every symbol include/kvtier.h declares, with its ctypes signature.

@@ -8,18 +8,20 @@
 // descriptor per contiguous segment.
 //
 // The work is pure data movement: no arithmetic on values, no MFMA. Each lane
-// moves 16-byte chunks, so one wave instruction covers 1 KiB of consecutive
+// moves 8-byte chunks, so one wave instruction covers 512 B of consecutive
 // chunks; rows are >= 16 B and 16-B aligned on both sides, and every row is
 // contiguous on both sides, so the layout transpose is row-granular and the
-// accesses stay fully coalesced on both sides. Loads and stores are
-// non-temporal: nothing is re-read, so nothing should stay in the caches.
+// accesses stay fully coalesced on both sides. Loads are non-temporal (nothing
+// is re-read); stores are ordinary, which sustained more host-link bandwidth
+// than non-temporal stores on this part.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
 
 namespace kvt {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t chunk_t __attribute__((ext_vector_type(2)));
+static_assert(sizeof(chunk_t) == kChunkBytes, "chunk size");
 
 namespace {
 
@@ -34,15 +36,15 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
 }  // namespace
 
 // Direct path: workgroup b moves rows [b*rows_per_block, ...) of the
-// host-order walk; lanes take consecutive 16-byte chunks of those rows.
+// host-order walk; lanes take consecutive chunks of those rows.
 template <bool kToHost>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   const uint32_t row0 = blockIdx.x * a.rows_per_block;
   const uint32_t nrows = min(a.rows_per_block, a.total_rows - row0);
   const uint32_t nchunks = nrows * a.cpr;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
-    u32x4 v[kXferUnroll];
-    u32x4 *dst[kXferUnroll];
+    chunk_t v[kXferUnroll];
+    chunk_t *dst[kXferUnroll];
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
       const uint32_t f = base + u * kXferThreads + threadIdx.x;
@@ -52,16 +54,16 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
         const uint32_t k = f - rr * a.cpr;
         uint32_t i, lc;
         walk_row(a, row0 + rr, i, lc);
-        u32x4 *d = reinterpret_cast<u32x4 *>(dev_row(a, i, lc)) + k;
-        u32x4 *h = reinterpret_cast<u32x4 *>(host_row(a, i, lc)) + k;
-        const u32x4 *src = kToHost ? d : h;
+        chunk_t *d = reinterpret_cast<chunk_t *>(dev_row(a, i, lc)) + k;
+        chunk_t *h = reinterpret_cast<chunk_t *>(host_row(a, i, lc)) + k;
+        const chunk_t *src = kToHost ? d : h;
         dst[u] = kToHost ? h : d;
         v[u] = __builtin_nontemporal_load(src);
       }
     }
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++)
-      if (dst[u]) __builtin_nontemporal_store(v[u], dst[u]);
+      if (dst[u]) *dst[u] = v[u];
   }
 }
 
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
 // host order is position-major for page_first and pair-major otherwise.
 template <bool kToHost>
 __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileArgs ta) {
-  extern __shared__ u32x4 lds[];
+  extern __shared__ chunk_t lds[];
   const Tile t = tile_of(a, ta, blockIdx.x);
   const uint32_t cpr = a.cpr;
   const uint32_t nchunks = t.nt * t.nl * cpr;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
   // phase 1: source -> LDS, in source order
   const bool src_pos_major = kToHost ? false : host_pos_major;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
-    u32x4 v[kXferUnroll];
+    chunk_t v[kXferUnroll];
     uint32_t slot[kXferUnroll];
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
@@ -90,7 +92,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
         uint32_t lc_t, p_t, k;
         tile_walk(t, cpr, src_pos_major, f, lc_t, p_t, k);
         const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(kToHost ? dev_row(a, i, lc)
+        const chunk_t *src = reinterpret_cast<const chunk_t *>(kToHost ? dev_row(a, i, lc)
                                                                     : host_row(a, i, lc)) + k;
         v[u] = __builtin_nontemporal_load(src);
         slot[u] = tile_slot(t, cpr, lc_t, p_t, k);
@@ -112,8 +114,8 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
         uint32_t lc_t, p_t, k;
         tile_walk(t, cpr, dst_pos_major, f, lc_t, p_t, k);
         const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
-        u32x4 *dst = reinterpret_cast<u32x4 *>(kToHost ? host_row(a, i, lc) : dev_row(a, i, lc)) + k;
-        __builtin_nontemporal_store(lds[tile_slot(t, cpr, lc_t, p_t, k)], dst);
+        chunk_t *dst = reinterpret_cast<chunk_t *>(kToHost ? host_row(a, i, lc) : dev_row(a, i, lc)) + k;
+        *dst = lds[tile_slot(t, cpr, lc_t, p_t, k)];
       }
     }
   }

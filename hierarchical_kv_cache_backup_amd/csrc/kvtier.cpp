@@ -29,7 +29,7 @@ void set_error(const std::string &msg) { g_err = msg; }
 
 namespace {
 
-constexpr int kStagingSlots = 4;  // index-staging buffers in flight per direction
+constexpr int kStagingSlots = 16;  // index-staging buffers in flight per direction
 constexpr int64_t kMaxRowsPerLaunch = (int64_t)1 << 31;
 
 int fail(int code, const std::string &msg) {
@@ -72,12 +72,13 @@ struct DirState {
   std::vector<Run> runs;
   std::vector<Copy> copies;
   Staging slots[kStagingSlots];
-  int next = 0;
+  int used = 0;  // slots opened so far
+  int next = 0;  // where the search for a free slot starts
   hipEvent_t done = nullptr;  // recorded at the end of every call of this direction
   bool done_pending = false;
   std::atomic<int32_t> last_path{-1};
   int64_t calls = 0, bytes = 0, launches = 0, dma = 0;
-  double submit_us = 0;
+  double submit_us = 0, blocked_us = 0;
 };
 
 }  // namespace
@@ -141,6 +142,12 @@ bool numa_node_exists(int node) {
   return access(path, F_OK) == 0;
 }
 
+double now_us() {
+  return std::chrono::duration<double, std::micro>(
+             std::chrono::steady_clock::now().time_since_epoch())
+      .count();
+}
+
 void free_staging(Staging &s) {
   if (s.pinned) (void)hipHostFree(s.pinned);
   if (s.dev) (void)hipFree(s.dev);
@@ -167,16 +174,38 @@ hipError_t drain_direction(DirState &d) {
   return first;
 }
 
-// Next staging slot with room for n positions. Blocks only when all slots
-// still carry work in flight (back-pressure after kStagingSlots calls).
-int acquire_staging(DirState &d, int64_t n, Staging **out) {
-  Staging &s = d.slots[d.next];
-  d.next = (d.next + 1) % kStagingSlots;
-  if (s.pending) {
+// A staging slot with room for n positions. Prefers a slot whose previous
+// use has completed (no wait); opens a new slot while fewer than
+// kStagingSlots exist; only when every slot still carries work in flight does
+// it wait for the oldest (back-pressure), adding the wait to *blocked_us.
+int acquire_staging(DirState &d, int64_t n, Staging **out, double *blocked_us) {
+  Staging *pick = nullptr;
+  for (int k = 0; k < d.used && !pick; k++) {
+    Staging &s = d.slots[(d.next + k) % d.used];
+    if (!s.pending) {
+      pick = &s;
+    } else {
+      hipError_t q = hipEventQuery(s.ev);
+      if (q == hipSuccess) {
+        s.pending = false;
+        pick = &s;
+      } else if (q != hipErrorNotReady) {
+        return hip_fail(q, "index staging event");
+      }
+    }
+  }
+  if (!pick && d.used < kStagingSlots) pick = &d.slots[d.used++];
+  if (!pick) {
+    Staging &s = d.slots[d.next % d.used];
+    const double t0 = now_us();
     hipError_t e = hipEventSynchronize(s.ev);
+    *blocked_us += now_us() - t0;
     s.pending = false;
     if (e != hipSuccess) return hip_fail(e, "waiting for an index staging buffer");
+    pick = &s;
   }
+  d.next = (int)(pick - d.slots) + 1;
+  Staging &s = *pick;
   if (s.cap < n) {
     free_staging(s);
     int64_t cap = 1024;
@@ -196,12 +225,6 @@ int acquire_staging(DirState &d, int64_t n, Staging **out) {
   }
   *out = &s;
   return KV_OK;
-}
-
-double now_us() {
-  return std::chrono::duration<double, std::micro>(
-             std::chrono::steady_clock::now().time_since_epoch())
-      .count();
 }
 
 // ---- copy-engine executor ------------------------------------------------
@@ -241,6 +264,7 @@ hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_
 static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
                     int64_t n, int32_t l0, int32_t l1, void *stream) {
   const double t0 = now_us();
+  double blocked = 0;
   if (!p) return fail(KV_EINVAL, "pool is null");
   DirState &d = p->dir[dir];
   std::lock_guard<std::mutex> lock(d.mu);
@@ -302,7 +326,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     d.dma += (int64_t)d.copies.size() * nlc_all;
   } else {
     Staging *st = nullptr;
-    rc = acquire_staging(d, n, &st);
+    rc = acquire_staging(d, n, &st, &blocked);
     if (rc) return rc;
     int64_t *tok = st->pinned;
     for (int64_t i = 0; i < n; i++) {
@@ -361,7 +385,8 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   d.last_path.store(path);
   d.calls++;
   d.bytes += bytes;
-  d.submit_us += now_us() - t0;
+  d.blocked_us += blocked;
+  d.submit_us += now_us() - t0 - blocked;
   return KV_OK;
 }
 
@@ -571,6 +596,7 @@ int kv_get_stats(const kv_pool_t *p, kv_stats_t *out) {
     out->kernel_launches[d] = s.launches;
     out->dma_copies[d] = s.dma;
     out->submit_us[d] = s.submit_us;
+    out->blocked_us[d] = s.blocked_us;
   }
   return KV_OK;
 }

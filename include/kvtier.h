@@ -255,7 +255,9 @@ typedef struct {
   int64_t bytes[2];         /* algorithmic bytes enqueued */
   int64_t kernel_launches[2];
   int64_t dma_copies[2];    /* copy-engine calls issued */
-  double submit_us[2];      /* host wall time spent inside the calls */
+  double submit_us[2];      /* host wall time spent inside the calls, minus blocked_us */
+  double blocked_us[2];     /* host time spent waiting for an index staging buffer
+                               (only when 16 calls of one direction are in flight) */
 } kv_stats_t;
 
 int kv_get_stats(const kv_pool_t *pool, kv_stats_t *out);

@@ -8,7 +8,7 @@
 //     over all layers and for per-layer launches;
 //   * every tile, phase and LDS slot of the LDS-staged kernel;
 //   * every copy of the copy-engine plan (runs merged into 2-D copies);
-// and checks that each 16-byte chunk of each row is moved exactly once, that
+// and checks that each chunk of each row is moved exactly once, that
 // every address and LDS slot stays in bounds, and that the resulting bytes equal
 // the oracle's. It also checks the segment counter against the oracle's.
 #include <algorithm>
@@ -94,16 +94,16 @@ static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, i
           CHECK(i < a.n && lc < a.nlc, "walk out of range i=%u lc=%u", i, lc);
           if (!(i < a.n && lc < a.nlc)) return;
           const int64_t dslot = tok[2 * i], key = tok[2 * i + 1];
-          const int64_t dev_off = dslot * g.R + 16 * (int64_t)k;
-          const int64_t host_off = ((int64_t)(a.lc0 + lc) * a.lc_stride + key) * g.R + 16 * (int64_t)k;
-          CHECK(dev_off >= 0 && dev_off + 16 <= g.S_dev * g.R, "device offset out of bounds");
-          CHECK(host_off >= 0 && host_off + 16 <= (int64_t)m.host.size(), "host offset out of bounds");
+          const int64_t dev_off = dslot * g.R + kChunkBytes * (int64_t)k;
+          const int64_t host_off = ((int64_t)(a.lc0 + lc) * a.lc_stride + key) * g.R + kChunkBytes * (int64_t)k;
+          CHECK(dev_off >= 0 && dev_off + kChunkBytes <= g.S_dev * g.R, "device offset out of bounds");
+          CHECK(host_off >= 0 && host_off + kChunkBytes <= (int64_t)m.host.size(), "host offset out of bounds");
           uint8_t *d = m.dev[a.lc0 + lc].data() + dev_off;
           uint8_t *h = m.host.data() + host_off;
           if (to_host)
-            std::memcpy(h, d, 16);
+            std::memcpy(h, d, kChunkBytes);
           else
-            std::memcpy(d, h, 16);
+            std::memcpy(d, h, kChunkBytes);
           const int64_t cell = ((int64_t)i * g.L * g.C + a.lc0 + lc) * a.cpr + k;
           cover[cell]++;
         }
@@ -137,19 +137,19 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
         uint32_t lc_t = 0, p_t = 0, k = 0;
         tile_walk(t, a.cpr, pos_major, f, lc_t, p_t, k);
         const uint32_t slot = tile_slot(t, a.cpr, lc_t, p_t, k);
-        CHECK((size_t)slot * 16 + 16 <= lds_bytes, "LDS slot out of bounds");
+        CHECK((size_t)slot * kChunkBytes + kChunkBytes <= lds_bytes, "LDS slot out of bounds");
         const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
-        const int64_t dev_off = tok[2 * i] * g.R + 16 * (int64_t)k;
+        const int64_t dev_off = tok[2 * i] * g.R + kChunkBytes * (int64_t)k;
         const int64_t host_off =
-            ((int64_t)(a.lc0 + lc) * a.lc_stride + tok[2 * i + 1]) * g.R + 16 * (int64_t)k;
-        CHECK(host_off >= 0 && host_off + 16 <= (int64_t)m.host.size(), "host offset OOB");
+            ((int64_t)(a.lc0 + lc) * a.lc_stride + tok[2 * i + 1]) * g.R + kChunkBytes * (int64_t)k;
+        CHECK(host_off >= 0 && host_off + kChunkBytes <= (int64_t)m.host.size(), "host offset OOB");
         uint8_t *d = m.dev[a.lc0 + lc].data() + dev_off;
         uint8_t *h = m.host.data() + host_off;
-        uint8_t *s = lds.data() + (size_t)slot * 16;
+        uint8_t *s = lds.data() + (size_t)slot * kChunkBytes;
         if (phase == 0) {
-          std::memcpy(s, to_host ? d : h, 16);
+          std::memcpy(s, to_host ? d : h, kChunkBytes);
         } else {
-          std::memcpy(to_host ? h : d, s, 16);
+          std::memcpy(to_host ? h : d, s, kChunkBytes);
           cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * a.cpr + k]++;
         }
       }
@@ -267,7 +267,7 @@ int main(int argc, char **argv) {
       tok[2 * i] = d[i];
       tok[2 * i + 1] = host_key(g, h[i]);
     }
-    const int64_t cells = n * g.L * g.C * (g.R / 16);
+    const int64_t cells = n * g.L * g.C * (g.R / kChunkBytes);
     for (int dir = 0; dir < 2; dir++) {
       const bool to_host = dir == 0;
       const Mirror &want = to_host ? want_b : want_l;
@@ -294,9 +294,9 @@ int main(int argc, char **argv) {
         if (variant != 3) {
           for (int64_t i = 0; i < n; i++)
             for (int32_t lc = 0; lc < g.L * g.C; lc++)
-              for (int64_t k = 0; k < g.R / 16; k++) {
+              for (int64_t k = 0; k < g.R / kChunkBytes; k++) {
                 const bool inside = lc >= l0 * g.C && lc < l1 * g.C;
-                const uint8_t cnt = cover[(size_t)((i * g.L * g.C + lc) * (g.R / 16) + k)];
+                const uint8_t cnt = cover[(size_t)((i * g.L * g.C + lc) * (g.R / kChunkBytes) + k)];
                 CHECK(cnt == (inside ? 1 : 0), "chunk moved %d times (variant %d)", cnt, variant);
               }
         }
