@@ -42,6 +42,8 @@ def parse():
     p.add_argument("--path", default="auto", choices=["auto", "kernel", "kernel_lds", "dma"])
     p.add_argument("--no-matrix", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the bidirectional mixed-batch and per-layer streamed legs")
     p.add_argument("--matrix-reps", type=int, default=5)
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
@@ -210,6 +212,14 @@ def main():
         matrix = layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args)
 
     pool.close()
+    del bufs
+    torch.cuda.empty_cache()
+    extra = {}
+    if not args.no_extra:
+        extra["bidirectional_mixed"] = leg_bidirectional(torch, kvt, workloads, args)
+        torch.cuda.empty_cache()
+        extra["streamed_per_layer"] = leg_streamed(torch, kvt, workloads, args)
+        torch.cuda.empty_cache()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape)
@@ -246,6 +256,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "matrix": matrix,
+        "extra": extra,
     }
     print(json.dumps(out), flush=True)
 
@@ -427,6 +438,222 @@ def layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak,
                 log("matrix %s" % json.dumps(cell))
                 rows.append(cell)
     return rows
+
+
+def _ev(torch):
+    return torch.cuda.Event(enable_timing=True)
+
+
+def _bidirectional_copy_peak(torch):
+    """Concurrent 1 GiB H2D and 1 GiB D2H copy-engine copies on two streams."""
+    GiB = 1 << 30
+    d1 = torch.empty(GiB, dtype=torch.uint8, device="cuda:0")
+    d2 = torch.empty(GiB, dtype=torch.uint8, device="cuda:0")
+    h1 = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    h2 = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    best = 0.0
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(sa):
+            d1.copy_(h1, non_blocking=True)
+        with torch.cuda.stream(sb):
+            h2.copy_(d2, non_blocking=True)
+        torch.cuda.synchronize()
+        best = max(best, 2 * GiB / (time.perf_counter() - t0) / 1e9)
+    return best
+
+
+def leg_bidirectional(torch, kvt, workloads, args):
+    """Mixed batch: 64 requests, lognormal lengths (median 4096, sigma 1.0, max
+    32768), 32 layers x K/V x 2048 B rows, page 64. The L2 hits (82% of each
+    request, whole pages) load H2D on one stream from one caller thread while
+    the new pages write back D2H on another stream from a second thread."""
+    import threading
+    shape = workloads.mixed()
+    plan = workloads.mixed_plan(shape, 4)
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S = plan["device_slots"]
+    h_dev, h_host = plan["h2d"]
+    w_dev, w_host = plan["d2h"]
+    t0 = time.perf_counter()
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, 4, l, c, torch)
+            bufs.append(b)
+    pool = kvt.KvPool(kvt.geometry(L, C, R, S, plan["host_slots"], ps, 0), bufs)
+    s_load, s_back = torch.cuda.Stream(), torch.cuda.Stream()
+    pool.backup(h_dev, h_host, 0, L, s_back)          # L2 holds the hits
+    s_back.synchronize()
+    log("bidirectional: setup %.1fs, %d requests, %.1f GB H2D, %.1f GB D2H" %
+        (time.perf_counter() - t0, plan["lens"].size, h_dev.size * L * C * R / 1e9,
+         w_dev.size * L * C * R / 1e9))
+    hb = h_dev.size * L * C * R
+    wb = w_dev.size * L * C * R
+
+    def alone(fn, s):
+        fn()
+        s.synchronize()
+        e0, e1 = _ev(torch), _ev(torch)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    load = lambda: pool.load(h_dev, h_host, 0, L, s_load)
+    back = lambda: pool.backup(w_dev, w_host, 0, L, s_back)
+    t_load = alone(load, s_load)
+    t_back = alone(back, s_back)
+    walls, h_rates, d_rates = [], [], []
+    for rep in range(1 + 3):
+        go = threading.Barrier(3)
+        ev = [_ev(torch) for _ in range(4)]
+
+        def run_load():
+            go.wait()
+            ev[0].record(s_load)
+            load()
+            ev[1].record(s_load)
+
+        def run_back():
+            go.wait()
+            ev[2].record(s_back)
+            back()
+            ev[3].record(s_back)
+
+        th = [threading.Thread(target=run_load), threading.Thread(target=run_back)]
+        for x in th:
+            x.start()
+        torch.cuda.synchronize()
+        go.wait()
+        t1 = time.perf_counter()
+        for x in th:
+            x.join()
+        s_load.synchronize()
+        s_back.synchronize()
+        wall = time.perf_counter() - t1
+        if rep == 0:
+            continue
+        walls.append(wall)
+        h_rates.append(hb / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
+        d_rates.append(wb / (ev[2].elapsed_time(ev[3]) / 1e3) / 1e9)
+    pool.close()
+    del bufs
+    torch.cuda.empty_cache()
+    peak = _bidirectional_copy_peak(torch)
+    wall = statistics.median(walls)
+    agg = (hb + wb) / wall / 1e9
+    out = {"workload": "64 requests, lognormal lengths (median 4096, sigma 1.0), 32 layers x "
+                       "K/V x 2048 B, page 64, hits 0.82 H2D || new D2H, two threads",
+           "tokens": int(S), "h2d_bytes": int(hb), "d2h_bytes": int(wb),
+           "h2d_alone_gbps": round(hb / t_load / 1e9, 3),
+           "d2h_alone_gbps": round(wb / t_back / 1e9, 3),
+           "h2d_concurrent_gbps": round(statistics.median(h_rates), 3),
+           "d2h_concurrent_gbps": round(statistics.median(d_rates), 3),
+           "aggregate_gbps": round(agg, 3),
+           "bidirectional_copy_peak_gbps": round(peak, 3),
+           "pct_of_bidirectional_peak": round(100 * agg / peak, 1),
+           "path": kvt.PATH_NAMES[kvt.PATH_AUTO]}
+    log("bidirectional %s" % json.dumps(out))
+    return out
+
+
+def leg_streamed(torch, kvt, workloads, args):
+    """Per-layer streamed load: 61 layers x K/V x 1024 B fp8 rows, 131072-token
+    prefix (256 MiB per layer). Layer l+1 loads on a side stream while a
+    synthetic HBM-bound consumer reads layer l's whole K and V buffers on the
+    compute stream, after kv_load_layer(l). The consumer repeats its pass k times
+    so that its time per layer matches the transfer's."""
+    shape = workloads.streamed()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S, n = shape.device_slots, shape.extra["tokens"]
+    dev_idx, host_idx = workloads.prefix_indices(shape, 5, n, fragmented=False)
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, 5, l, c, torch)
+            bufs.append(b)
+    pool = kvt.KvPool(kvt.geometry(L, C, R, S, shape.host_slots, ps, 0), bufs)
+    s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
+    pool.backup(dev_idx, host_idx, 0, L, s_load)
+    s_load.synchronize()
+    layer_bytes = n * C * R
+    acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+
+    def consume(l, k):
+        for _ in range(k):
+            for c in range(C):
+                acc.add_(bufs[l * C + c].view(torch.int64).sum())
+
+    # one consumer pass over a layer (both buffers), alone
+    with torch.cuda.stream(s_comp):
+        consume(0, 2)
+        s_comp.synchronize()
+        e0, e1 = _ev(torch), _ev(torch)
+        e0.record(s_comp)
+        consume(0, 10)
+        e1.record(s_comp)
+        e1.synchronize()
+    t_pass = e0.elapsed_time(e1) / 1e3 / 10
+    results = {}
+    for pname, p in (("kernel", kvt.PATH_KERNEL), ("dma", kvt.PATH_DMA)):
+        pool.set_path(p)
+        pool.load(dev_idx, host_idx, 0, L, s_load)
+        s_load.synchronize()
+        e0, e1 = _ev(torch), _ev(torch)
+        e0.record(s_load)
+        pool.load(dev_idx, host_idx, 0, L, s_load)
+        e1.record(s_load)
+        e1.synchronize()
+        t_h2d = e0.elapsed_time(e1) / 1e3
+        k = max(1, round(t_h2d / L / t_pass))
+        with torch.cuda.stream(s_comp):
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s_comp)
+            for l in range(L):
+                consume(l, k)
+            e1.record(s_comp)
+            e1.synchronize()
+        t_comp = e0.elapsed_time(e1) / 1e3
+        walls, h2d_ov = [], []
+        for rep in range(3):
+            torch.cuda.synchronize()
+            ev = [_ev(torch) for _ in range(3)]
+            ev[0].record(s_load)
+            s_comp.wait_event(ev[0])
+            pool.load(dev_idx, host_idx, 0, L, s_load)
+            ev[1].record(s_load)
+            with torch.cuda.stream(s_comp):
+                for l in range(L):
+                    pool.load_layer(l, s_comp)
+                    consume(l, k)
+                ev[2].record(s_comp)
+            ev[2].synchronize()
+            s_load.synchronize()
+            walls.append(ev[0].elapsed_time(ev[2]) / 1e3)
+            h2d_ov.append(L * layer_bytes / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
+        wall = statistics.median(walls)
+        eta = (t_h2d + t_comp - wall) / min(t_h2d, t_comp)
+        results[pname] = {"h2d_alone_gbps": round(L * layer_bytes / t_h2d / 1e9, 3),
+                          "h2d_overlapped_gbps": round(statistics.median(h2d_ov), 3),
+                          "compute_reps_per_layer": k,
+                          "sum_h2d_ms": round(t_h2d * 1e3, 2),
+                          "sum_compute_ms": round(t_comp * 1e3, 2),
+                          "wall_ms": round(wall * 1e3, 2),
+                          "overlap_efficiency": round(eta, 3)}
+        log("streamed %s %s" % (pname, json.dumps(results[pname])))
+    pool.close()
+    del bufs
+    torch.cuda.empty_cache()
+    return {"workload": "61 layers x K/V x 1024 B (fp8 random bytes), 131072-token prefix, "
+                        "per-layer H2D overlapped with an HBM-bound consumer",
+            "layer_bytes": layer_bytes, "consumer_pass_ms": round(t_pass * 1e3, 3),
+            "paths": results}
 
 
 def cpu_baseline(shape):

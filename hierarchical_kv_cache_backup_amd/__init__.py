@@ -45,7 +45,8 @@ class kv_pool_desc_t(ctypes.Structure):
 class kv_calib_t(ctypes.Structure):
     _fields_ = [("kernel_launch_us", ctypes.c_double * 2), ("kernel_gbps", ctypes.c_double * 2),
                 ("dma_copy_us", ctypes.c_double * 2), ("dma_gbps", ctypes.c_double * 2),
-                ("load_split_min_bytes", ctypes.c_double)]
+                ("load_split_min_bytes", ctypes.c_double),
+                ("kernel_max_workgroups", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):
@@ -261,7 +262,9 @@ class KvPool:
     def close(self):
         if getattr(self, "handle", None):
             h, self.handle = self.handle, None
-            _check(kv_pool_destroy(h))
+            rc = kv_pool_destroy(h)
+            self.tensors = []
+            _check(rc)
 
     def __del__(self):
         try:

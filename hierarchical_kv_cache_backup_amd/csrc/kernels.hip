@@ -39,7 +39,8 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
 // host-order walk; lanes take consecutive chunks of those rows.
 template <bool kToHost>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
-  const uint32_t row0 = blockIdx.x * a.rows_per_block;
+  for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
+  const uint32_t row0 = blk * a.rows_per_block;
   const uint32_t nrows = min(a.rows_per_block, a.total_rows - row0);
   const uint32_t nchunks = nrows * a.cpr;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
@@ -65,6 +66,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
     for (int u = 0; u < kXferUnroll; u++)
       if (dst[u]) *dst[u] = v[u];
   }
+  }
 }
 
 // LDS-staged path: a workgroup owns a tile of nt positions x nl pairs. It reads
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
 template <bool kToHost>
 __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileArgs ta) {
   extern __shared__ chunk_t lds[];
-  const Tile t = tile_of(a, ta, blockIdx.x);
+  for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
+  const Tile t = tile_of(a, ta, blk);
   const uint32_t cpr = a.cpr;
   const uint32_t nchunks = t.nt * t.nl * cpr;
   const bool host_pos_major = ta.token_major != 0;
@@ -119,9 +122,12 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
       }
     }
   }
+  __syncthreads();  // the next tile reuses the LDS
+  }
 }
 
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
   if (to_host)
     hipLaunchKernelGGL(xfer_rows<true>, dim3(blocks), dim3(kXferThreads), 0, s, a);
   else
@@ -129,9 +135,10 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, bool to_host, hipStream_t s) {
+hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t blocks, bool to_host,
+                            hipStream_t s) {
   const size_t lds = (size_t)t.tile_t * t.tile_lc * a.R;
-  const uint32_t blocks = t.tiles_t * t.tiles_lc;
+  if (blocks == 0) return hipSuccess;
   if (to_host)
     hipLaunchKernelGGL(xfer_tiles_lds<true>, dim3(blocks), dim3(kXferThreads), lds, s, a, t);
   else

@@ -7,7 +7,10 @@
 
 namespace kvt {
 
+// `blocks` is the number of workgroups to launch; the kernels stride over
+// a.nblocks blocks of work (plan_rows / plan_tiles), so blocks may be smaller.
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s);
-hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, bool to_host, hipStream_t s);
+hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t blocks, bool to_host,
+                            hipStream_t s);
 
 }  // namespace kvt

@@ -116,6 +116,7 @@ void default_calibration(kv_calib_t *c) {
     c->dma_gbps[d] = 55.0;
   }
   c->load_split_min_bytes = 4.0 * 1024 * 1024;
+  c->kernel_max_workgroups[0] = c->kernel_max_workgroups[1] = 0;
 }
 
 // Sets the calling thread's memory policy to bind to `node` (Linux mbind
@@ -347,16 +348,17 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       XferArgs b = a;
       b.lc0 = (uint32_t)(la * g.C);
       b.nlc = (uint32_t)((lb - la) * g.C);
+      const uint32_t cap = (uint32_t)c.kernel_max_workgroups[dir];
       if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
         TileArgs t{};
-        plan_tiles(b, g.layout, &t);
+        b.nblocks = plan_tiles(b, g.layout, &t);
         d.launches++;
-        return launch_tiles_lds(b, t, dir == 0, s);
+        return launch_tiles_lds(b, t, grid_for(b.nblocks, cap), dir == 0, s);
       }
       const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
       d.launches++;
-      return launch_rows(b, blocks, dir == 0, s);
+      return launch_rows(b, grid_for(blocks, cap), dir == 0, s);
     };
     if (per_layer) {
       for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
@@ -574,6 +576,9 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
         !(c->dma_copy_us[d] >= 0))
       return fail(KV_EINVAL, "calibration figures must be positive");
   if (!(c->load_split_min_bytes >= 0)) return fail(KV_EINVAL, "load_split_min_bytes must be >= 0");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_max_workgroups[d] >= 0) || c->kernel_max_workgroups[d] > 4294967295.0)
+      return fail(KV_EINVAL, "kernel_max_workgroups must be in [0, 2^32)");
   std::lock_guard<std::mutex> lock(p->calib_mu);
   p->calib = *c;
   return KV_OK;

@@ -29,6 +29,7 @@ struct XferArgs {
   uint32_t rows_per_block;  // rows one workgroup moves
   uint32_t rows_full;       // rows in complete groups (n / G * G * nlc)
   uint32_t total_rows;      // n * nlc  (< 2^31)
+  uint32_t nblocks;         // row blocks (or LDS tiles); workgroups stride over them
 };
 
 // Tiling of the LDS-staged variant: a workgroup owns tile_t request positions x
@@ -63,7 +64,15 @@ constexpr uint32_t plan_rows(XferArgs *a, int32_t layout, int32_t page_size) {
   a->rows_per_block = a->cpr >= kChunksPerBlock ? 1u : kChunksPerBlock / a->cpr;
   a->total_rows = a->n * a->nlc;
   a->rows_full = (a->n / a->G) * a->G * a->nlc;
-  return (a->total_rows + a->rows_per_block - 1) / a->rows_per_block;
+  a->nblocks = (a->total_rows + a->rows_per_block - 1) / a->rows_per_block;
+  return a->nblocks;
+}
+
+// Workgroups to launch for `blocks` blocks of work under a cap (0 = no cap):
+// the kernels stride over the blocks, so a capped grid leaves CUs free for
+// work on other streams while the host link stays full.
+constexpr uint32_t grid_for(uint32_t blocks, uint32_t cap) {
+  return (cap == 0 || blocks < cap) ? blocks : cap;
 }
 
 // Tile shape of the LDS variant (needs R <= kMaxLdsRowBytes); returns the

@@ -131,13 +131,18 @@ typedef struct {
  * load_split_min_bytes: kv_load issues one kernel per layer (so each layer's
  * event fires as soon as that layer has landed) when one layer of the request
  * holds at least this many bytes; below it, one kernel covers all layers and
- * every layer's event is recorded after it. */
+ * every layer's event is recorded after it.
+ * kernel_max_workgroups: cap on the workgroups one transfer kernel launches
+ * (0 = one per block of work). The kernels stride over their work, so a cap
+ * moves the same bytes while leaving compute units free for kernels on other
+ * streams (e.g. the layer that was just loaded). */
 typedef struct {
   double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
   double kernel_gbps[2];
   double dma_copy_us[2];
   double dma_gbps[2];
   double load_split_min_bytes;
+  double kernel_max_workgroups[2];
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

@@ -68,7 +68,7 @@ struct Mirror {
 
 // Replays one launch of xfer_rows on the mirrors. tok holds {dev slot, host key}.
 static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, int32_t la,
-                        int32_t lb, bool to_host, std::vector<uint8_t> &cover) {
+                        int32_t lb, bool to_host, std::vector<uint8_t> &cover, uint32_t cap) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -79,7 +79,11 @@ static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, i
   const uint32_t blocks = plan_rows(&a, g.layout, g.ps);
   CHECK((uint64_t)blocks * a.rows_per_block >= a.total_rows, "grid too small");
   CHECK(blocks == 0 || (uint64_t)(blocks - 1) * a.rows_per_block < a.total_rows, "idle block");
-  for (uint32_t b = 0; b < blocks; b++) {
+  CHECK(a.nblocks == blocks, "nblocks");
+  const uint32_t grid = grid_for(blocks, cap);
+  CHECK(grid >= 1 && grid <= blocks, "grid %u for %u blocks", grid, blocks);
+  for (uint32_t wg = 0; wg < grid; wg++)
+  for (uint32_t b = wg; b < a.nblocks; b += grid) {
     const uint32_t row0 = b * a.rows_per_block;
     const uint32_t nrows = umin(a.rows_per_block, a.total_rows - row0);
     const uint32_t nchunks = nrows * a.cpr;
@@ -112,7 +116,7 @@ static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, i
 
 // Replays one launch of xfer_tiles_lds.
 static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, int32_t la,
-                         int32_t lb, bool to_host, std::vector<uint8_t> &cover) {
+                         int32_t lb, bool to_host, std::vector<uint8_t> &cover, uint32_t cap) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -122,11 +126,13 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
   a.nlc = (uint32_t)((lb - la) * g.C);
   plan_rows(&a, g.layout, g.ps);
   TileArgs ta{};
-  const uint32_t blocks = plan_tiles(a, g.layout, &ta);
+  a.nblocks = plan_tiles(a, g.layout, &ta);
   const size_t lds_bytes = (size_t)ta.tile_t * ta.tile_lc * g.R;
   CHECK(lds_bytes <= 64 * 1024, "LDS tile of %zu bytes exceeds 64 KiB", lds_bytes);
   std::vector<uint8_t> lds(lds_bytes);
-  for (uint32_t b = 0; b < blocks; b++) {
+  const uint32_t grid = grid_for(a.nblocks, cap);
+  for (uint32_t wg = 0; wg < grid; wg++)
+  for (uint32_t b = wg; b < a.nblocks; b += grid) {
     const Tile t = tile_of(a, ta, b);
     CHECK(t.nt >= 1 && t.nl >= 1 && t.i0 + t.nt <= a.n && t.lcf + t.nl <= a.nlc, "bad tile");
     const uint32_t nchunks = t.nt * t.nl * a.cpr;
@@ -277,12 +283,13 @@ int main(int argc, char **argv) {
         Mirror m = base;
         std::vector<uint8_t> cover((size_t)cells, 0);
         int64_t copies = 0;
+        const uint32_t cap = (uint32_t)(std::vector<int>{0, 1, 3, 64})[uni(0, 3)];
         if (variant == 0) {
-          replay_rows(m, tok, n, l0, l1, to_host, cover);
+          replay_rows(m, tok, n, l0, l1, to_host, cover, cap);
         } else if (variant == 1) {
-          for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover);
+          for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover, cap);
         } else if (variant == 2) {
-          replay_tiles(m, tok, n, l0, l1, to_host, cover);
+          replay_tiles(m, tok, n, l0, l1, to_host, cover, cap);
         } else {
           replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
           int64_t counted = -1;

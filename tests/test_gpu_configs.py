@@ -1,0 +1,259 @@
+"""GPU parity at the full workload sizes, through the C ABI.
+
+Each workload runs in the launch configuration bench.py times. Full pools are
+too large to mirror on the host in every case, so the oracle computes sampled
+outputs: whole layers on compacted mirrors (the device rows a request touches,
+gathered by torch), or rows addressed one by one through the oracle's host-row
+map. Properties that hold at any size are checked on every buffer: device rows
+outside the request are untouched (sum over them unchanged), host slots outside
+the request keep the sentinel.
+"""
+import threading
+
+import numpy as np
+import pytest
+
+import hierarchical_kv_cache_backup_amd as kvt
+from hierarchical_kv_cache_backup_amd import workloads
+import oracle
+from oracle import Geometry
+
+from gpu_util import SENTINEL, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    t = torch_mod()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def make_bufs(torch, shape, cfg, S_dev):
+    bufs = []
+    for l in range(shape.layers):
+        for c in range(shape.components):
+            b = torch.empty(S_dev * shape.row_bytes, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, cfg, l, c, torch)
+            bufs.append(b)
+    return bufs
+
+
+def release(torch):
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def rows_of(torch, buf, R, idx):
+    """Device rows `idx` of one buffer, as a host numpy array (n, R)."""
+    t = torch.from_numpy(np.asarray(idx, dtype=np.int64)).cuda()
+    return buf.view(-1, R).index_select(0, t).cpu().numpy()
+
+
+def untouched_sum(torch, buf, R, idx):
+    mask = torch.ones(buf.numel() // R, dtype=torch.bool, device=buf.device)
+    mask[torch.from_numpy(np.asarray(idx, dtype=np.int64)).cuda()] = False
+    return int(buf.view(-1, R)[mask].to(torch.int64).sum())
+
+
+def check_backup_layers(torch, g, pool, bufs, dev_idx, host_idx, layers, samples=2048):
+    """Host rows written by a backup, for the given layers: a sample of positions,
+    each row addressed through the oracle's host-row map and compared with the
+    device row it must hold."""
+    n = len(dev_idx)
+    host = pool.host_array()
+    for l in layers:
+        pick = np.random.default_rng(l).choice(n, size=min(n, samples), replace=False)
+        for c in range(g.C):
+            m = rows_of(torch, bufs[l * g.C + c], g.R, np.asarray(dev_idx)[pick])
+            for j, i in enumerate(pick):
+                r = oracle.host_row(g, l, c, int(host_idx[i]))
+                assert np.array_equal(host[r * g.R:(r + 1) * g.R], m[j]), (l, c, int(i))
+
+
+def fill_host_random(torch, pool, seed):
+    """Seeded random bytes into the host pool, made on the device in 1 GiB pieces
+    and copied through a CPU tensor aliasing the pinned pool."""
+    host = torch.from_numpy(pool.host_array())
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(seed)
+    piece = 1 << 30
+    for off in range(0, host.numel(), piece):
+        m = min(piece, host.numel() - off)
+        host[off:off + m].copy_(torch.empty(m, dtype=torch.uint8, device="cuda:0")
+                                .random_(0, 256, generator=g))
+    torch.cuda.synchronize()
+
+
+def check_load_layers(torch, g, pool, bufs, dev_idx, host_idx, layers):
+    """Device rows written by a load, for the given layers, against the oracle run
+    on compacted mirrors reading the live host pool."""
+    n = len(dev_idx)
+    host = pool.host_array()
+    gl = g.replace(S_dev=n)
+    for l in layers:
+        mirrors = [np.zeros(0, np.uint8)] * (g.L * g.C)
+        for c in range(g.C):
+            mirrors[l * g.C + c] = np.zeros(n * g.R, np.uint8)
+        assert oracle.load(gl, mirrors, host, np.arange(n), host_idx, l, l + 1) == 0
+        for c in range(g.C):
+            got = rows_of(torch, bufs[l * g.C + c], g.R, dev_idx)
+            want = mirrors[l * g.C + c].reshape(n, g.R)
+            assert np.array_equal(got, want), (l, c)
+
+
+def sample_layers(L):
+    return sorted({0, L // 3, (2 * L) // 3, L - 1})
+
+
+# ---- llama8b: D2H of an 8192-token prefix from fragmented pages ------------------
+
+@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_DMA))
+def test_llama8b_fragmented_backup(torch, path):
+    shape = workloads.llama8b()
+    n = shape.extra["tokens"]
+    bufs = make_bufs(torch, shape, 2, shape.device_slots)
+    dev_idx, host_idx = workloads.prefix_indices(shape, 2, n, fragmented=True)
+    for layout in shape.layouts:
+        g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                     shape.host_slots, shape.page_size, layout)
+        print("llama8b layout=%d path=%d n=%d" % (layout, path, n), flush=True)
+        with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+            pool.set_path(path)
+            pool.host_array()[:] = SENTINEL
+            s = torch.cuda.Stream()
+            pool.backup(dev_idx, host_idx, 0, g.L, s)
+            s.synchronize()
+            # the whole host image: oracle on full compacted mirrors (8192 rows per buffer)
+            mirrors = [rows_of(torch, b, g.R, dev_idx).reshape(-1) for b in bufs]
+            want = np.full(g.host_bytes(), SENTINEL, np.uint8)
+            assert oracle.backup(g.replace(S_dev=n), mirrors, want, np.arange(n), host_idx) == 0
+            assert np.array_equal(pool.host_array(), want)
+    del bufs
+    release(torch)
+
+
+# ---- mla32k: H2D of a 32768-token prefix, page_first_direct vs layer_first -------
+
+@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA))
+@pytest.mark.timeout(300)
+def test_mla32k_load(torch, path):
+    shape = workloads.mla32k()
+    n = shape.extra["tokens"]
+    bufs = make_bufs(torch, shape, 3, shape.device_slots)
+    for fragmented in (False, True):
+        dev_idx, host_idx = workloads.prefix_indices(shape, 3, n, fragmented=fragmented)
+        before = [untouched_sum(torch, b, shape.row_bytes, dev_idx) for b in bufs]
+        for layout in shape.layouts:
+            g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                         shape.host_slots, shape.page_size, layout)
+            print("mla32k layout=%d path=%d fragmented=%d" % (layout, path, fragmented), flush=True)
+            with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+                pool.set_path(path)
+                fill_host_random(torch, pool, 30 + layout)
+                s = torch.cuda.Stream()
+                pool.load(dev_idx, host_idx, 0, g.L, s)
+                s.synchronize()
+                layers = range(g.L) if path == kvt.PATH_KERNEL else sample_layers(g.L)
+                check_load_layers(torch, g, pool, bufs, dev_idx, host_idx, layers)
+            after = [untouched_sum(torch, b, shape.row_bytes, dev_idx) for b in bufs]
+            assert after == before
+    del bufs
+    release(torch)
+
+
+# ---- mixed batch: H2D of L2 hits concurrent with D2H of new pages ---------------------
+
+@pytest.mark.timeout(400)
+def test_mixed_bidirectional(torch):
+    shape = workloads.mixed()
+    plan = workloads.mixed_plan(shape, 4)
+    S_dev, S_host = plan["device_slots"], plan["host_slots"]
+    h_dev, h_host = plan["h2d"]
+    w_dev, w_host = plan["d2h"]
+    print("mixed: %d tokens, %d hits, %d new" % (S_dev, h_dev.size, w_dev.size), flush=True)
+    bufs = make_bufs(torch, shape, 4, S_dev)
+    for layout in shape.layouts:
+        g = Geometry(shape.layers, shape.components, shape.row_bytes, S_dev, S_host,
+                     shape.page_size, layout)
+        with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+            pool.set_path(kvt.PATH_KERNEL)
+            s_load, s_back = torch.cuda.Stream(), torch.cuda.Stream()
+            # L2 holds the hit pages: write them back once, then scramble those device rows
+            pool.backup(h_dev, h_host, 0, g.L, s_back)
+            s_back.synchronize()
+            t = torch.from_numpy(h_dev).cuda()
+            for b in bufs:
+                b.view(-1, g.R)[t] = SENTINEL
+            torch.cuda.synchronize()
+            untouched = [untouched_sum(torch, b, g.R, np.concatenate([h_dev, w_dev])) for b in bufs]
+            go = threading.Barrier(2)
+            errors = []
+
+            def run(fn):
+                try:
+                    go.wait()
+                    fn()
+                except Exception as e:  # surfaced below
+                    errors.append(e)
+
+            th = [threading.Thread(target=run, args=(lambda: pool.load(h_dev, h_host, 0, g.L, s_load),)),
+                  threading.Thread(target=run, args=(lambda: pool.backup(w_dev, w_host, 0, g.L, s_back),))]
+            for x in th:
+                x.start()
+            for x in th:
+                x.join()
+            assert not errors, errors
+            s_load.synchronize()
+            s_back.synchronize()
+            print("mixed layout=%d concurrent done" % layout, flush=True)
+            layers = sample_layers(g.L)
+            check_load_layers(torch, g, pool, bufs, h_dev, h_host, layers)
+            check_backup_layers(torch, g, pool, bufs, w_dev, w_host, layers)
+            assert [untouched_sum(torch, b, g.R, np.concatenate([h_dev, w_dev])) for b in bufs] \
+                == untouched
+    del bufs
+    release(torch)
+
+
+# ---- streamed: per-layer H2D overlapped with a consumer on another stream ---------------
+
+@pytest.mark.timeout(300)
+def test_streamed_per_layer_events(torch):
+    shape = workloads.streamed()
+    n = shape.extra["tokens"]
+    bufs = make_bufs(torch, shape, 5, shape.device_slots)
+    dev_idx, host_idx = workloads.prefix_indices(shape, 5, n, fragmented=False)
+    t_idx = torch.from_numpy(dev_idx).cuda()
+    for layout in shape.layouts:
+        g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                     shape.host_slots, shape.page_size, layout)
+        print("streamed layout=%d" % layout, flush=True)
+        with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+            pool.set_path(kvt.PATH_KERNEL)
+            s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
+            # L2 content: written back from the device pool, then the device rows are cleared
+            pool.backup(dev_idx, host_idx, 0, g.L, s_load)
+            s_load.synchronize()
+            for b in bufs:
+                b.view(-1, g.R)[t_idx] = 0
+            torch.cuda.synchronize()
+            sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
+            pool.load(dev_idx, host_idx, 0, g.L, s_load)
+            with torch.cuda.stream(s_comp):
+                for l in range(g.L):
+                    pool.load_layer(l, s_comp)
+                    for c in range(g.C):
+                        rows = bufs[l * g.C + c].view(-1, g.R).index_select(0, t_idx)
+                        sums[l * g.C + c] = rows.to(torch.int64).sum()
+            s_comp.synchronize()
+            s_load.synchronize()
+            for l in range(g.L):
+                for c in range(g.C):
+                    rows = bufs[l * g.C + c].view(-1, g.R).index_select(0, t_idx)
+                    assert int(sums[l * g.C + c]) == int(rows.to(torch.int64).sum()), (l, c)
+            check_load_layers(torch, g, pool, bufs, dev_idx, host_idx, sample_layers(g.L))
+    del bufs
+    release(torch)
