@@ -578,10 +578,8 @@ def leg_streamed(torch, kvt, workloads, args):
             b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
             workloads.fill_device_buffer(b, shape, 5, l, c, torch)
             bufs.append(b)
-    pool = kvt.KvPool(kvt.geometry(L, C, R, S, shape.host_slots, ps, 0), bufs)
+    geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
     s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
-    pool.backup(dev_idx, host_idx, 0, L, s_load)
-    s_load.synchronize()
     layer_bytes = n * C * R
     acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
 
@@ -601,7 +599,13 @@ def leg_streamed(torch, kvt, workloads, args):
         e1.synchronize()
     t_pass = e0.elapsed_time(e1) / 1e3 / 10
     results = {}
-    for pname, p in (("kernel", kvt.PATH_KERNEL), ("dma", kvt.PATH_DMA)):
+    variants = (("kernel", kvt.PATH_KERNEL, 0), ("kernel_overlap_flag", kvt.PATH_KERNEL,
+                                                 kvt.F_LOAD_OVERLAP),
+                ("dma", kvt.PATH_DMA, 0), ("auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP))
+    for pname, p, extra_flags in variants:
+        pool = kvt.KvPool(geom, bufs, flags=kvt.F_CHECK_UNIQUE | extra_flags)
+        pool.backup(dev_idx, host_idx, 0, L, s_load)       # L2 holds the prefix
+        s_load.synchronize()
         pool.set_path(p)
         pool.load(dev_idx, host_idx, 0, L, s_load)
         s_load.synchronize()
@@ -639,7 +643,8 @@ def leg_streamed(torch, kvt, workloads, args):
             h2d_ov.append(L * layer_bytes / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
         wall = statistics.median(walls)
         eta = (t_h2d + t_comp - wall) / min(t_h2d, t_comp)
-        results[pname] = {"h2d_alone_gbps": round(L * layer_bytes / t_h2d / 1e9, 3),
+        results[pname] = {"path_used": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
+                          "h2d_alone_gbps": round(L * layer_bytes / t_h2d / 1e9, 3),
                           "h2d_overlapped_gbps": round(statistics.median(h2d_ov), 3),
                           "compute_reps_per_layer": k,
                           "sum_h2d_ms": round(t_h2d * 1e3, 2),
@@ -647,7 +652,7 @@ def leg_streamed(torch, kvt, workloads, args):
                           "wall_ms": round(wall * 1e3, 2),
                           "overlap_efficiency": round(eta, 3)}
         log("streamed %s %s" % (pname, json.dumps(results[pname])))
-    pool.close()
+        pool.close()
     del bufs
     torch.cuda.empty_cache()
     return {"workload": "61 layers x K/V x 1024 B (fp8 random bytes), 131072-token prefix, "

@@ -25,7 +25,7 @@ LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT = 0, 1, 2
 PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA = 0, 1, 2, 3
 PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel_lds",
               PATH_DMA: "dma", -1: "none"}
-F_CHECK_UNIQUE, F_HOST_NONCOHERENT = 0x1, 0x2
+F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP = 0x1, 0x2, 0x4
 BACKUP, LOAD = 0, 1
 
 
@@ -46,7 +46,10 @@ class kv_calib_t(ctypes.Structure):
     _fields_ = [("kernel_launch_us", ctypes.c_double * 2), ("kernel_gbps", ctypes.c_double * 2),
                 ("dma_copy_us", ctypes.c_double * 2), ("dma_gbps", ctypes.c_double * 2),
                 ("load_split_min_bytes", ctypes.c_double),
-                ("kernel_max_workgroups", ctypes.c_double * 2)]
+                ("kernel_max_workgroups", ctypes.c_double * 2),
+                ("overlap_kernel_penalty", ctypes.c_double),
+                ("overlap_dma_penalty", ctypes.c_double),
+                ("overlap_kernel_max_workgroups", ctypes.c_double)]
 
 
 class kv_stats_t(ctypes.Structure):

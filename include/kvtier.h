@@ -101,6 +101,10 @@ typedef enum {
 /* ---- pool flags -------------------------------------------------------- */
 #define KV_F_CHECK_UNIQUE     0x1u /* reject duplicate destination slots (KV_EDUP) */
 #define KV_F_HOST_NONCOHERENT 0x2u /* allocate the host pool non-coherent (coarse-grained) instead of coherent */
+#define KV_F_LOAD_OVERLAP     0x4u /* loads on this pool run while compute kernels occupy the GPU
+                                      (layer-wise load during the forward pass): the selector
+                                      charges each path the compute time it steals, and the
+                                      kernel path runs on a capped grid */
 
 /* Geometry of one pool. Needs no GPU; the planner calls below take it alone. */
 typedef struct {
@@ -135,7 +139,12 @@ typedef struct {
  * kernel_max_workgroups: cap on the workgroups one transfer kernel launches
  * (0 = one per block of work). The kernels stride over their work, so a cap
  * moves the same bytes while leaving compute units free for kernels on other
- * streams (e.g. the layer that was just loaded). */
+ * streams (e.g. the layer that was just loaded).
+ * With KV_F_LOAD_OVERLAP, a load's modelled time on each path is multiplied
+ * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
+ * fractions of the transfer time by which a concurrent HBM-bound kernel is
+ * slowed, measured per path; and the kernel path launches at most
+ * overlap_kernel_max_workgroups workgroups. */
 typedef struct {
   double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
   double kernel_gbps[2];
@@ -143,6 +152,9 @@ typedef struct {
   double dma_gbps[2];
   double load_split_min_bytes;
   double kernel_max_workgroups[2];
+  double overlap_kernel_penalty;
+  double overlap_dma_penalty;
+  double overlap_kernel_max_workgroups;
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

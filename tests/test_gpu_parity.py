@@ -234,3 +234,52 @@ def test_stats_and_calibration(torch, stream):
     with pytest.raises(kvt.KvError):
         pool.set_calibration(c)
     pool.close()
+
+
+# ---- capped grids: workgroups stride over many blocks of work ------------------------
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_capped_grid_matches_oracle(torch, stream, layout):
+    L, C, R, S_dev, S_host, ps = GEOMS[0]
+    g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+    bufs = device_buffers(g, seed=11)
+    rng = np.random.default_rng(11 + layout)
+    for path in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS):
+        pool = make_pool(g, bufs, path)
+        for cap in (1, 3, 7):
+            c = pool.calibration()
+            c.kernel_max_workgroups[0] = c.kernel_max_workgroups[1] = cap
+            pool.set_calibration(c)
+            d, h = _request(rng, g, "random")
+            print("capped layout=%d path=%d cap=%d" % (layout, path, cap), flush=True)
+            run_backup_and_compare(g, pool, bufs, d, h, 0, L, stream)
+            pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+            run_load_and_compare(g, pool, bufs, d, h, 0, L, stream)
+        pool.close()
+
+
+def test_overlap_flag_steers_selector(torch, stream):
+    g = Geometry(2, 1, 64, 32, 32, 8, 0)
+    bufs = device_buffers(g, seed=12)
+    d, h = np.arange(8), np.arange(8)
+    for flags, want in ((kvt.F_CHECK_UNIQUE, kvt.PATH_KERNEL),
+                        (kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP, kvt.PATH_DMA)):
+        pool = make_pool(g, bufs, kvt.PATH_AUTO, flags=flags)
+        c = pool.calibration()
+        # two 1-D copies at 10 us each against one launch at 15 us: the kernel wins
+        # alone; charged the default overlap penalties (x1.65 vs x1.15) the copy
+        # engines win
+        c.kernel_launch_us[1], c.dma_copy_us[1] = 15.0, 10.0
+        c.kernel_gbps[1] = c.dma_gbps[1] = 1e6
+        c.overlap_kernel_penalty, c.overlap_dma_penalty = 0.65, 0.15
+        pool.set_calibration(c)
+        run_load_and_compare(g, pool, bufs, d, h, 0, 2, stream)
+        assert pool.last_path(kvt.LOAD) == want
+        # backups are never charged the overlap penalty
+        c.kernel_launch_us[0], c.dma_copy_us[0] = 15.0, 10.0
+        c.kernel_gbps[0] = c.dma_gbps[0] = 1e6
+        pool.set_calibration(c)
+        pool.backup(d, h, 0, 2, stream)
+        stream.synchronize()
+        assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
+        pool.close()
