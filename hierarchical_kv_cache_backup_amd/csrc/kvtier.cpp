@@ -10,7 +10,9 @@
 #include <sys/syscall.h>
 #include <unistd.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <chrono>
 #include <cstdio>
 #include <cstring>
@@ -96,26 +98,36 @@ struct kv_pool {
   uint8_t *host = nullptr;          // host pool, CPU address
   uint8_t *host_dev = nullptr;      // host pool, device-visible address
   int64_t host_bytes = 0;
-  std::vector<hipEvent_t> layer_ev; // per-layer "landed" events of kv_load
-  std::vector<std::atomic<uint8_t>> layer_ev_set;
+  // Landed events of kv_load. Layers are loaded in groups (one launch or one
+  // batch of copies per group) and one event is recorded per group, on the
+  // group's first layer; layer_src[l] names the event that covers layer l
+  // (-1: no load has covered it yet).
+  std::vector<hipEvent_t> layer_ev;
+  std::vector<std::atomic<int32_t>> layer_src;
   DirState dir[2];
   std::atomic<int32_t> path{KV_PATH_AUTO};
   std::mutex calib_mu;
   kv_calib_t calib{};
-  explicit kv_pool(int L) : layer_ev_set(L) {}
+  explicit kv_pool(int L) : layer_src(L) {
+    for (auto &x : layer_src) x.store(-1);
+  }
 };
 
 namespace kvt {
 namespace {
 
+// Defaults measured on an MI355X (PCIe Gen5 x16 host link) with 1152-byte
+// rows: fixed cost per kernel call (launch, index staging, ramp) ~30 us and per
+// copy-engine call ~9.5 us, both from requests of 64..32768 tokens x 78 layers;
+// sustained rates at 2.9 GB per call. bench.py re-measures the rates live.
 void default_calibration(kv_calib_t *c) {
-  for (int d = 0; d < 2; d++) {
-    c->kernel_launch_us[d] = 8.0;
-    c->kernel_gbps[d] = 50.0;
-    c->dma_copy_us[d] = 4.0;
-    c->dma_gbps[d] = 55.0;
-  }
-  c->load_split_min_bytes = 4.0 * 1024 * 1024;
+  c->kernel_launch_us[0] = c->kernel_launch_us[1] = 30.0;
+  c->kernel_gbps[0] = 55.9;
+  c->kernel_gbps[1] = 56.1;
+  c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
+  c->dma_gbps[0] = 56.2;
+  c->dma_gbps[1] = 55.9;
+  c->load_split_min_bytes = 16.0 * 1024 * 1024;
   c->kernel_max_workgroups[0] = c->kernel_max_workgroups[1] = 0;
   // Measured on MI355X with a 61-layer streamed load and an HBM-bound consumer:
   // the consumer ran ~1.65x longer beside the kernel path (128-workgroup grid)
@@ -268,6 +280,15 @@ hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_
 
 // ---- transfers ----------------------------------------------------------------
 
+// Records the landed event of layers [la, lb) (one event, kept on layer la)
+// after the work enqueued so far on s.
+static hipError_t mark_landed(kv_pool *p, int32_t la, int32_t lb, hipStream_t s) {
+  hipError_t e = hipEventRecord(p->layer_ev[la], s);
+  if (e == hipSuccess)
+    for (int32_t l = la; l < lb; l++) p->layer_src[l].store(la);
+  return e;
+}
+
 static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
                     int64_t n, int32_t l0, int32_t l1, void *stream) {
   const double t0 = now_us();
@@ -295,7 +316,15 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     std::lock_guard<std::mutex> cl(p->calib_mu);
     c = p->calib;
   }
-  const bool per_layer = dir == 1 && (double)layer_bytes >= c.load_split_min_bytes && l1 - l0 > 1;
+  // Loads go out in groups of `group` layers, each followed by one event: one
+  // layer per group when a layer alone holds load_split_min_bytes, else as many
+  // layers as reach it. Backups go out in one group.
+  int32_t group = l1 - l0;
+  if (dir == 1 && layer_bytes > 0) {
+    const double want = c.load_split_min_bytes / (double)layer_bytes;
+    group = want <= 1.0 ? 1 : (want >= (double)(l1 - l0) ? l1 - l0 : (int32_t)std::ceil(want));
+  }
+  const int32_t ngroups = (l1 - l0 + group - 1) / group;
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
   // ---- path selection
@@ -305,7 +334,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     build_runs(g, dev_idx, host_idx, n, &d.runs);
     build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
     planned = true;
-    const double launches = per_layer ? (double)(l1 - l0) : 1.0;
+    const double launches = (double)ngroups;
     const double t_kernel = launches * c.kernel_launch_us[dir] + bytes / (c.kernel_gbps[dir] * 1e3);
     const double copies = (double)d.copies.size() * (double)nlc_all;
     double t_dma = copies * c.dma_copy_us[dir] + bytes / (c.dma_gbps[dir] * 1e3);
@@ -324,16 +353,15 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       build_runs(g, dev_idx, host_idx, n, &d.runs);
       build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
     }
-    for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
-      for (int32_t c = 0; c < g.C && e == hipSuccess; c++)
-        for (const Copy &cp : d.copies) {
-          e = issue_copy(p, dir, l * g.C + c, cp, s);
-          if (e != hipSuccess) break;
-        }
-      if (e == hipSuccess && dir == 1) {
-        e = hipEventRecord(p->layer_ev[l], s);
-        p->layer_ev_set[l].store(1);
-      }
+    for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
+      const int32_t lb = std::min(l1, la + group);
+      for (int32_t l = la; l < lb && e == hipSuccess; l++)
+        for (int32_t c = 0; c < g.C && e == hipSuccess; c++)
+          for (const Copy &cp : d.copies) {
+            e = issue_copy(p, dir, l * g.C + c, cp, s);
+            if (e != hipSuccess) break;
+          }
+      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
     }
     if (e != hipSuccess) return hip_fail(e, "enqueueing copy-engine transfers");
     d.dma += (int64_t)d.copies.size() * nlc_all;
@@ -375,21 +403,10 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       d.launches++;
       return launch_rows(b, grid_for(blocks, cap), dir == 0, s);
     };
-    if (per_layer) {
-      for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
-        e = launch(l, l + 1);
-        if (e == hipSuccess) {
-          e = hipEventRecord(p->layer_ev[l], s);
-          p->layer_ev_set[l].store(1);
-        }
-      }
-    } else {
-      e = launch(l0, l1);
-      if (e == hipSuccess && dir == 1)
-        for (int32_t l = l0; l < l1 && e == hipSuccess; l++) {
-          e = hipEventRecord(p->layer_ev[l], s);
-          p->layer_ev_set[l].store(1);
-        }
+    for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
+      const int32_t lb = std::min(l1, la + group);
+      e = launch(la, lb);
+      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
     }
     if (e != hipSuccess) return hip_fail(e, "launching the transfer kernel");
     e = hipEventRecord(st->ev, s);
@@ -564,10 +581,11 @@ int kv_load_layer(kv_pool_t *p, int32_t layer, void *compute_stream) {
   if (!p) return fail(KV_EINVAL, "pool is null");
   if (layer < 0 || layer >= p->g.L)
     return fail(KV_EINVAL, "layer " + std::to_string(layer) + " is outside [0, L)");
-  if (!p->layer_ev_set[layer].load()) return KV_OK;
+  const int32_t src = p->layer_src[layer].load();
+  if (src < 0) return KV_OK;
   DeviceGuard dg(p->device);
   if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
-  hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, p->layer_ev[layer], 0);
+  hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, p->layer_ev[src], 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
   return KV_OK;
 }

@@ -132,10 +132,11 @@ typedef struct {
  *   t_kernel = launches * kernel_launch_us + bytes / kernel_gbps
  *   t_dma    = copies * dma_copy_us + bytes / dma_gbps
  * The four figures are measured per direction on the target machine.
- * load_split_min_bytes: kv_load issues one kernel per layer (so each layer's
- * event fires as soon as that layer has landed) when one layer of the request
- * holds at least this many bytes; below it, one kernel covers all layers and
- * every layer's event is recorded after it.
+ * load_split_min_bytes: kv_load goes out in groups of consecutive layers, one
+ * kernel launch (or one batch of copies) and one landed event per group; a
+ * group is one layer when a layer of the request holds at least this many
+ * bytes, else the fewest layers that reach it. Small loads thus pay for few
+ * launches and events, large ones signal every layer as soon as it lands.
  * kernel_max_workgroups: cap on the workgroups one transfer kernel launches
  * (0 = one per block of work). The kernels stride over their work, so a cap
  * moves the same bytes while leaving compute units free for kernels on other
@@ -235,8 +236,8 @@ int kv_backup(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, 
               int32_t layer_begin, int32_t layer_end, void *stream);
 
 /* H2D load: the reverse copy, host row host_row(l,c,host_idx[i]) -> device row
- * dev_idx[i] of B[l][c]. Layers are issued in increasing order, and after the
- * last byte of layer l is enqueued the pool's event for layer l is recorded
+ * dev_idx[i] of B[l][c]. Layers are issued in increasing order, in groups
+ * (see load_split_min_bytes), and after each group a landed event is recorded
  * on `stream`, so a consumer can start on layer l while later layers are
  * still in flight (compute/transfer overlap: HiCache system design page,
  * "data transfer optimisation"; "H2D stream -> KV_READY event -> compute
@@ -249,8 +250,11 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
 /* Makes `compute_stream` wait (on the device, the host does not block) until
  * layer `layer` of the most recent kv_load that covered that layer on this
  * pool has landed in device memory. Call it after that kv_load has returned.
- * A layer no kv_load has covered yet: KV_OK, no wait. Errors: KV_EINVAL (layer
- * out of [0,L)), KV_EHIP. */
+ * The wait is on the landed event of the layer's group (see
+ * load_split_min_bytes), so it may also cover the other layers of that group;
+ * if a later load re-recorded that group's event, the wait covers the later
+ * load too (never less than asked). A layer no kv_load has covered yet: KV_OK,
+ * no wait. Errors: KV_EINVAL (layer out of [0,L)), KV_EHIP. */
 int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
 
 /* ---- path control, calibration and statistics -------------------------- */

@@ -283,3 +283,42 @@ def test_overlap_flag_steers_selector(torch, stream):
         stream.synchronize()
         assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
         pool.close()
+
+
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA))
+def test_load_layer_groups_gate_consumer(torch, path):
+    """Layers loaded in groups of three (one launch and one landed event per
+    group): a consumer that waits with kv_load_layer(l) sees layer l complete,
+    and the bytes equal the oracle's."""
+    g = Geometry(8, 2, 512, 4096, 4096, 16, oracle.LAYER_FIRST)
+    n = 4096
+    bufs = device_buffers(g, seed=13, fill=0)
+    pool = make_pool(g, bufs, path, host_fill=None)
+    pool.host_array()[:] = np.random.default_rng(13).integers(0, 256, g.host_bytes(), np.uint8)
+    c = pool.calibration()
+    c.load_split_min_bytes = 10 * 1024 * 1024        # a layer is 4 MiB -> groups of 3
+    pool.set_calibration(c)
+    d = np.random.default_rng(14).permutation(g.S_dev)[:n]
+    h = np.arange(n)
+    mirrors = [np.zeros(g.S_dev * g.R, np.uint8) for _ in range(g.L * g.C)]
+    assert oracle.load(g, mirrors, pool.host_array(), d, h) == 0
+    s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
+    sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
+    t_idx = torch.from_numpy(d).cuda()
+    before = pool.stats().kernel_launches[1]
+    pool.load(d, h, 0, g.L, s_load)
+    with torch.cuda.stream(s_comp):
+        for l in range(g.L):
+            pool.load_layer(l, s_comp)
+            for cc in range(g.C):
+                rows = bufs[l * g.C + cc].view(-1, g.R).index_select(0, t_idx)
+                sums[l * g.C + cc] = rows.to(torch.int64).sum()
+    s_comp.synchronize()
+    s_load.synchronize()
+    for k in range(g.L * g.C):
+        want = mirrors[k].reshape(g.S_dev, g.R)[d].astype(np.int64).sum()
+        assert int(sums[k]) == int(want), k
+        assert np.array_equal(bufs[k].cpu().numpy(), mirrors[k]), k
+    if path == kvt.PATH_KERNEL:
+        assert pool.stats().kernel_launches[1] - before == 3
+    pool.close()
