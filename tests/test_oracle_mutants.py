@@ -8,12 +8,19 @@ battery. Mistakes are planted only in copies, on the CPU.
 """
 import json
 import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
 
-import oracle
-from oracle import np_ref, Geometry, LAYOUTS, LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT
+_HERE = os.path.dirname(os.path.abspath(__file__))
+for _p in (_HERE, os.path.dirname(_HERE)):  # the child process runs this file directly
+    if _p not in sys.path:
+        sys.path.insert(0, _p)
+
+import oracle  # noqa: E402
+from oracle import np_ref, Geometry, LAYOUTS, LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT  # noqa: E402
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(os.path.dirname(HERE), "oracle", "kv_oracle.c")
@@ -134,16 +141,37 @@ def battery(o):
     return failed
 
 
+def _battery_in_child(lib):
+    return subprocess.run([sys.executable, os.path.abspath(__file__), lib], capture_output=True,
+                          text=True, timeout=300, cwd=os.path.dirname(HERE))
+
+
 def test_committed_oracle_passes_every_pin():
     assert battery(oracle.default()) == []
+    # the child-process harness itself must pass on the committed oracle,
+    # else a broken harness would make every planted mistake look caught
+    res = _battery_in_child(oracle.default().path)
+    assert res.returncode == 0, res.stdout + res.stderr
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_is_caught(tmp_path, name, old, new):
+    """The battery runs in a child process: a planted stride mistake can write
+    outside the arrays, and a crash there counts as a caught mistake without
+    corrupting this process."""
     text = open(SRC).read()
     assert text.count(old) == 1, "mutation anchor not found exactly once: %r" % old
     src = tmp_path / "mutant.c"
     src.write_text(text.replace(old, new))
     lib = oracle.build(str(src), str(tmp_path / "libmutant.so"), werror=False)
-    failed = battery(oracle.Oracle(lib))
-    assert failed, "planted mistake '%s' passed every pin" % name
+    res = _battery_in_child(lib)
+    assert "No module named" not in res.stderr, res.stderr
+    assert res.returncode != 0, "planted mistake '%s' passed every pin" % name
+
+
+if __name__ == "__main__":
+    # child process: run the battery against the oracle build given on the
+    # command line; exit 0 only if every pin passed
+    failed = battery(oracle.Oracle(sys.argv[1]))
+    print("failed pins:", failed)
+    sys.exit(1 if failed else 0)
