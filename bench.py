@@ -444,24 +444,38 @@ def _ev(torch):
     return torch.cuda.Event(enable_timing=True)
 
 
-def _bidirectional_copy_peak(torch):
-    """Concurrent 1 GiB H2D and 1 GiB D2H copy-engine copies on two streams."""
-    GiB = 1 << 30
-    d1 = torch.empty(GiB, dtype=torch.uint8, device="cuda:0")
-    d2 = torch.empty(GiB, dtype=torch.uint8, device="cuda:0")
-    h1 = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
-    h2 = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+def _duplex_peak(torch, kvt):
+    """Concurrent contiguous H2D and D2H of 1 GiB each on the copy engines, issued
+    through the library (layer_first, 2 layers x 512 MiB, two streams, two
+    threads); aggregate GB/s = 2 GiB / span of both."""
+    import threading
+    R, S = 4096, 131072                       # 512 MiB per layer buffer
+    bufs = [torch.empty(S * R, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
+    geom = kvt.geometry(2, 1, R, S, S, 64, 0)
+    pa, pb = kvt.KvPool(geom, bufs[:2]), kvt.KvPool(geom, bufs[2:])
+    pa.set_path(kvt.PATH_DMA)
+    pb.set_path(kvt.PATH_DMA)
+    idx = np.arange(S, dtype=np.int64)
     sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
     best = 0.0
-    for _ in range(5):
+    for _ in range(4):
+        go = threading.Barrier(3)
+        th = [threading.Thread(target=lambda: (go.wait(), pa.load(idx, idx, 0, 2, sa))),
+              threading.Thread(target=lambda: (go.wait(), pb.backup(idx, idx, 0, 2, sb)))]
+        for x in th:
+            x.start()
         torch.cuda.synchronize()
+        go.wait()
         t0 = time.perf_counter()
-        with torch.cuda.stream(sa):
-            d1.copy_(h1, non_blocking=True)
-        with torch.cuda.stream(sb):
-            h2.copy_(d2, non_blocking=True)
-        torch.cuda.synchronize()
-        best = max(best, 2 * GiB / (time.perf_counter() - t0) / 1e9)
+        for x in th:
+            x.join()
+        sa.synchronize()
+        sb.synchronize()
+        best = max(best, 2 * S * R * 2 / (time.perf_counter() - t0) / 1e9)
+    pa.close()
+    pb.close()
+    del bufs
+    torch.cuda.empty_cache()
     return best
 
 
@@ -544,7 +558,7 @@ def leg_bidirectional(torch, kvt, workloads, args):
     pool.close()
     del bufs
     torch.cuda.empty_cache()
-    peak = _bidirectional_copy_peak(torch)
+    peak = _duplex_peak(torch, kvt)
     wall = statistics.median(walls)
     agg = (hb + wb) / wall / 1e9
     out = {"workload": "64 requests, lognormal lengths (median 4096, sigma 1.0), 32 layers x "

@@ -22,10 +22,10 @@ OK, EINVAL, ERANGE, EDUP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
 ERROR_NAMES = {EINVAL: "KV_EINVAL", ERANGE: "KV_ERANGE", EDUP: "KV_EDUP",
                ENOMEM: "KV_ENOMEM", EHIP: "KV_EHIP"}
 LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT = 0, 1, 2
-PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA = 0, 1, 2, 3
+PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA, PATH_STAGED = 0, 1, 2, 3, 4
 PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel_lds",
-              PATH_DMA: "dma", -1: "none"}
-F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP = 0x1, 0x2, 0x4
+              PATH_DMA: "dma", PATH_STAGED: "staged", -1: "none"}
+F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP, F_DUPLEX = 0x1, 0x2, 0x4, 0x8
 BACKUP, LOAD = 0, 1
 
 
@@ -49,7 +49,10 @@ class kv_calib_t(ctypes.Structure):
                 ("kernel_max_workgroups", ctypes.c_double * 2),
                 ("overlap_kernel_penalty", ctypes.c_double),
                 ("overlap_dma_penalty", ctypes.c_double),
-                ("overlap_kernel_max_workgroups", ctypes.c_double)]
+                ("overlap_kernel_max_workgroups", ctypes.c_double),
+                ("duplex_kernel_penalty", ctypes.c_double),
+                ("staged_chunk_bytes", ctypes.c_double),
+                ("staged_gather_gbps", ctypes.c_double)]
 
 
 class kv_stats_t(ctypes.Structure):

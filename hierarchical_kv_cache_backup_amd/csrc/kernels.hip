@@ -35,13 +35,15 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
 
 }  // namespace
 
-// Direct path: workgroup b moves rows [b*rows_per_block, ...) of the
-// host-order walk; lanes take consecutive chunks of those rows.
-template <bool kToHost>
+// Direct path: block b moves walk rows [row_begin + b*rows_per_block, ...) of
+// the host-order walk; lanes take consecutive chunks of those rows. kDense
+// (staged path): the host side is a device staging buffer holding walk row r at
+// (r - row_begin) * R instead of the host pool.
+template <bool kToHost, bool kDense>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
-  const uint32_t row0 = blk * a.rows_per_block;
-  const uint32_t nrows = min(a.rows_per_block, a.total_rows - row0);
+  const uint32_t row0 = a.row_begin + blk * a.rows_per_block;
+  const uint32_t nrows = min(a.rows_per_block, a.row_end - row0);
   const uint32_t nchunks = nrows * a.cpr;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
     chunk_t v[kXferUnroll];
@@ -56,7 +58,9 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
         uint32_t i, lc;
         walk_row(a, row0 + rr, i, lc);
         chunk_t *d = reinterpret_cast<chunk_t *>(dev_row(a, i, lc)) + k;
-        chunk_t *h = reinterpret_cast<chunk_t *>(host_row(a, i, lc)) + k;
+        chunk_t *h = reinterpret_cast<chunk_t *>(
+                         kDense ? a.host + (int64_t)(row0 + rr - a.row_begin) * a.R
+                                : host_row(a, i, lc)) + k;
         const chunk_t *src = kToHost ? d : h;
         dst[u] = kToHost ? h : d;
         v[u] = __builtin_nontemporal_load(src);
@@ -126,12 +130,20 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
   }
 }
 
-hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, bool dense,
+                       hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  if (to_host)
-    hipLaunchKernelGGL(xfer_rows<true>, dim3(blocks), dim3(kXferThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(xfer_rows<false>, dim3(blocks), dim3(kXferThreads), 0, s, a);
+  if (dense) {
+    if (to_host)
+      hipLaunchKernelGGL((xfer_rows<true, true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((xfer_rows<false, true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+  } else {
+    if (to_host)
+      hipLaunchKernelGGL((xfer_rows<true, false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((xfer_rows<false, false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -78,6 +78,14 @@ struct DirState {
   int next = 0;  // where the search for a free slot starts
   hipEvent_t done = nullptr;  // recorded at the end of every call of this direction
   bool done_pending = false;
+  std::atomic<bool> done_recorded{false};  // read without the lock by the other direction
+  // staged path: device staging buffer (a dense image of walk rows) and its last use
+  std::vector<Extent> extents;
+  uint8_t *stage = nullptr;
+  int64_t stage_cap = 0;
+  hipEvent_t stage_ev = nullptr;
+  bool stage_pending = false;
+  hipStream_t stage_stream = nullptr;
   std::atomic<int32_t> last_path{-1};
   int64_t calls = 0, bytes = 0, launches = 0, dma = 0;
   double submit_us = 0, blocked_us = 0;
@@ -135,6 +143,12 @@ void default_calibration(kv_calib_t *c) {
   c->overlap_kernel_penalty = 0.65;
   c->overlap_dma_penalty = 0.15;
   c->overlap_kernel_max_workgroups = 128;
+  // Concurrent 1 GiB H2D + D2H: 97 GB/s aggregate on the copy engines, 69 GB/s
+  // with the kernel in both directions -> a kernel transfer takes ~1.4x longer
+  // while the other direction is busy.
+  c->duplex_kernel_penalty = 0.4;
+  c->staged_chunk_bytes = 256.0 * 1024 * 1024;
+  c->staged_gather_gbps = 2000.0;
 }
 
 // Sets the calling thread's memory policy to bind to `node` (Linux mbind
@@ -189,6 +203,11 @@ hipError_t drain_direction(DirState &d) {
     hipError_t e = hipEventSynchronize(d.done);
     if (e != hipSuccess && first == hipSuccess) first = e;
     d.done_pending = false;
+  }
+  if (d.stage_pending) {
+    hipError_t e = hipEventSynchronize(d.stage_ev);
+    if (e != hipSuccess && first == hipSuccess) first = e;
+    d.stage_pending = false;
   }
   return first;
 }
@@ -289,6 +308,96 @@ static hipError_t mark_landed(kv_pool *p, int32_t la, int32_t lb, hipStream_t s)
   return e;
 }
 
+// True while the other direction has a transfer in flight on this pool (its
+// completion event is recorded and not yet reached).
+static bool other_direction_busy(kv_pool *p, int dir) {
+  DirState &o = p->dir[1 - dir];
+  if (!o.done_recorded.load()) return false;
+  return hipEventQuery(o.done) == hipErrorNotReady;
+}
+
+// Workgroup cap of a transfer kernel launch (0 = none).
+static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap) {
+  uint32_t cap = (uint32_t)c.kernel_max_workgroups[dir];
+  if (overlap && c.overlap_kernel_max_workgroups > 0 &&
+      (cap == 0 || cap > (uint32_t)c.overlap_kernel_max_workgroups))
+    cap = (uint32_t)c.overlap_kernel_max_workgroups;
+  return cap;
+}
+
+// Staged path: makes the direction's staging buffer ready for a call on s that
+// moves at most unit_bytes per layer group: grows it (after its previous use
+// has finished) to min(staged_chunk_bytes, unit_bytes) rounded down to whole
+// rows, and orders s after its previous use on another stream.
+static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_calib_t &c,
+                       hipStream_t s) {
+  int64_t want = (int64_t)std::min<double>(c.staged_chunk_bytes, (double)unit_bytes);
+  want = std::max<int64_t>(g.R, want / g.R * g.R);
+  if (d.stage_cap < want) {
+    if (d.stage_pending) {
+      hipError_t e = hipEventSynchronize(d.stage_ev);
+      d.stage_pending = false;
+      if (e != hipSuccess) return hip_fail(e, "waiting for the staging buffer");
+    }
+    if (d.stage) (void)hipFree(d.stage);
+    d.stage = nullptr;
+    d.stage_cap = 0;
+    if (hipMalloc((void **)&d.stage, (size_t)want) != hipSuccess) {
+      d.stage = nullptr;
+      (void)hipGetLastError();
+      return fail(KV_ENOMEM, "hipMalloc of the staging buffer failed");
+    }
+    d.stage_cap = want;
+  } else if (d.stage_pending && d.stage_stream != s) {
+    hipError_t e = hipStreamWaitEvent(s, d.stage_ev, 0);
+    if (e != hipSuccess) return hip_fail(e, "ordering after the staging buffer's last use");
+  }
+  return KV_OK;
+}
+
+// Staged path, one layer group [la, lb): the walk rows go through the staging
+// buffer in chunks. D2H: gather kernel (device rows -> staging, HBM to HBM),
+// then one copy-engine call per host extent (staging -> host pool). H2D: the
+// copies first, then the scatter kernel. b is planned for the group.
+static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
+                              const int64_t *host_idx, int32_t la, int32_t lb, uint32_t cap,
+                              hipStream_t s) {
+  const Geom &g = p->g;
+  build_extents(g, host_idx, (int64_t)b.n, la, lb, &d.extents);
+  plan_rows(&b, g.layout, g.ps);
+  b.host = d.stage;
+  const int64_t chunk_rows = d.stage_cap / g.R;
+  const int64_t walk_rows = b.total_rows;
+  size_t x = 0;  // next extent that reaches into the current chunk
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < walk_rows && e == hipSuccess; r0 += chunk_rows) {
+    const int64_t r1 = std::min(walk_rows, r0 + chunk_rows);
+    const uint32_t blocks = set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
+    if (dir == 0) {
+      d.launches++;
+      e = launch_rows(b, grid_for(blocks, cap), true, true, s);
+    }
+    while (e == hipSuccess && x < d.extents.size() && d.extents[x].walk0 < r1) {
+      const Extent &ex = d.extents[x];
+      const int64_t a0 = std::max(ex.walk0, r0);
+      const int64_t a1 = std::min(ex.walk0 + ex.rows, r1);
+      uint8_t *host = p->host + (ex.host0 + (a0 - ex.walk0)) * g.R;
+      uint8_t *stage = d.stage + (a0 - r0) * g.R;
+      const size_t nbytes = (size_t)((a1 - a0) * g.R);
+      e = dir == 0 ? hipMemcpyAsync(host, stage, nbytes, hipMemcpyDeviceToHost, s)
+                   : hipMemcpyAsync(stage, host, nbytes, hipMemcpyHostToDevice, s);
+      d.dma++;
+      if (ex.walk0 + ex.rows > r1) break;  // continues in the next chunk
+      x++;
+    }
+    if (e == hipSuccess && dir == 1) {
+      d.launches++;
+      e = launch_rows(b, grid_for(blocks, cap), false, true, s);
+    }
+  }
+  return e;
+}
+
 static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
                     int64_t n, int32_t l0, int32_t l1, void *stream) {
   const double t0 = now_us();
@@ -327,29 +436,46 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   const int32_t ngroups = (l1 - l0 + group - 1) / group;
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
+  const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir);
+  const uint32_t cap = kernel_cap(c, dir, overlap);
+
   // ---- path selection
   int32_t path = p->path.load();
-  bool planned = false;
+  bool have_copies = false;
   if (path == KV_PATH_AUTO) {
     build_runs(g, dev_idx, host_idx, n, &d.runs);
     build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
-    planned = true;
-    const double launches = (double)ngroups;
-    const double t_kernel = launches * c.kernel_launch_us[dir] + bytes / (c.kernel_gbps[dir] * 1e3);
-    const double copies = (double)d.copies.size() * (double)nlc_all;
-    double t_dma = copies * c.dma_copy_us[dir] + bytes / (c.dma_gbps[dir] * 1e3);
-    double t_kern = t_kernel;
+    have_copies = true;
+    build_extents(g, host_idx, n, l0, l1, &d.extents);
+    const double mb = (double)bytes;
+    double t_kernel = ngroups * c.kernel_launch_us[dir] + mb / (c.kernel_gbps[dir] * 1e3);
+    double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
+                   mb / (c.dma_gbps[dir] * 1e3);
+    // a layer group cuts the page-major layouts' extents once per group
+    const double extents =
+        (double)d.extents.size() * (g.layout == KV_LAYER_FIRST ? 1.0 : (double)ngroups);
+    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + ngroups;
+    double t_staged = extents * c.dma_copy_us[dir] + chunks * c.kernel_launch_us[dir] +
+                      mb / (c.dma_gbps[dir] * 1e3) + mb / (c.staged_gather_gbps * 1e3);
     if (overlap) {
-      t_kern *= 1.0 + c.overlap_kernel_penalty;
+      t_kernel *= 1.0 + c.overlap_kernel_penalty;
       t_dma *= 1.0 + c.overlap_dma_penalty;
+      t_staged *= 1.0 + c.overlap_dma_penalty;
     }
-    path = t_dma < t_kern ? KV_PATH_DMA : KV_PATH_KERNEL;
+    if (duplex) t_kernel *= 1.0 + c.duplex_kernel_penalty;
+    path = KV_PATH_KERNEL;
+    double best = t_kernel;
+    if (t_dma < best) {
+      best = t_dma;
+      path = KV_PATH_DMA;
+    }
+    if (t_staged < best) path = KV_PATH_STAGED;
   }
   if (path == KV_PATH_KERNEL_LDS && g.R > kMaxLdsRowBytes) path = KV_PATH_KERNEL;
 
   hipError_t e = hipSuccess;
   if (path == KV_PATH_DMA) {
-    if (!planned) {
+    if (!have_copies) {
       build_runs(g, dev_idx, host_idx, n, &d.runs);
       build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
     }
@@ -384,31 +510,37 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     a.R = g.R;
     a.lc_stride = g.lc_stride;
     a.n = (uint32_t)n;
-    auto launch = [&](int32_t la, int32_t lb) -> hipError_t {
+    if (path == KV_PATH_STAGED) {
+      rc = stage_begin(d, g, n * (int64_t)std::min<int32_t>(group, l1 - l0) * g.C * g.R, c, s);
+      if (rc) return rc;
+    }
+    for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
+      const int32_t lb = std::min(l1, la + group);
       XferArgs b = a;
       b.lc0 = (uint32_t)(la * g.C);
       b.nlc = (uint32_t)((lb - la) * g.C);
-      uint32_t cap = (uint32_t)c.kernel_max_workgroups[dir];
-      if (overlap && c.overlap_kernel_max_workgroups > 0 &&
-          (cap == 0 || cap > (uint32_t)c.overlap_kernel_max_workgroups))
-        cap = (uint32_t)c.overlap_kernel_max_workgroups;
-      if (path == KV_PATH_KERNEL_LDS) {
+      if (path == KV_PATH_STAGED) {
+        e = staged_unit(p, d, dir, b, host_idx, la, lb, cap, s);
+      } else if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
         TileArgs t{};
         b.nblocks = plan_tiles(b, g.layout, &t);
         d.launches++;
-        return launch_tiles_lds(b, t, grid_for(b.nblocks, cap), dir == 0, s);
+        e = launch_tiles_lds(b, t, grid_for(b.nblocks, cap), dir == 0, s);
+      } else {
+        const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
+        d.launches++;
+        e = launch_rows(b, grid_for(blocks, cap), dir == 0, false, s);
       }
-      const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
-      d.launches++;
-      return launch_rows(b, grid_for(blocks, cap), dir == 0, s);
-    };
-    for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
-      const int32_t lb = std::min(l1, la + group);
-      e = launch(la, lb);
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
     }
-    if (e != hipSuccess) return hip_fail(e, "launching the transfer kernel");
+    if (e != hipSuccess) return hip_fail(e, "enqueueing the transfer");
+    if (path == KV_PATH_STAGED) {
+      e = hipEventRecord(d.stage_ev, s);
+      if (e != hipSuccess) return hip_fail(e, "recording the staging-buffer event");
+      d.stage_pending = true;
+      d.stage_stream = s;
+    }
     e = hipEventRecord(st->ev, s);
     if (e != hipSuccess) return hip_fail(e, "recording the staging event");
     st->pending = true;
@@ -416,6 +548,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   e = hipEventRecord(d.done, s);
   if (e != hipSuccess) return hip_fail(e, "recording the completion event");
   d.done_pending = true;
+  d.done_recorded.store(true);
   d.last_path.store(path);
   d.calls++;
   d.bytes += bytes;
@@ -444,6 +577,8 @@ int kv_pool_destroy(kv_pool_t *p) {
         if (s.ev) (void)hipEventDestroy(s.ev);
       }
       if (d.done) (void)hipEventDestroy(d.done);
+      if (d.stage_ev) (void)hipEventDestroy(d.stage_ev);
+      if (d.stage) (void)hipFree(d.stage);
     }
     for (hipEvent_t ev : p->layer_ev)
       if (ev) (void)hipEventDestroy(ev);
@@ -553,6 +688,7 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
     e = hipEventCreateWithFlags(&p->layer_ev[l], hipEventDisableTiming);
   for (DirState &d : p->dir) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&d.stage_ev, hipEventDisableTiming);
     for (Staging &s : d.slots)
       if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
   }
@@ -592,7 +728,7 @@ int kv_load_layer(kv_pool_t *p, int32_t layer, void *compute_stream) {
 
 int kv_set_path(kv_pool_t *p, int32_t path) {
   if (!p) return fail(KV_EINVAL, "pool is null");
-  if (path < KV_PATH_AUTO || path > KV_PATH_DMA) return fail(KV_EINVAL, "unknown path");
+  if (path < KV_PATH_AUTO || path > KV_PATH_STAGED) return fail(KV_EINVAL, "unknown path");
   p->path.store(path);
   return KV_OK;
 }
@@ -615,6 +751,9 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
   if (!(c->overlap_kernel_max_workgroups >= 0) || c->overlap_kernel_max_workgroups > 4294967295.0 ||
       !(c->overlap_kernel_penalty >= 0) || !(c->overlap_dma_penalty >= 0))
     return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
+  if (!(c->duplex_kernel_penalty >= 0) || !(c->staged_chunk_bytes >= 16) ||
+      !(c->staged_gather_gbps > 0))
+    return fail(KV_EINVAL, "duplex penalty >= 0, staged chunk >= 16 bytes and gather rate > 0");
   std::lock_guard<std::mutex> lock(p->calib_mu);
   p->calib = *c;
   return KV_OK;

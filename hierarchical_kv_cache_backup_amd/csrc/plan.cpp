@@ -4,6 +4,7 @@
 // on its own with the host compiler.
 #include "plan.hpp"
 
+#include <algorithm>
 #include <cstdio>
 #include <limits>
 
@@ -166,6 +167,52 @@ void build_copies(const Geom &g, const std::vector<Run> &runs, const int64_t *de
       }
     }
     copies->push_back({d, k, r.len, 1, 0, 0});
+  }
+}
+
+void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la, int32_t lb,
+                   std::vector<Extent> *out) {
+  out->clear();
+  if (n <= 0 || lb <= la) return;
+  const int64_t nlc = (int64_t)(lb - la) * g.C;
+  const int64_t lc0 = (int64_t)la * g.C;
+  const int64_t G = g.layout == KV_LAYER_FIRST ? n : g.layout == KV_PAGE_FIRST ? 1 : g.ps;
+  auto append = [out](int64_t walk0, int64_t host0, int64_t rows) {
+    if (!out->empty()) {
+      Extent &e = out->back();
+      if (e.walk0 + e.rows == walk0 && e.host0 + e.rows == host0) {
+        e.rows += rows;
+        return;
+      }
+    }
+    out->push_back({walk0, host0, rows});
+  };
+  if (g.lc_stride == 1 && G == 1) {
+    // page_first: a position's rows for all pairs are consecutive host rows
+    for (int64_t i = 0; i < n; i++) append(i * nlc, host_key(g, host_idx[i]) + lc0, nlc);
+    return;
+  }
+  // runs of positions whose host keys advance by one (independent of the pair)
+  std::vector<int64_t> run_start;
+  run_start.reserve(64);
+  run_start.push_back(0);
+  for (int64_t i = 1; i < n; i++)
+    if (host_key(g, host_idx[i]) != host_key(g, host_idx[i - 1]) + 1) run_start.push_back(i);
+  run_start.push_back(n);
+  size_t first_run = 0;  // first run that reaches into the current group
+  for (int64_t g0 = 0; g0 < n; g0 += G) {
+    const int64_t gsz = std::min(G, n - g0);
+    const int64_t g1 = g0 + gsz;
+    const int64_t walk_base = g0 * nlc;  // every earlier group is full: G * nlc rows each
+    while (run_start[first_run + 1] <= g0) first_run++;
+    for (int64_t lc = 0; lc < nlc; lc++) {
+      for (size_t k = first_run; run_start[k] < g1; k++) {
+        const int64_t i0 = std::max(run_start[k], g0);
+        const int64_t i1 = std::min(run_start[k + 1], g1);
+        append(walk_base + lc * gsz + (i0 - g0), (lc0 + lc) * g.lc_stride + host_key(g, host_idx[i0]),
+               i1 - i0);
+      }
+    }
   }
 }
 

@@ -85,4 +85,21 @@ struct Copy {
 void build_copies(const Geom &g, const std::vector<Run> &runs, const int64_t *dev_idx,
                   const int64_t *host_idx, std::vector<Copy> *copies);
 
+// Staged path: the rows (i, l, c), l in [la, lb), are enumerated in the
+// transfer kernels' host-order walk (groups of G request positions, then
+// (pair, position) inside a group; G = n, 1 or page_size for layer_first,
+// page_first, page_first_direct). A staging buffer holds walk row r at
+// r * R. An extent is a maximal range of walk rows whose host rows are
+// consecutive: one copy-engine call moves it between the staging buffer and
+// the host pool.
+struct Extent {
+  int64_t walk0, host0, rows;
+};
+
+// Extents of the walk over layers [la, lb), in walk order. Cost O(n) plus
+// O(pairs x host runs) (one pass per pair over the runs of consecutive host
+// slots), and O(n) for page_first whose token rows are contiguous.
+void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la, int32_t lb,
+                   std::vector<Extent> *out);
+
 }  // namespace kvt

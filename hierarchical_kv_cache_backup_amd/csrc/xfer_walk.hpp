@@ -28,7 +28,9 @@ struct XferArgs {
   uint32_t cpr;             // chunks (kChunkBytes each) per row
   uint32_t rows_per_block;  // rows one workgroup moves
   uint32_t rows_full;       // rows in complete groups (n / G * G * nlc)
-  uint32_t total_rows;      // n * nlc  (< 2^31)
+  uint32_t total_rows;      // n * nlc  (< 2^31): rows of the whole walk
+  uint32_t row_begin;       // this launch moves walk rows [row_begin, row_end)
+  uint32_t row_end;
   uint32_t nblocks;         // row blocks (or LDS tiles); workgroups stride over them
 };
 
@@ -64,7 +66,17 @@ constexpr uint32_t plan_rows(XferArgs *a, int32_t layout, int32_t page_size) {
   a->rows_per_block = a->cpr >= kChunksPerBlock ? 1u : kChunksPerBlock / a->cpr;
   a->total_rows = a->n * a->nlc;
   a->rows_full = (a->n / a->G) * a->G * a->nlc;
+  a->row_begin = 0;
+  a->row_end = a->total_rows;
   a->nblocks = (a->total_rows + a->rows_per_block - 1) / a->rows_per_block;
+  return a->nblocks;
+}
+
+// Restricts a planned launch to walk rows [begin, end); returns the blocks.
+constexpr uint32_t set_row_range(XferArgs *a, uint32_t begin, uint32_t end) {
+  a->row_begin = begin;
+  a->row_end = end;
+  a->nblocks = (end - begin + a->rows_per_block - 1) / a->rows_per_block;
   return a->nblocks;
 }
 

@@ -90,17 +90,30 @@ typedef enum {
  *                     (the page_first <-> layer_first transpose).
  * KV_PATH_DMA         coalesced copy-engine path: maximal contiguous runs,
  *                     uniform-stride runs merged into 2-D copies, issued as
- *                     hipMemcpyAsync / hipMemcpy2DAsync on the stream.      */
+ *                     hipMemcpyAsync / hipMemcpy2DAsync on the stream.
+ * KV_PATH_STAGED      batched gather/scatter through a device staging buffer:
+ *                     a kernel gathers the rows into host-address order in
+ *                     HBM (or scatters them from it), and the copy engines move
+ *                     each contiguous host extent in one call (Baidu KV cache
+ *                     page, "DMA segment explosion & batched gather/scatter").
+ *                     A page of a page-first layout is one extent, so the link
+ *                     moves on the copy engines with few calls whatever the
+ *                     device-side fragmentation.                            */
 typedef enum {
   KV_PATH_AUTO = 0,
   KV_PATH_KERNEL = 1,
   KV_PATH_KERNEL_LDS = 2,
-  KV_PATH_DMA = 3
+  KV_PATH_DMA = 3,
+  KV_PATH_STAGED = 4
 } kv_path_t;
 
 /* ---- pool flags -------------------------------------------------------- */
 #define KV_F_CHECK_UNIQUE     0x1u /* reject duplicate destination slots (KV_EDUP) */
 #define KV_F_HOST_NONCOHERENT 0x2u /* allocate the host pool non-coherent (coarse-grained) instead of coherent */
+#define KV_F_DUPLEX           0x8u /* backups and loads on this pool run at the same time: the
+                                      selector charges the kernel path the duplex penalty.
+                                      Without it the charge applies only while the other
+                                      direction has a transfer in flight at submission. */
 #define KV_F_LOAD_OVERLAP     0x4u /* loads on this pool run while compute kernels occupy the GPU
                                       (layer-wise load during the forward pass): the selector
                                       charges each path the compute time it steals, and the
@@ -145,7 +158,9 @@ typedef struct {
  * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
  * fractions of the transfer time by which a concurrent HBM-bound kernel is
  * slowed, measured per path; and the kernel path launches at most
- * overlap_kernel_max_workgroups workgroups. */
+ * overlap_kernel_max_workgroups workgroups.
+ * The staged path is modelled as extents * dma_copy_us + chunks *
+ * kernel_launch_us + bytes / dma_gbps + bytes / staged_gather_gbps. */
 typedef struct {
   double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
   double kernel_gbps[2];
@@ -156,6 +171,9 @@ typedef struct {
   double overlap_kernel_penalty;
   double overlap_dma_penalty;
   double overlap_kernel_max_workgroups;
+  double duplex_kernel_penalty; /* kernel-path slowdown while the other direction is busy */
+  double staged_chunk_bytes;    /* staged path: staging buffer size per direction */
+  double staged_gather_gbps;    /* staged path: device-side gather/scatter rate */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */
@@ -264,7 +282,8 @@ int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
 int kv_set_path(kv_pool_t *pool, int32_t path);
 
 /* Path the most recent call of `direction` (0 = backup, 1 = load) used: one of
- * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA, or -1 if none yet. */
+ * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA / KV_PATH_STAGED, or -1 if
+ * none yet. */
 int32_t kv_last_path(const kv_pool_t *pool, int32_t direction);
 
 /* Replaces / reads the selector calibration. */

@@ -7,7 +7,7 @@ import oracle
 from oracle import Geometry
 
 SENTINEL = 0xA5
-PATHS = (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA, kvt.PATH_AUTO)
+PATHS = (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA, kvt.PATH_STAGED, kvt.PATH_AUTO)
 
 
 def torch_mod():

@@ -163,6 +163,75 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
   }
 }
 
+// Replays the staged path over layers [la, lb): extents of the walk, then in
+// chunks of chunk_rows walk rows the dense gather (D2H) or scatter (H2D) through
+// a staging mirror and one memcpy per extent piece, as the executor issues them.
+static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int64_t *h, int64_t n,
+                          int32_t la, int32_t lb, bool to_host, std::vector<uint8_t> &cover,
+                          int64_t chunk_rows) {
+  const Geom &g = m.g;
+  XferArgs a{};
+  a.R = g.R;
+  a.lc_stride = g.lc_stride;
+  a.n = (uint32_t)n;
+  a.lc0 = (uint32_t)(la * g.C);
+  a.nlc = (uint32_t)((lb - la) * g.C);
+  plan_rows(&a, g.layout, g.ps);
+  std::vector<Extent> ext;
+  build_extents(g, h, n, la, lb, &ext);
+  // extents tile the walk in order, and map every walk row to its host row
+  int64_t next = 0;
+  for (const Extent &e : ext) {
+    CHECK(e.walk0 == next && e.rows > 0, "extent gap or overlap at walk row %lld", (long long)next);
+    for (int64_t r = e.walk0; r < e.walk0 + e.rows; r++) {
+      uint32_t i = 0, lc = 0;
+      walk_row(a, (uint32_t)r, i, lc);
+      const int64_t want = (int64_t)(a.lc0 + lc) * g.lc_stride + tok[2 * i + 1];
+      CHECK(e.host0 + (r - e.walk0) == want, "extent maps walk row %lld wrong", (long long)r);
+    }
+    next = e.walk0 + e.rows;
+  }
+  CHECK(next == (int64_t)a.total_rows, "extents cover %lld of %u rows", (long long)next,
+        a.total_rows);
+  std::vector<uint8_t> stage((size_t)(chunk_rows * g.R));
+  size_t x = 0;
+  for (int64_t r0 = 0; r0 < (int64_t)a.total_rows; r0 += chunk_rows) {
+    const int64_t r1 = std::min<int64_t>(a.total_rows, r0 + chunk_rows);
+    set_row_range(&a, (uint32_t)r0, (uint32_t)r1);
+    auto dense = [&](bool gather) {  // the dense kernel, row by row
+      for (int64_t r = a.row_begin; r < a.row_end; r++) {
+        uint32_t i = 0, lc = 0;
+        walk_row(a, (uint32_t)r, i, lc);
+        uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R;
+        uint8_t *sv = stage.data() + (r - a.row_begin) * g.R;
+        CHECK((r - a.row_begin + 1) * g.R <= (int64_t)stage.size(), "stage overrun");
+        if (gather)
+          std::memcpy(sv, dv, g.R);
+        else
+          std::memcpy(dv, sv, g.R);
+        for (int64_t k = 0; k < g.R / kChunkBytes; k++)
+          cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + k]++;
+      }
+    };
+    if (to_host) dense(true);
+    while (x < ext.size() && ext[x].walk0 < r1) {
+      const Extent &e = ext[x];
+      const int64_t a0 = std::max(e.walk0, r0), a1 = std::min(e.walk0 + e.rows, r1);
+      const int64_t host_off = (e.host0 + (a0 - e.walk0)) * g.R;
+      CHECK(host_off >= 0 && host_off + (a1 - a0) * g.R <= (int64_t)m.host.size(), "extent OOB");
+      uint8_t *hp = m.host.data() + host_off;
+      uint8_t *sp = stage.data() + (a0 - r0) * g.R;
+      if (to_host)
+        std::memcpy(hp, sp, (a1 - a0) * g.R);
+      else
+        std::memcpy(sp, hp, (a1 - a0) * g.R);
+      if (e.walk0 + e.rows > r1) break;
+      x++;
+    }
+    if (!to_host) dense(false);
+  }
+}
+
 // Executes the copy-engine plan with memcpy, line by line.
 static void replay_dma(Mirror &m, const int64_t *d, const int64_t *h, int64_t n, int32_t l0,
                        int32_t l1, bool to_host, int64_t *copies_out) {
@@ -277,7 +346,7 @@ int main(int argc, char **argv) {
     for (int dir = 0; dir < 2; dir++) {
       const bool to_host = dir == 0;
       const Mirror &want = to_host ? want_b : want_l;
-      for (int variant = 0; variant < 4; variant++) {
+      for (int variant = 0; variant < 5; variant++) {
         if (n == 0 || nlc == 0) break;
         if (variant == 2 && g.R > kMaxLdsRowBytes) continue;
         Mirror m = base;
@@ -290,6 +359,10 @@ int main(int argc, char **argv) {
           for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover, cap);
         } else if (variant == 2) {
           replay_tiles(m, tok, n, l0, l1, to_host, cover, cap);
+        } else if (variant == 4) {
+          const int64_t walk = n * (int64_t)(l1 - l0) * g.C;
+          const int64_t chunk = std::max<int64_t>(1, (std::vector<int64_t>{1, 7, walk / 3 + 1, walk})[uni(0, 3)]);
+          replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk);
         } else {
           replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
           int64_t counted = -1;
@@ -298,7 +371,7 @@ int main(int argc, char **argv) {
                 "dma copy count");
           CHECK(copies <= seg, "more copies than segments");
         }
-        if (variant != 3) {
+        if (variant != 3) {  // every kernel-driven variant moves each chunk exactly once
           for (int64_t i = 0; i < n; i++)
             for (int32_t lc = 0; lc < g.L * g.C; lc++)
               for (int64_t k = 0; k < g.R / kChunkBytes; k++) {

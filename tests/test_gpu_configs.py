@@ -110,7 +110,7 @@ def sample_layers(L):
 
 # ---- llama8b: D2H of an 8192-token prefix from fragmented pages ------------------
 
-@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_DMA))
+@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
 def test_llama8b_fragmented_backup(torch, path):
     shape = workloads.llama8b()
     n = shape.extra["tokens"]

@@ -103,7 +103,8 @@ def test_random_requests_match_oracle(torch, stream, gi, layout, path):
             run_backup_and_compare(g, pool, bufs, d, h, l0, l1, stream)
             pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
             run_load_and_compare(g, pool, bufs, d, h, l0, l1, stream)
-            assert pool.last_path(kvt.LOAD) in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA)
+            assert pool.last_path(kvt.LOAD) in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA,
+                                                kvt.PATH_STAGED)
             if path != kvt.PATH_AUTO:
                 assert pool.last_path(kvt.BACKUP) == path
     pool.close()
@@ -149,6 +150,7 @@ def test_edge_cases(torch, stream):
         assert kvt.kv_load_layer(pool.handle, 2, stream) == kvt.EINVAL
         assert kvt.kv_load_layer(pool.handle, -1, stream) == kvt.EINVAL
         assert kvt.kv_set_path(pool.handle, 7) == kvt.EINVAL
+        assert kvt.kv_set_path(pool.handle, -1) == kvt.EINVAL
         pool.close()
     # duplicates are accepted when the pool does not check them (last writer unspecified,
     # so only a non-overlapping request is compared)
@@ -321,4 +323,28 @@ def test_load_layer_groups_gate_consumer(torch, path):
         assert np.array_equal(bufs[k].cpu().numpy(), mirrors[k]), k
     if path == kvt.PATH_KERNEL:
         assert pool.stats().kernel_launches[1] - before == 3
+    pool.close()
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_staged_small_chunks_match_oracle(torch, stream, layout):
+    """A staging buffer of a few rows: many chunks, extents split across chunk
+    boundaries, layer groups on loads."""
+    L, C, R, S_dev, S_host, ps = GEOMS[0]
+    g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+    bufs = device_buffers(g, seed=15)
+    rng = np.random.default_rng(15 + layout)
+    pool = make_pool(g, bufs, kvt.PATH_STAGED)
+    for chunk_rows, split_rows in ((3, 10 ** 9), (37, 50), (1000, 1)):
+        c = pool.calibration()
+        c.staged_chunk_bytes = chunk_rows * R
+        c.load_split_min_bytes = split_rows * R
+        pool.set_calibration(c)
+        for kind in ("random", "contiguous", "pages"):
+            d, h = _request(rng, g, kind)
+            print("staged layout=%d chunk=%d kind=%s" % (layout, chunk_rows, kind), flush=True)
+            run_backup_and_compare(g, pool, bufs, d, h, 0, L, stream)
+            pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+            run_load_and_compare(g, pool, bufs, d, h, 1, L, stream)
+            assert pool.last_path(kvt.LOAD) == kvt.PATH_STAGED
     pool.close()
