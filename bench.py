@@ -79,6 +79,11 @@ def main():
     path = {"auto": kvt.PATH_AUTO, "kernel": kvt.PATH_KERNEL, "kernel_lds": kvt.PATH_KERNEL_LDS,
             "dma": kvt.PATH_DMA}[args.path]
 
+    # concurrent H2D + D2H capacity of the link, taken before the large device
+    # allocations below (copy-engine D2H beside H2D has measured slower after them)
+    duplex_fresh = (None if args.no_extra or args.profile_counters
+                    else _duplex_peak(torch, kvt))
+
     # ---- resident inputs: device pool (seeded bf16 N(0,1)), host pool, index sets
     t_setup = time.perf_counter()
     bufs = []
@@ -145,13 +150,20 @@ def main():
 
     calib = pool.calibration()
     meas = {}
+    gather = []
     for d in (kvt.BACKUP, kvt.LOAD):
-        for p in (kvt.PATH_KERNEL, kvt.PATH_DMA):
+        for p in (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED):
             meas[(d, p)] = run(d, p, pool)
             log("%s %s: %.2f GB/s" % ("D2H" if d == 0 else "H2D", kvt.PATH_NAMES[p],
                                       bytes_dir / meas[(d, p)] / 1e9))
         calib.kernel_gbps[d] = bytes_dir / meas[(d, kvt.PATH_KERNEL)] / 1e9
         calib.dma_gbps[d] = bytes_dir / meas[(d, kvt.PATH_DMA)] / 1e9
+        # staged time = copy-engine time + device-side gather/scatter time
+        extra = meas[(d, kvt.PATH_STAGED)] - meas[(d, kvt.PATH_DMA)]
+        if extra > 0:
+            gather.append(bytes_dir / extra / 1e9)
+    if gather:
+        calib.staged_gather_gbps = min(max(statistics.median(gather), 100.0), 8000.0)
     pool.set_calibration(calib)
     pool.set_path(path)
     link_peak = {"h2d": max(memcpy_peak["h2d"], calib.kernel_gbps[1], calib.dma_gbps[1]),
@@ -216,7 +228,8 @@ def main():
     torch.cuda.empty_cache()
     extra = {}
     if not args.no_extra:
-        extra["bidirectional_mixed"] = leg_bidirectional(torch, kvt, workloads, args)
+        extra["bidirectional_mixed"] = leg_bidirectional(torch, kvt, workloads, args,
+                                                         link_peak, duplex_fresh)
         torch.cuda.empty_cache()
         extra["streamed_per_layer"] = leg_streamed(torch, kvt, workloads, args)
         torch.cuda.empty_cache()
@@ -412,7 +425,7 @@ def layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak,
                 rc2, segs = kvt.kv_count_segments(geom, dev_b, host_idx, 0, L)
                 cell = {"layout": lname, "dir": dname, "segments": segs, "dma_copies": copies}
                 for pname, p in (("kernel", kvt.PATH_KERNEL), ("kernel_lds", kvt.PATH_KERNEL_LDS),
-                                 ("dma", kvt.PATH_DMA)):
+                                 ("dma", kvt.PATH_DMA), ("staged", kvt.PATH_STAGED)):
                     pool.set_path(p)
                     fn = ((lambda: pool.backup(dev_b, host_idx, 0, L, s)) if d == kvt.BACKUP
                           else (lambda: pool.load(dev_l, host_idx, 0, L, s)))
@@ -445,45 +458,62 @@ def _ev(torch):
 
 
 def _duplex_peak(torch, kvt):
-    """Concurrent contiguous H2D and D2H of 1 GiB each on the copy engines, issued
-    through the library (layer_first, 2 layers x 512 MiB, two streams, two
-    threads); aggregate GB/s = 2 GiB / span of both."""
-    import threading
+    """Concurrent contiguous H2D and D2H of 1 GiB each, issued through the library
+    (layer_first, 2 layers x 512 MiB per direction, one pool per direction, two
+    streams), for every pairing of copy engines and kernels. Returns the best
+    aggregate GB/s (2 GiB / span of both) and the per-pairing figures. Both calls
+    only enqueue, so one thread issues them."""
     R, S = 4096, 131072                       # 512 MiB per layer buffer
     bufs = [torch.empty(S * R, dtype=torch.uint8, device="cuda:0") for _ in range(4)]
     geom = kvt.geometry(2, 1, R, S, S, 64, 0)
     pa, pb = kvt.KvPool(geom, bufs[:2]), kvt.KvPool(geom, bufs[2:])
-    pa.set_path(kvt.PATH_DMA)
-    pb.set_path(kvt.PATH_DMA)
     idx = np.arange(S, dtype=np.int64)
-    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
-    best = 0.0
-    for _ in range(4):
-        go = threading.Barrier(3)
-        th = [threading.Thread(target=lambda: (go.wait(), pa.load(idx, idx, 0, 2, sa))),
-              threading.Thread(target=lambda: (go.wait(), pb.backup(idx, idx, 0, 2, sb)))]
-        for x in th:
-            x.start()
-        torch.cuda.synchronize()
-        go.wait()
-        t0 = time.perf_counter()
-        for x in th:
-            x.join()
-        sa.synchronize()
-        sb.synchronize()
-        best = max(best, 2 * S * R * 2 / (time.perf_counter() - t0) / 1e9)
+    sa, sb = kvt.Stream(), kvt.Stream()                # a hardware queue each
+    nb = 2 * S * R
+    pairs = {}
+    for h_name, h_path in (("dma", kvt.PATH_DMA), ("kernel", kvt.PATH_KERNEL)):
+        for d_name, d_path in (("dma", kvt.PATH_DMA), ("kernel", kvt.PATH_KERNEL)):
+            pa.set_path(h_path)
+            pb.set_path(d_path)
+            best = None
+            for _ in range(3):
+                torch.cuda.synchronize()
+                e = [_ev(torch) for _ in range(4)]
+                e[0].record(sa.torch)
+                pa.load(idx, idx, 0, 2, sa)
+                e[1].record(sa.torch)
+                e[2].record(sb.torch)
+                pb.backup(idx, idx, 0, 2, sb)
+                e[3].record(sb.torch)
+                torch.cuda.synchronize()
+                start = min(0.0, e[0].elapsed_time(e[2]))
+                end = max(e[0].elapsed_time(e[1]), e[0].elapsed_time(e[3]))
+                r = {"h2d_gbps": round(nb / (e[0].elapsed_time(e[1]) / 1e3) / 1e9, 2),
+                     "d2h_gbps": round(nb / (e[2].elapsed_time(e[3]) / 1e3) / 1e9, 2),
+                     "aggregate_gbps": round(2 * nb / ((end - start) / 1e3) / 1e9, 2)}
+                if best is None or r["aggregate_gbps"] > best["aggregate_gbps"]:
+                    best = r
+            pairs["h2d_%s+d2h_%s" % (h_name, d_name)] = best
     pa.close()
     pb.close()
+    sa.close()
+    sb.close()
     del bufs
     torch.cuda.empty_cache()
-    return best
+    log("duplex pairings %s" % json.dumps(pairs))
+    return max(v["aggregate_gbps"] for v in pairs.values()), pairs
 
 
-def leg_bidirectional(torch, kvt, workloads, args):
+def leg_bidirectional(torch, kvt, workloads, args, link_peak, duplex_fresh):
     """Mixed batch: 64 requests, lognormal lengths (median 4096, sigma 1.0, max
     32768), 32 layers x K/V x 2048 B rows, page 64. The L2 hits (82% of each
     request, whole pages) load H2D on one stream from one caller thread while
-    the new pages write back D2H on another stream from a second thread."""
+    the new pages write back D2H on another stream from a second thread.
+
+    Bound: the two volumes are unequal (H2D ~4.4x D2H), so no schedule beats
+    wall_min = max(h2d_bytes / h2d_peak, d2h_bytes / d2h_peak,
+    (h2d_bytes + d2h_bytes) / duplex_peak), with the one-direction peaks of the
+    1 GiB copy-engine copies and the duplex peak of the fresh process."""
     import threading
     shape = workloads.mixed()
     plan = workloads.mixed_plan(shape, 4)
@@ -498,82 +528,109 @@ def leg_bidirectional(torch, kvt, workloads, args):
             b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
             workloads.fill_device_buffer(b, shape, 4, l, c, torch)
             bufs.append(b)
-    pool = kvt.KvPool(kvt.geometry(L, C, R, S, plan["host_slots"], ps, 0), bufs)
-    s_load, s_back = torch.cuda.Stream(), torch.cuda.Stream()
-    pool.backup(h_dev, h_host, 0, L, s_back)          # L2 holds the hits
-    s_back.synchronize()
+    # the two directions on streams with a hardware queue each: on one queue
+    # they would run one after the other
+    s_load, s_back = kvt.Stream(), kvt.Stream()
     log("bidirectional: setup %.1fs, %d requests, %.1f GB H2D, %.1f GB D2H" %
         (time.perf_counter() - t0, plan["lens"].size, h_dev.size * L * C * R / 1e9,
          w_dev.size * L * C * R / 1e9))
     hb = h_dev.size * L * C * R
     wb = w_dev.size * L * C * R
-
-    def alone(fn, s):
-        fn()
-        s.synchronize()
-        e0, e1 = _ev(torch), _ev(torch)
-        e0.record(s)
-        fn()
-        e1.record(s)
-        e1.synchronize()
-        return e0.elapsed_time(e1) / 1e3
-
-    load = lambda: pool.load(h_dev, h_host, 0, L, s_load)
-    back = lambda: pool.backup(w_dev, w_host, 0, L, s_back)
-    t_load = alone(load, s_load)
-    t_back = alone(back, s_back)
-    walls, h_rates, d_rates = [], [], []
-    for rep in range(1 + 3):
-        go = threading.Barrier(3)
-        ev = [_ev(torch) for _ in range(4)]
-
-        def run_load():
-            go.wait()
-            ev[0].record(s_load)
-            load()
-            ev[1].record(s_load)
-
-        def run_back():
-            go.wait()
-            ev[2].record(s_back)
-            back()
-            ev[3].record(s_back)
-
-        th = [threading.Thread(target=run_load), threading.Thread(target=run_back)]
-        for x in th:
-            x.start()
-        torch.cuda.synchronize()
-        go.wait()
-        t1 = time.perf_counter()
-        for x in th:
-            x.join()
-        s_load.synchronize()
+    peak_here, pairs_here = _duplex_peak(torch, kvt)
+    peak, pairs = duplex_fresh
+    peak = max(peak, peak_here)
+    wall_min = max(hb / link_peak["h2d"], wb / link_peak["d2h"], (hb + wb) / peak) / 1e9
+    bound = (hb + wb) / wall_min / 1e9
+    results = {}
+    variants = (("layer_first", 0, "kernel", kvt.PATH_KERNEL),
+                ("layer_first", 0, "auto", kvt.PATH_AUTO),
+                ("page_first_direct", 2, "kernel", kvt.PATH_KERNEL),
+                ("page_first_direct", 2, "staged", kvt.PATH_STAGED),
+                ("page_first_direct", 2, "auto", kvt.PATH_AUTO))
+    for lname, lay, pname, p in variants:
+        pool = kvt.KvPool(kvt.geometry(L, C, R, S, plan["host_slots"], ps, lay), bufs,
+                          flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
+        pool.set_path(kvt.PATH_KERNEL)
+        pool.backup(h_dev, h_host, 0, L, s_back)      # L2 holds the hits
         s_back.synchronize()
-        wall = time.perf_counter() - t1
-        if rep == 0:
-            continue
-        walls.append(wall)
-        h_rates.append(hb / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
-        d_rates.append(wb / (ev[2].elapsed_time(ev[3]) / 1e3) / 1e9)
-    pool.close()
+        pool.set_path(p)
+        load = lambda: pool.load(h_dev, h_host, 0, L, s_load)
+        back = lambda: pool.backup(w_dev, w_host, 0, L, s_back)
+
+        def alone(fn, st):
+            fn()
+            st.synchronize()
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(st.torch)
+            fn()
+            e1.record(st.torch)
+            e1.synchronize()
+            return e0.elapsed_time(e1) / 1e3
+
+        t_load = alone(load, s_load)
+        t_back = alone(back, s_back)
+        walls, h_rates, d_rates = [], [], []
+        for rep in range(1 + 3):
+            go = threading.Barrier(3)
+            ev = [_ev(torch) for _ in range(4)]
+
+            def run_load():
+                go.wait()
+                ev[0].record(s_load.torch)
+                load()
+                ev[1].record(s_load.torch)
+
+            def run_back():
+                go.wait()
+                ev[2].record(s_back.torch)
+                back()
+                ev[3].record(s_back.torch)
+
+            th = [threading.Thread(target=run_load), threading.Thread(target=run_back)]
+            for x in th:
+                x.start()
+            torch.cuda.synchronize()
+            go.wait()
+            t1 = time.perf_counter()
+            for x in th:
+                x.join()
+            s_load.synchronize()
+            s_back.synchronize()
+            wall = time.perf_counter() - t1
+            if rep == 0:
+                continue
+            walls.append(wall)
+            h_rates.append(hb / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
+            d_rates.append(wb / (ev[2].elapsed_time(ev[3]) / 1e3) / 1e9)
+        wall = statistics.median(walls)
+        agg = (hb + wb) / wall / 1e9
+        key = "%s/%s" % (lname, pname)
+        results[key] = {"paths_used": {"h2d": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
+                                       "d2h": kvt.PATH_NAMES[pool.last_path(kvt.BACKUP)]},
+                        "h2d_alone_gbps": round(hb / t_load / 1e9, 3),
+                        "d2h_alone_gbps": round(wb / t_back / 1e9, 3),
+                        "h2d_concurrent_gbps": round(statistics.median(h_rates), 3),
+                        "d2h_concurrent_gbps": round(statistics.median(d_rates), 3),
+                        "aggregate_gbps": round(agg, 3),
+                        "pct_of_bound": round(100 * agg / bound, 1)}
+        log("bidirectional %s %s" % (key, json.dumps(results[key])))
+        pool.close()
+    s_load.close()
+    s_back.close()
     del bufs
     torch.cuda.empty_cache()
-    peak = _duplex_peak(torch, kvt)
-    wall = statistics.median(walls)
-    agg = (hb + wb) / wall / 1e9
-    out = {"workload": "64 requests, lognormal lengths (median 4096, sigma 1.0), 32 layers x "
-                       "K/V x 2048 B, page 64, hits 0.82 H2D || new D2H, two threads",
-           "tokens": int(S), "h2d_bytes": int(hb), "d2h_bytes": int(wb),
-           "h2d_alone_gbps": round(hb / t_load / 1e9, 3),
-           "d2h_alone_gbps": round(wb / t_back / 1e9, 3),
-           "h2d_concurrent_gbps": round(statistics.median(h_rates), 3),
-           "d2h_concurrent_gbps": round(statistics.median(d_rates), 3),
-           "aggregate_gbps": round(agg, 3),
-           "bidirectional_copy_peak_gbps": round(peak, 3),
-           "pct_of_bidirectional_peak": round(100 * agg / peak, 1),
-           "path": kvt.PATH_NAMES[kvt.PATH_AUTO]}
-    log("bidirectional %s" % json.dumps(out))
-    return out
+    best = max(results, key=lambda k: results[k]["aggregate_gbps"])
+    return {"workload": "64 requests, lognormal lengths (median 4096, sigma 1.0), 32 layers x "
+                        "K/V x 2048 B, page 64, hits 0.82 H2D || new D2H, two threads, pool "
+                        "flagged KV_F_DUPLEX",
+            "tokens": int(S), "h2d_bytes": int(hb), "d2h_bytes": int(wb),
+            "duplex_peak_gbps": round(peak, 3),
+            "duplex_pairings_1GiB_fresh": pairs,
+            "duplex_pairings_1GiB_beside_pools": pairs_here,
+            "bound_gbps": round(bound, 3),
+            "bound": "max(h2d/h2d_peak, d2h/d2h_peak, (h2d+d2h)/duplex_peak) as wall time",
+            "best": best, "aggregate_gbps": results[best]["aggregate_gbps"],
+            "variants": results}
 
 
 def leg_streamed(torch, kvt, workloads, args):
@@ -593,7 +650,7 @@ def leg_streamed(torch, kvt, workloads, args):
             workloads.fill_device_buffer(b, shape, 5, l, c, torch)
             bufs.append(b)
     geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
-    s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
+    s_load, s_comp = kvt.Stream(), torch.cuda.Stream()   # loads on a queue of their own
     layer_bytes = n * C * R
     acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
 
@@ -615,7 +672,8 @@ def leg_streamed(torch, kvt, workloads, args):
     results = {}
     variants = (("kernel", kvt.PATH_KERNEL, 0), ("kernel_overlap_flag", kvt.PATH_KERNEL,
                                                  kvt.F_LOAD_OVERLAP),
-                ("dma", kvt.PATH_DMA, 0), ("auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP))
+                ("dma", kvt.PATH_DMA, 0), ("staged", kvt.PATH_STAGED, 0),
+                ("auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP))
     for pname, p, extra_flags in variants:
         pool = kvt.KvPool(geom, bufs, flags=kvt.F_CHECK_UNIQUE | extra_flags)
         pool.backup(dev_idx, host_idx, 0, L, s_load)       # L2 holds the prefix
@@ -624,9 +682,9 @@ def leg_streamed(torch, kvt, workloads, args):
         pool.load(dev_idx, host_idx, 0, L, s_load)
         s_load.synchronize()
         e0, e1 = _ev(torch), _ev(torch)
-        e0.record(s_load)
+        e0.record(s_load.torch)
         pool.load(dev_idx, host_idx, 0, L, s_load)
-        e1.record(s_load)
+        e1.record(s_load.torch)
         e1.synchronize()
         t_h2d = e0.elapsed_time(e1) / 1e3
         k = max(1, round(t_h2d / L / t_pass))
@@ -642,10 +700,10 @@ def leg_streamed(torch, kvt, workloads, args):
         for rep in range(3):
             torch.cuda.synchronize()
             ev = [_ev(torch) for _ in range(3)]
-            ev[0].record(s_load)
+            ev[0].record(s_load.torch)
             s_comp.wait_event(ev[0])
             pool.load(dev_idx, host_idx, 0, L, s_load)
-            ev[1].record(s_load)
+            ev[1].record(s_load.torch)
             with torch.cuda.stream(s_comp):
                 for l in range(L):
                     pool.load_layer(l, s_comp)
@@ -667,6 +725,7 @@ def leg_streamed(torch, kvt, workloads, args):
                           "overlap_efficiency": round(eta, 3)}
         log("streamed %s %s" % (pname, json.dumps(results[pname])))
         pool.close()
+    s_load.close()
     del bufs
     torch.cuda.empty_cache()
     return {"workload": "61 layers x K/V x 1024 B (fp8 random bytes), 131072-token prefix, "

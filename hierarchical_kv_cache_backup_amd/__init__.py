@@ -79,6 +79,8 @@ SIGNATURES = {
     "kv_backup": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_load": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_load_layer": (_I32, [_VP, _I32, _VP]),
+    "kv_stream_create": (_I32, [_I32, ctypes.POINTER(_VP)]),
+    "kv_stream_destroy": (_I32, [_VP]),
     "kv_set_path": (_I32, [_VP, _I32]),
     "kv_last_path": (_I32, [_VP, _I32]),
     "kv_set_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
@@ -224,6 +226,38 @@ def kv_load(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None
 
 def kv_load_layer(pool, layer, compute_stream=None):
     return _lib.kv_load_layer(pool, layer, _stream_handle(compute_stream))
+
+
+def kv_stream_create(device=0):
+    """Returns (status, hipStream_t handle as int)."""
+    h = ctypes.c_void_p()
+    rc = _lib.kv_stream_create(device, ctypes.byref(h))
+    return rc, h.value
+
+
+def kv_stream_destroy(stream):
+    return _lib.kv_stream_destroy(stream)
+
+
+class Stream:
+    """A stream with a hardware queue of its own (kv_stream_create), usable
+    wherever the binding takes a stream; `.torch` is the same stream as a
+    torch.cuda.ExternalStream. Destroyed by close()."""
+
+    def __init__(self, device=0):
+        import torch
+        rc, h = kv_stream_create(device)
+        _check(rc)
+        self.cuda_stream = h
+        self.torch = torch.cuda.ExternalStream(h, device=torch.device("cuda", device))
+
+    def synchronize(self):
+        self.torch.synchronize()
+
+    def close(self):
+        if self.cuda_stream:
+            h, self.cuda_stream = self.cuda_stream, None
+            _check(kv_stream_destroy(h))
 
 
 def kv_set_path(pool, path):

@@ -79,13 +79,21 @@ struct DirState {
   hipEvent_t done = nullptr;  // recorded at the end of every call of this direction
   bool done_pending = false;
   std::atomic<bool> done_recorded{false};  // read without the lock by the other direction
-  // staged path: device staging buffer (a dense image of walk rows) and its last use
+  // staged path: two device staging halves (dense images of walk rows), an
+  // auxiliary stream for the gather/scatter kernels, and the events that pass
+  // each half between the copies (caller's stream) and the kernels (aux).
   std::vector<Extent> extents;
-  uint8_t *stage = nullptr;
-  int64_t stage_cap = 0;
-  hipEvent_t stage_ev = nullptr;
+  uint8_t *stage = nullptr;      // 2 * stage_cap bytes
+  int64_t stage_cap = 0;         // bytes per half
+  hipEvent_t stage_ev = nullptr;  // the call's last use of the halves (on the caller's stream)
   bool stage_pending = false;
   hipStream_t stage_stream = nullptr;
+  hipStream_t aux = nullptr;
+  hipEvent_t ev_start = nullptr, ev_ready[2] = {nullptr, nullptr}, ev_free[2] = {nullptr, nullptr};
+
+  bool free_recorded[2] = {false, false};
+  uint32_t next_half = 0;  // halves alternate across chunks, groups and calls
+  int last_half = -1;      // half of the latest chunk
   std::atomic<int32_t> last_path{-1};
   int64_t calls = 0, bytes = 0, launches = 0, dma = 0;
   double submit_us = 0, blocked_us = 0;
@@ -308,6 +316,54 @@ static hipError_t mark_landed(kv_pool *p, int32_t la, int32_t lb, hipStream_t s)
   return e;
 }
 
+// A stream with a hardware queue of its own. HIP maps streams onto a few
+// hardware queues round-robin, so a plain stream can land on another stream's
+// queue and serialise work that should overlap; a stream created with a CU mask
+// gets a hardware queue of its own. The mask enables every compute unit, so it
+// does not restrict where kernels run. Default priority.
+static hipError_t create_aux_stream(hipStream_t *out) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess && cus > 0) {
+    std::vector<uint32_t> mask((size_t)(cus + 31) / 32, 0xffffffffu);
+    if (cus % 32) mask.back() = (1u << (cus % 32)) - 1u;
+    e = hipExtStreamCreateWithCUMask(out, (uint32_t)mask.size(), mask.data());
+    if (e == hipSuccess) return e;
+    (void)hipGetLastError();
+  }
+  return hipStreamCreateWithFlags(out, hipStreamNonBlocking);
+}
+
+// The staged path's auxiliary streams, one per direction, shared by every pool
+// on a device and kept for the life of the process: two hardware queues per
+// device however many pools exist (more queues than the hardware runs at once
+// would be time-sliced).
+struct DeviceStreams {
+  hipStream_t aux[2] = {nullptr, nullptr};
+};
+
+static hipError_t device_streams(int device, DeviceStreams **out) {
+  static std::mutex mu;
+  static std::vector<DeviceStreams *> table;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)table.size() <= device) table.resize(device + 1, nullptr);
+  if (!table[device]) {
+    DeviceStreams *ds = new DeviceStreams;
+    hipError_t e = hipSuccess;
+    for (int d = 0; d < 2 && e == hipSuccess; d++) e = create_aux_stream(&ds->aux[d]);
+    if (e != hipSuccess) {
+      for (int d = 0; d < 2; d++)
+        if (ds->aux[d]) (void)hipStreamDestroy(ds->aux[d]);
+      delete ds;
+      return e;
+    }
+    table[device] = ds;
+  }
+  *out = table[device];
+  return hipSuccess;
+}
+
 // True while the other direction has a transfer in flight on this pool (its
 // completion event is recorded and not yet reached).
 static bool other_direction_busy(kv_pool *p, int dir) {
@@ -342,7 +398,7 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
     if (d.stage) (void)hipFree(d.stage);
     d.stage = nullptr;
     d.stage_cap = 0;
-    if (hipMalloc((void **)&d.stage, (size_t)want) != hipSuccess) {
+    if (hipMalloc((void **)&d.stage, 2 * (size_t)want) != hipSuccess) {
       d.stage = nullptr;
       (void)hipGetLastError();
       return fail(KV_ENOMEM, "hipMalloc of the staging buffer failed");
@@ -352,37 +408,64 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
     hipError_t e = hipStreamWaitEvent(s, d.stage_ev, 0);
     if (e != hipSuccess) return hip_fail(e, "ordering after the staging buffer's last use");
   }
+  // the halves are free once s reaches this point (the previous call's last
+  // use of them is ordered before it)
+  d.free_recorded[0] = d.free_recorded[1] = false;
+  d.last_half = -1;
   return KV_OK;
 }
 
 // Staged path, one layer group [la, lb): the walk rows go through the staging
-// buffer in chunks. D2H: gather kernel (device rows -> staging, HBM to HBM),
-// then one copy-engine call per host extent (staging -> host pool). H2D: the
-// copies first, then the scatter kernel. b is planned for the group.
+// halves in chunks, consecutive chunks (also across groups and calls) in
+// alternate halves, so the kernel of one chunk overlaps the copies of the other.
+//   D2H: aux gathers chunk k (device rows -> half, HBM to HBM) once the half is
+//        free; the caller's stream s copies it out, one copy-engine call per
+//        host extent piece, then frees the half.
+//   H2D: s copies chunk k in once the half is free; aux scatters it to the
+//        device rows, then frees the half; the group's landed event is recorded
+//        on aux after its last scatter, and the call makes s wait for aux
+//        after the last group.
+// b is planned for the group.
 static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
                               const int64_t *host_idx, int32_t la, int32_t lb, uint32_t cap,
                               hipStream_t s) {
   const Geom &g = p->g;
   build_extents(g, host_idx, (int64_t)b.n, la, lb, &d.extents);
   plan_rows(&b, g.layout, g.ps);
-  b.host = d.stage;
   const int64_t chunk_rows = d.stage_cap / g.R;
   const int64_t walk_rows = b.total_rows;
   size_t x = 0;  // next extent that reaches into the current chunk
   hipError_t e = hipSuccess;
+  if (dir == 0) {  // aux starts after everything already queued on s (the KV it reads)
+    e = hipEventRecord(d.ev_start, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(d.aux, d.ev_start, 0);
+  }
+  int last = -1;
   for (int64_t r0 = 0; r0 < walk_rows && e == hipSuccess; r0 += chunk_rows) {
     const int64_t r1 = std::min(walk_rows, r0 + chunk_rows);
+    const int half = (int)(d.next_half++ & 1);
+    last = half;
+    uint8_t *buf = d.stage + half * d.stage_cap;
+    b.host = buf;
     const uint32_t blocks = set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
+    hipStream_t kern_s = d.aux;
     if (dir == 0) {
-      d.launches++;
-      e = launch_rows(b, grid_for(blocks, cap), true, true, s);
+      if (d.free_recorded[half]) e = hipStreamWaitEvent(kern_s, d.ev_free[half], 0);
+      if (e == hipSuccess) {
+        d.launches++;
+        e = launch_rows(b, grid_for(blocks, cap), true, true, kern_s);
+      }
+      if (e == hipSuccess) e = hipEventRecord(d.ev_ready[half], kern_s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(s, d.ev_ready[half], 0);
+    } else if (d.free_recorded[half]) {
+      e = hipStreamWaitEvent(s, d.ev_free[half], 0);
     }
     while (e == hipSuccess && x < d.extents.size() && d.extents[x].walk0 < r1) {
       const Extent &ex = d.extents[x];
       const int64_t a0 = std::max(ex.walk0, r0);
       const int64_t a1 = std::min(ex.walk0 + ex.rows, r1);
       uint8_t *host = p->host + (ex.host0 + (a0 - ex.walk0)) * g.R;
-      uint8_t *stage = d.stage + (a0 - r0) * g.R;
+      uint8_t *stage = buf + (a0 - r0) * g.R;
       const size_t nbytes = (size_t)((a1 - a0) * g.R);
       e = dir == 0 ? hipMemcpyAsync(host, stage, nbytes, hipMemcpyDeviceToHost, s)
                    : hipMemcpyAsync(stage, host, nbytes, hipMemcpyHostToDevice, s);
@@ -390,11 +473,22 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
       if (ex.walk0 + ex.rows > r1) break;  // continues in the next chunk
       x++;
     }
-    if (e == hipSuccess && dir == 1) {
-      d.launches++;
-      e = launch_rows(b, grid_for(blocks, cap), false, true, s);
+    if (e != hipSuccess) break;
+    if (dir == 0) {
+      e = hipEventRecord(d.ev_free[half], s);
+    } else {
+      e = hipEventRecord(d.ev_ready[half], s);
+      if (e == hipSuccess) e = hipStreamWaitEvent(kern_s, d.ev_ready[half], 0);
+      if (e == hipSuccess) {
+        d.launches++;
+        e = launch_rows(b, grid_for(blocks, cap), false, true, kern_s);
+      }
+      if (e == hipSuccess) e = hipEventRecord(d.ev_free[half], kern_s);
     }
+    d.free_recorded[half] = true;
   }
+  if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, d.aux);  // after its last scatter
+  d.last_half = last;
   return e;
 }
 
@@ -451,10 +545,10 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     double t_kernel = ngroups * c.kernel_launch_us[dir] + mb / (c.kernel_gbps[dir] * 1e3);
     double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
                    mb / (c.dma_gbps[dir] * 1e3);
-    // a layer group cuts the page-major layouts' extents once per group
-    const double extents =
-        (double)d.extents.size() * (g.layout == KV_LAYER_FIRST ? 1.0 : (double)ngroups);
-    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + ngroups;
+    // the staged path moves page-major layouts in one unit (see below)
+    const double extents = (double)d.extents.size();
+    const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
+    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units;
     double t_staged = extents * c.dma_copy_us[dir] + chunks * c.kernel_launch_us[dir] +
                       mb / (c.dma_gbps[dir] * 1e3) + mb / (c.staged_gather_gbps * 1e3);
     if (overlap) {
@@ -472,6 +566,11 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     if (t_staged < best) path = KV_PATH_STAGED;
   }
   if (path == KV_PATH_KERNEL_LDS && g.R > kMaxLdsRowBytes) path = KV_PATH_KERNEL;
+  // In page_first / page_first_direct a host page holds every layer of its
+  // tokens contiguously; a per-layer unit would cut each page into one small
+  // extent per layer. The staged path therefore moves those layouts in one
+  // unit, and a load's layers all land together at its end.
+  if (path == KV_PATH_STAGED && g.layout != KV_LAYER_FIRST) group = l1 - l0;
 
   hipError_t e = hipSuccess;
   if (path == KV_PATH_DMA) {
@@ -521,6 +620,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       b.nlc = (uint32_t)((lb - la) * g.C);
       if (path == KV_PATH_STAGED) {
         e = staged_unit(p, d, dir, b, host_idx, la, lb, cap, s);
+        continue;  // staged_unit records the group's landed event itself
       } else if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
         TileArgs t{};
@@ -534,6 +634,8 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
     }
+    if (e == hipSuccess && path == KV_PATH_STAGED && dir == 1 && d.last_half >= 0)
+      e = hipStreamWaitEvent(s, d.ev_free[d.last_half], 0);  // s ends after aux's last scatter
     if (e != hipSuccess) return hip_fail(e, "enqueueing the transfer");
     if (path == KV_PATH_STAGED) {
       e = hipEventRecord(d.stage_ev, s);
@@ -577,7 +679,14 @@ int kv_pool_destroy(kv_pool_t *p) {
         if (s.ev) (void)hipEventDestroy(s.ev);
       }
       if (d.done) (void)hipEventDestroy(d.done);
+
       if (d.stage_ev) (void)hipEventDestroy(d.stage_ev);
+      if (d.ev_start) (void)hipEventDestroy(d.ev_start);
+      for (int h = 0; h < 2; h++) {
+        if (d.ev_ready[h]) (void)hipEventDestroy(d.ev_ready[h]);
+        if (d.ev_free[h]) (void)hipEventDestroy(d.ev_free[h]);
+      }
+
       if (d.stage) (void)hipFree(d.stage);
     }
     for (hipEvent_t ev : p->layer_ev)
@@ -686,9 +795,18 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
   p->layer_ev.assign(g.L, nullptr);
   for (int l = 0; l < g.L && e == hipSuccess; l++)
     e = hipEventCreateWithFlags(&p->layer_ev[l], hipEventDisableTiming);
+  DeviceStreams *ds = nullptr;
+  if (e == hipSuccess) e = device_streams(desc->device, &ds);
+  for (int k = 0; k < 2 && e == hipSuccess; k++) p->dir[k].aux = ds->aux[k];
   for (DirState &d : p->dir) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.stage_ev, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&d.ev_start, hipEventDisableTiming);
+    for (int h = 0; h < 2; h++) {
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&d.ev_ready[h], hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&d.ev_free[h], hipEventDisableTiming);
+    }
+
     for (Staging &s : d.slots)
       if (e == hipSuccess) e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
   }
@@ -723,6 +841,32 @@ int kv_load_layer(kv_pool_t *p, int32_t layer, void *compute_stream) {
   if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
   hipError_t e = hipStreamWaitEvent((hipStream_t)compute_stream, p->layer_ev[src], 0);
   if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+  return KV_OK;
+}
+
+int kv_stream_create(int32_t device, void **out) {
+  if (!out) return fail(KV_EINVAL, "out is null");
+  *out = nullptr;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+  if (device < 0 || device >= ndev)
+    return fail(KV_EINVAL, "device " + std::to_string(device) + " does not exist");
+  DeviceGuard dg(device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipStream_t st = nullptr;
+  e = create_aux_stream(&st);
+  if (e != hipSuccess) return hip_fail(e, "creating a stream");
+  *out = st;
+  return KV_OK;
+}
+
+int kv_stream_destroy(void *stream) {
+  if (!stream) return KV_OK;
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  hipError_t e2 = hipStreamDestroy((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronising the stream");
+  if (e2 != hipSuccess) return hip_fail(e2, "destroying the stream");
   return KV_OK;
 }
 

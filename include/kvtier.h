@@ -275,6 +275,23 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
  * no wait. Errors: KV_EINVAL (layer out of [0,L)), KV_EHIP. */
 int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
 
+/* ---- streams -------------------------------------------------------------- */
+
+/* Creates a HIP stream (returned as hipStream_t in *out) on `device` that has a
+ * hardware queue of its own. The runtime maps ordinary streams onto a few
+ * hardware queues round-robin; two streams on one queue run in order, so a
+ * backup stream and a load stream that share a queue cannot use both link
+ * directions at once, and a load stream that shares the compute stream's queue
+ * cannot overlap compute. Streams from this call never share a queue (they
+ * carry a CU mask that enables every compute unit, which gives them their own
+ * queue without restricting where kernels run). Default priority. The caller
+ * owns the stream and destroys it with kv_stream_destroy. Errors: KV_EINVAL,
+ * KV_EHIP. */
+int kv_stream_create(int32_t device, void **out);
+
+/* Waits for the stream's work and destroys it. NULL is a no-op. */
+int kv_stream_destroy(void *stream);
+
 /* ---- path control, calibration and statistics -------------------------- */
 
 /* Forces a path (kv_path_t) for later calls on this pool; KV_PATH_AUTO

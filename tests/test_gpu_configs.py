@@ -180,7 +180,7 @@ def test_mixed_bidirectional(torch):
                      shape.page_size, layout)
         with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
             pool.set_path(kvt.PATH_KERNEL)
-            s_load, s_back = torch.cuda.Stream(), torch.cuda.Stream()
+            s_load, s_back = kvt.Stream(), kvt.Stream()
             # L2 holds the hit pages: write them back once, then scramble those device rows
             pool.backup(h_dev, h_host, 0, g.L, s_back)
             s_back.synchronize()
@@ -214,6 +214,8 @@ def test_mixed_bidirectional(torch):
             check_backup_layers(torch, g, pool, bufs, w_dev, w_host, layers)
             assert [untouched_sum(torch, b, g.R, np.concatenate([h_dev, w_dev])) for b in bufs] \
                 == untouched
+            s_load.close()
+            s_back.close()
     del bufs
     release(torch)
 

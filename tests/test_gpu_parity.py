@@ -348,3 +348,41 @@ def test_staged_small_chunks_match_oracle(torch, stream, layout):
             run_load_and_compare(g, pool, bufs, d, h, 1, L, stream)
             assert pool.last_path(kvt.LOAD) == kvt.PATH_STAGED
     pool.close()
+
+
+# ---- streams with a hardware queue of their own ---------------------------------------
+
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+def test_library_streams_round_trip(torch, path):
+    """Backup and load issued on kv_stream_create streams, at the same time,
+    match the oracle; bad arguments are rejected."""
+    shape = workloads.tiny()
+    g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                 shape.host_slots, shape.page_size, oracle.LAYER_FIRST)
+    assert kvt.kv_stream_create(-1)[0] == kvt.EINVAL
+    assert kvt.kv_stream_create(torch.cuda.device_count())[0] == kvt.EINVAL
+    assert kvt.kv_stream_destroy(None) == kvt.OK
+    dev_idx, host_idx, reload_idx = workloads.tiny_indices(shape)
+    src = device_buffers(g, seed=11)
+    pool = make_pool(g, src, path)
+    s_back, s_load = kvt.Stream(), kvt.Stream()
+    print("library streams path=%d" % path, flush=True)
+    run_backup_and_compare(g, pool, src, dev_idx, host_idx, 0, g.L, s_back)
+    # load into a second pool on one stream while the first backs up again on the other
+    fresh = device_buffers(g, seed=12, fill=SENTINEL)
+    pool2 = make_pool(g, fresh, path, host_fill=None)
+    pool2.host_array()[:] = pool.host_array()
+    want_dev = mirrors(fresh)
+    assert oracle.load(g, want_dev, pool2.host_array().copy(), reload_idx, host_idx) == 0
+    want_host = pool.host_array().copy()
+    pool2.load(reload_idx, host_idx, 0, g.L, s_load)
+    pool.backup(dev_idx, host_idx, 0, g.L, s_back)
+    s_load.synchronize()
+    s_back.synchronize()
+    assert np.array_equal(pool.host_array(), want_host)
+    for k, b in enumerate(fresh):
+        assert np.array_equal(b.cpu().numpy(), want_dev[k]), k
+    s_back.close()
+    s_load.close()
+    pool.close()
+    pool2.close()
