@@ -327,7 +327,7 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
     t_h2d, k_h2d = measure(lambda: pool.load(dev_l, host_idx, 0, L, s), L)
     a_d2h = d2h_bytes / t_d2h / 1e9
     a_h2d = h2d_bytes / t_h2d / 1e9
-    return {"kernel": "kvt::xfer_rows<true> (D2H gather, whole prefix in one launch)",
+    return {"kernel": "kvt::xfer_rows<true, false> (D2H gather, whole prefix in one launch)",
             "bound": "host_link",
             "achieved": round(a_d2h, 3),
             "peak": PCIE_GEN5_X16_GBPS,
@@ -337,7 +337,7 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
             "algorithmic_bytes_per_launch": d2h_bytes,
             "mean_launch_us": round(t_d2h * 1e6, 2),
             "launches_timed": k_d2h,
-            "h2d_kernel": {"kernel": "kvt::xfer_rows<false> (H2D scatter, one launch per layer)",
+            "h2d_kernel": {"kernel": "kvt::xfer_rows<false, false> (H2D scatter, one launch per layer: each layer holds more than the 16 MiB load group threshold)",
                            "achieved": round(a_h2d, 3),
                            "frac": round(a_h2d / PCIE_GEN5_X16_GBPS, 4),
                            "algorithmic_bytes_per_launch": h2d_bytes,
@@ -391,8 +391,8 @@ def summarize_counters(fetch_dir, write_dir):
                 continue
             k = r["Kernel_Name"]
             key = ("copy" if "elementwise_kernel" in k and "copy" in k else
-                   "xfer_rows_d2h" if "xfer_rows<true>" in k else
-                   "xfer_rows_h2d" if "xfer_rows<false>" in k else None)
+                   "xfer_rows_d2h" if "xfer_rows<true, false>" in k else
+                   "xfer_rows_h2d" if "xfer_rows<false, false>" in k else None)
             if key is None:
                 continue
             per.setdefault((key, cname), []).append(float(r["Counter_Value"]) * 1024.0)

@@ -336,9 +336,10 @@ static hipError_t create_aux_stream(hipStream_t *out) {
 }
 
 // The staged path's auxiliary streams, one per direction, shared by every pool
-// on a device and kept for the life of the process: two hardware queues per
-// device however many pools exist (more queues than the hardware runs at once
-// would be time-sliced).
+// on a device, made on the device's first staged transfer and kept for the
+// life of the process: two hardware queues per device however many pools exist
+// (more queues than the hardware runs at once would be time-sliced), none for a
+// process that never takes the staged path.
 struct DeviceStreams {
   hipStream_t aux[2] = {nullptr, nullptr};
 };
@@ -610,6 +611,12 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     a.lc_stride = g.lc_stride;
     a.n = (uint32_t)n;
     if (path == KV_PATH_STAGED) {
+      if (!d.aux) {  // the device's auxiliary streams, made on the first staged call
+        DeviceStreams *ds = nullptr;
+        e = device_streams(p->device, &ds);
+        if (e != hipSuccess) return hip_fail(e, "creating the staged path's streams");
+        d.aux = ds->aux[dir];
+      }
       rc = stage_begin(d, g, n * (int64_t)std::min<int32_t>(group, l1 - l0) * g.C * g.R, c, s);
       if (rc) return rc;
     }
@@ -795,9 +802,6 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
   p->layer_ev.assign(g.L, nullptr);
   for (int l = 0; l < g.L && e == hipSuccess; l++)
     e = hipEventCreateWithFlags(&p->layer_ev[l], hipEventDisableTiming);
-  DeviceStreams *ds = nullptr;
-  if (e == hipSuccess) e = device_streams(desc->device, &ds);
-  for (int k = 0; k < 2 && e == hipSuccess; k++) p->dir[k].aux = ds->aux[k];
   for (DirState &d : p->dir) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.stage_ev, hipEventDisableTiming);
