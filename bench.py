@@ -44,7 +44,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true",
                    help="skip the bidirectional mixed-batch and per-layer streamed legs")
-    p.add_argument("--matrix-reps", type=int, default=5)
+    p.add_argument("--cell-seconds", type=float, default=0.4,
+                   help="timed repetitions per matrix cell: about this many seconds, 3..20 reps")
+    p.add_argument("--host-memory-study", type=float, nargs="+", metavar="GB",
+                   help="only measure the headline request against pinned host pools of "
+                        "these sizes (GB), then exit")
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -70,6 +74,9 @@ def main():
     from hierarchical_kv_cache_backup_amd import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.host_memory_study:
+        print(json.dumps(host_memory_study(torch, kvt, workloads, args.host_memory_study)))
+        return
     dev = torch.device("cuda:0")
     shape = workloads.mla32k()
     L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
@@ -145,29 +152,54 @@ def main():
     def run(direction, p, lay_pool):
         lay_pool.set_path(p)
         if direction == kvt.BACKUP:
-            return timed(lambda: lay_pool.backup(dev_b, host_idx, 0, L, s), args.matrix_reps)[0]
-        return timed(lambda: lay_pool.load(dev_l, host_idx, 0, L, s), args.matrix_reps)[0]
+            return timed(lambda: lay_pool.backup(dev_b, host_idx, 0, L, s), 5)[0]
+        return timed(lambda: lay_pool.load(dev_l, host_idx, 0, L, s), 5)[0]
 
+    # The selector models a call as fixed costs (per kernel launch, per copy-engine
+    # call) plus bytes / rate. The measured call time already holds the fixed
+    # costs, so each rate is fitted to the time left after the modelled fixed
+    # costs of the launches and copies that call made (counted by kv_get_stats).
     calib = pool.calibration()
-    meas = {}
+    meas, ops = {}, {}
     gather = []
     for d in (kvt.BACKUP, kvt.LOAD):
         for p in (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED):
             meas[(d, p)] = run(d, p, pool)
-            log("%s %s: %.2f GB/s" % ("D2H" if d == 0 else "H2D", kvt.PATH_NAMES[p],
-                                      bytes_dir / meas[(d, p)] / 1e9))
-        calib.kernel_gbps[d] = bytes_dir / meas[(d, kvt.PATH_KERNEL)] / 1e9
-        calib.dma_gbps[d] = bytes_dir / meas[(d, kvt.PATH_DMA)] / 1e9
-        # staged time = copy-engine time + device-side gather/scatter time
-        extra = meas[(d, kvt.PATH_STAGED)] - meas[(d, kvt.PATH_DMA)]
-        if extra > 0:
-            gather.append(bytes_dir / extra / 1e9)
-    if gather:
-        calib.staged_gather_gbps = min(max(statistics.median(gather), 100.0), 8000.0)
+            s0 = pool.stats()
+            (pool.backup(dev_b, host_idx, 0, L, s) if d == kvt.BACKUP
+             else pool.load(dev_l, host_idx, 0, L, s))
+            s.synchronize()
+            s1 = pool.stats()
+            ops[(d, p)] = (s1.kernel_launches[d] - s0.kernel_launches[d],
+                           s1.dma_copies[d] - s0.dma_copies[d])
+            log("%s %s: %.2f GB/s (%d launches, %d copies per call)" %
+                ("D2H" if d == 0 else "H2D", kvt.PATH_NAMES[p],
+                 bytes_dir / meas[(d, p)] / 1e9, *ops[(d, p)]))
+
+        def fixed_s(p):
+            k, c = ops[(d, p)]
+            kern = calib.kernel_launch_us[d] + (k - 1) * calib.kernel_group_us[d] if k else 0.0
+            return (kern + c * calib.dma_copy_us[d]) * 1e-6
+
+        def fit(p):
+            return bytes_dir / max(meas[(d, p)] - fixed_s(p), 0.5 * meas[(d, p)]) / 1e9
+
+        calib.kernel_gbps[d] = fit(kvt.PATH_KERNEL)
+        calib.dma_gbps[d] = fit(kvt.PATH_DMA)
+        # staged = its fixed costs + the copy-engine stream + the first chunk's
+        # device-side pass (the later ones overlap the copies)
+        extra = (meas[(d, kvt.PATH_STAGED)] - fixed_s(kvt.PATH_STAGED)
+                 - bytes_dir / (calib.dma_gbps[d] * 1e9))
+        first = min(bytes_dir, calib.staged_chunk_bytes)
+        gather.append(first / extra / 1e9 if extra > 0 else 8000.0)
+    calib.staged_gather_gbps = min(max(statistics.median(gather), 100.0), 8000.0)
     pool.set_calibration(calib)
     pool.set_path(path)
-    link_peak = {"h2d": max(memcpy_peak["h2d"], calib.kernel_gbps[1], calib.dma_gbps[1]),
-                 "d2h": max(memcpy_peak["d2h"], calib.kernel_gbps[0], calib.dma_gbps[0])}
+    best_rate = {dd: max(bytes_dir / meas[(dd, p)] / 1e9 for p in
+                         (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+                 for dd in (kvt.BACKUP, kvt.LOAD)}
+    link_peak = {"h2d": max(memcpy_peak["h2d"], best_rate[kvt.LOAD]),
+                 "d2h": max(memcpy_peak["d2h"], best_rate[kvt.BACKUP])}
 
     # ---- the timed steps
     def step(ev=None):
@@ -221,7 +253,9 @@ def main():
     # ---- layout x path matrix at the same geometry
     matrix = []
     if not args.no_matrix:
-        matrix = layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args)
+        for spec in matrix_specs(torch, kvt, workloads, shape, bufs, dev_b, dev_l, host_idx):
+            matrix += transfer_matrix(torch, kvt, spec, s, link_peak, calib, args)
+            del spec
 
     pool.close()
     del bufs
@@ -266,6 +300,13 @@ def main():
                                  "d2h": round(100 * d2h_gbps / PCIE_GEN5_X16_GBPS, 1)},
         "submit_us_per_call": submit,
         "pool_create_s": round(t_pool, 3),
+        "selector_calibration": {
+            "kernel_gbps": [round(x, 3) for x in calib.kernel_gbps],
+            "dma_gbps": [round(x, 3) for x in calib.dma_gbps],
+            "staged_gather_gbps": round(calib.staged_gather_gbps, 1),
+            "launches_copies_per_call": {"%s/%s" % ("d2h" if d == 0 else "h2d",
+                                                    kvt.PATH_NAMES[p]): list(v)
+                                         for (d, p), v in ops.items()}},
         "roofline": roof,
         "cpu_baseline": cpu,
         "matrix": matrix,
@@ -412,45 +453,122 @@ def summarize_counters(fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
-def layout_matrix(torch, kvt, shape, bufs, dev_b, dev_l, host_idx, s, link_peak, args):
-    rows = []
-    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+MATRIX_PATHS = (("kernel", "PATH_KERNEL"), ("kernel_lds", "PATH_KERNEL_LDS"),
+                ("dma", "PATH_DMA"), ("staged", "PATH_STAGED"), ("auto", "PATH_AUTO"))
+
+
+def transfer_matrix(torch, kvt, spec, s, link_peak, calib, args):
+    """Layout x direction x path cells for one geometry and request. Each cell:
+    GB/s from HIP events around the call on its stream (median), and GB/s from
+    the host wall clock taken from entering the call to the end of a
+    synchronize on an event recorded right after it (median, p10, p90), so
+    that planning and submission are inside. The auto column uses the fitted
+    calibration and names the path it chose."""
+    L, C, R = spec["L"], spec["C"], spec["R"]
+    dev_b, dev_l, host_idx = spec["dev_b"], spec["dev_l"], spec["host_idx"]
     n = host_idx.size
     bytes_dir = n * L * C * R
+    rows = []
     for lname, lay in LAYOUTS.items():
-        geom = kvt.geometry(L, C, R, shape.device_slots, shape.host_slots, ps, lay)
-        with kvt.KvPool(geom, bufs) as pool:
+        geom = kvt.geometry(L, C, R, spec["S_dev"], spec["S_host"], spec["ps"], lay)
+        with kvt.KvPool(geom, spec["bufs"]) as pool:
+            pool.set_calibration(calib)
             for dname, d in (("d2h", kvt.BACKUP), ("h2d", kvt.LOAD)):
-                rc, copies = kvt.kv_count_dma_copies(geom, dev_b, host_idx, 0, L)
-                rc2, segs = kvt.kv_count_segments(geom, dev_b, host_idx, 0, L)
-                cell = {"layout": lname, "dir": dname, "segments": segs, "dma_copies": copies}
-                for pname, p in (("kernel", kvt.PATH_KERNEL), ("kernel_lds", kvt.PATH_KERNEL_LDS),
-                                 ("dma", kvt.PATH_DMA), ("staged", kvt.PATH_STAGED)):
-                    pool.set_path(p)
+                _, copies = kvt.kv_count_dma_copies(geom, dev_b, host_idx, 0, L)
+                _, segs = kvt.kv_count_segments(geom, dev_b, host_idx, 0, L)
+                cell = {"geometry": spec["label"], "layout": lname, "dir": dname,
+                        "segments": segs, "dma_copies": copies}
+                for pname, pattr in MATRIX_PATHS:
+                    if pname not in spec["paths"]:
+                        continue
+                    pool.set_path(getattr(kvt, pattr))
                     fn = ((lambda: pool.backup(dev_b, host_idx, 0, L, s)) if d == kvt.BACKUP
                           else (lambda: pool.load(dev_l, host_idx, 0, L, s)))
+                    s.synchronize()
                     t0 = time.perf_counter()
                     fn()
                     s.synchronize()
                     first = time.perf_counter() - t0
-                    if first > 3.0:
-                        cell[pname] = {"gbps": round(bytes_dir / first / 1e9, 3), "reps": 1}
-                        continue
-                    ts = []
-                    for _ in range(args.matrix_reps):
+                    reps = max(3, min(20, int(args.cell_seconds / max(first, 1e-4))))
+                    ts, walls = [], []
+                    for _ in range(reps):
                         e0 = torch.cuda.Event(enable_timing=True)
                         e1 = torch.cuda.Event(enable_timing=True)
+                        s.synchronize()
+                        t0 = time.perf_counter()
                         e0.record(s)
                         fn()
                         e1.record(s)
                         e1.synchronize()
+                        walls.append(time.perf_counter() - t0)
                         ts.append(e0.elapsed_time(e1) / 1e3)
                     g = bytes_dir / statistics.median(ts) / 1e9
-                    cell[pname] = {"gbps": round(g, 3),
-                                   "pct_of_measured_peak": round(100 * g / link_peak[dname], 1)}
+                    q = np.percentile(np.asarray(walls), [10, 50, 90])
+                    c = {"gbps": round(g, 3),
+                         "pct_of_measured_peak": round(100 * g / link_peak[dname], 1),
+                         "wall_gbps": round(bytes_dir / q[1] / 1e9, 3),
+                         "wall_ms_p10_p50_p90": [round(x * 1e3, 3) for x in q],
+                         "reps": reps}
+                    if pname == "auto":
+                        c["chose"] = kvt.PATH_NAMES[pool.last_path(d)]
+                    cell[pname] = c
                 log("matrix %s" % json.dumps(cell))
                 rows.append(cell)
     return rows
+
+
+def matrix_specs(torch, kvt, workloads, shape, bufs, dev_b, dev_l, host_idx):
+    """The geometries of the layout x path matrix, one at a time (each yields its
+    device buffers, which are dropped before the next):
+      - the headline geometry (78 x 1152 B), 32768 tokens, contiguous pages;
+      - the same, 32768 tokens from 512 random pages of the 1024;
+      - a 32-layer K/V pool of 8 x 128 bf16 (2048 B rows) at 32768 tokens from
+        512 random pages of 2048 (4 GiB per direction);
+      - one tensor-parallel rank's share at TP 8: the K/V pool with one head
+        (256 B rows), 8192 tokens from random pages; and the headline geometry
+        with 4096 tokens (n/8)."""
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    base = {"L": L, "C": C, "R": R, "S_dev": shape.device_slots, "S_host": shape.host_slots,
+            "ps": ps, "bufs": bufs}
+    all_paths = tuple(p for p, _ in MATRIX_PATHS)
+    no_lds = ("kernel", "dma", "staged", "auto")
+    yield dict(base, label="mla 78x1152, 32768 tok, contiguous", dev_b=dev_b, dev_l=dev_l,
+               host_idx=host_idx, paths=all_paths)
+    pages_total = shape.device_slots // ps
+    np_ = host_idx.size // ps
+    fb = workloads.fragmented_pages(3, pages_total, np_, workloads.P_DEV)
+    rest = np.setdiff1d(np.arange(pages_total), fb)
+    fl = workloads.rng(3, workloads.P_RELOAD).permutation(rest)[:np_]
+    yield dict(base, label="mla 78x1152, 32768 tok, random pages",
+               dev_b=workloads.page_indices(fb, ps), dev_l=workloads.page_indices(fl, ps),
+               host_idx=host_idx, paths=no_lds)
+    k = 4096
+    yield dict(base, label="mla 78x1152, 4096 tok (TP8 share of 32768)", dev_b=dev_b[:k],
+               dev_l=dev_l[:k], host_idx=host_idx[:k], paths=no_lds)
+    g2 = workloads.llama8b()
+    for heads, tokens, label in ((8, 32768, "gqa 32x2x2048, 32768 tok, random pages"),
+                                 (1, 8192, "gqa 32x2x256 (TP8 share), 8192 tok, random pages")):
+        sh = g2.scaled(heads=heads, host_slots=tokens)
+        b2 = []
+        for l in range(sh.layers):
+            for c in range(sh.components):
+                t = torch.empty(sh.device_slots * sh.row_bytes, dtype=torch.uint8,
+                                device="cuda:0")
+                workloads.fill_device_buffer(t, sh, 2, l, c, torch)
+                b2.append(t)
+        tot = sh.device_slots // sh.page_size
+        npg = tokens // sh.page_size
+        pb = workloads.fragmented_pages(2, tot, npg, workloads.P_DEV)
+        rest = np.setdiff1d(np.arange(tot), pb)
+        pl = workloads.rng(2, workloads.P_RELOAD).permutation(rest)[:npg]
+        yield {"L": sh.layers, "C": sh.components, "R": sh.row_bytes, "S_dev": sh.device_slots,
+               "S_host": tokens, "ps": sh.page_size, "bufs": b2, "label": label,
+               "dev_b": workloads.page_indices(pb, sh.page_size),
+               "dev_l": workloads.page_indices(pl, sh.page_size),
+               "host_idx": np.arange(tokens, dtype=np.int64), "paths": no_lds}
+        del b2
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
 
 def _ev(torch):
@@ -696,10 +814,11 @@ def leg_streamed(torch, kvt, workloads, args):
             e1.record(s_comp)
             e1.synchronize()
         t_comp = e0.elapsed_time(e1) / 1e3
-        walls, h2d_ov = [], []
+        walls, h2d_ov, comp_ov = [], [], []
         for rep in range(3):
             torch.cuda.synchronize()
             ev = [_ev(torch) for _ in range(3)]
+            lev = [(_ev(torch), _ev(torch)) for _ in range(L)]
             ev[0].record(s_load.torch)
             s_comp.wait_event(ev[0])
             pool.load(dev_idx, host_idx, 0, L, s_load)
@@ -707,12 +826,15 @@ def leg_streamed(torch, kvt, workloads, args):
             with torch.cuda.stream(s_comp):
                 for l in range(L):
                     pool.load_layer(l, s_comp)
+                    lev[l][0].record(s_comp)          # layer l has landed
                     consume(l, k)
+                    lev[l][1].record(s_comp)
                 ev[2].record(s_comp)
             ev[2].synchronize()
             s_load.synchronize()
             walls.append(ev[0].elapsed_time(ev[2]) / 1e3)
             h2d_ov.append(L * layer_bytes / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
+            comp_ov.append(sum(a.elapsed_time(b) for a, b in lev) / 1e3)
         wall = statistics.median(walls)
         eta = (t_h2d + t_comp - wall) / min(t_h2d, t_comp)
         results[pname] = {"path_used": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
@@ -721,6 +843,8 @@ def leg_streamed(torch, kvt, workloads, args):
                           "compute_reps_per_layer": k,
                           "sum_h2d_ms": round(t_h2d * 1e3, 2),
                           "sum_compute_ms": round(t_comp * 1e3, 2),
+                          "sum_compute_overlapped_ms": round(statistics.median(comp_ov) * 1e3, 2),
+                          "compute_slowdown": round(statistics.median(comp_ov) / t_comp, 3),
                           "wall_ms": round(wall * 1e3, 2),
                           "overlap_efficiency": round(eta, 3)}
         log("streamed %s %s" % (pname, json.dumps(results[pname])))
@@ -734,9 +858,72 @@ def leg_streamed(torch, kvt, workloads, args):
             "paths": results}
 
 
+def host_memory_study(torch, kvt, workloads, sizes_gb):
+    """Pinned-size sweep: the headline request (32768 tokens x 78 layers x 1152 B,
+    contiguous device pages) against layer_first host pools of the given sizes.
+    The request's host rows are 512 random pages of the whole pool, so that the
+    pages it touches spread over all of it (a layer_first pool also puts each
+    layer in its own region). Per size: pool creation time, and device-event
+    GB/s of kernel and copy-engine backups and loads (median of 5)."""
+    shape = workloads.mla32k()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S_dev, n = shape.device_slots, shape.extra["tokens"]
+    bufs = []
+    for l in range(L):
+        b = torch.empty(S_dev * R, dtype=torch.uint8, device="cuda:0")
+        workloads.fill_device_buffer(b, shape, 3, l, 0, torch)
+        bufs.append(b)
+    first = workloads.contiguous_pages_at_offset(3, S_dev // ps, n // ps)
+    dev_idx = workloads.page_indices(first, ps)
+    s = torch.cuda.Stream()
+    nb = n * L * C * R
+    out = []
+    for gb in sizes_gb:
+        S_host = max(n, int(gb * 1e9 / (L * C * R)) // ps * ps)
+        host_pages = workloads.fragmented_pages(3, S_host // ps, n // ps, workloads.P_HOST)
+        host_idx = workloads.page_indices(host_pages, ps)
+        t0 = time.perf_counter()
+        try:
+            pool = kvt.KvPool(kvt.geometry(L, C, R, S_dev, S_host, ps, 0), bufs)
+        except kvt.KvError as e:        # the driver's pinned-memory limit
+            log("host pool of %.1f GB refused: %s" % (gb, e))
+            out.append({"host_pool_gb": round(S_host * L * C * R / 1e9, 2), "refused": str(e)})
+            continue
+        t_create = time.perf_counter() - t0
+        log("host pool %.1f GB created in %.1f s" % (pool.host_array().nbytes / 1e9, t_create))
+        cell = {"host_pool_gb": round(pool.host_array().nbytes / 1e9, 2),
+                "create_s": round(t_create, 2)}
+        for pname, p in (("kernel", kvt.PATH_KERNEL), ("dma", kvt.PATH_DMA)):
+            pool.set_path(p)
+            for dname, fn in (("d2h", lambda: pool.backup(dev_idx, host_idx, 0, L, s)),
+                              ("h2d", lambda: pool.load(dev_idx, host_idx, 0, L, s))):
+                fn()
+                s.synchronize()
+                ts = []
+                for _ in range(5):
+                    e0, e1 = _ev(torch), _ev(torch)
+                    e0.record(s)
+                    fn()
+                    e1.record(s)
+                    e1.synchronize()
+                    ts.append(e0.elapsed_time(e1) / 1e3)
+                cell["%s_%s_gbps" % (pname, dname)] = round(nb / statistics.median(ts) / 1e9, 3)
+        log("host memory %s" % json.dumps(cell))
+        out.append(cell)
+        t0 = time.perf_counter()
+        pool.close()
+        cell["destroy_s"] = round(time.perf_counter() - t0, 2)
+    return {"study": "pinned host pool size", "request": "32768 tokens x 78 x 1152 B, "
+            "512 random host pages, layer_first", "rows": out}
+
+
 def cpu_baseline(shape):
-    """The oracle (single thread, as it stands) on host mirrors: backup + load of a
-    4096-token prefix of the same 78-layer geometry, repeated for ~10 s."""
+    """The oracle as it stands on host mirrors: backup + load of a 4096-token
+    prefix of the same 78-layer geometry, repeated for ~6 s, first on one thread,
+    then on T threads that each run the oracle on their own slice of the layers
+    (T = the host's cores, at most 16; the oracle's C calls release the GIL).
+    `value` and `cores` are the T-thread figures."""
+    import threading
     import oracle
     L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
     n = 4096
@@ -747,18 +934,38 @@ def cpu_baseline(shape):
     d1 = np.arange(n, dtype=np.int64)
     d2 = np.arange(n, 2 * n, dtype=np.int64)
     h = np.arange(n, dtype=np.int64)
-    bytes_step = 2 * n * L * C * R
-    reps = 0
+
+    def loop(l0, l1, secs, out, k):
+        reps = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < secs or reps < 1:
+            assert oracle.backup(g, dev, host, d1, h, l0, l1) == 0
+            assert oracle.load(g, dev, host, d2, h, l0, l1) == 0
+            reps += 1
+        out[k] = reps * 2 * n * (l1 - l0) * C * R
+
+    one = [0]
+    loop(0, L, 0.0, one, 0)             # first touch of the mirrors, untimed
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 10.0 or reps < 2:
-        assert oracle.backup(g, dev, host, d1, h) == 0
-        assert oracle.load(g, dev, host, d2, h) == 0
-        reps += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(bytes_step * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+    loop(0, L, 6.0, one, 0)
+    dt1 = time.perf_counter() - t0
+    T = max(1, min(16, len(os.sched_getaffinity(0)), L))
+    cuts = np.linspace(0, L, T + 1).astype(int)
+    outs = [0] * T
+    th = [threading.Thread(target=loop, args=(int(cuts[k]), int(cuts[k + 1]), 6.0, outs, k))
+          for k in range(T)]
+    t0 = time.perf_counter()
+    for x in th:
+        x.start()
+    for x in th:
+        x.join()
+    dtT = time.perf_counter() - t0
+    return {"value": round(sum(outs) / dtT / 1e9, 3), "unit": "GB/s", "cores": T,
             "kind": "oracle",
-            "sample": "%d x (backup + load) of a 4096-token prefix, 78 layers x 1152 B rows, "
-                      "layer_first, host mirrors, one thread (%.1f s)" % (reps, dt)}
+            "single_thread_gbps": round(one[0] / dt1 / 1e9, 3),
+            "sample": "backup + load of a 4096-token prefix, 78 layers x 1152 B rows, "
+                      "layer_first, host mirrors: %d threads over layer slices for %.1f s "
+                      "(value), one thread for %.1f s (single_thread_gbps)" % (T, dtT, dt1)}
 
 
 if __name__ == "__main__":

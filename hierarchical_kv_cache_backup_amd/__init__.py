@@ -52,7 +52,9 @@ class kv_calib_t(ctypes.Structure):
                 ("overlap_kernel_max_workgroups", ctypes.c_double),
                 ("duplex_kernel_penalty", ctypes.c_double),
                 ("staged_chunk_bytes", ctypes.c_double),
-                ("staged_gather_gbps", ctypes.c_double)]
+                ("staged_gather_gbps", ctypes.c_double),
+                ("kernel_group_us", ctypes.c_double * 2),
+                ("staged_min_gain", ctypes.c_double)]
 
 
 class kv_stats_t(ctypes.Structure):

@@ -79,10 +79,12 @@ struct DirState {
   hipEvent_t done = nullptr;  // recorded at the end of every call of this direction
   bool done_pending = false;
   std::atomic<bool> done_recorded{false};  // read without the lock by the other direction
+  std::atomic<hipStream_t> done_stream{nullptr};  // the stream `done` was recorded on
   // staged path: two device staging halves (dense images of walk rows), an
   // auxiliary stream for the gather/scatter kernels, and the events that pass
   // each half between the copies (caller's stream) and the kernels (aux).
   std::vector<Extent> extents;
+  std::vector<int64_t> host_run_start;  // staged path: runs of host-consecutive positions
   uint8_t *stage = nullptr;      // 2 * stage_cap bytes
   int64_t stage_cap = 0;         // bytes per half
   hipEvent_t stage_ev = nullptr;  // the call's last use of the halves (on the caller's stream)
@@ -135,9 +137,15 @@ namespace {
 // Defaults measured on an MI355X (PCIe Gen5 x16 host link) with 1152-byte
 // rows: fixed cost per kernel call (launch, index staging, ramp) ~30 us and per
 // copy-engine call ~9.5 us, both from requests of 64..32768 tokens x 78 layers;
-// sustained rates at 2.9 GB per call. bench.py re-measures the rates live.
+// ~7 us between back-to-back per-layer launches of one load (kernel trace
+// against event time); sustained rates at 2.9 GB per call. bench.py re-fits
+// the rates live.
 void default_calibration(kv_calib_t *c) {
   c->kernel_launch_us[0] = c->kernel_launch_us[1] = 30.0;
+  c->kernel_group_us[0] = c->kernel_group_us[1] = 7.0;
+  // in isolation the staged path ties the direct paths (all at the link rate);
+  // it pays off where they are slowed (fragmented copies beside compute)
+  c->staged_min_gain = 0.05;
   c->kernel_gbps[0] = 55.9;
   c->kernel_gbps[1] = 56.1;
   c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
@@ -365,11 +373,13 @@ static hipError_t device_streams(int device, DeviceStreams **out) {
   return hipSuccess;
 }
 
-// True while the other direction has a transfer in flight on this pool (its
-// completion event is recorded and not yet reached).
-static bool other_direction_busy(kv_pool *p, int dir) {
+// True while the other direction has a transfer in flight on this pool on
+// another stream than s (its completion event is recorded and not yet
+// reached). Work of the other direction queued on s itself runs before this
+// call's, not beside it.
+static bool other_direction_busy(kv_pool *p, int dir, hipStream_t s) {
   DirState &o = p->dir[1 - dir];
-  if (!o.done_recorded.load()) return false;
+  if (!o.done_recorded.load() || o.done_stream.load() == s) return false;
   return hipEventQuery(o.done) == hipErrorNotReady;
 }
 
@@ -431,7 +441,7 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
                               const int64_t *host_idx, int32_t la, int32_t lb, uint32_t cap,
                               hipStream_t s) {
   const Geom &g = p->g;
-  build_extents(g, host_idx, (int64_t)b.n, la, lb, &d.extents);
+  build_extents(g, host_idx, (int64_t)b.n, d.host_run_start, la, lb, &d.extents);
   plan_rows(&b, g.layout, g.ps);
   const int64_t chunk_rows = d.stage_cap / g.R;
   const int64_t walk_rows = b.total_rows;
@@ -531,27 +541,32 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   const int32_t ngroups = (l1 - l0 + group - 1) / group;
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
-  const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir);
+  const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
   const uint32_t cap = kernel_cap(c, dir, overlap);
 
   // ---- path selection
   int32_t path = p->path.load();
-  bool have_copies = false;
+  bool have_copies = false, have_host_runs = false;
   if (path == KV_PATH_AUTO) {
     build_runs(g, dev_idx, host_idx, n, &d.runs);
     build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
     have_copies = true;
-    build_extents(g, host_idx, n, l0, l1, &d.extents);
+    host_runs(g, host_idx, n, &d.host_run_start);
+    have_host_runs = true;
+    build_extents(g, host_idx, n, d.host_run_start, l0, l1, &d.extents);
     const double mb = (double)bytes;
-    double t_kernel = ngroups * c.kernel_launch_us[dir] + mb / (c.kernel_gbps[dir] * 1e3);
+    double t_kernel = c.kernel_launch_us[dir] + (ngroups - 1) * c.kernel_group_us[dir] +
+                      mb / (c.kernel_gbps[dir] * 1e3);
     double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
                    mb / (c.dma_gbps[dir] * 1e3);
-    // the staged path moves page-major layouts in one unit (see below)
+    // the staged path moves page-major layouts in one unit (see below); its
+    // device-side passes overlap the copies except for the first chunk's
     const double extents = (double)d.extents.size();
     const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
     const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units;
-    double t_staged = extents * c.dma_copy_us[dir] + chunks * c.kernel_launch_us[dir] +
-                      mb / (c.dma_gbps[dir] * 1e3) + mb / (c.staged_gather_gbps * 1e3);
+    double t_staged = extents * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
+                      (chunks - 1) * c.kernel_group_us[dir] + mb / (c.dma_gbps[dir] * 1e3) +
+                      std::min(mb, c.staged_chunk_bytes) / (c.staged_gather_gbps * 1e3);
     if (overlap) {
       t_kernel *= 1.0 + c.overlap_kernel_penalty;
       t_dma *= 1.0 + c.overlap_dma_penalty;
@@ -564,7 +579,9 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       best = t_dma;
       path = KV_PATH_DMA;
     }
-    if (t_staged < best) path = KV_PATH_STAGED;
+    // the staged path also takes HBM bandwidth, compute units and a second
+    // stream, so it must win by a margin
+    if (t_staged < best * (1.0 - c.staged_min_gain)) path = KV_PATH_STAGED;
   }
   if (path == KV_PATH_KERNEL_LDS && g.R > kMaxLdsRowBytes) path = KV_PATH_KERNEL;
   // In page_first / page_first_direct a host page holds every layer of its
@@ -619,6 +636,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       }
       rc = stage_begin(d, g, n * (int64_t)std::min<int32_t>(group, l1 - l0) * g.C * g.R, c, s);
       if (rc) return rc;
+      if (!have_host_runs) host_runs(g, host_idx, n, &d.host_run_start);
     }
     for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
       const int32_t lb = std::min(l1, la + group);
@@ -657,6 +675,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   e = hipEventRecord(d.done, s);
   if (e != hipSuccess) return hip_fail(e, "recording the completion event");
   d.done_pending = true;
+  d.done_stream.store(s);
   d.done_recorded.store(true);
   d.last_path.store(path);
   d.calls++;
@@ -890,6 +909,7 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
   if (!p || !c) return fail(KV_EINVAL, "pool and calibration must be non-null");
   for (int d = 0; d < 2; d++)
     if (!(c->kernel_gbps[d] > 0) || !(c->dma_gbps[d] > 0) || !(c->kernel_launch_us[d] >= 0) ||
+        !(c->kernel_group_us[d] >= 0) ||
         !(c->dma_copy_us[d] >= 0))
       return fail(KV_EINVAL, "calibration figures must be positive");
   if (!(c->load_split_min_bytes >= 0)) return fail(KV_EINVAL, "load_split_min_bytes must be >= 0");
@@ -900,7 +920,7 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
       !(c->overlap_kernel_penalty >= 0) || !(c->overlap_dma_penalty >= 0))
     return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
   if (!(c->duplex_kernel_penalty >= 0) || !(c->staged_chunk_bytes >= 16) ||
-      !(c->staged_gather_gbps > 0))
+      !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
     return fail(KV_EINVAL, "duplex penalty >= 0, staged chunk >= 16 bytes and gather rate > 0");
   std::lock_guard<std::mutex> lock(p->calib_mu);
   p->calib = *c;

@@ -170,7 +170,17 @@ void build_copies(const Geom &g, const std::vector<Run> &runs, const int64_t *de
   }
 }
 
-void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la, int32_t lb,
+void host_runs(const Geom &g, const int64_t *host_idx, int64_t n, std::vector<int64_t> *start) {
+  start->clear();
+  if (n <= 0) return;
+  start->push_back(0);
+  for (int64_t i = 1; i < n; i++)
+    if (host_key(g, host_idx[i]) != host_key(g, host_idx[i - 1]) + 1) start->push_back(i);
+  start->push_back(n);
+}
+
+void build_extents(const Geom &g, const int64_t *host_idx, int64_t n,
+                   const std::vector<int64_t> &run_start, int32_t la, int32_t lb,
                    std::vector<Extent> *out) {
   out->clear();
   if (n <= 0 || lb <= la) return;
@@ -192,13 +202,6 @@ void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la
     for (int64_t i = 0; i < n; i++) append(i * nlc, host_key(g, host_idx[i]) + lc0, nlc);
     return;
   }
-  // runs of positions whose host keys advance by one (independent of the pair)
-  std::vector<int64_t> run_start;
-  run_start.reserve(64);
-  run_start.push_back(0);
-  for (int64_t i = 1; i < n; i++)
-    if (host_key(g, host_idx[i]) != host_key(g, host_idx[i - 1]) + 1) run_start.push_back(i);
-  run_start.push_back(n);
   size_t first_run = 0;  // first run that reaches into the current group
   for (int64_t g0 = 0; g0 < n; g0 += G) {
     const int64_t gsz = std::min(G, n - g0);
@@ -214,6 +217,13 @@ void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la
       }
     }
   }
+}
+
+void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la, int32_t lb,
+                   std::vector<Extent> *out) {
+  std::vector<int64_t> run_start;
+  host_runs(g, host_idx, n, &run_start);
+  build_extents(g, host_idx, n, run_start, la, lb, out);
 }
 
 }  // namespace kvt

@@ -102,4 +102,12 @@ struct Extent {
 void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la, int32_t lb,
                    std::vector<Extent> *out);
 
+// The same in two steps, so that a call split into layer groups finds the runs
+// of host-consecutive positions once (O(n)) and then pays O(pairs x runs) per
+// group: host_runs writes the first position of every run and then n.
+void host_runs(const Geom &g, const int64_t *host_idx, int64_t n, std::vector<int64_t> *start);
+void build_extents(const Geom &g, const int64_t *host_idx, int64_t n,
+                   const std::vector<int64_t> &run_start, int32_t la, int32_t lb,
+                   std::vector<Extent> *out);
+
 }  // namespace kvt

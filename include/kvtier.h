@@ -113,7 +113,9 @@ typedef enum {
 #define KV_F_DUPLEX           0x8u /* backups and loads on this pool run at the same time: the
                                       selector charges the kernel path the duplex penalty.
                                       Without it the charge applies only while the other
-                                      direction has a transfer in flight at submission. */
+                                      direction has a transfer in flight at submission on
+                                      another stream (work queued on the same stream runs
+                                      before this call, not beside it). */
 #define KV_F_LOAD_OVERLAP     0x4u /* loads on this pool run while compute kernels occupy the GPU
                                       (layer-wise load during the forward pass): the selector
                                       charges each path the compute time it steals, and the
@@ -142,9 +144,13 @@ typedef struct {
 } kv_pool_desc_t;
 
 /* Selector calibration: modelled time of a call on each path.
- *   t_kernel = launches * kernel_launch_us + bytes / kernel_gbps
+ *   t_kernel = kernel_launch_us + (launches - 1) * kernel_group_us
+ *              + bytes / kernel_gbps
  *   t_dma    = copies * dma_copy_us + bytes / dma_gbps
- * The four figures are measured per direction on the target machine.
+ * kernel_launch_us is the fixed cost of a call's first launch (launch, index
+ * staging, ramp), kernel_group_us the gap each further launch of the same
+ * call adds. The rates are fitted per direction on the target machine to the
+ * time a call takes less its modelled fixed costs.
  * load_split_min_bytes: kv_load goes out in groups of consecutive layers, one
  * kernel launch (or one batch of copies) and one landed event per group; a
  * group is one layer when a layer of the request holds at least this many
@@ -159,8 +165,10 @@ typedef struct {
  * fractions of the transfer time by which a concurrent HBM-bound kernel is
  * slowed, measured per path; and the kernel path launches at most
  * overlap_kernel_max_workgroups workgroups.
- * The staged path is modelled as extents * dma_copy_us + chunks *
- * kernel_launch_us + bytes / dma_gbps + bytes / staged_gather_gbps. */
+ * The staged path is modelled as extents * dma_copy_us + kernel_launch_us +
+ * (chunks - 1) * kernel_group_us + bytes / dma_gbps + min(bytes,
+ * staged_chunk_bytes) / staged_gather_gbps: its device-side passes overlap the
+ * copies except for the first chunk's. */
 typedef struct {
   double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
   double kernel_gbps[2];
@@ -174,6 +182,9 @@ typedef struct {
   double duplex_kernel_penalty; /* kernel-path slowdown while the other direction is busy */
   double staged_chunk_bytes;    /* staged path: staging buffer size per direction */
   double staged_gather_gbps;    /* staged path: device-side gather/scatter rate */
+  double kernel_group_us[2];    /* gap per further kernel launch of one call */
+  double staged_min_gain;       /* AUTO takes the staged path only if its modelled time is
+                                   below (1 - staged_min_gain) x the best direct path's */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

@@ -386,3 +386,37 @@ def test_library_streams_round_trip(torch, path):
     s_load.close()
     pool.close()
     pool2.close()
+
+
+def test_staged_margin_steers_selector(torch, stream):
+    """AUTO takes the staged path only when its modelled time beats the best
+    direct path by staged_min_gain; bytes match the oracle either way."""
+    g = Geometry(2, 1, 64, 256, 256, 8, oracle.LAYER_FIRST)
+    bufs = device_buffers(g, seed=14)
+    rng = np.random.default_rng(14)
+    d = rng.permutation(g.S_dev)[:64].astype(np.int64)   # 64 single-slot device runs
+    h = np.arange(64, dtype=np.int64)                     # one host run per layer
+    pool = make_pool(g, bufs, kvt.PATH_AUTO, flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
+    c = pool.calibration()
+    # kernel: 10 us x (1 + 100) = 1010 us; copy engines: 128 copies x 100 us;
+    # staged: 2 extents x 100 us + 10 us + 7 us + ~0 = ~217 us
+    c.kernel_launch_us[:] = [10.0, 10.0]
+    c.kernel_group_us[:] = [7.0, 7.0]
+    c.dma_copy_us[:] = [100.0, 100.0]
+    c.kernel_gbps[:] = [1e6, 1e6]
+    c.dma_gbps[:] = [1e6, 1e6]
+    c.staged_gather_gbps = 1e6
+    c.duplex_kernel_penalty = 100.0
+    for gain, want in ((0.9, kvt.PATH_KERNEL), (0.5, kvt.PATH_STAGED)):
+        c.staged_min_gain = gain
+        pool.set_calibration(c)
+        print("staged margin gain=%.1f" % gain, flush=True)
+        run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        assert pool.last_path(kvt.BACKUP) == want
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        assert pool.last_path(kvt.LOAD) == want
+    c.staged_min_gain = 1.0
+    with pytest.raises(kvt.KvError):
+        pool.set_calibration(c)
+    pool.close()

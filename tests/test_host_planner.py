@@ -154,3 +154,31 @@ def test_replay_driver_under_sanitizers(tmp_path):
     res = subprocess.run([str(exe), "160"], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "0 failures" in res.stdout
+
+
+def test_binding_structs_match_header(kvt, tmp_path):
+    """The ctypes structures have the header's size and field offsets (a C
+    program built against include/kvtier.h prints them)."""
+    import ctypes
+    structs = {"kv_geometry_t": kvt.kv_geometry_t, "kv_pool_desc_t": kvt.kv_pool_desc_t,
+               "kv_calib_t": kvt.kv_calib_t, "kv_stats_t": kvt.kv_stats_t}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "kvtier.h"',
+             "int main(void) {"]
+    for name, cls in structs.items():
+        lines.append('  printf("%s size %%zu\\n", sizeof(%s));' % (name, name))
+        for f, _ in cls._fields_:
+            lines.append('  printf("%s %s %%zu\\n", offsetof(%s, %s));' % (name, f, name, f))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src),
+                           "-o", str(exe)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        a, b, v = line.split()
+        got[(a, b)] = int(v)
+    for name, cls in structs.items():
+        assert got[(name, "size")] == ctypes.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)
