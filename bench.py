@@ -267,6 +267,7 @@ def main():
         torch.cuda.empty_cache()
         extra["streamed_per_layer"] = leg_streamed(torch, kvt, workloads, args)
         torch.cuda.empty_cache()
+        extra["ghost_list"] = leg_ghost_list(kvt, workloads)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(shape)
@@ -856,6 +857,80 @@ def leg_streamed(torch, kvt, workloads, args):
                         "per-layer H2D overlapped with an HBM-bound consumer",
             "layer_bytes": layer_bytes, "consumer_pass_ms": round(t_pass * 1e3, 3),
             "paths": results}
+
+
+def leg_ghost_list(kvt, workloads):
+    """The write-through-selective filter (host only): page-boundary hashing of
+    the mixed batch's token sequences (seeded random ids, page 64), inserting
+    evicted page hashes into a Ghost List of 1,048,576 entries (64 per call, as
+    a request's pages leave the GPU pool, and all in one call), and proven-reuse
+    scans of 64-page prefixes (half of them with a hit). The oracle is timed
+    beside it on a sample of the same operations."""
+    from oracle import ghost
+    rng = np.random.default_rng([4, 6])
+    ps = 64
+    lens, _, _ = workloads.mixed_requests(workloads.mixed(), 4)
+    seqs = [rng.integers(0, 150000, size=int(n), dtype=np.int64).astype(np.int32) for n in lens]
+    ntok = int(sum(x.size for x in seqs))
+    t0 = time.perf_counter()
+    hashes = [kvt.kv_page_hashes(x, ps) for x in seqs]
+    t_hash = time.perf_counter() - t0
+    cap = 1 << 20
+    g = kvt.GhostList(cap)
+    stream = rng.integers(0, 2**63, size=2 * cap, dtype=np.int64).astype(np.uint64)
+    batches = np.array_split(stream, stream.size // 64)
+    t0 = time.perf_counter()
+    for b in batches:
+        g.insert(b)
+    t_ins = time.perf_counter() - t0
+    g2 = kvt.GhostList(cap)                    # the same inserts in one call
+    t0 = time.perf_counter()
+    g2.insert(stream)
+    t_ins1 = time.perf_counter() - t0
+    g2.close()
+    held = np.asarray(g.order()[-cap // 2:], dtype=np.uint64)
+    queries = []
+    for k in range(10000):
+        q = rng.integers(0, 2**63, size=64, dtype=np.int64).astype(np.uint64)
+        if k % 2 == 0:
+            q[int(rng.integers(0, 64))] = held[int(rng.integers(0, held.size))]
+        queries.append(q)
+    t0 = time.perf_counter()
+    hits = sum(1 for q in queries if g.reuse_prefix(q) > 0)
+    t_scan = time.perf_counter() - t0
+    g.close()
+    # oracle on samples
+    og = ghost.GhostList(cap)
+    sample = stream[:200_000].tolist()
+    t0 = time.perf_counter()
+    for j in range(0, len(sample), 64):
+        og.insert(sample[j:j + 64])
+    t_oins = time.perf_counter() - t0
+    oq = [q.tolist() for q in queries[:2000]]
+    t0 = time.perf_counter()
+    for q in oq:
+        og.reuse_prefix(q)
+    t_oscan = time.perf_counter() - t0
+    tok_sample = seqs[0][:64 * ps].tolist()
+    t0 = time.perf_counter()
+    ghost.page_hashes(tok_sample, ps)
+    t_ohash = time.perf_counter() - t0
+    out = {"workload": "page 64; hashing: the mixed batch's %d tokens in %d requests; "
+                       "Ghost List of %d entries: %d inserts in batches of 64, 10000 "
+                       "proven-reuse scans of 64 pages (%d with a hit)"
+                       % (ntok, len(seqs), cap, stream.size, hits),
+           "hash_tokens_per_s": round(ntok / t_hash),
+           "insert_per_s_one_call": round(stream.size / t_ins1),
+           "insert_per_s": round(stream.size / t_ins),
+           "scan_pages_per_s": round(10000 * 64 / t_scan),
+           "oracle": {"hash_tokens_per_s": round(len(tok_sample) / t_ohash),
+                      "insert_per_s": round(len(sample) / t_oins),
+                      "scan_pages_per_s": round(len(oq) * 64 / t_oscan),
+                      "sample": "hashing: one 4096-token sequence (every page hash recomputed "
+                                "from the root, as the oracle defines it); 200,000 inserts; "
+                                "2,000 scans"}}
+    log("ghost list %s" % json.dumps(out))
+    return out
 
 
 def host_memory_study(torch, kvt, workloads, sizes_gb):

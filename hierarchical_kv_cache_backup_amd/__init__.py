@@ -63,11 +63,12 @@ class kv_stats_t(ctypes.Structure):
                 ("submit_us", ctypes.c_double * 2), ("blocked_us", ctypes.c_double * 2)]
 
 
-# Every symbol include/kvtier.h declares, with its ctypes signature.
+# Every symbol include/kvtier.h and include/kvghost.h declare, with its ctypes signature.
 _P64 = ctypes.POINTER(ctypes.c_int64)
 _VP = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
 _GEOM = ctypes.POINTER(kv_geometry_t)
+_PU64 = ctypes.POINTER(ctypes.c_uint64)
 SIGNATURES = {
     "kv_geometry_check": (_I32, [_GEOM]),
     "kv_host_row": (_I64, [_GEOM, _I32, _I32, _I64]),
@@ -89,6 +90,14 @@ SIGNATURES = {
     "kv_get_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
     "kv_get_stats": (_I32, [_VP, ctypes.POINTER(kv_stats_t)]),
     "kv_last_error": (ctypes.c_char_p, []),
+    "kv_page_hashes": (_I64, [ctypes.POINTER(ctypes.c_int32), _I64, _I32, _PU64]),
+    "kv_ghost_create": (_I32, [_I64, ctypes.POINTER(_VP)]),
+    "kv_ghost_destroy": (_I32, [_VP]),
+    "kv_ghost_insert": (_I32, [_VP, _PU64, _I64]),
+    "kv_ghost_reuse_prefix": (_I64, [_VP, _PU64, _I64]),
+    "kv_ghost_contains": (_I32, [_VP, ctypes.c_uint64]),
+    "kv_ghost_size": (_I64, [_VP]),
+    "kv_ghost_snapshot": (_I64, [_VP, _PU64, _I64]),
 }
 
 
@@ -287,6 +296,93 @@ def kv_get_stats(pool):
 
 
 # ---- convenience object over torch device buffers ------------------------------
+
+def _u64(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.uint64))
+    return a, a.ctypes.data_as(_PU64)
+
+
+def kv_page_hashes(tokens, page_size):
+    """Page-boundary hashes of a token sequence (uint64 numpy array)."""
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+    out = np.zeros(max(t.size // max(int(page_size), 1), 1), dtype=np.uint64)
+    rc = _lib.kv_page_hashes(t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), t.size,
+                             int(page_size), out.ctypes.data_as(_PU64))
+    _check(rc)
+    return out[:rc]
+
+
+def kv_ghost_create(capacity):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    rc = _lib.kv_ghost_create(int(capacity), ctypes.byref(h))
+    return rc, h.value
+
+
+def kv_ghost_destroy(g):
+    return _lib.kv_ghost_destroy(g)
+
+
+def kv_ghost_insert(g, hashes):
+    a, p = _u64(hashes)
+    return _lib.kv_ghost_insert(g, p, a.size)
+
+
+def kv_ghost_reuse_prefix(g, hashes):
+    a, p = _u64(hashes)
+    return _lib.kv_ghost_reuse_prefix(g, p, a.size)
+
+
+def kv_ghost_contains(g, h):
+    return _lib.kv_ghost_contains(g, int(h) & 0xFFFFFFFFFFFFFFFF)
+
+
+def kv_ghost_size(g):
+    return _lib.kv_ghost_size(g)
+
+
+def kv_ghost_snapshot(g, max_entries):
+    out = np.zeros(max(int(max_entries), 1), dtype=np.uint64)
+    rc = _lib.kv_ghost_snapshot(g, out.ctypes.data_as(_PU64), int(max_entries))
+    _check(rc)
+    return out[:rc]
+
+
+class GhostList:
+    """The Ghost List of evicted page hashes (kv_ghost_*)."""
+
+    def __init__(self, capacity):
+        rc, h = kv_ghost_create(capacity)
+        _check(rc)
+        self.handle = h
+        self.capacity = int(capacity)
+
+    def insert(self, hashes):
+        _check(kv_ghost_insert(self.handle, hashes))
+
+    def reuse_prefix(self, hashes):
+        return _check(kv_ghost_reuse_prefix(self.handle, hashes))
+
+    def contains(self, h):
+        return bool(_check(kv_ghost_contains(self.handle, h)))
+
+    def size(self):
+        return _check(kv_ghost_size(self.handle))
+
+    def order(self):
+        return [int(x) for x in kv_ghost_snapshot(self.handle, self.capacity)]
+
+    def close(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            kv_ghost_destroy(h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
 
 class KvPool:
     """Owns a library pool over L*C torch uint8 device tensors (borrowed: kept

@@ -1,12 +1,13 @@
 """Host-side checks of libkvtier.so that need no GPU.
 
-* the shared library loads and exports every function include/kvtier.h declares;
+* the shared library loads and exports every function include/*.h declares;
 * the planner's entry points (address map, validation, segment and copy counts)
   agree with the oracle, element by element;
 * a host-compiled replay driver (tests/host/walk_check.cpp, AddressSanitizer +
   UBSan) runs every launch plan of the kernels and of the copy-engine path on
   CPU mirrors and compares the bytes with the oracle.
 """
+import glob
 import os
 import re
 import subprocess
@@ -19,12 +20,12 @@ from oracle import Geometry, LAYOUTS
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-HEADER = os.path.join(ROOT, "include", "kvtier.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 CSRC = os.path.join(ROOT, "hierarchical_kv_cache_backup_amd", "csrc")
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(kv_[a-z_0-9]+)\s*\(", text)))
 
@@ -182,3 +183,14 @@ def test_binding_structs_match_header(kvt, tmp_path):
         assert got[(name, "size")] == ctypes.sizeof(cls), name
         for f, _ in cls._fields_:
             assert got[(name, f)] == getattr(cls, f).offset, (name, f)
+
+
+def test_ghost_list_under_sanitizers(tmp_path):
+    exe = tmp_path / "ghost_check"
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-I" + os.path.join(ROOT, "include"),
+                           os.path.join(HERE, "host", "ghost_check.cpp"),
+                           os.path.join(CSRC, "ghost.cpp"), "-o", str(exe), "-lpthread"] + san)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 failures" in res.stdout
