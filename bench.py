@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--host-memory-study", type=float, nargs="+", metavar="GB",
                    help="only measure the headline request against pinned host pools of "
                         "these sizes (GB), then exit")
+    p.add_argument("--free-list-study", action="store_true",
+                   help="only run the FIFO-vs-LIFO host free-list churn study, then exit")
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -76,6 +78,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.host_memory_study:
         print(json.dumps(host_memory_study(torch, kvt, workloads, args.host_memory_study)))
+        return
+    if args.free_list_study:
+        print(json.dumps(free_list_study(torch, kvt, workloads)))
         return
     dev = torch.device("cuda:0")
     shape = workloads.mla32k()
@@ -990,6 +995,105 @@ def host_memory_study(torch, kvt, workloads, sizes_gb):
         cell["destroy_s"] = round(time.perf_counter() - t0, 2)
     return {"study": "pinned host pool size", "request": "32768 tokens x 78 x 1152 B, "
             "512 random host pages, layer_first", "rows": out}
+
+
+def free_list_study(torch, kvt, workloads, count=160):
+    """FIFO vs LIFO host free list under churn. A stream of write-back requests
+    (lengths like the mixed batch's, at most 512 pages) goes into a host pool of
+    2048 pages (131072 tokens of the 78 x 1152 B MLA latent, 11.8 GB) while at
+    most 512 pages stay cached: before each request the oldest cached requests
+    are evicted (their pages freed) until it fits, then its pages are allocated
+    and its KV is backed up. The allocation sequence depends only on the policy,
+    so it is planned once per policy and replayed on each path. Reported per
+    layout and policy: distinct host pages written, runs of consecutive host
+    pages per request, copy-engine copies per request, allocator time per
+    request (median, binding included), and D2H GB/s (device events summed
+    over the requests) on the
+    kernel, copy-engine and AUTO paths."""
+    import collections
+    shape = workloads.mla32k()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S_dev = shape.device_slots
+    pool_pages, cap_pages = 2048, 512
+    S_host = pool_pages * ps
+    reqs = workloads.churn_requests(shape, 6, count, S_dev // ps, cap_pages)
+    bufs = []
+    for l in range(L):
+        b = torch.empty(S_dev * R, dtype=torch.uint8, device="cuda:0")
+        workloads.fill_device_buffer(b, shape, 6, l, 0, torch)
+        bufs.append(b)
+    s = torch.cuda.Stream()
+    rows = []
+    for layout in (kvt.LAYER_FIRST, kvt.PAGE_FIRST_DIRECT):
+        geom = kvt.geometry(L, C, R, S_dev, S_host, ps, layout)
+        pool = kvt.KvPool(geom, bufs)
+        for pname, policy in (("fifo", kvt.FREE_FIFO), ("lifo", kvt.FREE_LIFO)):
+            alloc = kvt.HostPages(pool_pages, policy)
+            live, live_pages, plan = collections.deque(), 0, []
+            t_alloc = []
+            for npg, first in reqs:
+                t0 = time.perf_counter()
+                while live_pages + npg > cap_pages:
+                    old = live.popleft()
+                    alloc.free(old)
+                    live_pages -= len(old)
+                pages = alloc.alloc(npg)
+                t_alloc.append(time.perf_counter() - t0)
+                live.append(pages)
+                live_pages += npg
+                plan.append((workloads.page_indices(np.arange(first, first + npg), ps),
+                             workloads.page_indices(pages, ps), pages))
+            alloc.close()
+            touched = len(set(int(p) for _, _, pg in plan for p in pg))
+            runs = [1 + int(np.count_nonzero(np.diff(pg) != 1)) for _, _, pg in plan]
+            copies = [kvt.kv_count_dma_copies(geom, d, h, 0, L)[1] for d, h, _ in plan]
+            total = sum(len(d) for d, _, _ in plan) * L * C * R
+            cell = {"layout": workloads.LAYOUT_NAMES[layout], "policy": pname,
+                    "requests": len(plan), "pool_pages": pool_pages, "cached_pages_max": cap_pages,
+                    "distinct_host_pages_written": touched,
+                    "host_page_runs_per_request": round(statistics.mean(runs), 2),
+                    "dma_copies_per_request": round(statistics.mean(copies), 1),
+                    "alloc_free_us_per_request_median": round(statistics.median(t_alloc) * 1e6, 2),
+                    "bytes": total}
+            for path_name, path in (("kernel", kvt.PATH_KERNEL), ("dma", kvt.PATH_DMA),
+                                    ("auto", kvt.PATH_AUTO)):
+                pool.set_path(path)
+                d0, h0, _ = plan[0]
+                pool.backup(d0, h0, 0, L, s)
+                s.synchronize()
+                evs = []
+                for d, h, _ in plan:
+                    e0, e1 = _ev(torch), _ev(torch)
+                    e0.record(s)
+                    pool.backup(d, h, 0, L, s)
+                    e1.record(s)
+                    evs.append((e0, e1))
+                s.synchronize()
+                t = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+                cell["%s_gbps" % path_name] = round(total / t / 1e9, 3)
+            log("free list %s" % json.dumps(cell))
+            rows.append(cell)
+        pool.close()
+    # the oracle's free list on the same churn (CPU baseline of the allocator)
+    from oracle import slots as oracle_slots
+    base = {}
+    for pname, policy in (("fifo", oracle_slots.FIFO), ("lifo", oracle_slots.LIFO)):
+        fl = oracle_slots.FreeList(pool_pages, policy)
+        live, live_pages, ts = collections.deque(), 0, []
+        for npg, _ in reqs:
+            t0 = time.perf_counter()
+            while live_pages + npg > cap_pages:
+                old = live.popleft()
+                fl.release(old)
+                live_pages -= len(old)
+            live.append(fl.alloc(npg)[1])
+            live_pages += npg
+            ts.append(time.perf_counter() - t0)
+        base[pname + "_alloc_free_us_per_request_median"] = round(statistics.median(ts) * 1e6, 2)
+    return {"study": "FIFO vs LIFO host free list under churn",
+            "request": "%d write-backs, 78 x 1152 B rows, page 64, lengths lognormal(median 4096 "
+                       "tokens, sigma 1) capped at 512 pages" % len(reqs),
+            "rows": rows, "cpu_baseline": dict(base, kind="oracle", cores=1)}
 
 
 def cpu_baseline(shape):

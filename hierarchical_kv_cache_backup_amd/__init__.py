@@ -27,6 +27,7 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel
               PATH_DMA: "dma", PATH_STAGED: "staged", -1: "none"}
 F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP, F_DUPLEX = 0x1, 0x2, 0x4, 0x8
 BACKUP, LOAD = 0, 1
+FREE_FIFO, FREE_LIFO = 0, 1
 
 
 class kv_geometry_t(ctypes.Structure):
@@ -63,7 +64,7 @@ class kv_stats_t(ctypes.Structure):
                 ("submit_us", ctypes.c_double * 2), ("blocked_us", ctypes.c_double * 2)]
 
 
-# Every symbol include/kvtier.h and include/kvghost.h declare, with its ctypes signature.
+# Every symbol include/*.h declare, with its ctypes signature.
 _P64 = ctypes.POINTER(ctypes.c_int64)
 _VP = ctypes.c_void_p
 _I32, _I64 = ctypes.c_int32, ctypes.c_int64
@@ -98,6 +99,12 @@ SIGNATURES = {
     "kv_ghost_contains": (_I32, [_VP, ctypes.c_uint64]),
     "kv_ghost_size": (_I64, [_VP]),
     "kv_ghost_snapshot": (_I64, [_VP, _PU64, _I64]),
+    "kv_slots_create": (_I32, [_I64, _I32, ctypes.POINTER(_VP)]),
+    "kv_slots_destroy": (_I32, [_VP]),
+    "kv_slots_alloc": (_I32, [_VP, _I64, _P64]),
+    "kv_slots_free": (_I32, [_VP, _P64, _I64]),
+    "kv_slots_available": (_I64, [_VP]),
+    "kv_slots_snapshot": (_I64, [_VP, _P64, _I64]),
 }
 
 
@@ -376,6 +383,75 @@ class GhostList:
         if self.handle:
             h, self.handle = self.handle, None
             kv_ghost_destroy(h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kv_slots_create(num_pages, policy):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    rc = _lib.kv_slots_create(int(num_pages), int(policy), ctypes.byref(h))
+    return rc, h.value
+
+
+def kv_slots_destroy(a):
+    return _lib.kv_slots_destroy(a)
+
+
+def kv_slots_alloc(a, n):
+    """Returns (status, int64 numpy array of the pages taken)."""
+    out = np.zeros(max(int(n), 1), dtype=np.int64)
+    rc = _lib.kv_slots_alloc(a, int(n), out.ctypes.data_as(_P64))
+    return rc, (out[:int(n)] if rc == OK else out[:0])
+
+
+def kv_slots_free(a, pages):
+    p, pp = _idx(pages)
+    return _lib.kv_slots_free(a, pp, p.size)
+
+
+def kv_slots_available(a):
+    return _lib.kv_slots_available(a)
+
+
+def kv_slots_snapshot(a, max_entries):
+    out = np.zeros(max(int(max_entries), 1), dtype=np.int64)
+    rc = _lib.kv_slots_snapshot(a, out.ctypes.data_as(_P64), int(max_entries))
+    _check(rc)
+    return out[:rc]
+
+
+class HostPages:
+    """Page allocator of the host pool with a FIFO or LIFO free list (kv_slots_*)."""
+
+    def __init__(self, num_pages, policy=FREE_FIFO):
+        rc, h = kv_slots_create(num_pages, policy)
+        _check(rc)
+        self.handle = h
+        self.num_pages = int(num_pages)
+
+    def alloc(self, n):
+        rc, pages = kv_slots_alloc(self.handle, n)
+        _check(rc)
+        return pages
+
+    def free(self, pages):
+        _check(kv_slots_free(self.handle, pages))
+
+    def available(self):
+        return _check(kv_slots_available(self.handle))
+
+    def order(self):
+        return kv_slots_snapshot(self.handle, self.num_pages)
+
+    def close(self):
+        if self.handle:
+            h, self.handle = self.handle, None
+            kv_slots_destroy(h)
 
     def __del__(self):
         try:

@@ -8,7 +8,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvtier.so")
-SOURCES = ["plan.cpp", "kernels.hip", "kvtier.cpp", "ghost.cpp"]
+SOURCES = ["plan.cpp", "kernels.hip", "kvtier.cpp", "ghost.cpp", "slots.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",

@@ -201,6 +201,25 @@ def mixed_plan(shape, cfg=4, scale=1.0, fragmented=False):
             "d2h": (cat(d2h_dev), cat(d2h_host))}
 
 
+def churn_requests(shape, cfg, count, device_pages, max_pages):
+    """A stream of `count` write-back requests for a free-list churn: each has a
+    length in whole pages, drawn like the mixed batch's (lognormal, median 4096
+    tokens, sigma 1.0, at most `max_pages` pages), and a contiguous run of device
+    pages at a seeded offset (the request's own KV in a fresh device pool).
+    Returns a list of (npages, first_device_page)."""
+    ex = mixed().extra
+    ps = shape.page_size
+    r_len = rng(cfg, P_LEN)
+    r_off = rng(cfg, P_OFFSET)
+    out = []
+    for _ in range(count):
+        tokens = r_len.lognormal(mean=np.log(ex["median"]), sigma=ex["sigma"])
+        npg = int(min(max_pages, max(1, np.ceil(tokens / ps))))
+        first = int(r_off.integers(0, device_pages - npg + 1))
+        out.append((npg, first))
+    return out
+
+
 # ---- data -------------------------------------------------------------------
 
 def host_rows_random(cfg, nbytes):

@@ -420,3 +420,53 @@ def test_staged_margin_steers_selector(torch, stream):
     with pytest.raises(kvt.KvError):
         pool.set_calibration(c)
     pool.close()
+
+
+# ---- host pages handed out by the free list under churn --------------------------------
+
+@pytest.mark.parametrize("policy", (kvt.FREE_FIFO, kvt.FREE_LIFO), ids=["fifo", "lifo"])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_churn_through_free_list(torch, stream, policy, layout):
+    """Write-backs into pages from the library's free list while old requests are
+    evicted (LIFO hands out fragmented runs of recently freed pages), then a load
+    of every cached request; the oracle gets its pages from the oracle's free list."""
+    from oracle import slots as oracle_slots
+    g = Geometry(3, 2, 272, 640, 640, 16, layout)
+    pages_total, cap = g.S_host // g.ps, 16
+    bufs = device_buffers(g, seed=31)
+    rng = np.random.default_rng(7 + policy)
+    lib_alloc = kvt.HostPages(pages_total, policy)
+    ref_alloc = oracle_slots.FreeList(pages_total, policy)
+    for path in (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED, kvt.PATH_AUTO):
+        pool = make_pool(g, bufs, path)
+        live, live_pages = [], 0
+        for r in range(24):
+            npg = int(rng.integers(1, 9))
+            while live_pages + npg > cap:
+                old = live.pop(0)
+                lib_alloc.free(old)
+                assert ref_alloc.release(old.tolist()) == oracle_slots.OK
+                live_pages -= old.size
+            pages = lib_alloc.alloc(npg)
+            rc, ref_pages = ref_alloc.alloc(npg)
+            assert rc == oracle_slots.OK and pages.tolist() == ref_pages
+            live.append(pages)
+            live_pages += npg
+            first = int(rng.integers(0, g.S_dev // g.ps - npg + 1))
+            d = workloads.page_indices(np.arange(first, first + npg), g.ps)
+            h = workloads.page_indices(np.asarray(ref_pages), g.ps)
+            print("churn policy=%d layout=%d path=%d request=%d pages=%s" %
+                  (policy, layout, path, r, ref_pages), flush=True)
+            run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        h_all = workloads.page_indices(np.concatenate(live), g.ps)
+        d_all = np.arange(h_all.size, dtype=np.int64)
+        fresh = device_buffers(g, seed=32, fill=SENTINEL)
+        pool2 = make_pool(g, fresh, path, host_fill=None)
+        pool2.host_array()[:] = pool.host_array()
+        run_load_and_compare(g, pool2, fresh, d_all, h_all, 0, g.L, stream)
+        pool2.close()
+        pool.close()
+        for old in live:
+            lib_alloc.free(old)
+            assert ref_alloc.release(old.tolist()) == oracle_slots.OK
+    lib_alloc.close()

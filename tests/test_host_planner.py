@@ -5,7 +5,9 @@
   agree with the oracle, element by element;
 * a host-compiled replay driver (tests/host/walk_check.cpp, AddressSanitizer +
   UBSan) runs every launch plan of the kernels and of the copy-engine path on
-  CPU mirrors and compares the bytes with the oracle.
+  CPU mirrors and compares the bytes with the oracle;
+* the Ghost List and the host page allocator run random operation streams
+  under the same sanitizers (tests/host/ghost_check.cpp, slots_check.cpp).
 """
 import glob
 import os
@@ -191,6 +193,17 @@ def test_ghost_list_under_sanitizers(tmp_path):
     subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-I" + os.path.join(ROOT, "include"),
                            os.path.join(HERE, "host", "ghost_check.cpp"),
                            os.path.join(CSRC, "ghost.cpp"), "-o", str(exe), "-lpthread"] + san)
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 failures" in res.stdout
+
+
+def test_host_page_allocator_under_sanitizers(tmp_path):
+    exe = tmp_path / "slots_check"
+    san = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=all"]
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-I" + os.path.join(ROOT, "include"),
+                           os.path.join(HERE, "host", "slots_check.cpp"),
+                           os.path.join(CSRC, "slots.cpp"), "-o", str(exe), "-lpthread"] + san)
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "0 failures" in res.stdout
