@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--host-memory-study", type=float, nargs="+", metavar="GB",
                    help="only measure the headline request against pinned host pools of "
                         "these sizes (GB), then exit")
+    p.add_argument("--tp-shared-study", type=int, default=0, metavar="TP",
+                   help="only run the tensor-parallel shared host pool study for a group of "
+                        "TP pools on this GPU, then exit")
     p.add_argument("--free-list-study", action="store_true",
                    help="only run the FIFO-vs-LIFO host free-list churn study, then exit")
     p.add_argument("--profile-counters", action="store_true",
@@ -81,6 +84,9 @@ def main():
         return
     if args.free_list_study:
         print(json.dumps(free_list_study(torch, kvt, workloads)))
+        return
+    if args.tp_shared_study:
+        print(json.dumps(tp_shared_study(torch, kvt, workloads, args.tp_shared_study)))
         return
     dev = torch.device("cuda:0")
     shape = workloads.mla32k()
@@ -995,6 +1001,98 @@ def host_memory_study(torch, kvt, workloads, sizes_gb):
         cell["destroy_s"] = round(time.perf_counter() - t0, 2)
     return {"study": "pinned host pool size", "request": "32768 tokens x 78 x 1152 B, "
             "512 random host pages, layer_first", "rows": out}
+
+
+def tp_shared_study(torch, kvt, workloads, tp, reps=5):
+    """A tensor-parallel group of `tp` ranks holding the same MLA latent (78 x 1152 B
+    rows, 32768-token prefix), each rank a pool over its own device buffers, all
+    on this one GPU. Shared: one host pool (kv_pool_create_shared); the writer
+    backs up, the other ranks' backups move nothing and wait for it. Private:
+    every rank has its own host pool and backs up. Per mode: pinned host bytes,
+    bytes written over the host link, the group write-back's time (all ranks'
+    calls, device events; ranks share one link here, where a real group has
+    one per GPU), the sharing ranks' submit time, and every rank's load rate.
+    Before timing, each sharing rank's loaded rows are checked against the
+    writer's source rows on the device."""
+    shape = workloads.mla32k()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S_dev, S_host, n = shape.device_slots, shape.host_slots, shape.extra["tokens"]
+    geom = kvt.geometry(L, C, R, S_dev, S_host, ps, kvt.LAYER_FIRST)
+    ranks = []
+    for r in range(tp):
+        bufs = []
+        for l in range(L):
+            b = torch.empty(S_dev * R, dtype=torch.uint8, device="cuda:0")
+            if r == 0:
+                workloads.fill_device_buffer(b, shape, 3, l, 0, torch)
+            bufs.append(b)
+        ranks.append(bufs)
+    first = workloads.contiguous_pages_at_offset(3, S_dev // ps, n // ps)
+    dev_idx = workloads.page_indices(first, ps)
+    host_idx = np.arange(n, dtype=np.int64)
+    nbytes = n * L * C * R
+    s = torch.cuda.Stream()
+    out = {"tp": tp, "workload": "mla latent 78 x 1152 B, 32768-token prefix, layer_first",
+           "bytes_per_rank": nbytes}
+    for mode in ("shared", "private"):
+        pools = []
+        for r in range(tp):
+            share = pools[0] if (mode == "shared" and r > 0) else None
+            pools.append(kvt.KvPool(geom, ranks[r], share_with=share))
+        pinned = sum(p.host_array().nbytes for p in pools[:1 if mode == "shared" else tp])
+        if mode == "private":   # every rank's L1 holds the same latent
+            for r in range(1, tp):
+                for a, b in zip(ranks[r], ranks[0]):
+                    a.copy_(b)
+        torch.cuda.synchronize()
+
+        def group_backup():
+            for p in pools:
+                p.backup(dev_idx, host_idx, 0, L, s)
+
+        def group_load():
+            for p in pools:
+                p.load(dev_idx, host_idx, 0, L, s)
+
+        group_backup()
+        group_load()
+        s.synchronize()
+        if mode == "shared":   # the loaded rows (a contiguous run of slots) match the writer's
+            lo, hi = int(dev_idx[0]), int(dev_idx[0]) + n
+            assert np.array_equal(dev_idx, np.arange(lo, hi))
+            for r in range(1, tp):
+                for l in range(L):
+                    assert torch.equal(ranks[r][l].view(S_dev, R)[lo:hi],
+                                       ranks[0][l].view(S_dev, R)[lo:hi]), (r, l)
+        t_b, t_l, sub = [], [], []
+        for _ in range(reps):
+            e0, e1, e2 = _ev(torch), _ev(torch), _ev(torch)
+            e0.record(s)
+            pools[0].backup(dev_idx, host_idx, 0, L, s)
+            t0 = time.perf_counter()
+            for p in pools[1:]:
+                p.backup(dev_idx, host_idx, 0, L, s)
+            sub.append((time.perf_counter() - t0) / max(1, tp - 1))
+            e1.record(s)
+            group_load()
+            e2.record(s)
+            e2.synchronize()
+            t_b.append(e0.elapsed_time(e1) / 1e3)
+            t_l.append(e1.elapsed_time(e2) / 1e3)
+        tb, tl = statistics.median(t_b), statistics.median(t_l)
+        link_d2h = nbytes * (1 if mode == "shared" else tp)
+        cell = {"pinned_host_bytes": pinned, "d2h_link_bytes": link_d2h,
+                "group_backup_ms": round(tb * 1e3, 3),
+                "group_backup_link_gbps": round(link_d2h / tb / 1e9, 3),
+                "other_ranks_backup_submit_us": round(statistics.median(sub) * 1e6, 1),
+                "paths": {"writer": kvt.PATH_NAMES[pools[0].last_path(kvt.BACKUP)],
+                          "others": kvt.PATH_NAMES[pools[-1].last_path(kvt.BACKUP)]},
+                "load_per_rank_gbps": round(nbytes * tp / tl / 1e9, 3)}
+        log("tp shared %s %s" % (mode, json.dumps(cell)))
+        out[mode] = cell
+        for p in pools:
+            p.close()
+    return out
 
 
 def free_list_study(torch, kvt, workloads, count=160):

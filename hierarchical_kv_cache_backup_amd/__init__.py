@@ -22,10 +22,11 @@ OK, EINVAL, ERANGE, EDUP, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
 ERROR_NAMES = {EINVAL: "KV_EINVAL", ERANGE: "KV_ERANGE", EDUP: "KV_EDUP",
                ENOMEM: "KV_ENOMEM", EHIP: "KV_EHIP"}
 LAYER_FIRST, PAGE_FIRST, PAGE_FIRST_DIRECT = 0, 1, 2
-PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA, PATH_STAGED = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_KERNEL, PATH_KERNEL_LDS, PATH_DMA, PATH_STAGED, PATH_SHARED = 0, 1, 2, 3, 4, 5
 PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel_lds",
-              PATH_DMA: "dma", PATH_STAGED: "staged", -1: "none"}
-F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP, F_DUPLEX = 0x1, 0x2, 0x4, 0x8
+              PATH_DMA: "dma", PATH_STAGED: "staged", PATH_SHARED: "shared", -1: "none"}
+F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP, F_DUPLEX, F_SHARE_CHECK = (
+    0x1, 0x2, 0x4, 0x8, 0x10)
 BACKUP, LOAD = 0, 1
 FREE_FIFO, FREE_LIFO = 0, 1
 
@@ -77,6 +78,7 @@ SIGNATURES = {
     "kv_count_segments": (_I32, [_GEOM, _P64, _P64, _I64, _I32, _I32, _P64]),
     "kv_count_dma_copies": (_I32, [_GEOM, _P64, _P64, _I64, _I32, _I32, _P64]),
     "kv_pool_create": (_I32, [ctypes.POINTER(kv_pool_desc_t), ctypes.POINTER(_VP)]),
+    "kv_pool_create_shared": (_I32, [ctypes.POINTER(kv_pool_desc_t), _VP, ctypes.POINTER(_VP)]),
     "kv_pool_destroy": (_I32, [_VP]),
     "kv_pool_host_ptr": (_VP, [_VP]),
     "kv_pool_host_bytes": (_I64, [_VP]),
@@ -213,6 +215,16 @@ def kv_pool_create(geom, device_buffer_ptrs, device=0, numa_node=-1, flags=F_CHE
                           numa_node, flags)
     h = ctypes.c_void_p()
     rc = _lib.kv_pool_create(ctypes.byref(desc), ctypes.byref(h))
+    return rc, h.value
+
+
+def kv_pool_create_shared(geom, device_buffer_ptrs, group, device=0, flags=F_CHECK_UNIQUE):
+    """Returns (status, handle) of a pool sharing `group`'s host pool."""
+    arr = (ctypes.c_void_p * len(device_buffer_ptrs))(*device_buffer_ptrs)
+    desc = kv_pool_desc_t(geom, ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)), device,
+                          -1, flags)
+    h = ctypes.c_void_p()
+    rc = _lib.kv_pool_create_shared(ctypes.byref(desc), group, ctypes.byref(h))
     return rc, h.value
 
 
@@ -464,12 +476,18 @@ class KvPool:
     """Owns a library pool over L*C torch uint8 device tensors (borrowed: kept
     referenced here so they outlive the pool). Methods raise KvError on failure."""
 
-    def __init__(self, geom, device_tensors, device=0, numa_node=-1, flags=F_CHECK_UNIQUE):
+    def __init__(self, geom, device_tensors, device=0, numa_node=-1, flags=F_CHECK_UNIQUE,
+                 share_with=None):
+        """share_with: another KvPool whose host pool this one shares
+        (kv_pool_create_shared); numa_node is then ignored."""
         self.geom = geom
         self.tensors = list(device_tensors)
         assert len(self.tensors) == geom.num_layers * geom.num_components
         ptrs = [t.data_ptr() for t in self.tensors]
-        rc, h = kv_pool_create(geom, ptrs, device, numa_node, flags)
+        if share_with is None:
+            rc, h = kv_pool_create(geom, ptrs, device, numa_node, flags)
+        else:
+            rc, h = kv_pool_create_shared(geom, ptrs, share_with.handle, device, flags)
         _check(rc)
         self.handle = h
 

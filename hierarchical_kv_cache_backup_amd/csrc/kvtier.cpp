@@ -16,6 +16,7 @@
 #include <chrono>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -101,6 +102,22 @@ struct DirState {
   double submit_us = 0, blocked_us = 0;
 };
 
+// The pinned host pool, owned jointly by the pools of a group that share it
+// (kv_pool_create_shared): freed with the last of them. The writer (the pool
+// kv_pool_create made) records `written` after each of its backups; a sharing
+// pool's backup makes its stream wait for that event.
+struct HostShare {
+  int device = 0;               // the writer's device (the event lives there)
+  uint8_t *host = nullptr;      // CPU address
+  int64_t bytes = 0;
+  bool check = false;           // KV_F_SHARE_CHECK on the writer
+  std::mutex mu;
+  hipEvent_t written = nullptr;
+  bool recorded = false;        // the writer has backed up at least once
+  uint64_t digest = 0;          // of the writer's latest backup (host slots, layer range)
+  ~HostShare();
+};
+
 }  // namespace
 }  // namespace kvt
 
@@ -116,6 +133,8 @@ struct kv_pool {
   uint8_t *host = nullptr;          // host pool, CPU address
   uint8_t *host_dev = nullptr;      // host pool, device-visible address
   int64_t host_bytes = 0;
+  std::shared_ptr<HostShare> share; // the host pool and the group's write event
+  bool reader = false;              // shares another pool's host pool; its backups move nothing
   // Landed events of kv_load. Layers are loaded in groups (one launch or one
   // batch of copies per group) and one event is recorded per group, on the
   // group's first layer; layer_src[l] names the event that covers layer l
@@ -195,6 +214,29 @@ double now_us() {
   return std::chrono::duration<double, std::micro>(
              std::chrono::steady_clock::now().time_since_epoch())
       .count();
+}
+
+HostShare::~HostShare() {
+  DeviceGuard dg(device);
+  if (written) (void)hipEventDestroy(written);
+  if (host) (void)hipHostFree(host);
+}
+
+// 64-bit FNV-1a over a backup request's host slots and layer range: the
+// fingerprint two ranks of a group compare to confirm they name the same host
+// rows (KV_F_SHARE_CHECK).
+uint64_t request_digest(const int64_t *host_idx, int64_t n, int32_t l0, int32_t l1) {
+  uint64_t h = 0xcbf29ce484222325ull;
+  auto mix = [&h](uint64_t v, int bytes) {
+    for (int b = 0; b < bytes; b++) {
+      h ^= (v >> (8 * b)) & 0xffu;
+      h *= 0x100000001b3ull;
+    }
+  };
+  mix((uint64_t)(uint32_t)l0, 4);
+  mix((uint64_t)(uint32_t)l1, 4);
+  for (int64_t i = 0; i < n; i++) mix((uint64_t)host_idx[i], 8);
+  return h;
 }
 
 void free_staging(Staging &s) {
@@ -503,6 +545,34 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
   return e;
 }
 
+// Backup on a pool that shares the group writer's host pool: the writer has
+// moved (or is moving) the bytes; this call only orders `s` after the writer's
+// most recent backup, so the rank's completion is gated by the write, and with
+// KV_F_SHARE_CHECK confirms the request names the writer's host rows.
+static int shared_backup(kv_pool *p, DirState &d, const int64_t *host_idx, int64_t n,
+                         int32_t l0, int32_t l1, hipStream_t s, double t0) {
+  HostShare &sh = *p->share;
+  hipError_t e = hipSuccess;
+  {
+    std::lock_guard<std::mutex> sl(sh.mu);
+    if (sh.check && (!sh.recorded || request_digest(host_idx, n, l0, l1) != sh.digest))
+      return fail(KV_EINVAL,
+                  "backup names other host slots or layers than the group writer's latest "
+                  "backup (host allocation differs across the group)");
+    if (sh.recorded) e = hipStreamWaitEvent(s, sh.written, 0);
+  }
+  if (e != hipSuccess) return hip_fail(e, "waiting for the group writer's backup");
+  e = hipEventRecord(d.done, s);
+  if (e != hipSuccess) return hip_fail(e, "recording the completion event");
+  d.done_pending = true;
+  d.done_stream.store(s);
+  d.done_recorded.store(true);
+  d.last_path.store(KV_PATH_SHARED);
+  d.calls++;
+  d.submit_us += now_us() - t0;
+  return KV_OK;
+}
+
 static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
                     int64_t n, int32_t l0, int32_t l1, void *stream) {
   const double t0 = now_us();
@@ -523,6 +593,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   DeviceGuard dg(p->device);
   if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
   hipStream_t s = (hipStream_t)stream;
+  if (dir == 0 && p->reader) return shared_backup(p, d, host_idx, n, l0, l1, s, t0);
   const int64_t bytes = n * nlc_all * g.R;
   const int64_t layer_bytes = n * g.C * g.R;
   kv_calib_t c;
@@ -677,6 +748,14 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   d.done_pending = true;
   d.done_stream.store(s);
   d.done_recorded.store(true);
+  if (dir == 0) {  // the writer of the host pool: sharing pools' backups wait for this
+    HostShare &sh = *p->share;
+    std::lock_guard<std::mutex> sl(sh.mu);
+    e = hipEventRecord(sh.written, s);
+    if (e != hipSuccess) return hip_fail(e, "recording the host pool's write event");
+    sh.recorded = true;
+    if (sh.check) sh.digest = request_digest(host_idx, n, l0, l1);
+  }
   d.last_path.store(path);
   d.calls++;
   d.bytes += bytes;
@@ -718,13 +797,15 @@ int kv_pool_destroy(kv_pool_t *p) {
     for (hipEvent_t ev : p->layer_ev)
       if (ev) (void)hipEventDestroy(ev);
     if (p->dev_tab) (void)hipFree(p->dev_tab);
-    if (p->host) (void)hipHostFree(p->host);
   }
+  p->share.reset();  // the host pool goes with the group's last pool
   delete p;
   return rc;
 }
 
-int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
+// kv_pool_create (group == nullptr: allocates the host pool) and
+// kv_pool_create_shared (shares group's host pool).
+static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **out) {
   if (!desc || !out) return fail(KV_EINVAL, "desc and out must be non-null");
   *out = nullptr;
   Geom g;
@@ -732,8 +813,15 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
   int rc = make_geom(&desc->geom, &g, &why);
   if (rc) return fail(rc, why);
   if (!desc->device_buffers) return fail(KV_EINVAL, "device_buffers is null");
-  if (desc->numa_node >= 0 && !numa_node_exists(desc->numa_node))
+  if (group) {
+    const Geom &w = group->g;
+    if (g.L != w.L || g.C != w.C || g.R != w.R || g.S_host != w.S_host || g.ps != w.ps ||
+        g.layout != w.layout)
+      return fail(KV_EINVAL,
+                  "a pool sharing a host pool must have the group's geometry (all but device_slots)");
+  } else if (desc->numa_node >= 0 && !numa_node_exists(desc->numa_node)) {
     return fail(KV_EINVAL, "numa_node " + std::to_string(desc->numa_node) + " does not exist");
+  }
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
@@ -777,30 +865,50 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
     p->bufs[k] = b;
   }
 
-  // host pool: pinned and mapped for the device, optionally bound to a node
-  p->host_bytes = nbuf * g.S_host * g.R;
-  unsigned int hflags = hipHostMallocMapped | hipHostMallocPortable |
-                        ((desc->flags & KV_F_HOST_NONCOHERENT) ? hipHostMallocNonCoherent
-                                                               : hipHostMallocCoherent);
-  int old_mode = 0;
-  unsigned long old_mask = 0;
-  bool bound = false;
-  if (desc->numa_node >= 0) {
-    bound = bind_thread_to_node(desc->numa_node, &old_mode, &old_mask);
-    if (!bound) {
-      delete p;
-      return fail(KV_EINVAL, "set_mempolicy to node " + std::to_string(desc->numa_node) + " failed");
+  if (group) {  // the group's host pool
+    p->share = group->share;
+    p->reader = true;
+    p->host = p->share->host;
+    p->host_bytes = p->share->bytes;
+  } else {
+    // host pool: pinned, mapped for the device and portable (a pool on another
+    // device may share it), optionally bound to a node
+    p->host_bytes = nbuf * g.S_host * g.R;
+    unsigned int hflags = hipHostMallocMapped | hipHostMallocPortable |
+                          ((desc->flags & KV_F_HOST_NONCOHERENT) ? hipHostMallocNonCoherent
+                                                                 : hipHostMallocCoherent);
+    int old_mode = 0;
+    unsigned long old_mask = 0;
+    bool bound = false;
+    if (desc->numa_node >= 0) {
+      bound = bind_thread_to_node(desc->numa_node, &old_mode, &old_mask);
+      if (!bound) {
+        delete p;
+        return fail(KV_EINVAL,
+                    "set_mempolicy to node " + std::to_string(desc->numa_node) + " failed");
+      }
+      hflags |= hipHostMallocNumaUser;
     }
-    hflags |= hipHostMallocNumaUser;
-  }
-  e = hipHostMalloc((void **)&p->host, (size_t)p->host_bytes, hflags);
-  if (bound) restore_thread_policy(old_mode, old_mask);
-  if (e != hipSuccess) {
-    p->host = nullptr;
-    (void)hipGetLastError();
-    kv_pool_destroy(p);
-    return fail(KV_ENOMEM, "hipHostMalloc of " + std::to_string(p->host_bytes) +
-                               " bytes failed: " + hipGetErrorString(e));
+    uint8_t *host = nullptr;
+    e = hipHostMalloc((void **)&host, (size_t)p->host_bytes, hflags);
+    if (bound) restore_thread_policy(old_mode, old_mask);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      kv_pool_destroy(p);
+      return fail(KV_ENOMEM, "hipHostMalloc of " + std::to_string(nbuf * g.S_host * g.R) +
+                                 " bytes failed: " + hipGetErrorString(e));
+    }
+    p->share = std::make_shared<HostShare>();
+    p->share->device = desc->device;
+    p->share->host = host;
+    p->share->bytes = p->host_bytes;
+    p->share->check = (desc->flags & KV_F_SHARE_CHECK) != 0;
+    p->host = host;
+    e = hipEventCreateWithFlags(&p->share->written, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      kv_pool_destroy(p);
+      return hip_fail(e, "creating the host pool's write event");
+    }
   }
   void *hd = nullptr;
   e = hipHostGetDevicePointer(&hd, p->host, 0);
@@ -839,6 +947,16 @@ int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
   }
   *out = p;
   return KV_OK;
+}
+
+int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
+  return create_pool(desc, nullptr, out);
+}
+
+int kv_pool_create_shared(const kv_pool_desc_t *desc, kv_pool_t *group, kv_pool_t **out) {
+  if (out) *out = nullptr;
+  if (!group) return fail(KV_EINVAL, "group is null");
+  return create_pool(desc, group, out);
 }
 
 void *kv_pool_host_ptr(const kv_pool_t *p) { return p ? p->host : nullptr; }

@@ -104,7 +104,10 @@ typedef enum {
   KV_PATH_KERNEL = 1,
   KV_PATH_KERNEL_LDS = 2,
   KV_PATH_DMA = 3,
-  KV_PATH_STAGED = 4
+  KV_PATH_STAGED = 4,
+  KV_PATH_SHARED = 5 /* reported by kv_last_path only: the backup of a pool that
+                        shares another pool's host pool (kv_pool_create_shared)
+                        moved no data and waited for the writer's backup */
 } kv_path_t;
 
 /* ---- pool flags -------------------------------------------------------- */
@@ -116,6 +119,10 @@ typedef enum {
                                       direction has a transfer in flight at submission on
                                       another stream (work queued on the same stream runs
                                       before this call, not beside it). */
+#define KV_F_SHARE_CHECK      0x10u /* on the writer of a shared host pool (kv_pool_create_shared):
+                                       each backup of a sharing pool must name the same host
+                                       slots and layer range as the writer's latest backup,
+                                       else KV_EINVAL (host allocation differs across the group) */
 #define KV_F_LOAD_OVERLAP     0x4u /* loads on this pool run while compute kernels occupy the GPU
                                       (layer-wise load during the forward pass): the selector
                                       charges each path the compute time it steals, and the
@@ -240,9 +247,39 @@ int kv_count_dma_copies(const kv_geometry_t *geom, const int64_t *dev_idx,
  * KV_EHIP. */
 int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out);
 
-/* Waits for every transfer enqueued through the pool, then frees the host
- * pool, events and staging. Returns the first HIP error seen while waiting,
- * if any. NULL is a no-op returning KV_OK. */
+/* Creates a pool over its own device buffers that SHARES the host pool of
+ * `group` (any pool made by kv_pool_create, or by this call from one), instead
+ * of allocating one: the tensor-parallel group's shared host KV buffer
+ * ("Tuning SGLang HiCache L2 on Kunlunxin P800/P900", section 2.7, "TP group
+ * shared Host KV"; "Baidu's KVCache Overhaul", "TP-group shared host KV
+ * buffer"). Where every rank holds bit-identical KV (a replicated MLA latent),
+ * one host copy serves the group: the pool made by kv_pool_create (the
+ * writer) does the write-back, every pool of the group loads from the same
+ * host bytes with its own indices into its own device buffers.
+ *   - desc->geom must equal the writer's except device_slots; desc->device
+ *     may name another device (the host pool is allocated portable and mapped);
+ *     desc->numa_node and KV_F_HOST_NONCOHERENT are ignored (the host memory is
+ *     the writer's); the other flags apply to this pool.
+ *   - kv_backup on a sharing pool moves no data. It validates the request as a
+ *     backup would (same error codes), then makes `stream` wait for the
+ *     writer's most recent backup: the rank still reports completion through
+ *     its own stream, and that completion is gated by the writer's write. Call
+ *     it after the writer's matching backup has been enqueued. With
+ *     KV_F_SHARE_CHECK on the writer, a request whose host slots or layer
+ *     range differ from the writer's most recent backup is refused (KV_EINVAL):
+ *     the group's host allocation must be the same on every rank.
+ *     kv_last_path then reports KV_PATH_SHARED and no bytes are counted.
+ *   - kv_load on a sharing pool is an ordinary load from the shared host pool.
+ *   - The host pool lives until every pool of the group is destroyed, in any
+ *     order.
+ * Errors: KV_EINVAL (null group/desc/out, geometry differing from the
+ * writer's, bad device buffers), KV_ENOMEM, KV_EHIP. */
+int kv_pool_create_shared(const kv_pool_desc_t *desc, kv_pool_t *group, kv_pool_t **out);
+
+/* Waits for every transfer enqueued through the pool, then frees its events
+ * and staging, and the host pool once no pool of its group uses it. Returns
+ * the first HIP error seen while waiting, if any. NULL is a no-op returning
+ * KV_OK. */
 int kv_pool_destroy(kv_pool_t *pool);
 
 /* Host (CPU) address of the host pool and its size in bytes. The pointer stays
@@ -310,8 +347,9 @@ int kv_stream_destroy(void *stream);
 int kv_set_path(kv_pool_t *pool, int32_t path);
 
 /* Path the most recent call of `direction` (0 = backup, 1 = load) used: one of
- * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA / KV_PATH_STAGED, or -1 if
- * none yet. */
+ * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA / KV_PATH_STAGED (or
+ * KV_PATH_SHARED for the backup of a pool sharing another's host pool), or -1
+ * if none yet. */
 int32_t kv_last_path(const kv_pool_t *pool, int32_t direction);
 
 /* Replaces / reads the selector calibration. */

@@ -470,3 +470,125 @@ def test_churn_through_free_list(torch, stream, policy, layout):
             lib_alloc.free(old)
             assert ref_alloc.release(old.tolist()) == oracle_slots.OK
     lib_alloc.close()
+
+
+# ---- one host pool shared by a tensor-parallel group -----------------------------------
+
+def _random_request(rng, g, n, S_dev=None):
+    S_dev = g.S_dev if S_dev is None else S_dev
+    return (rng.choice(S_dev, n, replace=False).astype(np.int64),
+            rng.choice(g.S_host, n, replace=False).astype(np.int64))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED, kvt.PATH_AUTO))
+def test_shared_host_pool_group(torch, stream, layout, path):
+    """The writer backs up; the sharing pools' backups move nothing; every pool
+    loads the writer's bytes into its own device buffers at its own slots."""
+    g = Geometry(3, 2, 272, 600, 512, 16, layout)
+    rng = np.random.default_rng(40 + 10 * layout + path)
+    src = device_buffers(g, seed=41)
+    writer = make_pool(g, src, path)
+    g2 = Geometry(3, 2, 272, 900, 512, 16, layout)         # a rank with a larger device pool
+    readers = []
+    for gr, seed in ((g, 42), (g2, 43)):
+        bufs = device_buffers(gr, seed=seed, fill=SENTINEL)
+        pr = kvt.KvPool(kv_geom(gr), bufs, share_with=writer)
+        pr.set_path(path)
+        readers.append((gr, pr, bufs))
+    assert readers[0][1].host_array().ctypes.data == writer.host_array().ctypes.data
+    d, h = _random_request(rng, g, 300)
+    print("shared layout=%d path=%d" % (layout, path), flush=True)
+    run_backup_and_compare(g, writer, src, d, h, 0, g.L, stream)
+    image = writer.host_array().copy()
+    for gr, pr, bufs in readers:
+        d_r = rng.choice(gr.S_dev, h.size, replace=False).astype(np.int64)
+        pr.backup(d_r, h, 0, g.L, stream)
+        stream.synchronize()
+        assert pr.last_path(kvt.BACKUP) == kvt.PATH_SHARED
+        assert pr.stats().bytes[0] == 0 and pr.stats().calls[0] == 1
+        assert np.array_equal(writer.host_array(), image)
+        run_load_and_compare(gr, pr, bufs, d_r, h, 0, g.L, stream)
+        for k in range(g.L * g.C):   # the rank's rows are the writer's source rows
+            a = src[k].view(g.S_dev, g.R)[torch.from_numpy(d).cuda()]
+            b = bufs[k].view(gr.S_dev, gr.R)[torch.from_numpy(d_r).cuda()]
+            assert torch.equal(a, b)
+    for _, pr, _ in readers:
+        pr.close()
+    writer.close()
+
+
+def test_shared_backup_waits_for_the_writer(torch):
+    """A sharing pool's backup and load on another stream, issued right after
+    the writer's backup with no host synchronisation, see the written bytes."""
+    g = Geometry(8, 2, 2048, 8192, 8192, 64, kvt.LAYER_FIRST)   # 256 MiB per direction
+    rng = np.random.default_rng(44)
+    src = device_buffers(g, seed=45)
+    writer = make_pool(g, src, kvt.PATH_DMA)
+    bufs = device_buffers(g, seed=46, fill=SENTINEL)
+    reader = kvt.KvPool(kv_geom(g), bufs, share_with=writer)
+    reader.set_path(kvt.PATH_KERNEL)
+    s_w, s_r = torch.cuda.Stream(), torch.cuda.Stream()
+    pages = rng.permutation(g.S_dev // g.ps)
+    d = workloads.page_indices(pages, g.ps)
+    h = np.arange(g.S_host, dtype=np.int64)
+    d_r = workloads.page_indices(rng.permutation(g.S_dev // g.ps), g.ps)
+    for rep in range(3):
+        writer.host_array()[:] = SENTINEL
+        for b in bufs:
+            b.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        print("shared gating rep=%d" % rep, flush=True)
+        writer.backup(d, h, 0, g.L, s_w)
+        reader.backup(d_r, h, 0, g.L, s_r)
+        reader.load(d_r, h, 0, g.L, s_r)
+        s_r.synchronize()
+        for k in range(g.L * g.C):
+            a = src[k].view(g.S_dev, g.R)[torch.from_numpy(d).cuda()]
+            b = bufs[k].view(g.S_dev, g.R)[torch.from_numpy(d_r).cuda()]
+            assert torch.equal(a, b), (rep, k)
+        s_w.synchronize()
+    reader.close()
+    writer.close()
+
+
+def test_shared_check_and_errors(torch, stream):
+    g = Geometry(2, 1, 64, 128, 128, 8, kvt.PAGE_FIRST_DIRECT)
+    rng = np.random.default_rng(47)
+    src = device_buffers(g, seed=48)
+    writer = make_pool(g, src, kvt.PATH_KERNEL, flags=kvt.F_CHECK_UNIQUE | kvt.F_SHARE_CHECK)
+    bufs = device_buffers(g, seed=49, fill=SENTINEL)
+    reader = kvt.KvPool(kv_geom(g), bufs, share_with=writer)
+    lib = kvt.library()
+    d, h = _random_request(rng, g, 40)
+    # before the writer has backed up anything
+    assert kvt.kv_backup(reader.handle, d, h, 0, g.L, stream) == kvt.EINVAL
+    writer.backup(d, h, 0, g.L, stream)
+    assert kvt.kv_backup(reader.handle, d[::-1], h, 0, g.L, stream) == kvt.OK  # own device slots
+    assert kvt.kv_backup(reader.handle, d, h[::-1], 0, g.L, stream) == kvt.EINVAL
+    assert "host allocation differs" in kvt.kv_last_error()
+    assert kvt.kv_backup(reader.handle, d, h, 1, g.L, stream) == kvt.EINVAL
+    # validation comes first, with the codes a backup gives
+    bad = h.copy()
+    bad[3] = g.S_host
+    assert kvt.kv_backup(reader.handle, d, bad, 0, g.L, stream) == kvt.ERANGE
+    dup = h.copy()
+    dup[3] = dup[4]
+    assert kvt.kv_backup(reader.handle, d, dup, 0, g.L, stream) == kvt.EDUP
+    assert kvt.kv_backup(reader.handle, d, h, 0, 0, stream) == kvt.OK        # empty: no check
+    # geometry must match the group's (all but device_slots)
+    for other in (Geometry(2, 1, 80, 128, 128, 8, g.layout), Geometry(2, 1, 64, 128, 256, 8, g.layout),
+                  Geometry(2, 1, 64, 128, 128, 8, kvt.LAYER_FIRST)):
+        ob = device_buffers(other, seed=1, fill=0)
+        rc, hnd = kvt.kv_pool_create_shared(kv_geom(other), [b.data_ptr() for b in ob],
+                                            writer.handle)
+        assert rc == kvt.EINVAL and not hnd
+    assert kvt.kv_pool_create_shared(kv_geom(g), [b.data_ptr() for b in bufs], None)[0] == kvt.EINVAL
+    # the host pool outlives the writer
+    stream.synchronize()
+    image = writer.host_array().copy()
+    writer.close()
+    assert np.array_equal(reader.host_array(), image)
+    run_load_and_compare(g, reader, bufs, d, h, 0, g.L, stream)
+    reader.close()
+    assert lib.kv_pool_destroy(None) == kvt.OK
