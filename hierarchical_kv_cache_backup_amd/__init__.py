@@ -52,7 +52,7 @@ class kv_calib_t(ctypes.Structure):
                 ("overlap_kernel_penalty", ctypes.c_double),
                 ("overlap_dma_penalty", ctypes.c_double),
                 ("overlap_kernel_max_workgroups", ctypes.c_double),
-                ("duplex_kernel_penalty", ctypes.c_double),
+                ("duplex_kernel_penalty", ctypes.c_double * 2),
                 ("staged_chunk_bytes", ctypes.c_double),
                 ("staged_gather_gbps", ctypes.c_double),
                 ("kernel_group_us", ctypes.c_double * 2),

@@ -178,10 +178,15 @@ void default_calibration(kv_calib_t *c) {
   c->overlap_kernel_penalty = 0.65;
   c->overlap_dma_penalty = 0.15;
   c->overlap_kernel_max_workgroups = 128;
-  // Concurrent 1 GiB H2D + D2H: 97 GB/s aggregate on the copy engines, 69 GB/s
-  // with the kernel in both directions -> a kernel transfer takes ~1.4x longer
-  // while the other direction is busy.
-  c->duplex_kernel_penalty = 0.4;
+  // Concurrent 1 GiB H2D + D2H (GB/s, H2D / D2H): copy engines both ways
+  // 56.4 / 48.5; H2D kernel beside D2H copy engines 56.4 / 31.0; H2D copy
+  // engines beside a D2H kernel 42.3 / 51.3; kernels both ways 37.8 / 38.1.
+  // On the mixed batch an H2D kernel beside a staged D2H kept 56.2. A load's
+  // kernel keeps the link whatever the write-back runs on, unless the
+  // write-back is a kernel too, which this charge steers it away from; a
+  // backup's kernel loses ~0.4 of its rate beside a busy load.
+  c->duplex_kernel_penalty[0] = 0.4;
+  c->duplex_kernel_penalty[1] = 0.0;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
   c->staged_gather_gbps = 2000.0;
 }
@@ -643,7 +648,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       t_dma *= 1.0 + c.overlap_dma_penalty;
       t_staged *= 1.0 + c.overlap_dma_penalty;
     }
-    if (duplex) t_kernel *= 1.0 + c.duplex_kernel_penalty;
+    if (duplex) t_kernel *= 1.0 + c.duplex_kernel_penalty[dir];
     path = KV_PATH_KERNEL;
     double best = t_kernel;
     if (t_dma < best) {
@@ -1037,7 +1042,8 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
   if (!(c->overlap_kernel_max_workgroups >= 0) || c->overlap_kernel_max_workgroups > 4294967295.0 ||
       !(c->overlap_kernel_penalty >= 0) || !(c->overlap_dma_penalty >= 0))
     return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
-  if (!(c->duplex_kernel_penalty >= 0) || !(c->staged_chunk_bytes >= 16) ||
+  if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
+      !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
     return fail(KV_EINVAL, "duplex penalty >= 0, staged chunk >= 16 bytes and gather rate > 0");
   std::lock_guard<std::mutex> lock(p->calib_mu);

@@ -186,7 +186,9 @@ typedef struct {
   double overlap_kernel_penalty;
   double overlap_dma_penalty;
   double overlap_kernel_max_workgroups;
-  double duplex_kernel_penalty; /* kernel-path slowdown while the other direction is busy */
+  double duplex_kernel_penalty[2]; /* kernel-path slowdown of this direction while the other
+                                      one is busy ([0] backup beside a load, [1] load beside a
+                                      backup) */
   double staged_chunk_bytes;    /* staged path: staging buffer size per direction */
   double staged_gather_gbps;    /* staged path: device-side gather/scatter rate */
   double kernel_group_us[2];    /* gap per further kernel launch of one call */

@@ -406,7 +406,7 @@ def test_staged_margin_steers_selector(torch, stream):
     c.kernel_gbps[:] = [1e6, 1e6]
     c.dma_gbps[:] = [1e6, 1e6]
     c.staged_gather_gbps = 1e6
-    c.duplex_kernel_penalty = 100.0
+    c.duplex_kernel_penalty[:] = [100.0, 100.0]
     for gain, want in ((0.9, kvt.PATH_KERNEL), (0.5, kvt.PATH_STAGED)):
         c.staged_min_gain = gain
         pool.set_calibration(c)
