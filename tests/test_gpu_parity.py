@@ -592,3 +592,32 @@ def test_shared_check_and_errors(torch, stream):
     run_load_and_compare(g, reader, bufs, d, h, 0, g.L, stream)
     reader.close()
     assert lib.kv_pool_destroy(None) == kvt.OK
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("path", PATHS)
+def test_back_to_back_on_one_stream(torch, stream, layout, path):
+    """A backup and a load of the same host slots chained on one stream with no
+    host synchronisation between them (the load must read what the backup
+    wrote), three times over with different device slots."""
+    g = Geometry(4, 2, 1152, 2048, 1024, 64, layout)
+    rng = np.random.default_rng(60 + 10 * layout + path)
+    src = device_buffers(g, seed=61)
+    pool = make_pool(g, src, path)
+    dst = device_buffers(g, seed=62, fill=SENTINEL)
+    pool2 = kvt.KvPool(kv_geom(g), dst, share_with=pool)   # loads into other buffers
+    pool2.set_path(path)
+    h = rng.permutation(g.S_host).astype(np.int64)
+    for rep in range(3):
+        d_src = rng.choice(g.S_dev, g.S_host, replace=False).astype(np.int64)
+        d_dst = rng.choice(g.S_dev, g.S_host, replace=False).astype(np.int64)
+        print("back-to-back layout=%d path=%d rep=%d" % (layout, path, rep), flush=True)
+        pool.backup(d_src, h, 0, g.L, stream)
+        pool2.load(d_dst, h, 0, g.L, stream)
+        stream.synchronize()
+        for k in range(g.L * g.C):
+            a = src[k].view(g.S_dev, g.R)[torch.from_numpy(d_src).cuda()]
+            b = dst[k].view(g.S_dev, g.R)[torch.from_numpy(d_dst).cuda()]
+            assert torch.equal(a, b), (rep, k)
+    pool2.close()
+    pool.close()
