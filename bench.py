@@ -946,7 +946,9 @@ def leg_ghost_list(kvt, workloads):
 
 def host_memory_study(torch, kvt, workloads, sizes_gb):
     """Pinned-size sweep: the headline request (32768 tokens x 78 layers x 1152 B,
-    contiguous device pages) against layer_first host pools of the given sizes.
+    contiguous device pages) against layer_first host pools of the given sizes,
+    each placed three ways: the default policy, bound to NUMA node 0, and
+    interleaved over the online nodes (KV_F_HOST_INTERLEAVE).
     The request's host rows are 512 random pages of the whole pool, so that the
     pages it touches spread over all of it (a layer_first pool also puts each
     layer in its own region). Per size: pool creation time, and device-event
@@ -964,20 +966,25 @@ def host_memory_study(torch, kvt, workloads, sizes_gb):
     s = torch.cuda.Stream()
     nb = n * L * C * R
     out = []
-    for gb in sizes_gb:
+    placements = (("default", -1, 0), ("bind_node0", 0, 0),
+                  ("interleave", -1, kvt.F_HOST_INTERLEAVE))
+    for gb, (pl_name, numa, pl_flag) in [(g, pl) for g in sizes_gb for pl in placements]:
         S_host = max(n, int(gb * 1e9 / (L * C * R)) // ps * ps)
         host_pages = workloads.fragmented_pages(3, S_host // ps, n // ps, workloads.P_HOST)
         host_idx = workloads.page_indices(host_pages, ps)
         t0 = time.perf_counter()
         try:
-            pool = kvt.KvPool(kvt.geometry(L, C, R, S_dev, S_host, ps, 0), bufs)
+            pool = kvt.KvPool(kvt.geometry(L, C, R, S_dev, S_host, ps, 0), bufs, numa_node=numa,
+                              flags=kvt.F_CHECK_UNIQUE | pl_flag)
         except kvt.KvError as e:        # the driver's pinned-memory limit
-            log("host pool of %.1f GB refused: %s" % (gb, e))
-            out.append({"host_pool_gb": round(S_host * L * C * R / 1e9, 2), "refused": str(e)})
+            log("host pool of %.1f GB (%s) refused: %s" % (gb, pl_name, e))
+            out.append({"host_pool_gb": round(S_host * L * C * R / 1e9, 2),
+                        "placement": pl_name, "refused": str(e)})
             continue
         t_create = time.perf_counter() - t0
-        log("host pool %.1f GB created in %.1f s" % (pool.host_array().nbytes / 1e9, t_create))
-        cell = {"host_pool_gb": round(pool.host_array().nbytes / 1e9, 2),
+        log("host pool %.1f GB (%s) created in %.1f s" %
+            (pool.host_array().nbytes / 1e9, pl_name, t_create))
+        cell = {"host_pool_gb": round(pool.host_array().nbytes / 1e9, 2), "placement": pl_name,
                 "create_s": round(t_create, 2)}
         for pname, p in (("kernel", kvt.PATH_KERNEL), ("dma", kvt.PATH_DMA)):
             pool.set_path(p)
@@ -999,8 +1006,11 @@ def host_memory_study(torch, kvt, workloads, sizes_gb):
         t0 = time.perf_counter()
         pool.close()
         cell["destroy_s"] = round(time.perf_counter() - t0, 2)
-    return {"study": "pinned host pool size", "request": "32768 tokens x 78 x 1152 B, "
-            "512 random host pages, layer_first", "rows": out}
+    nodes = sorted(os.listdir("/sys/devices/system/node")) if os.path.isdir(
+        "/sys/devices/system/node") else []
+    return {"study": "pinned host pool size and placement",
+            "request": "32768 tokens x 78 x 1152 B, 512 random host pages, layer_first",
+            "numa_nodes": [d for d in nodes if d.startswith("node")], "rows": out}
 
 
 def tp_shared_study(torch, kvt, workloads, tp, reps=5):

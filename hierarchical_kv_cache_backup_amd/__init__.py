@@ -27,6 +27,7 @@ PATH_NAMES = {PATH_AUTO: "auto", PATH_KERNEL: "kernel", PATH_KERNEL_LDS: "kernel
               PATH_DMA: "dma", PATH_STAGED: "staged", PATH_SHARED: "shared", -1: "none"}
 F_CHECK_UNIQUE, F_HOST_NONCOHERENT, F_LOAD_OVERLAP, F_DUPLEX, F_SHARE_CHECK = (
     0x1, 0x2, 0x4, 0x8, 0x10)
+F_HOST_INTERLEAVE = 0x20
 BACKUP, LOAD = 0, 1
 FREE_FIFO, FREE_LIFO = 0, 1
 

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <chrono>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <memory>
 #include <mutex>
@@ -191,17 +192,18 @@ void default_calibration(kv_calib_t *c) {
   c->staged_gather_gbps = 2000.0;
 }
 
-// Sets the calling thread's memory policy to bind to `node` (Linux mbind
-// semantics through set_mempolicy), returning the previous policy in
-// *old_mode / old_mask so it can be restored.
-constexpr int kMpolDefault = 0, kMpolBind = 2;
-bool bind_thread_to_node(int node, int *old_mode, unsigned long *old_mask) {
+// Sets the calling thread's memory policy (Linux set_mempolicy: kMpolBind to
+// the nodes of `mask`, or kMpolInterleave page by page across them), returning
+// the previous policy in *old_mode / *old_mask so it can be restored. Node
+// masks are one unsigned long: nodes 0..63.
+constexpr int kMpolDefault = 0, kMpolBind = 2, kMpolInterleave = 3;
+constexpr int kMaxNumaNodes = 8 * sizeof(unsigned long);
+bool set_thread_policy(int mode, unsigned long mask, int *old_mode, unsigned long *old_mask) {
   *old_mode = kMpolDefault;
   *old_mask = 0;
   if (syscall(SYS_get_mempolicy, old_mode, old_mask, 8 * sizeof(unsigned long), nullptr, 0) != 0)
     return false;
-  unsigned long mask = 1ul << node;
-  return syscall(SYS_set_mempolicy, kMpolBind, &mask, 8 * sizeof(unsigned long)) == 0;
+  return syscall(SYS_set_mempolicy, mode, &mask, 8 * sizeof(unsigned long)) == 0;
 }
 
 void restore_thread_policy(int mode, unsigned long mask) {
@@ -210,9 +212,35 @@ void restore_thread_policy(int mode, unsigned long mask) {
 }
 
 bool numa_node_exists(int node) {
+  if (node < 0 || node >= kMaxNumaNodes) return false;
   char path[96];
   std::snprintf(path, sizeof path, "/sys/devices/system/node/node%d", node);
   return access(path, F_OK) == 0;
+}
+
+// Mask of the online NUMA nodes below kMaxNumaNodes, from the kernel's list
+// ("0", "0-3", "0-1,4"); 0 if it cannot be read.
+unsigned long online_numa_nodes() {
+  FILE *f = std::fopen("/sys/devices/system/node/online", "r");
+  if (!f) return 0;
+  char buf[256] = {0};
+  const size_t got = std::fread(buf, 1, sizeof buf - 1, f);
+  std::fclose(f);
+  buf[got] = 0;
+  unsigned long mask = 0;
+  const char *c = buf;
+  while (*c >= '0' && *c <= '9') {
+    char *end = nullptr;
+    long a = std::strtol(c, &end, 10), b = a;
+    c = end;
+    if (*c == '-') {
+      b = std::strtol(c + 1, &end, 10);
+      c = end;
+    }
+    for (long k = a; k <= b && k < kMaxNumaNodes; k++) mask |= 1ul << k;
+    if (*c == ',') c++;
+  }
+  return mask;
 }
 
 double now_us() {
@@ -826,6 +854,8 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
                   "a pool sharing a host pool must have the group's geometry (all but device_slots)");
   } else if (desc->numa_node >= 0 && !numa_node_exists(desc->numa_node)) {
     return fail(KV_EINVAL, "numa_node " + std::to_string(desc->numa_node) + " does not exist");
+  } else if (desc->numa_node >= 0 && (desc->flags & KV_F_HOST_INTERLEAVE)) {
+    return fail(KV_EINVAL, "numa_node and KV_F_HOST_INTERLEAVE are exclusive");
   }
   int ndev = 0;
   hipError_t e = hipGetDeviceCount(&ndev);
@@ -886,11 +916,19 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
     unsigned long old_mask = 0;
     bool bound = false;
     if (desc->numa_node >= 0) {
-      bound = bind_thread_to_node(desc->numa_node, &old_mode, &old_mask);
+      bound = set_thread_policy(kMpolBind, 1ul << desc->numa_node, &old_mode, &old_mask);
       if (!bound) {
         delete p;
         return fail(KV_EINVAL,
                     "set_mempolicy to node " + std::to_string(desc->numa_node) + " failed");
+      }
+      hflags |= hipHostMallocNumaUser;
+    } else if (desc->flags & KV_F_HOST_INTERLEAVE) {
+      const unsigned long nodes = online_numa_nodes();
+      bound = nodes != 0 && set_thread_policy(kMpolInterleave, nodes, &old_mode, &old_mask);
+      if (!bound) {
+        delete p;
+        return fail(KV_EINVAL, "set_mempolicy to interleave over the online nodes failed");
       }
       hflags |= hipHostMallocNumaUser;
     }

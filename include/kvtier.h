@@ -119,6 +119,10 @@ typedef enum {
                                       direction has a transfer in flight at submission on
                                       another stream (work queued on the same stream runs
                                       before this call, not beside it). */
+#define KV_F_HOST_INTERLEAVE  0x20u /* spread the host pool's pages across all online NUMA
+                                       nodes (interleaved placement: capacity first; Baidu KV
+                                       cache page, "shared buffer placement"); exclusive with
+                                       numa_node >= 0 (socket-local placement) */
 #define KV_F_SHARE_CHECK      0x10u /* on the writer of a shared host pool (kv_pool_create_shared):
                                        each backup of a sharing pool must name the same host
                                        slots and layer range as the writer's latest backup,
@@ -146,7 +150,8 @@ typedef struct {
    * buffers it points to are borrowed. */
   void *const *device_buffers;
   int32_t device;    /* HIP device ordinal the buffers live on */
-  int32_t numa_node; /* -1: no binding; else the host pool's pages are bound to this node */
+  int32_t numa_node; /* -1: no binding; else the host pool's pages are bound to this node
+                        (0..63) */
   uint32_t flags;    /* KV_F_* */
 } kv_pool_desc_t;
 

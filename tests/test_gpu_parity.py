@@ -197,6 +197,25 @@ def test_pool_create_rejects_bad_buffers(torch):
     assert kvt.kv_pool_host_bytes(h) == 2 * 16 * 32
     assert kvt.kv_pool_destroy(h) == kvt.OK
     assert kvt.kv_pool_destroy(None) == kvt.OK
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), good[1].data_ptr()], numa_node=64)
+    assert rc == kvt.EINVAL
+    rc, h = kvt.kv_pool_create(kg, [good[0].data_ptr(), good[1].data_ptr()], numa_node=0,
+                               flags=kvt.F_CHECK_UNIQUE | kvt.F_HOST_INTERLEAVE)
+    assert rc == kvt.EINVAL and "exclusive" in kvt.kv_last_error()
+
+
+def test_interleaved_host_pool_parity(torch, stream):
+    """A host pool spread over every online NUMA node moves the same bytes."""
+    g = Geometry(3, 2, 272, 700, 640, 16, oracle.PAGE_FIRST_DIRECT)
+    bufs = device_buffers(g, seed=19)
+    rng = np.random.default_rng(19)
+    for path in (kvt.PATH_KERNEL, kvt.PATH_DMA):
+        pool = make_pool(g, bufs, path, flags=kvt.F_CHECK_UNIQUE | kvt.F_HOST_INTERLEAVE)
+        d, h = _request(rng, g, "random")
+        run_backup_and_compare(g, pool, bufs, d, h, 0, 3, stream)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, 0, 3, stream)
+        pool.close()
 
 
 def test_noncoherent_host_pool_parity(torch, stream):
