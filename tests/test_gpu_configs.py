@@ -259,3 +259,47 @@ def test_streamed_per_layer_events(torch):
             check_load_layers(torch, g, pool, bufs, dev_idx, host_idx, sample_layers(g.L))
     del bufs
     release(torch)
+
+
+# ---- mla32k with a host pool shared by a tensor-parallel group of two ---------------
+
+@pytest.mark.timeout(300)
+def test_mla32k_shared_host_pool(torch):
+    """The 32768-token MLA prefix in a group of two pools sharing one host pool:
+    the writer backs up (fragmented device pages), the other rank's backup moves
+    nothing, and the other rank loads into its own device pool at other slots,
+    on a second stream, with no host synchronisation after the writer's call."""
+    shape = workloads.mla32k()
+    n = shape.extra["tokens"]
+    src = make_bufs(torch, shape, 3, shape.device_slots)
+    dst = [torch.empty_like(b) for b in src]
+    for b in dst:
+        b.fill_(SENTINEL)
+    dev_w, host_idx = workloads.prefix_indices(shape, 3, n, fragmented=True)
+    dev_r, _ = workloads.prefix_indices(shape, 5, n, fragmented=True)
+    g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
+                 shape.host_slots, shape.page_size, oracle.PAGE_FIRST_DIRECT)
+    before = [untouched_sum(torch, b, shape.row_bytes, dev_r) for b in dst]
+    writer = kvt.KvPool(kvt.geometry(*g.args()), src,
+                        flags=kvt.F_CHECK_UNIQUE | kvt.F_SHARE_CHECK)
+    reader = kvt.KvPool(kvt.geometry(*g.args()), dst, share_with=writer)
+    s_w, s_r = torch.cuda.Stream(), torch.cuda.Stream()
+    print("mla32k shared: writer backup, reader backup + load", flush=True)
+    writer.backup(dev_w, host_idx, 0, g.L, s_w)
+    reader.backup(dev_r, host_idx, 0, g.L, s_r)
+    reader.load(dev_r, host_idx, 0, g.L, s_r)
+    s_r.synchronize()
+    s_w.synchronize()
+    assert reader.last_path(kvt.BACKUP) == kvt.PATH_SHARED
+    check_backup_layers(torch, g, writer, src, dev_w, host_idx, sample_layers(g.L))
+    check_load_layers(torch, g, reader, dst, dev_r, host_idx, range(g.L))
+    for l in range(g.L):        # every row the reader holds is the writer's source row
+        a = src[l].view(-1, g.R).index_select(0, torch.from_numpy(dev_w).cuda())
+        b = dst[l].view(-1, g.R).index_select(0, torch.from_numpy(dev_r).cuda())
+        assert torch.equal(a, b), l
+    after = [untouched_sum(torch, b, shape.row_bytes, dev_r) for b in dst]
+    assert after == before
+    reader.close()
+    writer.close()
+    del src, dst
+    release(torch)
