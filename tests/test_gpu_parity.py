@@ -640,3 +640,26 @@ def test_back_to_back_on_one_stream(torch, stream, layout, path):
             assert torch.equal(a, b), (rep, k)
     pool2.close()
     pool.close()
+
+
+def test_request_row_limit(torch, stream):
+    """A call moves fewer than 2^31 rows (n x layers x components): a request of
+    exactly 2^31 rows is refused in both directions before anything is enqueued.
+    2048 (layer, component) buffers alias one 16 MiB device allocation and every
+    request position names host slot 0 (no uniqueness check), so the pools stay
+    small; only the refusal is exercised, no transfer runs."""
+    L, C, R, S_dev = 1024, 2, 16, 1 << 20
+    one = torch.zeros(S_dev * R, dtype=torch.uint8, device="cuda:0")
+    kg = kvt.geometry(L, C, R, S_dev, 1, 1, kvt.LAYER_FIRST)
+    rc, h = kvt.kv_pool_create(kg, [one.data_ptr()] * (L * C), flags=0)
+    assert rc == kvt.OK, kvt.kv_last_error()
+    n = (1 << 31) // (L * C)                       # exactly 2^31 rows over all layers
+    d = np.arange(n, dtype=np.int64)
+    hz = np.zeros(n, dtype=np.int64)
+    for direction in (kvt.kv_backup, kvt.kv_load):
+        assert direction(h, d, hz, 0, L, stream) == kvt.EINVAL
+        assert "2^31" in kvt.kv_last_error()
+    assert kvt.kv_get_stats(h)[1].calls[0] == 0 and kvt.kv_get_stats(h)[1].calls[1] == 0
+    stream.synchronize()
+    assert int(one.sum()) == 0
+    assert kvt.kv_pool_destroy(h) == kvt.OK
