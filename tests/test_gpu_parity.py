@@ -663,3 +663,60 @@ def test_request_row_limit(torch, stream):
     stream.synchronize()
     assert int(one.sum()) == 0
     assert kvt.kv_pool_destroy(h) == kvt.OK
+
+
+def _fuzz_case(seed):
+    """A seeded random geometry, request, layer range, layout and path."""
+    rng = np.random.default_rng([7001, seed])
+    L = int(rng.integers(1, 7))
+    C = int(rng.integers(1, 3))
+    R = 16 * int(rng.choice([1, 2, 3, 5, 8, 17, 64, 72, 128, 257]))
+    ps = int(rng.choice([1, 2, 4, 16, 64]))
+    S_host = ps * int(rng.integers(1, max(2, 1500 // ps)))
+    S_dev = int(rng.integers(1, 1600))
+    layout = int(rng.integers(0, 3))
+    path = int(rng.choice(PATHS))
+    n_max = min(S_dev, S_host)
+    kind = rng.choice(["random", "contiguous", "pages", "tiny"])
+    if kind == "tiny" or n_max < 2:
+        n = int(rng.integers(0, min(3, n_max) + 1))
+    else:
+        n = int(rng.integers(1, n_max + 1))
+    if kind == "contiguous":
+        d0 = int(rng.integers(0, S_dev - n + 1))
+        h0 = int(rng.integers(0, S_host - n + 1))
+        d, h = np.arange(d0, d0 + n), np.arange(h0, h0 + n)
+    elif kind == "pages" and S_host // ps >= 1 and S_dev >= ps:
+        npg = int(rng.integers(1, min(S_dev // ps, S_host // ps) + 1))
+        dp = rng.permutation(S_dev // ps)[:npg]
+        hp = rng.permutation(S_host // ps)[:npg]
+        d, h = workloads.page_indices(dp, ps), workloads.page_indices(hp, ps)
+        cut = int(rng.integers(1, d.size + 1))       # a ragged last page
+        d, h = d[:cut], h[:cut]
+    else:
+        d = rng.choice(S_dev, n, replace=False)
+        h = rng.choice(S_host, n, replace=False)
+    l0 = int(rng.integers(0, L + 1))
+    l1 = int(rng.integers(l0, L + 1))
+    if rng.random() < 0.5:
+        l0, l1 = 0, L
+    return (Geometry(L, C, R, S_dev, S_host, ps, layout), path, d.astype(np.int64),
+            h.astype(np.int64), l0, l1)
+
+
+@pytest.mark.parametrize("block", range(6))
+def test_random_geometry_sweep(torch, stream, block):
+    """100 seeded random cases per block: every layout and path, row sizes from 16
+    bytes to 4 KiB, ragged page tails, partial layer ranges, empty requests."""
+    for seed in range(100 * block, 100 * (block + 1)):
+        g, path, d, h, l0, l1 = _fuzz_case(seed)
+        print("sweep seed=%d L=%d C=%d R=%d S_dev=%d S_host=%d ps=%d layout=%d path=%d n=%d "
+              "layers=[%d,%d)" % (seed, g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, path,
+                                  d.size, l0, l1), flush=True)
+        bufs = device_buffers(g, seed=seed)
+        pool = make_pool(g, bufs, path)
+        run_backup_and_compare(g, pool, bufs, d, h, l0, l1, stream)
+        pool.host_array()[:] = np.random.default_rng(seed).integers(
+            0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, l0, l1, stream)
+        pool.close()
