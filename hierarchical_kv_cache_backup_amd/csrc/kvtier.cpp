@@ -45,6 +45,19 @@ int hip_fail(hipError_t e, const char *what) {
   return fail(KV_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// Runs an entry point's body so that no C++ exception crosses the C ABI: an
+// allocation failure of the library's own host bookkeeping becomes KV_ENOMEM.
+template <typename F>
+int guarded(const char *what, F &&body) {
+  try {
+    return body();
+  } catch (const std::bad_alloc &) {
+    return fail(KV_ENOMEM, std::string(what) + ": out of host memory");
+  } catch (const std::exception &ex) {
+    return fail(KV_EINVAL, std::string(what) + ": " + ex.what());
+  }
+}
+
 struct DeviceGuard {
   int prev = -1;
   bool changed = false;
@@ -993,13 +1006,13 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
 }
 
 int kv_pool_create(const kv_pool_desc_t *desc, kv_pool_t **out) {
-  return create_pool(desc, nullptr, out);
+  return guarded("kv_pool_create", [&] { return create_pool(desc, nullptr, out); });
 }
 
 int kv_pool_create_shared(const kv_pool_desc_t *desc, kv_pool_t *group, kv_pool_t **out) {
   if (out) *out = nullptr;
   if (!group) return fail(KV_EINVAL, "group is null");
-  return create_pool(desc, group, out);
+  return guarded("kv_pool_create_shared", [&] { return create_pool(desc, group, out); });
 }
 
 void *kv_pool_host_ptr(const kv_pool_t *p) { return p ? p->host : nullptr; }
@@ -1007,12 +1020,16 @@ int64_t kv_pool_host_bytes(const kv_pool_t *p) { return p ? p->host_bytes : 0; }
 
 int kv_backup(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
               int32_t layer_begin, int32_t layer_end, void *stream) {
-  return transfer(p, 0, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  return guarded("kv_backup", [&] {
+    return transfer(p, 0, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  });
 }
 
 int kv_load(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
             int32_t layer_begin, int32_t layer_end, void *stream) {
-  return transfer(p, 1, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  return guarded("kv_load", [&] {
+    return transfer(p, 1, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  });
 }
 
 int kv_load_layer(kv_pool_t *p, int32_t layer, void *compute_stream) {
@@ -1039,7 +1056,11 @@ int kv_stream_create(int32_t device, void **out) {
   DeviceGuard dg(device);
   if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
   hipStream_t st = nullptr;
-  e = create_aux_stream(&st);
+  int rc = guarded("kv_stream_create", [&] {
+    e = create_aux_stream(&st);
+    return KV_OK;
+  });
+  if (rc) return rc;
   if (e != hipSuccess) return hip_fail(e, "creating a stream");
   *out = st;
   return KV_OK;

@@ -7,6 +7,8 @@
 #include <algorithm>
 #include <cstdio>
 #include <limits>
+#include <new>
+#include <utility>
 
 namespace kvt {
 
@@ -105,21 +107,41 @@ int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t
   if (check_unique && n > 1) {
     const int64_t *dst = direction == 0 ? host_idx : dev_idx;
     const int64_t slots = direction == 0 ? g.S_host : g.S_dev;
-    if ((int64_t)scratch->stamp.size() < slots) scratch->stamp.assign(slots, 0);
-    if (++scratch->gen == 0) {  // wrapped: clear once every 2^32 calls
-      std::fill(scratch->stamp.begin(), scratch->stamp.end(), 0u);
-      scratch->gen = 1;
-    }
-    const uint32_t gen = scratch->gen;
-    uint32_t *st = scratch->stamp.data();
-    for (int64_t i = 0; i < n; i++) {
-      if (st[dst[i]] == gen) {
-        *why = fmt(direction == 0 ? "host slot %lld is a destination twice (position %lld)"
-                                  : "device slot %lld is a destination twice (position %lld)",
-                   dst[i], i);
-        return KV_EDUP;
+    // The first position whose destination appeared earlier in the request.
+    int64_t dup = -1;
+    try {
+      if (slots <= std::max<int64_t>(kStampSlotsMin, 4 * n)) {
+        // one stamp per slot, kept between calls; a generation counter instead
+        // of clearing
+        if ((int64_t)scratch->stamp.size() < slots) scratch->stamp.assign(slots, 0);
+        if (++scratch->gen == 0) {  // wrapped: clear once every 2^32 calls
+          std::fill(scratch->stamp.begin(), scratch->stamp.end(), 0u);
+          scratch->gen = 1;
+        }
+        const uint32_t gen = scratch->gen;
+        uint32_t *st = scratch->stamp.data();
+        for (int64_t i = 0; i < n && dup < 0; i++) {
+          if (st[dst[i]] == gen) dup = i;
+          st[dst[i]] = gen;
+        }
+      } else {
+        // far more slots than positions: sort (slot, position) pairs instead of
+        // holding a stamp per slot
+        std::vector<std::pair<int64_t, int64_t>> v((size_t)n);
+        for (int64_t i = 0; i < n; i++) v[(size_t)i] = {dst[i], i};
+        std::sort(v.begin(), v.end());
+        for (size_t k = 1; k < v.size(); k++)
+          if (v[k].first == v[k - 1].first && (dup < 0 || v[k].second < dup)) dup = v[k].second;
       }
-      st[dst[i]] = gen;
+    } catch (const std::bad_alloc &) {
+      *why = "out of memory in the destination uniqueness check";
+      return KV_ENOMEM;
+    }
+    if (dup >= 0) {
+      *why = fmt(direction == 0 ? "host slot %lld is a destination twice (position %lld)"
+                                : "device slot %lld is a destination twice (position %lld)",
+                 dst[dup], dup);
+      return KV_EDUP;
     }
   }
   return KV_OK;
@@ -290,13 +312,19 @@ static int count_common(const kv_geometry_t *geom, const int64_t *dev_idx, const
     set_error(why);
     return rc;
   }
-  std::vector<Run> runs;
-  build_runs(g, dev_idx, host_idx, n, &runs);
-  int64_t per_lc = (int64_t)runs.size();
-  if (merge2d) {
-    std::vector<Copy> copies;
-    build_copies(g, runs, dev_idx, host_idx, &copies);
-    per_lc = (int64_t)copies.size();
+  int64_t per_lc = 0;
+  try {
+    std::vector<Run> runs;
+    build_runs(g, dev_idx, host_idx, n, &runs);
+    per_lc = (int64_t)runs.size();
+    if (merge2d) {
+      std::vector<Copy> copies;
+      build_copies(g, runs, dev_idx, host_idx, &copies);
+      per_lc = (int64_t)copies.size();
+    }
+  } catch (const std::bad_alloc &) {
+    set_error("out of host memory while counting segments");
+    return KV_ENOMEM;
   }
   *out = per_lc * (int64_t)(l1 - l0) * g.C;
   return KV_OK;

@@ -51,7 +51,10 @@ inline int64_t host_row(const Geom &g, int32_t l, int32_t c, int64_t h) {
 }
 
 // Reusable scratch for the O(n) destination-uniqueness check: one stamp per
-// slot and a generation counter, so no clearing between calls.
+// slot and a generation counter, so no clearing between calls. Used while the
+// pool has at most max(kStampSlotsMin, 4 n) destination slots; beyond that the
+// check sorts a copy of the request instead (O(n log n), no per-slot memory).
+constexpr int64_t kStampSlotsMin = int64_t(1) << 22;
 struct UniqueScratch {
   std::vector<uint32_t> stamp;
   uint32_t gen = 0;

@@ -52,6 +52,9 @@
  * kv_last_error() gives a message for the calling thread. When validation
  * fails nothing is enqueued and no byte of either pool is modified. A HIP
  * failure of already-enqueued work surfaces at a later call or at destroy.
+ * No C++ exception leaves the library: if the library's own host bookkeeping
+ * cannot be allocated, the call returns KV_ENOMEM (a transfer may then have
+ * been partly enqueued).
  */
 #ifndef KVTIER_H
 #define KVTIER_H
@@ -221,8 +224,11 @@ int64_t kv_host_row(const kv_geometry_t *geom, int32_t layer, int32_t comp, int6
  *              0 <= layer_begin <= layer_end <= L;
  *   KV_ERANGE  some dev_idx[i] outside [0,S_dev) or host_idx[i] outside [0,S_host);
  *   KV_EDUP    (check_unique != 0) a destination slot repeats: host_idx for
- *              backup, dev_idx for load.
- * The first failing rule in this order decides the code. n == 0 is KV_OK. */
+ *              backup, dev_idx for load; the message names the first position
+ *              whose slot appeared earlier in the request.
+ * The first failing rule in this order decides the code. n == 0 is KV_OK.
+ * The duplicate check costs O(n) with a per-slot table while the pool has at
+ * most max(2^22, 4n) destination slots, else O(n log n) on a sorted copy. */
 int kv_validate(const kv_geometry_t *geom, int32_t direction, const int64_t *dev_idx,
                 const int64_t *host_idx, int64_t n, int32_t layer_begin, int32_t layer_end,
                 int32_t check_unique);

@@ -104,6 +104,35 @@ def test_geometry_and_validation_codes_match_oracle(kvt):
                     == oracle.validate(g, direction, d, h, l0, l1, True))
 
 
+def test_uniqueness_check_on_huge_pools(kvt):
+    """Pools with far more slots than a request's positions (2^40 here): the
+    duplicate check must not hold memory per slot, and it agrees with the oracle,
+    including the position the message names."""
+    g = Geometry(1, 1, 16, 1 << 40, 1 << 40, 1, 0)
+    kg = _geom(kvt, g)
+    rng = np.random.default_rng(5)
+    for trial in range(40):
+        n = int(rng.integers(2, 3000))
+        d = rng.choice(1 << 40, n, replace=False)
+        h = rng.choice(1 << 40, n, replace=False)
+        if trial % 2:
+            j, k = sorted(rng.choice(n, 2, replace=False))
+            d[k] = d[j]
+            h[k] = h[j]
+        for direction in (0, 1):
+            want = oracle.validate(g, direction, d, h, 0, 1, True)
+            assert kvt.kv_validate(kg, direction, d, h, 0, 1, True) == want
+            if want == kvt.EDUP:
+                assert ("position %d)" % k) in kvt.kv_last_error()
+    # the stamp array and the sorted copy name the same first repeat
+    small = Geometry(1, 1, 16, 64, 64, 1, 0)
+    for big in (False, True):
+        gg = Geometry(1, 1, 16, 1 << 40, 1 << 40, 1, 0) if big else small
+        assert kvt.kv_validate(_geom(kvt, gg), 0, [1, 2, 3, 4, 5], [9, 7, 8, 7, 9], 0, 1,
+                               True) == kvt.EDUP
+        assert "host slot 7 is a destination twice (position 3)" in kvt.kv_last_error()
+
+
 def test_segment_counts_match_oracle(kvt):
     rng = np.random.default_rng(2)
     for _ in range(150):
