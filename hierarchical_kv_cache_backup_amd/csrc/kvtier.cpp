@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kStagingSlots = 16;  // index-staging buffers in flight per direction
 constexpr int64_t kMaxRowsPerLaunch = (int64_t)1 << 31;
+constexpr double kExtentPlanLimit = 4.0 * 1024 * 1024;  // staged extents AUTO lists exactly
 
 int fail(int code, const std::string &msg) {
   set_error(msg);
@@ -670,7 +671,15 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     have_copies = true;
     host_runs(g, host_idx, n, &d.host_run_start);
     have_host_runs = true;
-    build_extents(g, host_idx, n, d.host_run_start, l0, l1, &d.extents);
+    // Exact staging extents cost O(pairs x host runs) to list; past
+    // kExtentPlanLimit the upper bound pairs x runs prices the staged path (at
+    // one copy per extent it cannot win there anyway).
+    const double runs_x_pairs = (double)(d.host_run_start.size() - 1) * (double)nlc_all;
+    double extents = runs_x_pairs;
+    if (g.layout == KV_PAGE_FIRST || runs_x_pairs <= kExtentPlanLimit) {
+      build_extents(g, host_idx, n, d.host_run_start, l0, l1, &d.extents);
+      extents = (double)d.extents.size();
+    }
     const double mb = (double)bytes;
     double t_kernel = c.kernel_launch_us[dir] + (ngroups - 1) * c.kernel_group_us[dir] +
                       mb / (c.kernel_gbps[dir] * 1e3);
@@ -678,7 +687,6 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
                    mb / (c.dma_gbps[dir] * 1e3);
     // the staged path moves page-major layouts in one unit (see below); its
     // device-side passes overlap the copies except for the first chunk's
-    const double extents = (double)d.extents.size();
     const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
     const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units;
     double t_staged = extents * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
