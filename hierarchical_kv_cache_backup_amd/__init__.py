@@ -57,7 +57,8 @@ class kv_calib_t(ctypes.Structure):
                 ("staged_chunk_bytes", ctypes.c_double),
                 ("staged_gather_gbps", ctypes.c_double),
                 ("kernel_group_us", ctypes.c_double * 2),
-                ("staged_min_gain", ctypes.c_double)]
+                ("staged_min_gain", ctypes.c_double),
+                ("index_zero_copy_max_bytes", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):

@@ -202,6 +202,10 @@ typedef struct {
   double kernel_group_us[2];    /* gap per further kernel launch of one call */
   double staged_min_gain;       /* AUTO takes the staged path only if its modelled time is
                                    below (1 - staged_min_gain) x the best direct path's */
+  double index_zero_copy_max_bytes[2]; /* kernel and staged paths: a request whose index
+                                   pairs (16 bytes per position) fit in this many bytes
+                                   has them read by the kernels from the mapped pinned
+                                   staging buffer, skipping the copy to the device */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

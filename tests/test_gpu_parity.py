@@ -720,3 +720,29 @@ def test_random_geometry_sweep(torch, stream, block):
             0, 256, size=g.host_bytes(), dtype=np.uint8)
         run_load_and_compare(g, pool, bufs, d, h, l0, l1, stream)
         pool.close()
+
+
+@pytest.mark.parametrize("zero_copy", (False, True), ids=["copied", "zero_copy"])
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_STAGED))
+def test_index_pairs_copied_or_read_in_place(torch, stream, zero_copy, path):
+    """The kernels take the request's index pairs either from a device copy or
+    straight from the mapped pinned staging buffer (index_zero_copy_max_bytes);
+    both give the oracle's bytes, for requests far above and below the default
+    threshold, in every layout."""
+    for layout in LAYOUTS:
+        g = Geometry(3, 2, 272, 700, 640, 16, layout)
+        bufs = device_buffers(g, seed=70 + layout)
+        pool = make_pool(g, bufs, path)
+        c = pool.calibration()
+        c.index_zero_copy_max_bytes[:] = [1e18, 1e18] if zero_copy else [0.0, 0.0]
+        pool.set_calibration(c)
+        rng = np.random.default_rng(71 + layout)
+        for n in (1, 5, 127, 600):
+            d = rng.choice(g.S_dev, n, replace=False).astype(np.int64)
+            h = rng.choice(g.S_host, n, replace=False).astype(np.int64)
+            print("index pairs zero_copy=%d path=%d layout=%d n=%d" % (zero_copy, path, layout, n),
+                  flush=True)
+            run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+            pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+            run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        pool.close()
