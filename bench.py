@@ -779,7 +779,6 @@ def leg_streamed(torch, kvt, workloads, args):
             b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
             workloads.fill_device_buffer(b, shape, 5, l, c, torch)
             bufs.append(b)
-    geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
     s_load, s_comp = kvt.Stream(), torch.cuda.Stream()   # loads on a queue of their own
     layer_bytes = n * C * R
     acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
@@ -800,11 +799,15 @@ def leg_streamed(torch, kvt, workloads, args):
         e1.synchronize()
     t_pass = e0.elapsed_time(e1) / 1e3 / 10
     results = {}
-    variants = (("kernel", kvt.PATH_KERNEL, 0), ("kernel_overlap_flag", kvt.PATH_KERNEL,
-                                                 kvt.F_LOAD_OVERLAP),
-                ("dma", kvt.PATH_DMA, 0), ("staged", kvt.PATH_STAGED, 0),
-                ("auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP))
-    for pname, p, extra_flags in variants:
+    pfd = kvt.PAGE_FIRST_DIRECT
+    variants = (("kernel", kvt.PATH_KERNEL, 0, 0),
+                ("kernel_overlap_flag", kvt.PATH_KERNEL, kvt.F_LOAD_OVERLAP, 0),
+                ("dma", kvt.PATH_DMA, 0, 0), ("staged", kvt.PATH_STAGED, 0, 0),
+                ("auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP, 0),
+                ("page_first_direct/kernel_overlap_flag", kvt.PATH_KERNEL, kvt.F_LOAD_OVERLAP, pfd),
+                ("page_first_direct/auto_overlap_flag", kvt.PATH_AUTO, kvt.F_LOAD_OVERLAP, pfd))
+    for pname, p, extra_flags, lay in variants:
+        geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, lay)
         pool = kvt.KvPool(geom, bufs, flags=kvt.F_CHECK_UNIQUE | extra_flags)
         pool.backup(dev_idx, host_idx, 0, L, s_load)       # L2 holds the prefix
         s_load.synchronize()
@@ -865,7 +868,8 @@ def leg_streamed(torch, kvt, workloads, args):
     del bufs
     torch.cuda.empty_cache()
     return {"workload": "61 layers x K/V x 1024 B (fp8 random bytes), 131072-token prefix, "
-                        "per-layer H2D overlapped with an HBM-bound consumer",
+                        "per-layer H2D overlapped with an HBM-bound consumer; host layout "
+                        "layer_first unless the variant names page_first_direct",
             "layer_bytes": layer_bytes, "consumer_pass_ms": round(t_pass * 1e3, 3),
             "paths": results}
 
