@@ -9,6 +9,16 @@ timed region. Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layout layer_first]
                     [--path auto|kernel|kernel_lds|dma] [--no-matrix] [--no-cpu-baseline]
+                    [--no-extra]
+
+Besides the headline step it reports the layout x path matrix, the bidirectional
+mixed batch, the per-layer streamed load, the write filter and the oracle as CPU
+baseline. Studies that print their own JSON line and exit:
+
+    python bench.py --host-memory-study 3 24    # pinned pool size and NUMA placement
+    python bench.py --free-list-study           # FIFO vs LIFO host free list under churn
+    python bench.py --tp-shared-study 8         # tensor-parallel group sharing one host pool
+    python bench.py --profile-counters          # the kernels a rocprofv3 --pmc pass needs
 """
 import argparse
 import hashlib
