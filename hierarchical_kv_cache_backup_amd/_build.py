@@ -11,7 +11,7 @@ LIB = os.path.join(PKG, "libkvtier.so")
 SOURCES = ["plan.cpp", "kernels.hip", "kvtier.cpp", "ghost.cpp", "slots.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wno-unused-parameter",
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-Wshadow", "-Wno-unused-parameter",
           "-I" + INCLUDE, "-I" + CSRC]
 # gfx950 only; packed-fp32 instruction selection switched off for all device code.
 DEVICE = ["-x", "hip", "--offload-arch=gfx950",

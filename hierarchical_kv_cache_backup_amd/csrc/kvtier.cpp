@@ -739,9 +739,9 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
       const int32_t lb = std::min(l1, la + group);
       for (int32_t l = la; l < lb && e == hipSuccess; l++)
-        for (int32_t c = 0; c < g.C && e == hipSuccess; c++)
+        for (int32_t comp = 0; comp < g.C && e == hipSuccess; comp++)
           for (const Copy &cp : d.copies) {
-            e = issue_copy(p, dir, l * g.C + c, cp, s);
+            e = issue_copy(p, dir, l * g.C + comp, cp, s);
             if (e != hipSuccess) break;
           }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
