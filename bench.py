@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
                         "into profiles/counters.json and exit")
+    p.add_argument("--summarize-link-counters", nargs=2, metavar=("WRREQ_DIR", "RDREQ_DIR"),
+                   help="add the host-link bytes of two rocprofv3 --pmc output directories "
+                        "(TCC_EA0_WRREQ*_sum, TCC_EA0_RDREQ*_sum) to profiles/counters.json "
+                        "and exit")
     return p.parse_args()
 
 
@@ -76,6 +80,9 @@ def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_link_counters:
+        summarize_link_counters(*args.summarize_link_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -345,19 +352,31 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel_name, src_hash):
-    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def _counter_record(kernel_name):
     path = os.path.join(ROOT, "profiles", "counters.json")
     try:
         with open(path) as f:
-            d = json.load(f)
+            return json.load(f).get(kernel_name) or {}
     except (OSError, ValueError):
-        return None
-    rec = d.get(kernel_name)
-    if not rec or rec.get("kernel_source_hash") != src_hash:
+        return {}
+
+
+def counter_traffic(kernel_name, src_hash):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    rec = _counter_record(kernel_name)
+    if rec.get("kernel_source_hash") != src_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def counter_link_bytes(kernel_name, src_hash):
+    """Host-link bytes per launch (remote L2-to-fabric requests) from the
+    committed counter summary, if taken on the current kernel source; else None."""
+    link = _counter_record(kernel_name).get("link") or {}
+    if link.get("kernel_source_hash") != src_hash:
+        return None
+    return link.get("host_link_bytes_per_launch")
 
 
 def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, args):
@@ -397,6 +416,7 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
             "unit": "GB/s",
             "frac": round(a_d2h / PCIE_GEN5_X16_GBPS, 4),
             "traffic": counter_traffic("xfer_rows_d2h", src_hash),
+            "host_link_bytes_per_launch": counter_link_bytes("xfer_rows_d2h", src_hash),
             "algorithmic_bytes_per_launch": d2h_bytes,
             "mean_launch_us": round(t_d2h * 1e6, 2),
             "launches_timed": k_d2h,
@@ -406,7 +426,9 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
                            "algorithmic_bytes_per_launch": h2d_bytes,
                            "mean_launch_us_incl_gap": round(t_h2d * 1e6, 2),
                            "launches_timed": k_h2d,
-                           "traffic": counter_traffic("xfer_rows_h2d", src_hash)},
+                           "traffic": counter_traffic("xfer_rows_h2d", src_hash),
+                           "host_link_bytes_per_launch": counter_link_bytes("xfer_rows_h2d",
+                                                                             src_hash)},
             "hbm_secondary": {"peak": HBM_PEAK_GBPS, "frac": round(a_d2h / HBM_PEAK_GBPS, 5)},
             "kernel_source_hash": src_hash}
 
@@ -442,6 +464,71 @@ def _counter_rows(d):
     return rows
 
 
+def _kernel_key(name):
+    return ("copy" if "elementwise_kernel" in name and "copy" in name else
+            "xfer_rows_d2h" if "xfer_rows<true, false>" in name else
+            "xfer_rows_h2d" if "xfer_rows<false, false>" in name else None)
+
+
+def summarize_link_counters(wr_dir, rd_dir):
+    """Host-link bytes per launch of the transfer kernels from the L2-to-fabric
+    request counters: all requests minus those bound for local DRAM are remote,
+    i.e. cross the host link. Writes are 64 or 32 bytes (TCC_EA0_WRREQ_64B
+    counts the 64-byte ones); reads are 128, 64 or 32 bytes (TCC_EA0_RDREQ_64B
+    and _32B count the smaller ones). Remote writes are sized 64 bytes when the
+    kernel's 64-byte writes cover them, else 32; remote reads 128 bytes up to the
+    kernel's count of 128-byte reads, the rest 64. The plain copy kernel of known
+    size (all DRAM) checks the sizes."""
+    per = {}
+    for d in (wr_dir, rd_dir):
+        for r in _counter_rows(d):
+            key = _kernel_key(r["Kernel_Name"])
+            if key is None:
+                continue
+            per.setdefault((key, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    med = {k: statistics.median(v) for k, v in per.items()}
+
+    def get(key, c):
+        return med.get((key, c), 0.0)
+
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    with open(path) as fh:
+        out = json.load(fh)
+    src_hash = kernel_source_hash()
+    known = 4 * (64 << 20)
+    copy_w = get("copy", "TCC_EA0_WRREQ_64B_sum") * 64 + (
+        get("copy", "TCC_EA0_WRREQ_sum") - get("copy", "TCC_EA0_WRREQ_64B_sum")) * 32
+    copy_r = (get("copy", "TCC_EA0_RDREQ_32B_sum") * 32 + get("copy", "TCC_EA0_RDREQ_64B_sum") * 64
+              + (get("copy", "TCC_EA0_RDREQ_sum") - get("copy", "TCC_EA0_RDREQ_32B_sum")
+                 - get("copy", "TCC_EA0_RDREQ_64B_sum")) * 128)
+    for key in ("xfer_rows_d2h", "xfer_rows_h2d"):
+        wr, wr_dram = get(key, "TCC_EA0_WRREQ_sum"), get(key, "TCC_EA0_WRREQ_DRAM_sum")
+        wr64 = get(key, "TCC_EA0_WRREQ_64B_sum")
+        rd, rd_dram = get(key, "TCC_EA0_RDREQ_sum"), get(key, "TCC_EA0_RDREQ_DRAM_sum")
+        rd32, rd64 = get(key, "TCC_EA0_RDREQ_32B_sum"), get(key, "TCC_EA0_RDREQ_64B_sum")
+        rd128 = rd - rd32 - rd64
+        # remote writes: sized 64 B unless the kernel issued 32 B writes
+        wr_remote = wr - wr_dram
+        wr_remote_bytes = wr_remote * (64 if wr64 >= wr_remote else 32)
+        # remote reads: the 128 B requests beyond the DRAM ones (the kernels' host
+        # reads are full lines; the DRAM side holds the small index reads)
+        rd_remote = rd - rd_dram
+        rd_remote_128 = min(rd_remote, rd128)
+        rd_remote_bytes = rd_remote_128 * 128 + (rd_remote - rd_remote_128) * 64
+        rec = out.setdefault(key, {})
+        rec["link"] = {"remote_write_requests": wr_remote, "remote_write_bytes": wr_remote_bytes,
+                       "dram_write_requests": wr_dram,
+                       "remote_read_requests": rd_remote, "remote_read_bytes": rd_remote_bytes,
+                       "dram_read_requests": rd_dram,
+                       "host_link_bytes_per_launch": wr_remote_bytes + rd_remote_bytes,
+                       "kernel_source_hash": src_hash}
+    out["link_check_copy_kernel"] = {"known_bytes_each_way": known, "write_bytes": copy_w,
+                                     "read_bytes": copy_r}
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def summarize_counters(fetch_dir, write_dir):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the transfer kernels, scaled by
     what the same counters read for the plain copy kernel of known size."""
@@ -452,24 +539,27 @@ def summarize_counters(fetch_dir, write_dir):
         for r in _counter_rows(d):
             if r.get("Counter_Name") != cname:
                 continue
-            k = r["Kernel_Name"]
-            key = ("copy" if "elementwise_kernel" in k and "copy" in k else
-                   "xfer_rows_d2h" if "xfer_rows<true, false>" in k else
-                   "xfer_rows_h2d" if "xfer_rows<false, false>" in k else None)
+            key = _kernel_key(r["Kernel_Name"])
             if key is None:
                 continue
             per.setdefault((key, cname), []).append(float(r["Counter_Value"]) * 1024.0)
     fetch_scale = known / statistics.median(per[("copy", "FETCH_SIZE")])
     write_scale = known / statistics.median(per[("copy", "WRITE_SIZE")])
     src_hash = kernel_source_hash()
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:            # keep the host-link section of an earlier summary
+        with open(path) as fh:
+            out = json.load(fh)
+    except (OSError, ValueError):
+        out = {}
     for key in ("xfer_rows_d2h", "xfer_rows_h2d"):
         f = statistics.median(per[(key, "FETCH_SIZE")]) * fetch_scale
         w = statistics.median(per[(key, "WRITE_SIZE")]) * write_scale
-        out[key] = {"fetch_bytes_per_launch": round(f), "write_bytes_per_launch": round(w),
-                    "hbm_bytes_per_launch": round(f + w), "kernel_source_hash": src_hash}
+        out.setdefault(key, {}).update(
+            {"fetch_bytes_per_launch": round(f), "write_bytes_per_launch": round(w),
+             "hbm_bytes_per_launch": round(f + w), "kernel_source_hash": src_hash})
     out["scale"] = {"fetch": fetch_scale, "write": write_scale,
                     "copy_kernel_bytes_each_way": known}
-    path = os.path.join(ROOT, "profiles", "counters.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
