@@ -915,6 +915,7 @@ def leg_streamed(torch, kvt, workloads, args):
     s_load, s_comp = kvt.Stream(), torch.cuda.Stream()   # loads on a queue of their own
     layer_bytes = n * C * R
     acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    torch.cuda.synchronize()   # the fill above ran on the default stream; acc is used on s_comp
 
     def consume(l, k):
         for _ in range(k):

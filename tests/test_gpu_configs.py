@@ -242,9 +242,11 @@ def test_streamed_per_layer_events(torch):
             for b in bufs:
                 b.view(-1, g.R)[t_idx] = 0
             torch.cuda.synchronize()
-            sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
             pool.load(dev_idx, host_idx, 0, g.L, s_load)
             with torch.cuda.stream(s_comp):
+                # made on the consumer's stream: a tensor filled on the default
+                # stream and written here would race with that fill
+                sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
                 for l in range(g.L):
                     pool.load_layer(l, s_comp)
                     for c in range(g.C):
@@ -302,4 +304,57 @@ def test_mla32k_shared_host_pool(torch):
     reader.close()
     writer.close()
     del src, dst
+    release(torch)
+
+
+# ---- kv_load_layer gating at full size, on every path and kind of load stream --------
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("stream_kind", ("torch", "library"))
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+def test_load_layer_gates_consumer_at_full_size(torch, path, stream_kind):
+    """The MLA prefix (16384 and 32768 tokens, one landed event per layer) loads
+    on a torch stream or on a library stream (kv_stream_create); a consumer on
+    another stream reads each layer right after kv_load_layer(l) and must see the
+    loaded bytes in every layer, on the kernel, copy-engine and staged paths (the
+    staged path records its landed events on its own auxiliary stream). A wait
+    that does not hold shows as a layer read before it landed."""
+    shape = workloads.mla32k()
+    L, R, S_dev = shape.layers, shape.row_bytes, shape.device_slots
+    bufs = make_bufs(torch, shape, 3, S_dev)
+    g = Geometry(L, 1, R, S_dev, shape.host_slots, shape.page_size, oracle.LAYER_FIRST)
+    pool = kvt.KvPool(kvt.geometry(*g.args()), bufs)
+    lib_stream = kvt.Stream() if stream_kind == "library" else None
+    s = lib_stream.torch if lib_stream else torch.cuda.Stream()
+    c = torch.cuda.Stream()
+    for n in (16384, 32768):
+        src = np.arange(n, dtype=np.int64)
+        dst = src + (S_dev - n)
+        host = np.arange(n, dtype=np.int64)
+        pool.set_path(kvt.PATH_KERNEL)
+        pool.backup(src, host, 0, L, s)
+        s.synchronize()
+        pool.set_path(path)
+        want = torch.stack([bufs[l].view(S_dev, R)[:n].to(torch.int64).sum() for l in range(L)])
+        for rep in range(3):
+            for l in range(L):
+                bufs[l].view(S_dev, R)[S_dev - n:].zero_()
+            torch.cuda.synchronize()
+            print("gating path=%d stream=%s n=%d rep=%d" % (path, stream_kind, n, rep), flush=True)
+            pool.load(dst, host, 0, L, s)
+            with torch.cuda.stream(c):
+                sums = torch.zeros(L, dtype=torch.int64, device="cuda:0")
+                for l in range(L):
+                    pool.load_layer(l, c)
+                    sums[l] = bufs[l].view(S_dev, R)[S_dev - n:].to(torch.int64).sum()
+            c.synchronize()
+            s.synchronize()
+            early = [l for l in range(L) if int(sums[l]) != int(want[l])]
+            assert not early, ("layers read before they landed", early[:10], len(early))
+            for l in sample_layers(L):
+                assert torch.equal(bufs[l].view(S_dev, R)[S_dev - n:], bufs[l].view(S_dev, R)[:n])
+    pool.close()
+    if lib_stream:
+        lib_stream.close()
+    del bufs
     release(torch)

@@ -324,11 +324,13 @@ def test_load_layer_groups_gate_consumer(torch, path):
     mirrors = [np.zeros(g.S_dev * g.R, np.uint8) for _ in range(g.L * g.C)]
     assert oracle.load(g, mirrors, pool.host_array(), d, h) == 0
     s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
-    sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
     t_idx = torch.from_numpy(d).cuda()
+    torch.cuda.synchronize()
     before = pool.stats().kernel_launches[1]
     pool.load(d, h, 0, g.L, s_load)
     with torch.cuda.stream(s_comp):
+        # made on the consumer's stream, so no other stream's fill can land on it late
+        sums = torch.zeros(g.L * g.C, dtype=torch.int64, device="cuda:0")
         for l in range(g.L):
             pool.load_layer(l, s_comp)
             for cc in range(g.C):
