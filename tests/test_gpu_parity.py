@@ -6,13 +6,15 @@ size, row sizes that are not a power of two), every host layout, every path,
 both directions, partial layer ranges, and the edge cases (empty requests,
 empty layer ranges, one-token requests, 16-byte rows, rejected requests).
 """
+import itertools
+
 import numpy as np
 import pytest
 
 import hierarchical_kv_cache_backup_amd as kvt
 from hierarchical_kv_cache_backup_amd import workloads
 import oracle
-from oracle import Geometry, LAYOUTS
+from oracle import Geometry, LAYOUTS, np_ref
 
 from gpu_util import (PATHS, SENTINEL, device_buffers, make_pool, mirrors,
                       run_backup_and_compare, run_load_and_compare, kv_geom, torch_mod)
@@ -748,3 +750,54 @@ def test_index_pairs_copied_or_read_in_place(torch, stream, zero_copy, path):
             pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
             run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
         pool.close()
+
+
+# ---- brute force: every permutation of tiny requests, oracle == NumPy == GPU ---------
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("path", PATHS)
+def test_brute_force_tiny_pools_on_gpu(torch, stream, layout, path):
+    """Pools of L, C in {1, 2}, R in {16, 32} bytes, page size 1, 2 or 4 over 4 host
+    slots (5 device slots): every ordered choice of 1-4 host slots is backed up from
+    seeded device slots and loaded back into other seeded device slots. The C
+    oracle and the NumPy cross-derivation agree on each result, and the library
+    matches them byte for byte, the rest of both pools included."""
+    S_host, S_dev = 4, 5
+    cases = 0
+    for L, C, R, ps in itertools.product((1, 2), (1, 2), (16, 32), (1, 2, 4)):
+        g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+        rng = np.random.default_rng([8100, L, C, R, ps, layout, path])
+        bufs = device_buffers(g, seed=int(rng.integers(1 << 30)))
+        pool = make_pool(g, bufs, path)
+        print("brute layout=%d path=%d L=%d C=%d R=%d ps=%d" % (layout, path, L, C, R, ps),
+              flush=True)
+        for n in (1, 2, 3, 4):
+            for hs in itertools.permutations(range(S_host), n):
+                h = np.asarray(hs, dtype=np.int64)
+                d = rng.choice(S_dev, n, replace=False).astype(np.int64)
+                # backup: oracle and NumPy from the same mirrors, then the library
+                dev_m = mirrors(bufs)
+                want = pool.host_array().copy()
+                want_np = want.copy()
+                assert oracle.backup(g, dev_m, want, d, h) == 0
+                np_ref.backup(np.stack(dev_m).reshape(L, C, S_dev, R), want_np, layout, L, C,
+                              S_host, ps, R, d, h)
+                assert np.array_equal(want, want_np)
+                pool.backup(d, h, 0, L, stream)
+                stream.synchronize()
+                assert np.array_equal(pool.host_array(), want), (L, C, R, ps, hs)
+                # load into another seeded choice of device slots
+                d2 = rng.choice(S_dev, n, replace=False).astype(np.int64)
+                host = pool.host_array().copy()
+                dev_m = mirrors(bufs)
+                dev_np = np.stack(dev_m).reshape(L, C, S_dev, R).copy()
+                assert oracle.load(g, dev_m, host, d2, h) == 0
+                np_ref.load(dev_np, host, layout, L, C, S_host, ps, R, d2, h)
+                pool.load(d2, h, 0, L, stream)
+                stream.synchronize()
+                for k, b in enumerate(bufs):
+                    assert np.array_equal(dev_m[k], dev_np.reshape(L * C, -1)[k])
+                    assert np.array_equal(b.cpu().numpy(), dev_m[k]), (L, C, R, ps, hs, k)
+                cases += 1
+        pool.close()
+    assert cases == 24 * 64
