@@ -805,17 +805,25 @@ def leg_bidirectional(torch, kvt, workloads, args, link_peak, duplex_fresh):
     wall_min = max(hb / link_peak["h2d"], wb / link_peak["d2h"], (hb + wb) / peak) / 1e9
     bound = (hb + wb) / wall_min / 1e9
     results = {}
-    variants = (("layer_first", 0, "kernel", kvt.PATH_KERNEL),
-                ("layer_first", 0, "auto", kvt.PATH_AUTO),
-                ("page_first_direct", 2, "kernel", kvt.PATH_KERNEL),
-                ("page_first_direct", 2, "staged", kvt.PATH_STAGED),
-                ("page_first_direct", 2, "auto", kvt.PATH_AUTO))
-    for lname, lay, pname, p in variants:
+    # "full_grids": the duplex grid caps switched off (every kernel launch one
+    # workgroup per block of work), to show what the caps buy
+    variants = (("layer_first", 0, "kernel", kvt.PATH_KERNEL, True),
+                ("layer_first", 0, "kernel_full_grids", kvt.PATH_KERNEL, False),
+                ("layer_first", 0, "auto", kvt.PATH_AUTO, True),
+                ("page_first_direct", 2, "kernel", kvt.PATH_KERNEL, True),
+                ("page_first_direct", 2, "staged", kvt.PATH_STAGED, True),
+                ("page_first_direct", 2, "auto", kvt.PATH_AUTO, True),
+                ("page_first_direct", 2, "auto_full_grids", kvt.PATH_AUTO, False))
+    for lname, lay, pname, p, caps in variants:
         pool = kvt.KvPool(kvt.geometry(L, C, R, S, plan["host_slots"], ps, lay), bufs,
                           flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
         pool.set_path(kvt.PATH_KERNEL)
         pool.backup(h_dev, h_host, 0, L, s_back)      # L2 holds the hits
         s_back.synchronize()
+        if not caps:
+            cal = pool.calibration()
+            cal.duplex_kernel_max_workgroups[:] = [0, 0]
+            pool.set_calibration(cal)
         pool.set_path(p)
         load = lambda: pool.load(h_dev, h_host, 0, L, s_load)
         back = lambda: pool.backup(w_dev, w_host, 0, L, s_back)
@@ -868,8 +876,12 @@ def leg_bidirectional(torch, kvt, workloads, args, link_peak, duplex_fresh):
         wall = statistics.median(walls)
         agg = (hb + wb) / wall / 1e9
         key = "%s/%s" % (lname, pname)
+        st = pool.stats()
+        kpaths = (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS)
+        grid = lambda d: int(st.last_workgroups[d]) if pool.last_path(d) in kpaths else None
         results[key] = {"paths_used": {"h2d": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
                                        "d2h": kvt.PATH_NAMES[pool.last_path(kvt.BACKUP)]},
+                        "kernel_workgroups": {"h2d": grid(kvt.LOAD), "d2h": grid(kvt.BACKUP)},
                         "h2d_alone_gbps": round(hb / t_load / 1e9, 3),
                         "d2h_alone_gbps": round(wb / t_back / 1e9, 3),
                         "h2d_concurrent_gbps": round(statistics.median(h_rates), 3),

@@ -58,13 +58,15 @@ class kv_calib_t(ctypes.Structure):
                 ("staged_gather_gbps", ctypes.c_double),
                 ("kernel_group_us", ctypes.c_double * 2),
                 ("staged_min_gain", ctypes.c_double),
-                ("index_zero_copy_max_bytes", ctypes.c_double * 2)]
+                ("index_zero_copy_max_bytes", ctypes.c_double * 2),
+                ("duplex_kernel_max_workgroups", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64 * 2), ("bytes", ctypes.c_int64 * 2),
                 ("kernel_launches", ctypes.c_int64 * 2), ("dma_copies", ctypes.c_int64 * 2),
-                ("submit_us", ctypes.c_double * 2), ("blocked_us", ctypes.c_double * 2)]
+                ("submit_us", ctypes.c_double * 2), ("blocked_us", ctypes.c_double * 2),
+                ("last_workgroups", ctypes.c_int64 * 2)]
 
 
 # Every symbol include/*.h declare, with its ctypes signature.

@@ -116,7 +116,7 @@ struct DirState {
   uint32_t next_half = 0;  // halves alternate across chunks, groups and calls
   int last_half = -1;      // half of the latest chunk
   std::atomic<int32_t> last_path{-1};
-  int64_t calls = 0, bytes = 0, launches = 0, dma = 0;
+  int64_t calls = 0, bytes = 0, launches = 0, dma = 0, last_workgroups = 0;
   double submit_us = 0, blocked_us = 0;
 };
 
@@ -199,12 +199,23 @@ void default_calibration(kv_calib_t *c) {
   // Concurrent 1 GiB H2D + D2H (GB/s, H2D / D2H): copy engines both ways
   // 56.4 / 48.5; H2D kernel beside D2H copy engines 56.4 / 31.0; H2D copy
   // engines beside a D2H kernel 42.3 / 51.3; kernels both ways 37.8 / 38.1.
-  // On the mixed batch an H2D kernel beside a staged D2H kept 56.2. A load's
-  // kernel keeps the link whatever the write-back runs on, unless the
-  // write-back is a kernel too, which this charge steers it away from; a
-  // backup's kernel loses ~0.4 of its rate beside a busy load.
+  // A load's kernel keeps the link whatever the write-back runs on, unless the
+  // write-back is a full-grid kernel too. With the duplex caps below (load 128
+  // workgroups, backup 24) the mixed batch measured H2D 56.5 beside a D2H
+  // kernel of 33 GB/s (52 alone): the backup's kernel runs at ~0.6 of its
+  // uncapped rate, charged here as ~0.4 more time.
   c->duplex_kernel_penalty[0] = 0.4;
   c->duplex_kernel_penalty[1] = 0.0;
+  // Full-grid transfer kernels occupy every compute unit with workgroups that
+  // wait microseconds on the host link; kernels of the other direction (and the
+  // staged path's gathers) that land beside them stall. On the mixed batch
+  // (load 51.2 GB || write-back 11.6 GB) a load kernel of 128 workgroups and a
+  // write-back kernel of 16-24 kept the load at 56.5 GB/s with the write-back
+  // at 22-34 (98.6% of the duplex bound, against 86% with full grids); at 48
+  // write-back workgroups the load fell to 50, at 8 the write-back became the
+  // longer of the two.
+  c->duplex_kernel_max_workgroups[0] = 24;
+  c->duplex_kernel_max_workgroups[1] = 128;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
   c->staged_gather_gbps = 2000.0;
   // Reading the index pairs from mapped pinned memory instead of copying them
@@ -487,12 +498,16 @@ static bool other_direction_busy(kv_pool *p, int dir, hipStream_t s) {
   return hipEventQuery(o.done) == hipErrorNotReady;
 }
 
-// Workgroup cap of a transfer kernel launch (0 = none).
-static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap) {
+// Workgroup cap of a transfer kernel launch (0 = none): the smallest of the
+// caps that apply (the direction's own, the overlap cap for a load flagged
+// KV_F_LOAD_OVERLAP, the duplex cap while the other direction is busy).
+static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool duplex) {
   uint32_t cap = (uint32_t)c.kernel_max_workgroups[dir];
-  if (overlap && c.overlap_kernel_max_workgroups > 0 &&
-      (cap == 0 || cap > (uint32_t)c.overlap_kernel_max_workgroups))
-    cap = (uint32_t)c.overlap_kernel_max_workgroups;
+  auto tighten = [&cap](double limit) {
+    if (limit > 0 && (cap == 0 || cap > (uint32_t)limit)) cap = (uint32_t)limit;
+  };
+  if (overlap) tighten(c.overlap_kernel_max_workgroups);
+  if (duplex) tighten(c.duplex_kernel_max_workgroups[dir]);
   return cap;
 }
 
@@ -675,7 +690,8 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
   const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
-  const uint32_t cap = kernel_cap(c, dir, overlap);
+  const uint32_t cap = kernel_cap(c, dir, overlap, duplex);          // kernel paths
+  const uint32_t stage_cap = kernel_cap(c, dir, overlap, false);     // staged device passes
 
   // ---- path selection
   int32_t path = p->path.load();
@@ -791,18 +807,20 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       b.lc0 = (uint32_t)(la * g.C);
       b.nlc = (uint32_t)((lb - la) * g.C);
       if (path == KV_PATH_STAGED) {
-        e = staged_unit(p, d, dir, b, host_idx, la, lb, cap, s);
+        e = staged_unit(p, d, dir, b, host_idx, la, lb, stage_cap, s);
         continue;  // staged_unit records the group's landed event itself
       } else if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
         TileArgs t{};
         b.nblocks = plan_tiles(b, g.layout, &t);
         d.launches++;
-        e = launch_tiles_lds(b, t, grid_for(b.nblocks, cap), dir == 0, s);
+        d.last_workgroups = grid_for(b.nblocks, cap);
+        e = launch_tiles_lds(b, t, (uint32_t)d.last_workgroups, dir == 0, s);
       } else {
         const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
         d.launches++;
-        e = launch_rows(b, grid_for(blocks, cap), dir == 0, false, s);
+        d.last_workgroups = grid_for(blocks, cap);
+        e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, false, s);
       }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
     }
@@ -1133,6 +1151,10 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
     return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
   if (!(c->index_zero_copy_max_bytes[0] >= 0) || !(c->index_zero_copy_max_bytes[1] >= 0))
     return fail(KV_EINVAL, "index_zero_copy_max_bytes must be >= 0");
+  for (int d = 0; d < 2; d++)
+    if (!(c->duplex_kernel_max_workgroups[d] >= 0) ||
+        c->duplex_kernel_max_workgroups[d] > 4294967295.0)
+      return fail(KV_EINVAL, "duplex_kernel_max_workgroups must be in [0, 2^32)");
   if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
       !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
@@ -1160,6 +1182,7 @@ int kv_get_stats(const kv_pool_t *p, kv_stats_t *out) {
     out->dma_copies[d] = s.dma;
     out->submit_us[d] = s.submit_us;
     out->blocked_us[d] = s.blocked_us;
+    out->last_workgroups[d] = s.last_workgroups;
   }
   return KV_OK;
 }

@@ -180,6 +180,14 @@ typedef struct {
  * fractions of the transfer time by which a concurrent HBM-bound kernel is
  * slowed, measured per path; and the kernel path launches at most
  * overlap_kernel_max_workgroups workgroups.
+ * duplex_kernel_max_workgroups: cap on the workgroups of a kernel-path
+ * transfer while the other direction is busy (KV_F_DUPLEX, or a transfer of
+ * the other direction in flight at submission on another stream); [0] for a
+ * backup, [1] for a load, 0 = no cap. A load's kernel holds the link with 128
+ * workgroups; a write-back kernel with a small grid leaves the load most of the
+ * link and, together with the load's cap, leaves compute units free for the
+ * other direction's kernels. The staged path's device-side passes are not
+ * capped by it.
  * The staged path is modelled as extents * dma_copy_us + kernel_launch_us +
  * (chunks - 1) * kernel_group_us + bytes / dma_gbps + min(bytes,
  * staged_chunk_bytes) / staged_gather_gbps: its device-side passes overlap the
@@ -206,6 +214,8 @@ typedef struct {
                                    pairs (16 bytes per position) fit in this many bytes
                                    has them read by the kernels from the mapped pinned
                                    staging buffer, skipping the copy to the device */
+  double duplex_kernel_max_workgroups[2]; /* kernel-path grid cap while the other
+                                   direction is busy ([0] backup, [1] load; 0 = none) */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */
@@ -381,6 +391,8 @@ typedef struct {
   double submit_us[2];      /* host wall time spent inside the calls, minus blocked_us */
   double blocked_us[2];     /* host time spent waiting for an index staging buffer
                                (only when 16 calls of one direction are in flight) */
+  int64_t last_workgroups[2]; /* grid of the latest kernel-path launch (direct or LDS
+                               kernel), after any cap; 0 before the first */
 } kv_stats_t;
 
 int kv_get_stats(const kv_pool_t *pool, kv_stats_t *out);

@@ -281,6 +281,56 @@ def test_capped_grid_matches_oracle(torch, stream, layout):
         pool.close()
 
 
+def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
+    """The kernel paths launch at most duplex_kernel_max_workgroups[dir]
+    workgroups on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load),
+    at most overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP,
+    and the smallest cap that applies; without a cap a launch has one workgroup
+    per block of work. The bytes match the oracle under every cap."""
+    g = Geometry(4, 2, 2048, 4096, 4096, 64, 0)
+    bufs = device_buffers(g, seed=15)
+    rng = np.random.default_rng(15)
+    d = rng.permutation(g.S_dev).astype(np.int64)
+    h = np.arange(g.S_host, dtype=np.int64)
+
+    def grids(pool, path):
+        pool.set_path(path)
+        run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        return tuple(pool.stats().last_workgroups)
+
+    plain = make_pool(g, bufs)
+    c = plain.calibration()
+    assert list(c.duplex_kernel_max_workgroups) == [24.0, 128.0]
+    assert tuple(plain.stats().last_workgroups) == (0, 0)
+    free = grids(plain, kvt.PATH_KERNEL)
+    assert free[0] > 1000 and free[1] > 1000, free     # one workgroup per 16 KiB block
+    c.duplex_kernel_max_workgroups[0] = -1
+    with pytest.raises(kvt.KvError):
+        plain.set_calibration(c)
+    plain.close()
+
+    duplex = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
+    assert grids(duplex, kvt.PATH_KERNEL) == (24, 128)
+    lds = grids(duplex, kvt.PATH_KERNEL_LDS)
+    assert 0 < lds[0] <= 24 and 0 < lds[1] <= 128, lds
+    c = duplex.calibration()
+    c.kernel_max_workgroups[:] = [0, 64]             # the tighter cap wins
+    duplex.set_calibration(c)
+    assert grids(duplex, kvt.PATH_KERNEL) == (24, 64)
+    c.kernel_max_workgroups[:] = [0, 0]
+    c.duplex_kernel_max_workgroups[:] = [0, 0]       # duplex caps off
+    duplex.set_calibration(c)
+    assert grids(duplex, kvt.PATH_KERNEL) == free
+    duplex.close()
+
+    overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
+    got = grids(overlap, kvt.PATH_KERNEL)
+    assert got == (free[0], 128), got               # the overlap cap is a load's only
+    overlap.close()
+
+
 def test_overlap_flag_steers_selector(torch, stream):
     g = Geometry(2, 1, 64, 32, 32, 8, 0)
     bufs = device_buffers(g, seed=12)
