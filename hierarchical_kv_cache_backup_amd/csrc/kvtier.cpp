@@ -768,6 +768,20 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     Staging *st = nullptr;
     rc = acquire_staging(d, n, &st, &blocked);
     if (rc) return rc;
+    // When a step fails after others of this call were enqueued, the index slot
+    // (and, on the staged path, the staging halves) stay in use until the
+    // stream passes that work: record that point before reporting the error,
+    // so that a later call does not overwrite them under work in flight.
+    auto settle = [&](int code) {
+      if (path == KV_PATH_STAGED && d.aux && hipEventRecord(d.ev_start, d.aux) == hipSuccess)
+        (void)hipStreamWaitEvent(s, d.ev_start, 0);  // s after the call's work on aux
+      if (hipEventRecord(st->ev, s) == hipSuccess) st->pending = true;
+      if (path == KV_PATH_STAGED && hipEventRecord(d.stage_ev, s) == hipSuccess) {
+        d.stage_pending = true;
+        d.stage_stream = s;
+      }
+      return code;
+    };
     int64_t *tok = st->pinned;
     for (int64_t i = 0; i < n; i++) {
       tok[2 * i] = dev_idx[i];
@@ -780,7 +794,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     const bool index_zero_copy = (double)n * 16 <= c.index_zero_copy_max_bytes[dir];
     if (!index_zero_copy) {
       e = hipMemcpyAsync(st->dev, st->pinned, (size_t)n * 16, hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail(e, "staging indices");
+      if (e != hipSuccess) return settle(hip_fail(e, "staging indices"));
     }
 
     XferArgs a{};
@@ -794,11 +808,11 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       if (!d.aux) {  // the device's auxiliary streams, made on the first staged call
         DeviceStreams *ds = nullptr;
         e = device_streams(p->device, &ds);
-        if (e != hipSuccess) return hip_fail(e, "creating the staged path's streams");
+        if (e != hipSuccess) return settle(hip_fail(e, "creating the staged path's streams"));
         d.aux = ds->aux[dir];
       }
       rc = stage_begin(d, g, n * (int64_t)std::min<int32_t>(group, l1 - l0) * g.C * g.R, c, s);
-      if (rc) return rc;
+      if (rc) return settle(rc);
       if (!have_host_runs) host_runs(g, host_idx, n, &d.host_run_start);
     }
     for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
@@ -826,15 +840,15 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     }
     if (e == hipSuccess && path == KV_PATH_STAGED && dir == 1 && d.last_half >= 0)
       e = hipStreamWaitEvent(s, d.ev_free[d.last_half], 0);  // s ends after aux's last scatter
-    if (e != hipSuccess) return hip_fail(e, "enqueueing the transfer");
+    if (e != hipSuccess) return settle(hip_fail(e, "enqueueing the transfer"));
     if (path == KV_PATH_STAGED) {
       e = hipEventRecord(d.stage_ev, s);
-      if (e != hipSuccess) return hip_fail(e, "recording the staging-buffer event");
+      if (e != hipSuccess) return settle(hip_fail(e, "recording the staging-buffer event"));
       d.stage_pending = true;
       d.stage_stream = s;
     }
     e = hipEventRecord(st->ev, s);
-    if (e != hipSuccess) return hip_fail(e, "recording the staging event");
+    if (e != hipSuccess) return settle(hip_fail(e, "recording the staging event"));
     st->pending = true;
   }
   e = hipEventRecord(d.done, s);

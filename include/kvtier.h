@@ -347,7 +347,9 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
  * load_split_min_bytes), so it may also cover the other layers of that group;
  * if a later load re-recorded that group's event, the wait covers the later
  * load too (never less than asked). A layer no kv_load has covered yet: KV_OK,
- * no wait. Errors: KV_EINVAL (layer out of [0,L)), KV_EHIP. */
+ * no wait. After a kv_load that returned an error, which of its layers were
+ * enqueued is unspecified, and so is this wait for them. Errors: KV_EINVAL
+ * (layer out of [0,L)), KV_EHIP. */
 int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
 
 /* ---- streams -------------------------------------------------------------- */
