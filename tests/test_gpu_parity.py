@@ -331,6 +331,75 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     overlap.close()
 
 
+def _hold_stream(torch, st, gate):
+    """Enqueues on `st` a host function that returns once `gate` is set (or after
+    10 s): work queued behind it stays in flight until then."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")     # the runtime torch has loaded
+    fn_t = ctypes.CFUNCTYPE(None, ctypes.c_void_p)
+    cb = fn_t(lambda _: gate.wait(10.0))
+    hip.hipLaunchHostFunc.argtypes = [ctypes.c_void_p, fn_t, ctypes.c_void_p]
+    assert hip.hipLaunchHostFunc(ctypes.c_void_p(st.cuda_stream), cb, None) == 0
+    return cb                                  # keep the callback alive until the stream passes it
+
+
+def test_duplex_caps_follow_the_other_direction(torch):
+    """Without KV_F_DUPLEX the duplex grid caps apply while the other direction
+    has a transfer in flight on another stream at submission: a backup issued
+    while a load is held in flight gets 24 workgroups and a load issued while a
+    backup is held gets 128; issued alone, each gets the full grid. Both
+    directions' bytes match the oracle."""
+    import threading
+    g = Geometry(4, 2, 2048, 8192, 8192, 64, 0)
+    bufs = device_buffers(g, seed=16)
+    pool = make_pool(g, bufs, kvt.PATH_KERNEL, host_fill=None)
+    rng = np.random.default_rng(16)
+    pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+    half = g.S_dev // 2
+    d_load, h_load = np.arange(half, dtype=np.int64), rng.permutation(half).astype(np.int64)
+    d_back = np.arange(half, g.S_dev, dtype=np.int64)
+    h_back = (half + rng.permutation(half)).astype(np.int64)
+    s_load, s_back = torch.cuda.Stream(), torch.cuda.Stream()
+    full_backup = g.S_dev // 2 * g.L * g.C * g.R // (16 * 1024)
+    full_load = g.S_dev // 2 * g.C * g.R // (16 * 1024)      # one layer per launch
+
+    for first in ("load", "backup"):
+        print("duplex caps, %s held in flight" % first, flush=True)
+        dev_m = mirrors(bufs)
+        host_m = pool.host_array().copy()
+        assert oracle.backup(g, dev_m, host_m, d_back, h_back) == 0   # disjoint rows:
+        assert oracle.load(g, dev_m, host_m, d_load, h_load) == 0     # order is irrelevant
+        gate = threading.Event()
+        torch.cuda.synchronize()
+        if first == "load":
+            cb = _hold_stream(torch, s_load, gate)
+            pool.load(d_load, h_load, 0, g.L, s_load)
+            pool.backup(d_back, h_back, 0, g.L, s_back)
+            grids = tuple(pool.stats().last_workgroups)
+            assert grids == (24, full_load), grids
+        else:
+            cb = _hold_stream(torch, s_back, gate)
+            pool.backup(d_back, h_back, 0, g.L, s_back)
+            pool.load(d_load, h_load, 0, g.L, s_load)
+            grids = tuple(pool.stats().last_workgroups)
+            assert grids == (full_backup, 128), grids
+        gate.set()
+        s_load.synchronize()
+        s_back.synchronize()
+        torch.cuda.synchronize()
+        del cb
+        assert np.array_equal(pool.host_array(), host_m)
+        for k, b in enumerate(bufs):
+            assert np.array_equal(b.cpu().numpy(), dev_m[k]), k
+    # alone again: full grids
+    pool.backup(d_back, h_back, 0, g.L, s_back)
+    s_back.synchronize()
+    pool.load(d_load, h_load, 0, g.L, s_load)
+    s_load.synchronize()
+    assert tuple(pool.stats().last_workgroups) == (full_backup, full_load)
+    pool.close()
+
+
 def test_overlap_flag_steers_selector(torch, stream):
     g = Geometry(2, 1, 64, 32, 32, 8, 0)
     bufs = device_buffers(g, seed=12)
