@@ -400,6 +400,39 @@ def test_duplex_caps_follow_the_other_direction(torch):
     pool.close()
 
 
+@pytest.mark.parametrize("path", PATHS)
+def test_null_stream_round_trip(torch, path):
+    """A NULL stream means the null stream: backup and load issued there (no
+    stream argument) match the oracle on every path, and kv_load_layer on the
+    null stream orders a consumer there after the layer."""
+    L, C, R, S_dev, S_host, ps = GEOMS[0]
+    for layout in LAYOUTS:
+        g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+        bufs = device_buffers(g, seed=17 + layout)
+        pool = make_pool(g, bufs, path)
+        rng = np.random.default_rng(17 + layout)
+        d, h = _request(rng, g, "random")
+        print("null stream path=%d layout=%d" % (path, layout), flush=True)
+        want = pool.host_array().copy()
+        assert oracle.backup(g, mirrors(bufs), want, d, h) == 0
+        torch.cuda.synchronize()
+        pool.backup(d, h, 0, L)
+        torch.cuda.synchronize()
+        assert np.array_equal(pool.host_array(), want)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        dev_m = mirrors(bufs)
+        assert oracle.load(g, dev_m, pool.host_array().copy(), d, h) == 0
+        pool.load(d, h, 0, L)
+        pool.load_layer(L - 1)
+        t_idx = torch.from_numpy(d).cuda()
+        last = bufs[(L - 1) * C].view(-1, g.R).index_select(0, t_idx).cpu().numpy()
+        assert np.array_equal(last, dev_m[(L - 1) * C].reshape(-1, g.R)[d])
+        torch.cuda.synchronize()
+        for k, b in enumerate(bufs):
+            assert np.array_equal(b.cpu().numpy(), dev_m[k]), k
+        pool.close()
+
+
 def test_overlap_flag_steers_selector(torch, stream):
     g = Geometry(2, 1, 64, 32, 32, 8, 0)
     bufs = device_buffers(g, seed=12)
