@@ -236,3 +236,19 @@ def test_host_page_allocator_under_sanitizers(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "0 failures" in res.stdout
+
+
+def test_allocator_and_ghost_list_threads_under_tsan(tmp_path):
+    """Four threads on one page allocator and on one Ghost List at once, built
+    with ThreadSanitizer: no data race, no page handed to two holders, every
+    page free at the end, the Ghost List within capacity."""
+    exe = tmp_path / "threads_check"
+    subprocess.check_call(["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread",
+                           "-I" + os.path.join(ROOT, "include"),
+                           os.path.join(HERE, "host", "threads_check.cpp"),
+                           os.path.join(CSRC, "slots.cpp"), os.path.join(CSRC, "ghost.cpp"),
+                           "-o", str(exe), "-lpthread"])
+    res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "0 failures" in res.stdout
+    assert "ThreadSanitizer" not in res.stderr, res.stderr
