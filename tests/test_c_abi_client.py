@@ -37,3 +37,14 @@ def test_c_client_round_trip(tmp_path):
     res = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
     assert "0 failures" in res.stdout, res.stdout
+
+
+def test_headers_are_c11(tmp_path):
+    """Every header of the C ABI compiles in a C11 translation unit, with the
+    compiler's warnings as errors."""
+    src = tmp_path / "headers.c"
+    src.write_text('#include "kvtier.h"\n#include "kvslots.h"\n#include "kvghost.h"\n'
+                   "int main(void) { return (int)sizeof(kv_calib_t) == 0; }\n")
+    subprocess.check_call(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-pedantic",
+                           "-I" + os.path.join(ROOT, "include"), str(src), "-o",
+                           str(tmp_path / "headers")])
