@@ -223,7 +223,17 @@ def test_mixed_bidirectional(torch):
 # ---- streamed: per-layer H2D overlapped with a consumer on another stream ---------------
 
 @pytest.mark.timeout(300)
-def test_streamed_per_layer_events(torch):
+@pytest.mark.parametrize("variant", ("kernel", "dma", "staged", "auto_overlap"))
+def test_streamed_per_layer_events(torch, variant):
+    """The 61-layer fp8 prefix (256 MiB per layer) loads while a consumer on
+    another stream sums each layer right after kv_load_layer(l), on the kernel,
+    copy-engine and staged paths and on AUTO with KV_F_LOAD_OVERLAP; every
+    layer's sum and sampled layers' bytes match."""
+    path, flags = {"kernel": (kvt.PATH_KERNEL, kvt.F_CHECK_UNIQUE),
+                   "dma": (kvt.PATH_DMA, kvt.F_CHECK_UNIQUE),
+                   "staged": (kvt.PATH_STAGED, kvt.F_CHECK_UNIQUE),
+                   "auto_overlap": (kvt.PATH_AUTO,
+                                    kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)}[variant]
     shape = workloads.streamed()
     n = shape.extra["tokens"]
     bufs = make_bufs(torch, shape, 5, shape.device_slots)
@@ -232,13 +242,14 @@ def test_streamed_per_layer_events(torch):
     for layout in shape.layouts:
         g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
                      shape.host_slots, shape.page_size, layout)
-        print("streamed layout=%d" % layout, flush=True)
-        with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+        print("streamed %s layout=%d" % (variant, layout), flush=True)
+        with kvt.KvPool(kvt.geometry(*g.args()), bufs, flags=flags) as pool:
             pool.set_path(kvt.PATH_KERNEL)
             s_load, s_comp = torch.cuda.Stream(), torch.cuda.Stream()
             # L2 content: written back from the device pool, then the device rows are cleared
             pool.backup(dev_idx, host_idx, 0, g.L, s_load)
             s_load.synchronize()
+            pool.set_path(path)
             for b in bufs:
                 b.view(-1, g.R)[t_idx] = 0
             torch.cuda.synchronize()
