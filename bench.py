@@ -1026,6 +1026,50 @@ def leg_streamed(torch, kvt, workloads, args):
                           "overlap_efficiency": round(eta, 3)}
         log("streamed %s %s" % (pname, json.dumps(results[pname])))
         pool.close()
+
+    # Write-back beside compute: layers 1..60 written back while the consumer
+    # repeats its pass over layer 0 (60 passes); the consumer's time against its
+    # time alone, per path and write-back grid.
+    writeback = {}
+    geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
+    pool = kvt.KvPool(geom, bufs)
+
+    def consume_timed(reps):
+        with torch.cuda.stream(s_comp):
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s_comp)
+            consume(0, reps)
+            e1.record(s_comp)
+            e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    t_alone = statistics.median([consume_timed(60) for _ in range(3)])
+    wb_bytes = n * (L - 1) * C * R
+    for wname, p, cap in (("kernel_default_grid", kvt.PATH_KERNEL, 24),
+                          ("kernel_full_grid", kvt.PATH_KERNEL, 0),
+                          ("dma", kvt.PATH_DMA, 24), ("staged", kvt.PATH_STAGED, 24)):
+        pool.set_path(p)
+        cal = pool.calibration()
+        cal.kernel_max_workgroups[0] = cap
+        pool.set_calibration(cal)
+        slow, rates = [], []
+        for rep in range(3):
+            torch.cuda.synchronize()
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s_load.torch)
+            pool.backup(dev_idx, host_idx, 1, L, s_load)
+            e1.record(s_load.torch)
+            slow.append(consume_timed(60) / t_alone)
+            e1.synchronize()
+            rates.append(wb_bytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
+        st = pool.stats()
+        writeback[wname] = {"path_used": kvt.PATH_NAMES[pool.last_path(kvt.BACKUP)],
+                            "workgroups": (int(st.last_workgroups[0]) if p == kvt.PATH_KERNEL
+                                           else None),
+                            "d2h_gbps_beside_compute": round(statistics.median(rates), 3),
+                            "compute_slowdown": round(statistics.median(slow), 3)}
+        log("streamed write-back %s %s" % (wname, json.dumps(writeback[wname])))
+    pool.close()
     s_load.close()
     del bufs
     torch.cuda.empty_cache()
@@ -1033,7 +1077,12 @@ def leg_streamed(torch, kvt, workloads, args):
                         "per-layer H2D overlapped with an HBM-bound consumer; host layout "
                         "layer_first unless the variant names page_first_direct",
             "layer_bytes": layer_bytes, "consumer_pass_ms": round(t_pass * 1e3, 3),
-            "paths": results}
+            "paths": results,
+            "write_back_beside_compute": {
+                "workload": "layers 1..60 written back (15.8 GB) while the consumer repeats "
+                            "its pass over layer 0 60 times; slowdown against the consumer "
+                            "alone", "consumer_alone_ms": round(t_alone * 1e3, 3),
+                "paths": writeback}}
 
 
 def leg_ghost_list(kvt, workloads):

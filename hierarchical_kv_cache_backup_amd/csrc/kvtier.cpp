@@ -183,13 +183,24 @@ void default_calibration(kv_calib_t *c) {
   // in isolation the staged path ties the direct paths (all at the link rate);
   // it pays off where they are slowed (fragmented copies beside compute)
   c->staged_min_gain = 0.05;
-  c->kernel_gbps[0] = 55.9;
+  c->kernel_gbps[0] = 52.0;  // on the default 24-workgroup grid (55.9 on a full grid)
   c->kernel_gbps[1] = 56.1;
   c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
   c->dma_gbps[0] = 56.2;
   c->dma_gbps[1] = 55.9;
   c->load_split_min_bytes = 16.0 * 1024 * 1024;
-  c->kernel_max_workgroups[0] = c->kernel_max_workgroups[1] = 0;
+  // A write-back kernel on a full grid keeps the link full with posted host
+  // writes, and an HBM-bound kernel running beside it (the model's next
+  // prefill or decode) then ran 35-41x longer (61-layer fp8 write-back beside
+  // a stream of 2 x 256 MiB reductions); on 24 workgroups it ran 1.15x longer
+  // (the copy engines: 1.12x) while the write-back still moved 51.6-53.6 GB/s
+  // against 55.9-56.5 on a full grid. Per workgroup the write-back moves
+  // ~2.15 GB/s up to 24 workgroups; 28-48 workgroups moved less in total
+  // (38-48 GB/s), 64 moved 52 but slowed the other kernel 6x. Loads keep the
+  // full grid: a load's host reads slow a neighbour 1.65-1.9x at any grid (a
+  // load beside compute is KV_F_LOAD_OVERLAP's case).
+  c->kernel_max_workgroups[0] = 24;
+  c->kernel_max_workgroups[1] = 0;
   // Measured on MI355X with a 61-layer streamed load and an HBM-bound consumer:
   // the consumer ran ~1.65x longer beside the kernel path (128-workgroup grid)
   // and ~1.15x longer beside the copy engines.

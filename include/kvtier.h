@@ -174,7 +174,12 @@ typedef struct {
  * kernel_max_workgroups: cap on the workgroups one transfer kernel launches
  * (0 = one per block of work). The kernels stride over their work, so a cap
  * moves the same bytes while leaving compute units free for kernels on other
- * streams (e.g. the layer that was just loaded).
+ * streams (e.g. the layer that was just loaded). Default: 24 for a backup, none
+ * for a load. A write-back kernel on a large grid keeps so many posted host
+ * writes queued that HBM-bound kernels running beside it slow by up to ~40x;
+ * with 24 workgroups it still moves 92-96% of its full-grid rate and they slow
+ * by ~1.15x, as beside the copy engines. Set [0] to 0 for the full grid when
+ * nothing else runs during backups.
  * With KV_F_LOAD_OVERLAP, a load's modelled time on each path is multiplied
  * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
  * fractions of the transfer time by which a concurrent HBM-bound kernel is

@@ -282,11 +282,12 @@ def test_capped_grid_matches_oracle(torch, stream, layout):
 
 
 def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
-    """The kernel paths launch at most duplex_kernel_max_workgroups[dir]
-    workgroups on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load),
-    at most overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP,
-    and the smallest cap that applies; without a cap a launch has one workgroup
-    per block of work. The bytes match the oracle under every cap."""
+    """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
+    (default 24); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
+    on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load), at most
+    overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP, and the
+    smallest cap that applies; without a cap a launch has one workgroup per
+    block of work. The bytes match the oracle under every cap."""
     g = Geometry(4, 2, 2048, 4096, 4096, 64, 0)
     bufs = device_buffers(g, seed=15)
     rng = np.random.default_rng(15)
@@ -303,9 +304,14 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     plain = make_pool(g, bufs)
     c = plain.calibration()
     assert list(c.duplex_kernel_max_workgroups) == [24.0, 128.0]
+    assert list(c.kernel_max_workgroups) == [24.0, 0.0]
     assert tuple(plain.stats().last_workgroups) == (0, 0)
+    default = grids(plain, kvt.PATH_KERNEL)
+    c.kernel_max_workgroups[0] = 0
+    plain.set_calibration(c)
     free = grids(plain, kvt.PATH_KERNEL)
     assert free[0] > 1000 and free[1] > 1000, free     # one workgroup per 16 KiB block
+    assert default == (24, free[1]), default
     c.duplex_kernel_max_workgroups[0] = -1
     with pytest.raises(kvt.KvError):
         plain.set_calibration(c)
@@ -327,7 +333,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
     got = grids(overlap, kvt.PATH_KERNEL)
-    assert got == (free[0], 128), got               # the overlap cap is a load's only
+    assert got == (24, 128), got                    # the overlap cap is a load's only
     overlap.close()
 
 
@@ -353,6 +359,9 @@ def test_duplex_caps_follow_the_other_direction(torch):
     g = Geometry(4, 2, 2048, 8192, 8192, 64, 0)
     bufs = device_buffers(g, seed=16)
     pool = make_pool(g, bufs, kvt.PATH_KERNEL, host_fill=None)
+    c = pool.calibration()
+    c.kernel_max_workgroups[0] = 0           # backups alone on a full grid
+    pool.set_calibration(c)
     rng = np.random.default_rng(16)
     pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
     half = g.S_dev // 2
