@@ -510,15 +510,18 @@ static bool other_direction_busy(kv_pool *p, int dir, hipStream_t s) {
 }
 
 // Workgroup cap of a transfer kernel launch (0 = none): the smallest of the
-// caps that apply (the direction's own, the overlap cap for a load flagged
-// KV_F_LOAD_OVERLAP, the duplex cap while the other direction is busy).
-static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool duplex) {
-  uint32_t cap = (uint32_t)c.kernel_max_workgroups[dir];
+// caps that apply. A direct kernel (kernel and LDS paths) takes the
+// direction's own cap, the overlap cap for a load flagged KV_F_LOAD_OVERLAP
+// and the duplex cap while the other direction is busy; the staged path's
+// device-side passes (HBM to HBM, no host traffic) take only the overlap cap.
+static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool duplex,
+                           bool direct) {
+  uint32_t cap = direct ? (uint32_t)c.kernel_max_workgroups[dir] : 0u;
   auto tighten = [&cap](double limit) {
     if (limit > 0 && (cap == 0 || cap > (uint32_t)limit)) cap = (uint32_t)limit;
   };
   if (overlap) tighten(c.overlap_kernel_max_workgroups);
-  if (duplex) tighten(c.duplex_kernel_max_workgroups[dir]);
+  if (duplex && direct) tighten(c.duplex_kernel_max_workgroups[dir]);
   return cap;
 }
 
@@ -701,8 +704,8 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
   const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
-  const uint32_t cap = kernel_cap(c, dir, overlap, duplex);          // kernel paths
-  const uint32_t stage_cap = kernel_cap(c, dir, overlap, false);     // staged device passes
+  const uint32_t cap = kernel_cap(c, dir, overlap, duplex, true);          // kernel paths
+  const uint32_t stage_cap = kernel_cap(c, dir, overlap, duplex, false);   // staged passes
 
   // ---- path selection
   int32_t path = p->path.load();

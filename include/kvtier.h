@@ -171,8 +171,9 @@ typedef struct {
  * group is one layer when a layer of the request holds at least this many
  * bytes, else the fewest layers that reach it. Small loads thus pay for few
  * launches and events, large ones signal every layer as soon as it lands.
- * kernel_max_workgroups: cap on the workgroups one transfer kernel launches
- * (0 = one per block of work). The kernels stride over their work, so a cap
+ * kernel_max_workgroups: cap on the workgroups one direct transfer kernel
+ * (kernel and LDS paths) launches (0 = one per block of work; the staged
+ * path's device-side passes, HBM to HBM, are not capped by it). The kernels stride over their work, so a cap
  * moves the same bytes while leaving compute units free for kernels on other
  * streams (e.g. the layer that was just loaded). Default: 24 for a backup, none
  * for a load. A write-back kernel on a large grid keeps so many posted host
