@@ -442,6 +442,43 @@ def test_null_stream_round_trip(torch, path):
         pool.close()
 
 
+@pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+def test_destroy_waits_for_work_in_flight(torch, path):
+    """kv_pool_destroy right after enqueueing: it waits for the pool's transfers
+    before freeing anything. A load's rows land in full; a writer's backup lands
+    in the host pool a sharing pool keeps alive, and both match the oracle."""
+    g = Geometry(4, 2, 2048, 16384, 16384, 64, 0)
+    rng = np.random.default_rng(18)
+    d = rng.permutation(g.S_dev)[:12288].astype(np.int64)
+    h = rng.permutation(g.S_host)[:12288].astype(np.int64)
+    s = torch.cuda.Stream()
+    # load, then destroy at once
+    bufs = device_buffers(g, seed=18)
+    pool = make_pool(g, bufs, path, host_fill=None)
+    pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+    dev_m = mirrors(bufs)
+    assert oracle.load(g, dev_m, pool.host_array().copy(), d, h) == 0
+    torch.cuda.synchronize()
+    print("destroy during a load, path=%d" % path, flush=True)
+    pool.load(d, h, 0, g.L, s)
+    pool.close()
+    torch.cuda.synchronize()
+    for k, b in enumerate(bufs):
+        assert np.array_equal(b.cpu().numpy(), dev_m[k]), k
+    # backup by a writer destroyed at once; a sharing pool holds the host pool
+    writer = make_pool(g, bufs, path)
+    reader = kvt.KvPool(kv_geom(g), device_buffers(g, seed=19), share_with=writer)
+    want = writer.host_array().copy()
+    assert oracle.backup(g, mirrors(bufs), want, d, h) == 0
+    torch.cuda.synchronize()
+    print("destroy during a backup, path=%d" % path, flush=True)
+    writer.backup(d, h, 0, g.L, s)
+    writer.close()
+    torch.cuda.synchronize()
+    assert np.array_equal(reader.host_array(), want)
+    reader.close()
+
+
 def test_overlap_flag_steers_selector(torch, stream):
     g = Geometry(2, 1, 64, 32, 32, 8, 0)
     bufs = device_buffers(g, seed=12)
