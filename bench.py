@@ -401,7 +401,8 @@ def counter_link_bytes(kernel_name, src_hash):
     return link.get("host_link_bytes_per_launch")
 
 
-KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true, false> (D2H gather, whole prefix in one launch)",
+KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true, false> (D2H gather, whole prefix in one launch, "
+                       "on the default write-back grid)",
                 "h2d": "kvt::xfer_rows<false, false> (H2D scatter, one launch per layer: each "
                        "layer holds more than the 16 MiB load group threshold)"}
 
@@ -458,6 +459,7 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
 
     loop = {"d2h": measure(lambda: pool.backup(dev_b, host_idx, 0, L, s), 1),
             "h2d": measure(lambda: pool.load(dev_l, host_idx, 0, L, s), L)}
+    grids = pool.stats().last_workgroups      # the kernels' grids in that loop
     entries = {}
     for dname in ("d2h", "h2d"):
         t_call, launches = timed[dname]
@@ -470,6 +472,7 @@ def kernel_roofline(torch, kvt, pool, s, dev_b, dev_l, host_idx, L, C, R, n, arg
                                          loop[dname][1], src_hash,
                                          "loop of its own, kernel path forced (the timed steps "
                                          "ran this direction on the copy engines)")
+        entries[dname]["workgroups"] = int(grids[0 if dname == "d2h" else 1])
         entries[dname]["own_loop"] = {"mean_launch_us": round(loop[dname][0] * 1e6, 2),
                                       "achieved": round(per_launch_bytes[dname] / loop[dname][0]
                                                         / 1e9, 3)}
