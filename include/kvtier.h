@@ -82,12 +82,14 @@ typedef enum {
 } kv_layout_t;
 
 /* ---- execution paths ---------------------------------------------------
- * KV_PATH_AUTO        per call, pick the cheaper of KERNEL and DMA from the
- *                     byte count and the number of DMA copies the request
- *                     needs, using the pool's calibration (kv_calib_t).
+ * KV_PATH_AUTO        per call, pick the cheapest of KERNEL, DMA and STAGED
+ *                     from the byte count, the number of DMA copies and of
+ *                     staging extents the request needs, using the pool's
+ *                     calibration (kv_calib_t).
  * KV_PATH_KERNEL      zero-copy gather/scatter kernel: the GPU reads/writes the
- *                     mapped host pool directly, 16 bytes per lane, rows taken
- *                     in host-address order.
+ *                     mapped host pool directly, 8 bytes per lane (a wave's
+ *                     access covers 512 consecutive bytes), rows taken in
+ *                     host-address order.
  * KV_PATH_KERNEL_LDS  as KERNEL, but each workgroup stages a tile of rows in
  *                     LDS: read in source order, written in destination order
  *                     (the page_first <-> layer_first transpose).
@@ -117,8 +119,10 @@ typedef enum {
 #define KV_F_CHECK_UNIQUE     0x1u /* reject duplicate destination slots (KV_EDUP) */
 #define KV_F_HOST_NONCOHERENT 0x2u /* allocate the host pool non-coherent (coarse-grained) instead of coherent */
 #define KV_F_DUPLEX           0x8u /* backups and loads on this pool run at the same time: the
-                                      selector charges the kernel path the duplex penalty.
-                                      Without it the charge applies only while the other
+                                      selector charges the kernel path the duplex penalty and
+                                      the kernel paths run on the duplex grids
+                                      (duplex_kernel_max_workgroups).
+                                      Without it both apply only while the other
                                       direction has a transfer in flight at submission on
                                       another stream (work queued on the same stream runs
                                       before this call, not beside it). */
