@@ -181,6 +181,7 @@ def main():
     peak_pool.set_path(kvt.PATH_KERNEL)
     pc = peak_pool.calibration()
     pc.load_split_min_bytes = 2.0 * GiB             # one launch
+    pc.kernel_max_workgroups[:] = [0, 0]            # full grid both ways
     peak_pool.set_calibration(pc)
     all_rows = np.arange(rows, dtype=np.int64)
     k_d2h, _ = timed(lambda: peak_pool.backup(all_rows, all_rows, 0, 1, s), 20)
@@ -202,11 +203,16 @@ def main():
     # call) plus bytes / rate. The measured call time already holds the fixed
     # costs, so each rate is fitted to the time left after the modelled fixed
     # costs of the launches and copies that call made (counted by kv_get_stats).
+    # The kernel rate is the link-bound rate of a full grid; what a capped grid
+    # moves is modelled per workgroup (kernel_wg_gbps / kernel_wg_row_ns).
     calib = pool.calibration()
     meas, ops = {}, {}
     gather = []
+    full = pool.calibration()
+    full.kernel_max_workgroups[:] = [0, 0]
     for d in (kvt.BACKUP, kvt.LOAD):
         for p in (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED):
+            pool.set_calibration(full if p == kvt.PATH_KERNEL else calib)
             meas[(d, p)] = run(d, p, pool)
             s0 = pool.stats()
             (pool.backup(dev_b, host_idx, 0, L, s) if d == kvt.BACKUP

@@ -59,7 +59,9 @@ class kv_calib_t(ctypes.Structure):
                 ("kernel_group_us", ctypes.c_double * 2),
                 ("staged_min_gain", ctypes.c_double),
                 ("index_zero_copy_max_bytes", ctypes.c_double * 2),
-                ("duplex_kernel_max_workgroups", ctypes.c_double * 2)]
+                ("duplex_kernel_max_workgroups", ctypes.c_double * 2),
+                ("kernel_wg_gbps", ctypes.c_double * 2),
+                ("kernel_wg_row_ns", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):

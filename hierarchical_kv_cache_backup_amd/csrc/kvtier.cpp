@@ -183,8 +183,16 @@ void default_calibration(kv_calib_t *c) {
   // in isolation the staged path ties the direct paths (all at the link rate);
   // it pays off where they are slowed (fragmented copies beside compute)
   c->staged_min_gain = 0.05;
-  c->kernel_gbps[0] = 52.0;  // on the default 24-workgroup grid (55.9 on a full grid)
+  c->kernel_gbps[0] = 55.9;  // full grid; a capped grid is modelled per workgroup below
   c->kernel_gbps[1] = 56.1;
+  // What W workgroups move on a capped grid, fitted on the 24-workgroup
+  // write-back of two geometries (2.94 GB of 1152-byte rows in 56.7 ms, 134 MB
+  // of 256-byte rows in 3.09 ms): 2.29 GB/s per workgroup plus 29.8 ns per row.
+  // A load's workgroup moves ~0.78 GB/s (link-rate sweep of 4-64 workgroups).
+  c->kernel_wg_gbps[0] = 2.29;
+  c->kernel_wg_gbps[1] = 0.78;
+  c->kernel_wg_row_ns[0] = 29.8;
+  c->kernel_wg_row_ns[1] = 0.0;
   c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
   c->dma_gbps[0] = 56.2;
   c->dma_gbps[1] = 55.9;
@@ -726,8 +734,18 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       extents = (double)d.extents.size();
     }
     const double mb = (double)bytes;
+    // a capped grid moves what its workgroups can: blocks of 16 KiB of rows
+    // per launch, W = min(cap, blocks)
+    const int64_t rows_per_block =
+        g.R >= (int64_t)kChunksPerBlock * kChunkBytes ? 1 : (int64_t)kChunksPerBlock * kChunkBytes / g.R;
+    const double launch_rows = (double)n * std::min<int32_t>(group, l1 - l0) * g.C;
+    const double blocks = std::ceil(launch_rows / (double)rows_per_block);
+    const double wgs = cap > 0 ? std::min<double>(cap, blocks) : blocks;
+    const double rows_all = (double)n * nlc_all;
+    const double t_wg = (rows_all * c.kernel_wg_row_ns[dir] * 1e-3 +
+                         mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
     double t_kernel = c.kernel_launch_us[dir] + (ngroups - 1) * c.kernel_group_us[dir] +
-                      mb / (c.kernel_gbps[dir] * 1e3);
+                      std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
     double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
                    mb / (c.dma_gbps[dir] * 1e3);
     // the staged path moves page-major layouts in one unit (see below); its
@@ -1183,6 +1201,9 @@ int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
     if (!(c->duplex_kernel_max_workgroups[d] >= 0) ||
         c->duplex_kernel_max_workgroups[d] > 4294967295.0)
       return fail(KV_EINVAL, "duplex_kernel_max_workgroups must be in [0, 2^32)");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_wg_gbps[d] > 0) || !(c->kernel_wg_row_ns[d] >= 0))
+      return fail(KV_EINVAL, "kernel_wg_gbps must be > 0 and kernel_wg_row_ns >= 0");
   if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
       !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))

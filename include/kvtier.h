@@ -168,7 +168,10 @@ typedef struct {
  *   t_dma    = copies * dma_copy_us + bytes / dma_gbps
  * kernel_launch_us is the fixed cost of a call's first launch (launch, index
  * staging, ramp), kernel_group_us the gap each further launch of the same
- * call adds. The rates are fitted per direction on the target machine to the
+ * call adds. On a capped grid of W workgroups the kernel is limited by what W
+ * workgroups move: bytes / kernel_gbps is replaced by the larger of itself and
+ * (rows * kernel_wg_row_ns * 1e-3 + bytes / (kernel_wg_gbps * 1e3)) / W
+ * (microseconds), rows being the call's n * layers * C rows. The rates are fitted per direction on the target machine to the
  * time a call takes less its modelled fixed costs.
  * load_split_min_bytes: kv_load goes out in groups of consecutive layers, one
  * kernel launch (or one batch of copies) and one landed event per group; a
@@ -226,6 +229,8 @@ typedef struct {
                                    staging buffer, skipping the copy to the device */
   double duplex_kernel_max_workgroups[2]; /* kernel-path grid cap while the other
                                    direction is busy ([0] backup, [1] load; 0 = none) */
+  double kernel_wg_gbps[2];     /* kernel path: bytes one workgroup moves per second (GB/s) */
+  double kernel_wg_row_ns[2];   /* kernel path: a workgroup's extra time per row (ns) */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

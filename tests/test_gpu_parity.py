@@ -479,6 +479,33 @@ def test_destroy_waits_for_work_in_flight(torch, path):
     reader.close()
 
 
+def test_selector_models_capped_grids_per_workgroup(torch, stream):
+    """AUTO prices a capped kernel by what its workgroups move: a backup of 512
+    blocks on the default 24-workgroup grid, at 10 GB/s per workgroup, loses to
+    two copy-engine copies; on a full grid (512 workgroups) it wins. Bytes match
+    the oracle on both paths."""
+    g = Geometry(2, 1, 4096, 1024, 1024, 8, 0)
+    bufs = device_buffers(g, seed=20)
+    pool = make_pool(g, bufs, kvt.PATH_AUTO)
+    d, h = np.arange(1024, dtype=np.int64), np.arange(1024, dtype=np.int64)
+    c = pool.calibration()
+    assert c.kernel_wg_gbps[0] > 0 and c.kernel_wg_row_ns[0] >= 0
+    c.kernel_launch_us[0], c.dma_copy_us[0] = 15.0, 10.0        # kernel 15 us, copies 2 x 10 us
+    c.kernel_gbps[0] = c.dma_gbps[0] = 1e6                       # link terms negligible
+    c.kernel_wg_gbps[0], c.kernel_wg_row_ns[0] = 10.0, 0.0      # 8 MiB / (24 x 10 GB/s) = 35 us
+    pool.set_calibration(c)
+    run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+    assert pool.last_path(kvt.BACKUP) == kvt.PATH_DMA
+    c.kernel_max_workgroups[0] = 0                                # 512 workgroups: 1.6 us
+    pool.set_calibration(c)
+    run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+    assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
+    c.kernel_wg_gbps[0] = 0.0
+    with pytest.raises(kvt.KvError):
+        pool.set_calibration(c)
+    pool.close()
+
+
 def test_overlap_flag_steers_selector(torch, stream):
     g = Geometry(2, 1, 64, 32, 32, 8, 0)
     bufs = device_buffers(g, seed=12)
