@@ -11,9 +11,10 @@ timed region. Prints ONE JSON line.
                     [--path auto|kernel|kernel_lds|dma] [--no-matrix] [--no-cpu-baseline]
                     [--no-extra]
 
-Besides the headline step it reports the layout x path matrix, the bidirectional
-mixed batch, the per-layer streamed load, the write filter and the oracle as CPU
-baseline. Studies that print their own JSON line and exit:
+Besides the headline step it reports the measured link peak (1 GiB copies on
+the copy engines and on the zero-copy kernel), the layout x path matrix, the
+bidirectional mixed batch, the per-layer streamed load and a write-back beside
+compute, the write filter and the oracle as CPU baseline. Studies that print their own JSON line and exit:
 
     python bench.py --host-memory-study 3 24    # pinned pool size and NUMA placement
     python bench.py --free-list-study           # FIFO vs LIFO host free list under churn
