@@ -137,7 +137,8 @@ def test_llama8b_fragmented_backup(torch, path):
 
 # ---- mla32k: H2D of a 32768-token prefix, page_first_direct vs layer_first -------
 
-@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA))
+@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS, kvt.PATH_DMA,
+                                  kvt.PATH_STAGED))
 @pytest.mark.timeout(300)
 def test_mla32k_load(torch, path):
     shape = workloads.mla32k()
