@@ -110,7 +110,8 @@ def sample_layers(L):
 
 # ---- llama8b: D2H of an 8192-token prefix from fragmented pages ------------------
 
-@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+@pytest.mark.parametrize("path", (kvt.PATH_AUTO, kvt.PATH_KERNEL, "kernel_full_grid",
+                                  kvt.PATH_KERNEL_LDS, kvt.PATH_DMA, kvt.PATH_STAGED))
 def test_llama8b_fragmented_backup(torch, path):
     shape = workloads.llama8b()
     n = shape.extra["tokens"]
@@ -119,9 +120,15 @@ def test_llama8b_fragmented_backup(torch, path):
     for layout in shape.layouts:
         g = Geometry(shape.layers, shape.components, shape.row_bytes, shape.device_slots,
                      shape.host_slots, shape.page_size, layout)
-        print("llama8b layout=%d path=%d n=%d" % (layout, path, n), flush=True)
+        print("llama8b layout=%d path=%s n=%d" % (layout, path, n), flush=True)
         with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
-            pool.set_path(path)
+            if path == "kernel_full_grid":        # the write-back kernel without its cap
+                c = pool.calibration()
+                c.kernel_max_workgroups[0] = 0
+                pool.set_calibration(c)
+                pool.set_path(kvt.PATH_KERNEL)
+            else:
+                pool.set_path(path)
             pool.host_array()[:] = SENTINEL
             s = torch.cuda.Stream()
             pool.backup(dev_idx, host_idx, 0, g.L, s)
