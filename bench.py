@@ -208,7 +208,6 @@ def main():
     # moves is modelled per workgroup (kernel_wg_gbps / kernel_wg_row_ns).
     calib = pool.calibration()
     meas, ops = {}, {}
-    gather = []
     full = pool.calibration()
     full.kernel_max_workgroups[:] = [0, 0]
     for d in (kvt.BACKUP, kvt.LOAD):
@@ -236,13 +235,10 @@ def main():
 
         calib.kernel_gbps[d] = fit(kvt.PATH_KERNEL)
         calib.dma_gbps[d] = fit(kvt.PATH_DMA)
-        # staged = its fixed costs + the copy-engine stream + the first chunk's
-        # device-side pass (the later ones overlap the copies)
-        extra = (meas[(d, kvt.PATH_STAGED)] - fixed_s(kvt.PATH_STAGED)
-                 - bytes_dir / (calib.dma_gbps[d] * 1e9))
-        first = min(bytes_dir, calib.staged_chunk_bytes)
-        gather.append(first / extra / 1e9 if extra > 0 else 8000.0)
-    calib.staged_gather_gbps = min(max(statistics.median(gather), 100.0), 8000.0)
+    # The staged path is modelled as its fixed costs + the copy-engine stream +
+    # one small ramp chunk's device-side pass (the others overlap the copies);
+    # that pass rate (staged_gather_gbps) keeps the library's value, as a few
+    # microseconds of a 50 ms call cannot be fitted from it.
     pool.set_calibration(calib)
     pool.set_path(path)
     best_rate = {dd: max(bytes_dir / meas[(dd, p)] / 1e9 for p in

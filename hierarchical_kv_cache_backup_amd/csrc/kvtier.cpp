@@ -36,6 +36,12 @@ namespace {
 constexpr int kStagingSlots = 16;  // index-staging buffers in flight per direction
 constexpr int64_t kMaxRowsPerLaunch = (int64_t)1 << 31;
 constexpr double kExtentPlanLimit = 4.0 * 1024 * 1024;  // staged extents AUTO lists exactly
+// Staged path: where a device-side pass runs alone, chunks grow from
+// 1/kRampFirst of a staging half by kRampGrowth per chunk, on halves of at
+// least staged_chunk_bytes / kRampMinDiv (below that the pass is shorter than
+// the launches and copies the ramp adds).
+constexpr int64_t kRampFirst = 64, kRampGrowth = 8;
+constexpr double kRampMinDiv = 16.0;
 
 int fail(int code, const std::string &msg) {
   set_error(msg);
@@ -104,8 +110,10 @@ struct DirState {
   // each half between the copies (caller's stream) and the kernels (aux).
   std::vector<Extent> extents;
   std::vector<int64_t> host_run_start;  // staged path: runs of host-consecutive positions
+  std::vector<int64_t> chunk_len;       // staged path: the unit's chunk lengths (rows)
   uint8_t *stage = nullptr;      // 2 * stage_cap bytes
   int64_t stage_cap = 0;         // bytes per half
+  int64_t stage_use = 0;         // bytes per half the current call fills (<= stage_cap)
   hipEvent_t stage_ev = nullptr;  // the call's last use of the halves (on the caller's stream)
   bool stage_pending = false;
   hipStream_t stage_stream = nullptr;
@@ -236,7 +244,9 @@ void default_calibration(kv_calib_t *c) {
   c->duplex_kernel_max_workgroups[0] = 24;
   c->duplex_kernel_max_workgroups[1] = 128;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
-  c->staged_gather_gbps = 2000.0;
+  // the device-side gather / scatter of a staged chunk (HBM to HBM, full
+  // grid): 256 MiB of 1152-byte rows in 330 us, 37.7 MB in 45 us (kernel trace)
+  c->staged_gather_gbps = 800.0;
   // Reading the index pairs from mapped pinned memory instead of copying them
   // first measured +0.6..1.6% at 64 tokens, even at 256, and down to -2% for
   // loads of 1K tokens and more (the reads share the link and lengthen each
@@ -534,9 +544,10 @@ static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool dupl
 }
 
 // Staged path: makes the direction's staging buffer ready for a call on s that
-// moves at most unit_bytes per layer group: grows it (after its previous use
-// has finished) to min(staged_chunk_bytes, unit_bytes) rounded down to whole
-// rows, and orders s after its previous use on another stream.
+// moves at most unit_bytes per layer group: the call fills halves of
+// min(staged_chunk_bytes, unit_bytes) rounded down to whole rows (stage_use);
+// grows the buffer to that (after its previous use has finished) if smaller,
+// and orders s after its previous use on another stream.
 static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_calib_t &c,
                        hipStream_t s) {
   int64_t want = (int64_t)std::min<double>(c.staged_chunk_bytes, (double)unit_bytes);
@@ -560,6 +571,7 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
     hipError_t e = hipStreamWaitEvent(s, d.stage_ev, 0);
     if (e != hipSuccess) return hip_fail(e, "ordering after the staging buffer's last use");
   }
+  d.stage_use = want;
   // the halves are free once s reaches this point (the previous call's last
   // use of them is ordered before it)
   d.free_recorded[0] = d.free_recorded[1] = false;
@@ -567,9 +579,33 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
   return KV_OK;
 }
 
+// Chunk lengths (rows, in walk order) of a staged unit of walk_rows rows. A
+// chunk fills a staging half, except where a chunk's device-side pass has no
+// copy to overlap: a write-back's first gather (nothing is ready to copy out
+// yet) and a call's last scatter (nothing is left to copy in). There the
+// chunks grow from 1/kRampFirst of a half by kRampGrowth per chunk (ascending
+// at the start, mirrored at the end), so the pass that runs alone is short.
+// Each ramp chunk's copy over the host link outlasts the next chunk's pass in
+// HBM (the passes run >10x the link rate), so the ramp adds launches and
+// copies but no stall.
+static void chunk_plan(int64_t walk_rows, int64_t chunk_rows, bool ramp_first, bool ramp_last,
+                       std::vector<int64_t> *out) {
+  out->clear();
+  int64_t len = (ramp_first || ramp_last) ? std::max<int64_t>(1, chunk_rows / kRampFirst)
+                                          : chunk_rows;
+  for (int64_t r = 0; r < walk_rows;) {
+    const int64_t take = std::min(len, walk_rows - r);
+    out->push_back(take);
+    r += take;
+    len = std::min(chunk_rows, len * kRampGrowth);
+  }
+  if (ramp_last && !ramp_first) std::reverse(out->begin(), out->end());
+}
+
 // Staged path, one layer group [la, lb): the walk rows go through the staging
-// halves in chunks, consecutive chunks (also across groups and calls) in
-// alternate halves, so the kernel of one chunk overlaps the copies of the other.
+// halves in chunks (chunk_plan), consecutive chunks (also across groups and
+// calls) in alternate halves, so the kernel of one chunk overlaps the copies
+// of the other.
 //   D2H: aux gathers chunk k (device rows -> half, HBM to HBM) once the half is
 //        free; the caller's stream s copies it out, one copy-engine call per
 //        host extent piece, then frees the half.
@@ -577,15 +613,15 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
 //        device rows, then frees the half; the group's landed event is recorded
 //        on aux after its last scatter, and the call makes s wait for aux
 //        after the last group.
-// b is planned for the group.
+// b is planned for the group; ramp_first / ramp_last select chunk_plan's ramps.
 static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
-                              const int64_t *host_idx, int32_t la, int32_t lb, uint32_t cap,
-                              hipStream_t s) {
+                              const int64_t *host_idx, int32_t la, int32_t lb, bool ramp_first,
+                              bool ramp_last, uint32_t cap, hipStream_t s) {
   const Geom &g = p->g;
   build_extents(g, host_idx, (int64_t)b.n, d.host_run_start, la, lb, &d.extents);
   plan_rows(&b, g.layout, g.ps);
-  const int64_t chunk_rows = d.stage_cap / g.R;
   const int64_t walk_rows = b.total_rows;
+  chunk_plan(walk_rows, d.stage_use / g.R, ramp_first, ramp_last, &d.chunk_len);
   size_t x = 0;  // next extent that reaches into the current chunk
   hipError_t e = hipSuccess;
   if (dir == 0) {  // aux starts after everything already queued on s (the KV it reads)
@@ -593,8 +629,9 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
     if (e == hipSuccess) e = hipStreamWaitEvent(d.aux, d.ev_start, 0);
   }
   int last = -1;
-  for (int64_t r0 = 0; r0 < walk_rows && e == hipSuccess; r0 += chunk_rows) {
-    const int64_t r1 = std::min(walk_rows, r0 + chunk_rows);
+  int64_t r0 = 0;
+  for (size_t k = 0; k < d.chunk_len.size() && e == hipSuccess; r0 += d.chunk_len[k++]) {
+    const int64_t r1 = r0 + d.chunk_len[k];
     const int half = (int)(d.next_half++ & 1);
     last = half;
     uint8_t *buf = d.stage + half * d.stage_cap;
@@ -713,7 +750,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
 
   const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
   const uint32_t cap = kernel_cap(c, dir, overlap, duplex, true);          // kernel paths
-  const uint32_t stage_cap = kernel_cap(c, dir, overlap, duplex, false);   // staged passes
+  const uint32_t pass_cap = kernel_cap(c, dir, overlap, duplex, false);    // staged passes
 
   // ---- path selection
   int32_t path = p->path.load();
@@ -749,12 +786,17 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
     double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
                    mb / (c.dma_gbps[dir] * 1e3);
     // the staged path moves page-major layouts in one unit (see below); its
-    // device-side passes overlap the copies except for the first chunk's
+    // device-side passes overlap the copies except for the smallest ramp
+    // chunk's (chunk_plan), and the ramp adds up to two chunks, each one more
+    // launch and one more copy where it splits an extent
     const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
-    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units;
-    double t_staged = extents * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
+    const double half = std::min(c.staged_chunk_bytes, mb / units);
+    const bool ramped = half * kRampMinDiv >= c.staged_chunk_bytes;
+    const double ramp = ramped ? 2.0 : 0.0;
+    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units + ramp;
+    double t_staged = (extents + ramp) * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
                       (chunks - 1) * c.kernel_group_us[dir] + mb / (c.dma_gbps[dir] * 1e3) +
-                      std::min(mb, c.staged_chunk_bytes) / (c.staged_gather_gbps * 1e3);
+                      (ramped ? half / kRampFirst : half) / (c.staged_gather_gbps * 1e3);
     if (overlap) {
       t_kernel *= 1.0 + c.overlap_kernel_penalty;
       t_dma *= 1.0 + c.overlap_dma_penalty;
@@ -853,7 +895,9 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       b.lc0 = (uint32_t)(la * g.C);
       b.nlc = (uint32_t)((lb - la) * g.C);
       if (path == KV_PATH_STAGED) {
-        e = staged_unit(p, d, dir, b, host_idx, la, lb, stage_cap, s);
+        const bool ramp = (double)d.stage_use * kRampMinDiv >= c.staged_chunk_bytes;
+        e = staged_unit(p, d, dir, b, host_idx, la, lb, ramp && dir == 0,
+                        ramp && dir == 1 && lb == l1, pass_cap, s);
         continue;  // staged_unit records the group's landed event itself
       } else if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows

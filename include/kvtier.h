@@ -201,10 +201,16 @@ typedef struct {
  * link and, together with the load's cap, leaves compute units free for the
  * other direction's kernels. The staged path's device-side passes are not
  * capped by it.
- * The staged path is modelled as extents * dma_copy_us + kernel_launch_us +
- * (chunks - 1) * kernel_group_us + bytes / dma_gbps + min(bytes,
- * staged_chunk_bytes) / staged_gather_gbps: its device-side passes overlap the
- * copies except for the first chunk's. */
+ * The staged path moves a unit (all layers, or one load group in layer_first)
+ * through two staging halves of min(staged_chunk_bytes, unit bytes) each, in
+ * chunks that fill a half, except where a device-side pass cannot overlap a
+ * copy: on a half of at least staged_chunk_bytes / 16, a backup's first chunks
+ * and a load's last ones grow by 8x from 1/64 of a half. It is modelled as
+ * (extents + ramp) * dma_copy_us + kernel_launch_us + (chunks - 1) *
+ * kernel_group_us + bytes / dma_gbps + first / staged_gather_gbps, with
+ * ramp = 2 chunks and first = half / 64 where the ramp applies (else ramp = 0
+ * and first = half): the device-side passes overlap the copies except for
+ * that one. */
 typedef struct {
   double kernel_launch_us[2]; /* [0] = D2H backup, [1] = H2D load */
   double kernel_gbps[2];

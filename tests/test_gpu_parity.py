@@ -598,6 +598,55 @@ def test_staged_small_chunks_match_oracle(torch, stream, layout):
     pool.close()
 
 
+def _ramp_chunks(walk_rows, chunk_rows, ramp):
+    """Chunk count of a staged unit: full chunks, or chunks growing 8x from
+    1/64 of a chunk where the ramp applies (same count at either end)."""
+    if not ramp:
+        return -(-walk_rows // chunk_rows)
+    n, r, ln = 0, 0, max(1, chunk_rows // 64)
+    while r < walk_rows:
+        r += min(ln, walk_rows - r)
+        n += 1
+        ln = min(chunk_rows, ln * 8)
+    return n
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_staged_ramp_chunks(torch, stream, layout):
+    """The staged path's chunk ramp: a backup's first chunks and a load's last
+    ones grow 8x from 1/64 of a staging half when the half is at least 1/16
+    of staged_chunk_bytes, else every chunk fills the half. One launch per
+    chunk (kv_get_stats); bytes match the oracle."""
+    g = Geometry(2, 1, 64, 2048, 2048, 8, layout)
+    bufs = device_buffers(g, seed=16)
+    rng = np.random.default_rng(16 + layout)
+    pool = make_pool(g, bufs, kvt.PATH_STAGED)
+    n = 500
+    d = rng.permutation(g.S_dev)[:n].astype(np.int64)
+    h = np.arange(100, 100 + n, dtype=np.int64)
+    walk = n * g.L * g.C
+    # (chunk rows, load group rows, expected backup / load launches)
+    cases = [(64, 10 ** 9, _ramp_chunks(walk, 64, True), _ramp_chunks(walk, 64, True)),
+             (100000, 10 ** 9, 1, 1)]
+    if layout == oracle.LAYER_FIRST:   # per-layer load groups: only the last one ramps
+        cases.append((64, 1, _ramp_chunks(walk, 64, True),
+                      _ramp_chunks(n, 64, False) + _ramp_chunks(n, 64, True)))
+    for chunk_rows, split_rows, want_b, want_l in cases:
+        c = pool.calibration()
+        c.staged_chunk_bytes = chunk_rows * g.R
+        c.load_split_min_bytes = split_rows * g.R
+        pool.set_calibration(c)
+        print("staged ramp layout=%d chunk=%d split=%d" % (layout, chunk_rows, split_rows),
+              flush=True)
+        before = pool.stats().kernel_launches[:]
+        run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        after = pool.stats().kernel_launches[:]
+        assert (after[0] - before[0], after[1] - before[1]) == (want_b, want_l)
+    pool.close()
+
+
 # ---- streams with a hardware queue of their own ---------------------------------------
 
 @pytest.mark.parametrize("path", (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
