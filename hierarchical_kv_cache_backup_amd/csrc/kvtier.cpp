@@ -36,11 +36,9 @@ namespace {
 constexpr int kStagingSlots = 16;  // index-staging buffers in flight per direction
 constexpr int64_t kMaxRowsPerLaunch = (int64_t)1 << 31;
 constexpr double kExtentPlanLimit = 4.0 * 1024 * 1024;  // staged extents AUTO lists exactly
-// Staged path: where a device-side pass runs alone, chunks grow from
-// 1/kRampFirst of a staging half by kRampGrowth per chunk, on halves of at
-// least staged_chunk_bytes / kRampMinDiv (below that the pass is shorter than
-// the launches and copies the ramp adds).
-constexpr int64_t kRampFirst = 64, kRampGrowth = 8;
+// Staged path: chunks ramp (chunk_plan) on halves of at least
+// staged_chunk_bytes / kRampMinDiv; below that the pass the ramp shortens is
+// shorter than the launches and copies it adds.
 constexpr double kRampMinDiv = 16.0;
 
 int fail(int code, const std::string &msg) {
@@ -577,29 +575,6 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
   d.free_recorded[0] = d.free_recorded[1] = false;
   d.last_half = -1;
   return KV_OK;
-}
-
-// Chunk lengths (rows, in walk order) of a staged unit of walk_rows rows. A
-// chunk fills a staging half, except where a chunk's device-side pass has no
-// copy to overlap: a write-back's first gather (nothing is ready to copy out
-// yet) and a call's last scatter (nothing is left to copy in). There the
-// chunks grow from 1/kRampFirst of a half by kRampGrowth per chunk (ascending
-// at the start, mirrored at the end), so the pass that runs alone is short.
-// Each ramp chunk's copy over the host link outlasts the next chunk's pass in
-// HBM (the passes run >10x the link rate), so the ramp adds launches and
-// copies but no stall.
-static void chunk_plan(int64_t walk_rows, int64_t chunk_rows, bool ramp_first, bool ramp_last,
-                       std::vector<int64_t> *out) {
-  out->clear();
-  int64_t len = (ramp_first || ramp_last) ? std::max<int64_t>(1, chunk_rows / kRampFirst)
-                                          : chunk_rows;
-  for (int64_t r = 0; r < walk_rows;) {
-    const int64_t take = std::min(len, walk_rows - r);
-    out->push_back(take);
-    r += take;
-    len = std::min(chunk_rows, len * kRampGrowth);
-  }
-  if (ramp_last && !ramp_first) std::reverse(out->begin(), out->end());
 }
 
 // Staged path, one layer group [la, lb): the walk rows go through the staging

@@ -248,6 +248,20 @@ void build_extents(const Geom &g, const int64_t *host_idx, int64_t n, int32_t la
   build_extents(g, host_idx, n, run_start, la, lb, out);
 }
 
+void chunk_plan(int64_t walk_rows, int64_t chunk_rows, bool ramp_first, bool ramp_last,
+                std::vector<int64_t> *out) {
+  out->clear();
+  int64_t len = (ramp_first || ramp_last) ? std::max<int64_t>(1, chunk_rows / kRampFirst)
+                                          : chunk_rows;
+  for (int64_t r = 0; r < walk_rows;) {
+    const int64_t take = std::min(len, walk_rows - r);
+    out->push_back(take);
+    r += take;
+    len = std::min(chunk_rows, len * kRampGrowth);
+  }
+  if (ramp_last && !ramp_first) std::reverse(out->begin(), out->end());
+}
+
 }  // namespace kvt
 
 // ---- C ABI: planner entry points --------------------------------------------

@@ -113,4 +113,18 @@ void build_extents(const Geom &g, const int64_t *host_idx, int64_t n,
                    const std::vector<int64_t> &run_start, int32_t la, int32_t lb,
                    std::vector<Extent> *out);
 
+// Chunk lengths (rows, in walk order) of a staged unit of walk_rows rows
+// through staging halves of chunk_rows rows. A chunk fills a half, except
+// where its device-side pass has no copy to overlap: a write-back's first
+// gather (nothing is ready to copy out yet; ramp_first) and a call's last
+// scatter (nothing is left to copy in; ramp_last). There the chunks grow from
+// 1/kRampFirst of a half by kRampGrowth per chunk (ascending at the start,
+// mirrored at the end), so the pass that runs alone is short. Each ramp
+// chunk's copy over the host link outlasts the next chunk's pass in HBM (the
+// passes run >10x the link rate), so the ramp adds launches and copies but no
+// stall.
+constexpr int64_t kRampFirst = 64, kRampGrowth = 8;
+void chunk_plan(int64_t walk_rows, int64_t chunk_rows, bool ramp_first, bool ramp_last,
+                std::vector<int64_t> *out);
+
 }  // namespace kvt

@@ -163,12 +163,13 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
   }
 }
 
-// Replays the staged path over layers [la, lb): extents of the walk, then in
-// chunks of chunk_rows walk rows the dense gather (D2H) or scatter (H2D) through
-// a staging mirror and one memcpy per extent piece, as the executor issues them.
+// Replays the staged path over layers [la, lb): extents of the walk, then the
+// chunks of chunk_plan (halves of chunk_rows rows, ramped as asked) with the
+// dense gather (D2H) or scatter (H2D) through a staging mirror and one memcpy
+// per extent piece, as the executor issues them.
 static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int64_t *h, int64_t n,
                           int32_t la, int32_t lb, bool to_host, std::vector<uint8_t> &cover,
-                          int64_t chunk_rows) {
+                          int64_t chunk_rows, bool ramp_first, bool ramp_last) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -193,10 +194,29 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
   }
   CHECK(next == (int64_t)a.total_rows, "extents cover %lld of %u rows", (long long)next,
         a.total_rows);
+  std::vector<int64_t> chunks;
+  chunk_plan(a.total_rows, chunk_rows, ramp_first, ramp_last, &chunks);
+  int64_t sum = 0;
+  for (size_t k = 0; k < chunks.size(); k++) {
+    CHECK(chunks[k] >= 1 && chunks[k] <= chunk_rows, "chunk of %lld rows (half %lld)",
+          (long long)chunks[k], (long long)chunk_rows);
+    // a ramp grows by kRampGrowth at most per chunk, towards the full half
+    if (ramp_first && k + 1 < chunks.size())
+      CHECK(chunks[k + 1] <= chunks[k] * kRampGrowth, "ramp grows too fast");
+    sum += chunks[k];
+  }
+  CHECK(sum == (int64_t)a.total_rows, "chunks cover %lld of %u rows", (long long)sum,
+        a.total_rows);
+  if (ramp_first || ramp_last) {
+    const int64_t edge = ramp_first ? chunks.front() : chunks.back();
+    CHECK(edge <= std::max<int64_t>(1, chunk_rows / kRampFirst), "ramp starts at %lld rows",
+          (long long)edge);
+  }
   std::vector<uint8_t> stage((size_t)(chunk_rows * g.R));
   size_t x = 0;
-  for (int64_t r0 = 0; r0 < (int64_t)a.total_rows; r0 += chunk_rows) {
-    const int64_t r1 = std::min<int64_t>(a.total_rows, r0 + chunk_rows);
+  int64_t r0 = 0;
+  for (int64_t len : chunks) {
+    const int64_t r1 = r0 + len;
     set_row_range(&a, (uint32_t)r0, (uint32_t)r1);
     auto dense = [&](bool gather) {  // the dense kernel, row by row
       for (int64_t r = a.row_begin; r < a.row_end; r++) {
@@ -229,6 +249,7 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
       x++;
     }
     if (!to_host) dense(false);
+    r0 = r1;
   }
 }
 
@@ -362,7 +383,8 @@ int main(int argc, char **argv) {
         } else if (variant == 4) {
           const int64_t walk = n * (int64_t)(l1 - l0) * g.C;
           const int64_t chunk = std::max<int64_t>(1, (std::vector<int64_t>{1, 7, walk / 3 + 1, walk})[uni(0, 3)]);
-          replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk);
+          const int ramp = (int)uni(0, 2);  // none, first, last
+          replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk, ramp == 1, ramp == 2);
         } else {
           replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
           int64_t counted = -1;
