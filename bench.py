@@ -65,6 +65,9 @@ def parse():
                         "TP pools on this GPU, then exit")
     p.add_argument("--free-list-study", action="store_true",
                    help="only run the FIFO-vs-LIFO host free-list churn study, then exit")
+    p.add_argument("--size-sweep", action="store_true",
+                   help="only time write-backs and loads of 64..32768 tokens on every path "
+                        "and layout (one JSON line per size on stderr), then exit")
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -102,6 +105,9 @@ def main():
         return
     if args.free_list_study:
         print(json.dumps(free_list_study(torch, kvt, workloads)))
+        return
+    if args.size_sweep:
+        print(json.dumps(size_sweep(torch, kvt, workloads)))
         return
     if args.tp_shared_study:
         print(json.dumps(tp_shared_study(torch, kvt, workloads, args.tp_shared_study)))
@@ -227,7 +233,11 @@ def main():
 
         def fixed_s(p):
             k, c = ops[(d, p)]
-            kern = calib.kernel_launch_us[d] + (k - 1) * calib.kernel_group_us[d] if k else 0.0
+            # the kernel path's further launches also leave the link idle; the
+            # staged path's overlap its copies
+            gap = calib.kernel_group_us[d] + (calib.kernel_link_gap_us[d]
+                                              if p == kvt.PATH_KERNEL else 0.0)
+            kern = calib.kernel_launch_us[d] + (k - 1) * gap if k else 0.0
             return (kern + c * calib.dma_copy_us[d]) * 1e-6
 
         def fit(p):
@@ -1324,6 +1334,71 @@ def tp_shared_study(torch, kvt, workloads, tp, reps=5):
         for p in pools:
             p.close()
     return out
+
+
+def size_sweep(torch, kvt, workloads):
+    """Request size against path: write-backs and loads of 64 to 32768 tokens of
+    the 78 x 1152 B MLA latent (contiguous device and host slots), in each host
+    layout, on the kernel path (write-backs on the default capped grid and on
+    a full grid), the copy engines, the staged path and AUTO (with the path it
+    chose). Per call: the median over 6-12 calls of HIP events around the call
+    on its stream, in microseconds; one JSON line per layout and size on
+    stderr, and the rows in the return value."""
+    shape = workloads.mla32k()
+    L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
+    S_dev, S_host = shape.device_slots, shape.host_slots
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S_dev * R, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, 3, l, c, torch)
+            bufs.append(b)
+    s = torch.cuda.Stream()
+
+    def call_us(fn, reps):
+        for _ in range(2):
+            fn()
+        s.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s)
+            fn()
+            e1.record(s)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        return statistics.median(ts)
+
+    rows = []
+    for lname, lay in LAYOUTS.items():
+        with kvt.KvPool(kvt.geometry(L, C, R, S_dev, S_host, ps, lay), bufs) as pool:
+            base = pool.calibration()
+            full = pool.calibration()
+            full.kernel_max_workgroups[:] = [0, 0]
+            for n in (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768):
+                d = np.arange(n, dtype=np.int64) + 128
+                h = np.arange(n, dtype=np.int64)
+                reps = 12 if n <= 4096 else 6
+                row = {"layout": lname, "tokens": n, "bytes": n * L * C * R}
+                for dname, dd in (("d2h", kvt.BACKUP), ("h2d", kvt.LOAD)):
+                    fn = ((lambda: pool.backup(d, h, 0, L, s)) if dd == kvt.BACKUP
+                          else (lambda: pool.load(d, h, 0, L, s)))
+                    legs = [("kernel", kvt.PATH_KERNEL, base), ("dma", kvt.PATH_DMA, base),
+                            ("staged", kvt.PATH_STAGED, base), ("auto", kvt.PATH_AUTO, base)]
+                    if dd == kvt.BACKUP:
+                        legs.insert(1, ("kernel_full_grid", kvt.PATH_KERNEL, full))
+                    for pname, p, cal in legs:
+                        pool.set_path(p)
+                        pool.set_calibration(cal)
+                        row["%s_%s_us" % (dname, pname)] = round(call_us(fn, reps), 1)
+                        if p == kvt.PATH_AUTO:
+                            row[dname + "_auto_chose"] = kvt.PATH_NAMES[pool.last_path(dd)]
+                    pool.set_calibration(base)
+                log("size sweep", json.dumps(row))
+                rows.append(row)
+    del bufs
+    torch.cuda.synchronize()
+    return {"size_sweep": rows}
 
 
 def free_list_study(torch, kvt, workloads, count=160):

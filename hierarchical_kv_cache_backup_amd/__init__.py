@@ -61,7 +61,10 @@ class kv_calib_t(ctypes.Structure):
                 ("index_zero_copy_max_bytes", ctypes.c_double * 2),
                 ("duplex_kernel_max_workgroups", ctypes.c_double * 2),
                 ("kernel_wg_gbps", ctypes.c_double * 2),
-                ("kernel_wg_row_ns", ctypes.c_double * 2)]
+                ("kernel_wg_row_ns", ctypes.c_double * 2),
+                ("kernel_wg_start_bytes", ctypes.c_double * 2),
+                ("kernel_wg_start_us", ctypes.c_double * 2),
+                ("kernel_link_gap_us", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):

@@ -136,8 +136,10 @@ typedef enum {
                                        else KV_EINVAL (host allocation differs across the group) */
 #define KV_F_LOAD_OVERLAP     0x4u /* loads on this pool run while compute kernels occupy the GPU
                                       (layer-wise load during the forward pass): the selector
-                                      charges each path the compute time it steals, and the
-                                      kernel path runs on a capped grid */
+                                      charges each path the compute time it steals, the
+                                      kernel path runs on a capped grid, and in page_first /
+                                      page_first_direct AUTO leaves out the staged path (it
+                                      lands every layer at the end of the load) */
 
 /* Geometry of one pool. Needs no GPU; the planner calls below take it alone. */
 typedef struct {
@@ -163,16 +165,23 @@ typedef struct {
 } kv_pool_desc_t;
 
 /* Selector calibration: modelled time of a call on each path.
- *   t_kernel = kernel_launch_us + (launches - 1) * kernel_group_us
+ *   t_kernel = kernel_launch_us
+ *              + (launches - 1) * (kernel_group_us + kernel_link_gap_us)
  *              + bytes / kernel_gbps
  *   t_dma    = copies * dma_copy_us + bytes / dma_gbps
  * kernel_launch_us is the fixed cost of a call's first launch (launch, index
  * staging, ramp), kernel_group_us the gap each further launch of the same
- * call adds. On a capped grid of W workgroups the kernel is limited by what W
+ * call adds, and kernel_link_gap_us the time the host link then also stands
+ * idle while one launch drains and the next ramps up (the staged path's
+ * launches overlap its copies, so it pays kernel_group_us alone). On a capped grid of W workgroups the kernel is limited by what W
  * workgroups move: bytes / kernel_gbps is replaced by the larger of itself and
  * (rows * kernel_wg_row_ns * 1e-3 + bytes / (kernel_wg_gbps * 1e3)) / W
- * (microseconds), rows being the call's n * layers * C rows. The rates are fitted per direction on the target machine to the
- * time a call takes less its modelled fixed costs.
+ * + kernel_wg_start_us * min(1, bytes / kernel_wg_start_bytes)
+ * (microseconds), rows being the call's n * layers * C rows: a capped grid
+ * moves the first kernel_wg_start_bytes of a call more slowly, which costs up
+ * to kernel_wg_start_us more (a capped grid has W < the launch's blocks).
+ * The rates are fitted per direction on the target machine to the time a
+ * call takes less its modelled fixed costs.
  * load_split_min_bytes: kv_load goes out in groups of consecutive layers, one
  * kernel launch (or one batch of copies) and one landed event per group; a
  * group is one layer when a layer of the request holds at least this many
@@ -237,6 +246,10 @@ typedef struct {
                                    direction is busy ([0] backup, [1] load; 0 = none) */
   double kernel_wg_gbps[2];     /* kernel path: bytes one workgroup moves per second (GB/s) */
   double kernel_wg_row_ns[2];   /* kernel path: a workgroup's extra time per row (ns) */
+  double kernel_wg_start_bytes[2]; /* capped kernel grid: bytes at the start of a call
+                                      that move more slowly (0 = none) */
+  double kernel_wg_start_us[2]; /* capped kernel grid: what those bytes cost in full (us) */
+  double kernel_link_gap_us[2]; /* kernel path: link idle time per further launch (us) */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

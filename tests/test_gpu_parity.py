@@ -500,6 +500,23 @@ def test_selector_models_capped_grids_per_workgroup(torch, stream):
     pool.set_calibration(c)
     run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
     assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
+    # the capped grid's slow start: 100 us over the first 16 MiB, of which the
+    # 8 MiB call pays half; the per-workgroup rate itself is made negligible
+    c.kernel_max_workgroups[0] = 24
+    c.kernel_wg_gbps[0] = 1e6
+    for start_us, want in ((0.0, kvt.PATH_KERNEL), (100.0, kvt.PATH_DMA)):
+        c.kernel_wg_start_bytes[0], c.kernel_wg_start_us[0] = 16 * 2 ** 20, start_us
+        pool.set_calibration(c)
+        run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+        assert pool.last_path(kvt.BACKUP) == want, start_us
+    c.kernel_max_workgroups[0] = 0                                # not capped: no slow start
+    pool.set_calibration(c)
+    run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+    assert pool.last_path(kvt.BACKUP) == kvt.PATH_KERNEL
+    c.kernel_wg_start_us[0] = -1.0
+    with pytest.raises(kvt.KvError):
+        pool.set_calibration(c)
+    c.kernel_wg_start_us[0] = 0.0
     c.kernel_wg_gbps[0] = 0.0
     with pytest.raises(kvt.KvError):
         pool.set_calibration(c)
@@ -717,6 +734,40 @@ def test_staged_margin_steers_selector(torch, stream):
     with pytest.raises(kvt.KvError):
         pool.set_calibration(c)
     pool.close()
+
+
+def test_overlapped_page_major_loads_skip_staged(torch, stream):
+    """With KV_F_LOAD_OVERLAP, AUTO leaves the staged path out of page_first /
+    page_first_direct loads (one unit: every layer would land at the end), but
+    keeps it for layer_first loads, whose layer groups land one by one. The
+    calibration makes the staged path the cheapest in every case; bytes match
+    the oracle."""
+    rng = np.random.default_rng(21)
+    d = rng.permutation(256)[:64].astype(np.int64)   # 64 single-slot device runs
+    h = np.arange(64, dtype=np.int64)                 # one host run
+    for layout in LAYOUTS:
+        g = Geometry(2, 1, 64, 256, 256, 8, layout)
+        bufs = device_buffers(g, seed=21)
+        for flags in (kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX,
+                      kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX | kvt.F_LOAD_OVERLAP):
+            pool = make_pool(g, bufs, kvt.PATH_AUTO, flags=flags)
+            c = pool.calibration()
+            # kernel: 10 us x (1 + 100) (x 1.65 overlapped); copy engines: one
+            # copy per device run at 100 us; staged: a copy per host extent
+            c.kernel_launch_us[:] = [10.0, 10.0]
+            c.kernel_group_us[:] = [7.0, 7.0]
+            c.dma_copy_us[:] = [100.0, 100.0]
+            c.kernel_gbps[:] = [1e6, 1e6]
+            c.dma_gbps[:] = [1e6, 1e6]
+            c.staged_gather_gbps = 1e6
+            c.duplex_kernel_penalty[:] = [100.0, 100.0]
+            pool.set_calibration(c)
+            pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+            print("overlap staged layout=%d flags=%d" % (layout, flags), flush=True)
+            run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+            skip = (flags & kvt.F_LOAD_OVERLAP) and layout != oracle.LAYER_FIRST
+            assert (pool.last_path(kvt.LOAD) == kvt.PATH_STAGED) != skip, (layout, flags)
+            pool.close()
 
 
 # ---- host pages handed out by the free list under churn --------------------------------
