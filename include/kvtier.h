@@ -367,10 +367,12 @@ int kv_backup(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, 
  * (see load_split_min_bytes), and after each group a landed event is recorded
  * on `stream`, so a consumer can start on layer l while later layers are
  * still in flight (compute/transfer overlap: HiCache system design page,
- * "data transfer optimisation"; "H2D stream -> KV_READY event -> compute
- * stream": runtime-boundary page, "why compute, H2D and D2H should stay in one
- * GPU execution domain"). The caller must not overwrite those host rows until
- * the load has completed. */
+ * "data transfer optimisation"; the load stream signalling a per-layer ready
+ * event that the compute stream waits on: runtime-boundary page, "why
+ * compute, H2D and D2H should stay in one GPU execution domain"). On the
+ * staged path a page_first / page_first_direct load is one group: every layer
+ * lands at its end (AUTO leaves that path out under KV_F_LOAD_OVERLAP). The
+ * caller must not overwrite those host rows until the load has completed. */
 int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
             int32_t layer_begin, int32_t layer_end, void *stream);
 
