@@ -101,6 +101,10 @@ SIGNATURES = {
     "kv_set_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
     "kv_get_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
     "kv_get_stats": (_I32, [_VP, ctypes.POINTER(kv_stats_t)]),
+    "kv_default_calibration": (_I32, [ctypes.POINTER(kv_calib_t)]),
+    "kv_model_path": (_I32, [ctypes.POINTER(kv_geometry_t), ctypes.POINTER(kv_calib_t), _I32,
+                             _P64, _P64, _I64, _I32, _I32, ctypes.c_uint32,
+                             ctypes.POINTER(ctypes.c_double)]),
     "kv_last_error": (ctypes.c_char_p, []),
     "kv_page_hashes": (_I64, [ctypes.POINTER(ctypes.c_int32), _I64, _I32, _PU64]),
     "kv_ghost_create": (_I32, [_I64, ctypes.POINTER(_VP)]),
@@ -215,6 +219,22 @@ def kv_count_dma_copies(geom, dev_idx, host_idx, layer_begin, layer_end):
     rc = _lib.kv_count_dma_copies(ctypes.byref(geom), dp, hp, len(d), layer_begin, layer_end,
                                   ctypes.byref(out))
     return rc, out.value
+
+
+def kv_default_calibration():
+    """Returns (status, kv_calib_t)."""
+    c = kv_calib_t()
+    return _lib.kv_default_calibration(ctypes.byref(c)), c
+
+
+def kv_model_path(geom, calib, direction, dev_idx, host_idx, layer_begin, layer_end, flags=0):
+    """Returns (path or status, [kernel_us, dma_us, staged_us])."""
+    d, dp = _idx(dev_idx)
+    h, hp = _idx(host_idx)
+    t = (ctypes.c_double * 3)()
+    rc = _lib.kv_model_path(ctypes.byref(geom), ctypes.byref(calib), direction, dp, hp, len(d),
+                            layer_begin, layer_end, flags, t)
+    return rc, list(t)
 
 
 def kv_pool_create(geom, device_buffer_ptrs, device=0, numa_node=-1, flags=F_CHECK_UNIQUE):

@@ -703,6 +703,101 @@ static int shared_backup(kv_pool *p, DirState &d, const int64_t *host_idx, int64
   return KV_OK;
 }
 
+// Layers per load group: loads go out in groups of `group` layers, each
+// followed by one event: one layer per group when a layer alone holds
+// load_split_min_bytes, else as many layers as reach it. Backups go out in one
+// group.
+static int32_t load_group(const Geom &g, const kv_calib_t &c, int dir, int64_t n, int32_t l0,
+                          int32_t l1) {
+  const int64_t layer_bytes = n * g.C * g.R;
+  if (dir != 1 || layer_bytes <= 0) return l1 - l0;
+  const double want = c.load_split_min_bytes / (double)layer_bytes;
+  return want <= 1.0 ? 1 : (want >= (double)(l1 - l0) ? l1 - l0 : (int32_t)std::ceil(want));
+}
+
+// The path selector (AUTO): the modelled time of a validated, non-empty
+// request on the kernel, copy-engine and staged paths (times[0..2], us), and
+// the path it takes. group: layers per load group (load_group); overlap: a
+// load flagged KV_F_LOAD_OVERLAP; duplex: the other direction is busy; cap:
+// the kernel paths' grid cap (kernel_cap). Leaves the request's runs, copies,
+// host runs and (where listed) staging extents in the vectors.
+static int32_t model_path(const Geom &g, const kv_calib_t &c, int dir, const int64_t *dev_idx,
+                          const int64_t *host_idx, int64_t n, int32_t l0, int32_t l1,
+                          int32_t group, bool overlap, bool duplex, uint32_t cap,
+                          std::vector<Run> *runs, std::vector<Copy> *copies,
+                          std::vector<int64_t> *run_start, std::vector<Extent> *extents_out,
+                          double times[3]) {
+  const int64_t nlc_all = (int64_t)(l1 - l0) * g.C;
+  const int64_t bytes = n * nlc_all * g.R;
+  const int32_t ngroups = (l1 - l0 + group - 1) / group;
+  build_runs(g, dev_idx, host_idx, n, runs);
+  build_copies(g, *runs, dev_idx, host_idx, copies);
+  host_runs(g, host_idx, n, run_start);
+  // Exact staging extents cost O(pairs x host runs) to list; past
+  // kExtentPlanLimit the upper bound pairs x runs prices the staged path (at
+  // one copy per extent it cannot win there anyway).
+  const double runs_x_pairs = (double)(run_start->size() - 1) * (double)nlc_all;
+  double extents = runs_x_pairs;
+  if (g.layout == KV_PAGE_FIRST || runs_x_pairs <= kExtentPlanLimit) {
+    build_extents(g, host_idx, n, *run_start, l0, l1, extents_out);
+    extents = (double)extents_out->size();
+  }
+  const double mb = (double)bytes;
+  // a capped grid moves what its workgroups can: blocks of 16 KiB of rows
+  // per launch, W = min(cap, blocks)
+  const int64_t rows_per_block =
+      g.R >= (int64_t)kChunksPerBlock * kChunkBytes ? 1 : (int64_t)kChunksPerBlock * kChunkBytes / g.R;
+  const double launch_rows = (double)n * std::min<int32_t>(group, l1 - l0) * g.C;
+  const double blocks = std::ceil(launch_rows / (double)rows_per_block);
+  const double wgs = cap > 0 ? std::min<double>(cap, blocks) : blocks;
+  const double rows_all = (double)n * nlc_all;
+  double t_wg = (rows_all * c.kernel_wg_row_ns[dir] * 1e-3 +
+                 mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
+  if (cap > 0 && blocks > cap)  // a capped grid's slow start
+    t_wg += c.kernel_wg_start_us[dir] *
+            (c.kernel_wg_start_bytes[dir] > 0 ? std::min(1.0, mb / c.kernel_wg_start_bytes[dir])
+                                              : 1.0);
+  double t_kernel = c.kernel_launch_us[dir] +
+                    (ngroups - 1) * (c.kernel_group_us[dir] + c.kernel_link_gap_us[dir]) +
+                    std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
+  double t_dma = (double)copies->size() * nlc_all * c.dma_copy_us[dir] +
+                 mb / (c.dma_gbps[dir] * 1e3);
+  // the staged path moves page-major layouts in one unit (see transfer); its
+  // device-side passes overlap the copies except for the smallest ramp
+  // chunk's (chunk_plan), and the ramp adds up to two chunks, each one more
+  // launch and one more copy where it splits an extent
+  const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
+  const double half = std::min(c.staged_chunk_bytes, mb / units);
+  const bool ramped = half * kRampMinDiv >= c.staged_chunk_bytes;
+  const double ramp = ramped ? 2.0 : 0.0;
+  const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units + ramp;
+  double t_staged = (extents + ramp) * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
+                    (chunks - 1) * c.kernel_group_us[dir] + mb / (c.dma_gbps[dir] * 1e3) +
+                    (ramped ? half / kRampFirst : half) / (c.staged_gather_gbps * 1e3);
+  if (overlap) {
+    t_kernel *= 1.0 + c.overlap_kernel_penalty;
+    t_dma *= 1.0 + c.overlap_dma_penalty;
+    t_staged *= 1.0 + c.overlap_dma_penalty;
+    // a page-major staged load is one unit: every layer lands at its end,
+    // which a layer-wise consumer cannot overlap
+    if (g.layout != KV_LAYER_FIRST) t_staged = std::numeric_limits<double>::infinity();
+  }
+  if (duplex) t_kernel *= 1.0 + c.duplex_kernel_penalty[dir];
+  int32_t path = KV_PATH_KERNEL;
+  double best = t_kernel;
+  if (t_dma < best) {
+    best = t_dma;
+    path = KV_PATH_DMA;
+  }
+  // the staged path also takes HBM bandwidth, compute units and a second
+  // stream, so it must win by a margin
+  if (t_staged < best * (1.0 - c.staged_min_gain)) path = KV_PATH_STAGED;
+  times[0] = t_kernel;
+  times[1] = t_dma;
+  times[2] = t_staged;
+  return path;
+}
+
 static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
                     int64_t n, int32_t l0, int32_t l1, void *stream) {
   const double t0 = now_us();
@@ -725,21 +820,12 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   hipStream_t s = (hipStream_t)stream;
   if (dir == 0 && p->reader) return shared_backup(p, d, host_idx, n, l0, l1, s, t0);
   const int64_t bytes = n * nlc_all * g.R;
-  const int64_t layer_bytes = n * g.C * g.R;
   kv_calib_t c;
   {
     std::lock_guard<std::mutex> cl(p->calib_mu);
     c = p->calib;
   }
-  // Loads go out in groups of `group` layers, each followed by one event: one
-  // layer per group when a layer alone holds load_split_min_bytes, else as many
-  // layers as reach it. Backups go out in one group.
-  int32_t group = l1 - l0;
-  if (dir == 1 && layer_bytes > 0) {
-    const double want = c.load_split_min_bytes / (double)layer_bytes;
-    group = want <= 1.0 ? 1 : (want >= (double)(l1 - l0) ? l1 - l0 : (int32_t)std::ceil(want));
-  }
-  const int32_t ngroups = (l1 - l0 + group - 1) / group;
+  int32_t group = load_group(g, c, dir, n, l0, l1);
   const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
 
   const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
@@ -750,70 +836,10 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   int32_t path = p->path.load();
   bool have_copies = false, have_host_runs = false;
   if (path == KV_PATH_AUTO) {
-    build_runs(g, dev_idx, host_idx, n, &d.runs);
-    build_copies(g, d.runs, dev_idx, host_idx, &d.copies);
-    have_copies = true;
-    host_runs(g, host_idx, n, &d.host_run_start);
-    have_host_runs = true;
-    // Exact staging extents cost O(pairs x host runs) to list; past
-    // kExtentPlanLimit the upper bound pairs x runs prices the staged path (at
-    // one copy per extent it cannot win there anyway).
-    const double runs_x_pairs = (double)(d.host_run_start.size() - 1) * (double)nlc_all;
-    double extents = runs_x_pairs;
-    if (g.layout == KV_PAGE_FIRST || runs_x_pairs <= kExtentPlanLimit) {
-      build_extents(g, host_idx, n, d.host_run_start, l0, l1, &d.extents);
-      extents = (double)d.extents.size();
-    }
-    const double mb = (double)bytes;
-    // a capped grid moves what its workgroups can: blocks of 16 KiB of rows
-    // per launch, W = min(cap, blocks)
-    const int64_t rows_per_block =
-        g.R >= (int64_t)kChunksPerBlock * kChunkBytes ? 1 : (int64_t)kChunksPerBlock * kChunkBytes / g.R;
-    const double launch_rows = (double)n * std::min<int32_t>(group, l1 - l0) * g.C;
-    const double blocks = std::ceil(launch_rows / (double)rows_per_block);
-    const double wgs = cap > 0 ? std::min<double>(cap, blocks) : blocks;
-    const double rows_all = (double)n * nlc_all;
-    double t_wg = (rows_all * c.kernel_wg_row_ns[dir] * 1e-3 +
-                   mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
-    if (cap > 0 && blocks > cap)  // a capped grid's slow start
-      t_wg += c.kernel_wg_start_us[dir] *
-              (c.kernel_wg_start_bytes[dir] > 0 ? std::min(1.0, mb / c.kernel_wg_start_bytes[dir])
-                                                : 1.0);
-    double t_kernel = c.kernel_launch_us[dir] +
-                      (ngroups - 1) * (c.kernel_group_us[dir] + c.kernel_link_gap_us[dir]) +
-                      std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
-    double t_dma = (double)d.copies.size() * nlc_all * c.dma_copy_us[dir] +
-                   mb / (c.dma_gbps[dir] * 1e3);
-    // the staged path moves page-major layouts in one unit (see below); its
-    // device-side passes overlap the copies except for the smallest ramp
-    // chunk's (chunk_plan), and the ramp adds up to two chunks, each one more
-    // launch and one more copy where it splits an extent
-    const double units = g.layout == KV_LAYER_FIRST ? (double)ngroups : 1.0;
-    const double half = std::min(c.staged_chunk_bytes, mb / units);
-    const bool ramped = half * kRampMinDiv >= c.staged_chunk_bytes;
-    const double ramp = ramped ? 2.0 : 0.0;
-    const double chunks = std::ceil(mb / c.staged_chunk_bytes) + units + ramp;
-    double t_staged = (extents + ramp) * c.dma_copy_us[dir] + c.kernel_launch_us[dir] +
-                      (chunks - 1) * c.kernel_group_us[dir] + mb / (c.dma_gbps[dir] * 1e3) +
-                      (ramped ? half / kRampFirst : half) / (c.staged_gather_gbps * 1e3);
-    if (overlap) {
-      t_kernel *= 1.0 + c.overlap_kernel_penalty;
-      t_dma *= 1.0 + c.overlap_dma_penalty;
-      t_staged *= 1.0 + c.overlap_dma_penalty;
-      // a page-major staged load is one unit: every layer lands at its end,
-      // which a layer-wise consumer cannot overlap
-      if (g.layout != KV_LAYER_FIRST) t_staged = std::numeric_limits<double>::infinity();
-    }
-    if (duplex) t_kernel *= 1.0 + c.duplex_kernel_penalty[dir];
-    path = KV_PATH_KERNEL;
-    double best = t_kernel;
-    if (t_dma < best) {
-      best = t_dma;
-      path = KV_PATH_DMA;
-    }
-    // the staged path also takes HBM bandwidth, compute units and a second
-    // stream, so it must win by a margin
-    if (t_staged < best * (1.0 - c.staged_min_gain)) path = KV_PATH_STAGED;
+    double times[3];
+    path = model_path(g, c, dir, dev_idx, host_idx, n, l0, l1, group, overlap, duplex, cap,
+                      &d.runs, &d.copies, &d.host_run_start, &d.extents, times);
+    have_copies = have_host_runs = true;
   }
   if (path == KV_PATH_KERNEL_LDS && g.R > kMaxLdsRowBytes) path = KV_PATH_KERNEL;
   // In page_first / page_first_direct a host page holds every layer of its
@@ -951,6 +977,39 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
 }
 
 // ---- C ABI ---------------------------------------------------------------------
+
+// Rejects a calibration with a figure out of range (KV_EINVAL).
+static int check_calibration(const kv_calib_t *c) {
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_gbps[d] > 0) || !(c->dma_gbps[d] > 0) || !(c->kernel_launch_us[d] >= 0) ||
+        !(c->kernel_group_us[d] >= 0) ||
+        !(c->dma_copy_us[d] >= 0))
+      return fail(KV_EINVAL, "calibration figures must be positive");
+  if (!(c->load_split_min_bytes >= 0)) return fail(KV_EINVAL, "load_split_min_bytes must be >= 0");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_max_workgroups[d] >= 0) || c->kernel_max_workgroups[d] > 4294967295.0)
+      return fail(KV_EINVAL, "kernel_max_workgroups must be in [0, 2^32)");
+  if (!(c->overlap_kernel_max_workgroups >= 0) || c->overlap_kernel_max_workgroups > 4294967295.0 ||
+      !(c->overlap_kernel_penalty >= 0) || !(c->overlap_dma_penalty >= 0))
+    return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
+  if (!(c->index_zero_copy_max_bytes[0] >= 0) || !(c->index_zero_copy_max_bytes[1] >= 0))
+    return fail(KV_EINVAL, "index_zero_copy_max_bytes must be >= 0");
+  for (int d = 0; d < 2; d++)
+    if (!(c->duplex_kernel_max_workgroups[d] >= 0) ||
+        c->duplex_kernel_max_workgroups[d] > 4294967295.0)
+      return fail(KV_EINVAL, "duplex_kernel_max_workgroups must be in [0, 2^32)");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_wg_gbps[d] > 0) || !(c->kernel_wg_row_ns[d] >= 0) ||
+        !(c->kernel_wg_start_bytes[d] >= 0) || !(c->kernel_wg_start_us[d] >= 0) ||
+        !(c->kernel_link_gap_us[d] >= 0))
+      return fail(KV_EINVAL, "kernel_wg_gbps must be > 0, kernel_wg_row_ns, kernel_wg_start_* "
+                             "and kernel_link_gap_us >= 0");
+  if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
+      !(c->staged_chunk_bytes >= 16) ||
+      !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
+    return fail(KV_EINVAL, "duplex penalty >= 0, staged chunk >= 16 bytes and gather rate > 0");
+  return KV_OK;
+}
 
 extern "C" {
 
@@ -1229,34 +1288,8 @@ int32_t kv_last_path(const kv_pool_t *p, int32_t direction) {
 
 int kv_set_calibration(kv_pool_t *p, const kv_calib_t *c) {
   if (!p || !c) return fail(KV_EINVAL, "pool and calibration must be non-null");
-  for (int d = 0; d < 2; d++)
-    if (!(c->kernel_gbps[d] > 0) || !(c->dma_gbps[d] > 0) || !(c->kernel_launch_us[d] >= 0) ||
-        !(c->kernel_group_us[d] >= 0) ||
-        !(c->dma_copy_us[d] >= 0))
-      return fail(KV_EINVAL, "calibration figures must be positive");
-  if (!(c->load_split_min_bytes >= 0)) return fail(KV_EINVAL, "load_split_min_bytes must be >= 0");
-  for (int d = 0; d < 2; d++)
-    if (!(c->kernel_max_workgroups[d] >= 0) || c->kernel_max_workgroups[d] > 4294967295.0)
-      return fail(KV_EINVAL, "kernel_max_workgroups must be in [0, 2^32)");
-  if (!(c->overlap_kernel_max_workgroups >= 0) || c->overlap_kernel_max_workgroups > 4294967295.0 ||
-      !(c->overlap_kernel_penalty >= 0) || !(c->overlap_dma_penalty >= 0))
-    return fail(KV_EINVAL, "overlap penalties must be >= 0 and the grid cap in [0, 2^32)");
-  if (!(c->index_zero_copy_max_bytes[0] >= 0) || !(c->index_zero_copy_max_bytes[1] >= 0))
-    return fail(KV_EINVAL, "index_zero_copy_max_bytes must be >= 0");
-  for (int d = 0; d < 2; d++)
-    if (!(c->duplex_kernel_max_workgroups[d] >= 0) ||
-        c->duplex_kernel_max_workgroups[d] > 4294967295.0)
-      return fail(KV_EINVAL, "duplex_kernel_max_workgroups must be in [0, 2^32)");
-  for (int d = 0; d < 2; d++)
-    if (!(c->kernel_wg_gbps[d] > 0) || !(c->kernel_wg_row_ns[d] >= 0) ||
-        !(c->kernel_wg_start_bytes[d] >= 0) || !(c->kernel_wg_start_us[d] >= 0) ||
-        !(c->kernel_link_gap_us[d] >= 0))
-      return fail(KV_EINVAL, "kernel_wg_gbps must be > 0, kernel_wg_row_ns, kernel_wg_start_* "
-                             "and kernel_link_gap_us >= 0");
-  if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
-      !(c->staged_chunk_bytes >= 16) ||
-      !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
-    return fail(KV_EINVAL, "duplex penalty >= 0, staged chunk >= 16 bytes and gather rate > 0");
+  const int rc = check_calibration(c);
+  if (rc) return rc;
   std::lock_guard<std::mutex> lock(p->calib_mu);
   p->calib = *c;
   return KV_OK;
@@ -1283,6 +1316,46 @@ int kv_get_stats(const kv_pool_t *p, kv_stats_t *out) {
     out->last_workgroups[d] = s.last_workgroups;
   }
   return KV_OK;
+}
+
+int kv_default_calibration(kv_calib_t *c) {
+  if (!c) return fail(KV_EINVAL, "calibration is null");
+  default_calibration(c);
+  return KV_OK;
+}
+
+int32_t kv_model_path(const kv_geometry_t *geom, const kv_calib_t *calib, int32_t direction,
+                      const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+                      int32_t layer_begin, int32_t layer_end, uint32_t flags,
+                      double *times_us) {
+  return guarded("kv_model_path", [&]() -> int {
+    if (!geom || !calib || !times_us)
+      return fail(KV_EINVAL, "geom, calib and times_us must be non-null");
+    if (direction != 0 && direction != 1) return fail(KV_EINVAL, "direction must be 0 or 1");
+    Geom g;
+    std::string why;
+    int rc = make_geom(geom, &g, &why);
+    if (rc) return fail(rc, why);
+    rc = check_calibration(calib);
+    if (rc) return rc;
+    rc = validate(g, direction, dev_idx, host_idx, n, layer_begin, layer_end, false, nullptr,
+                  &why);
+    if (rc) return fail(rc, why);
+    if (n == 0 || layer_begin == layer_end) return fail(KV_EINVAL, "empty request");
+    if (n * (int64_t)(layer_end - layer_begin) * g.C >= kMaxRowsPerLaunch)
+      return fail(KV_EINVAL, "request has >= 2^31 rows; split it into several calls");
+    const bool overlap = direction == 1 && (flags & KV_F_LOAD_OVERLAP) != 0;
+    const bool duplex = (flags & KV_F_DUPLEX) != 0;
+    const uint32_t cap = kernel_cap(*calib, direction, overlap, duplex, true);
+    const int32_t group = load_group(g, *calib, direction, n, layer_begin, layer_end);
+    std::vector<Run> runs;
+    std::vector<Copy> copies;
+    std::vector<int64_t> run_start;
+    std::vector<Extent> extents;
+    return (int)model_path(g, *calib, direction, dev_idx, host_idx, n, layer_begin, layer_end,
+                           group, overlap, duplex, cap, &runs, &copies, &run_start, &extents,
+                           times_us);
+  });
 }
 
 }  // extern "C"

@@ -435,6 +435,23 @@ typedef struct {
 
 int kv_get_stats(const kv_pool_t *pool, kv_stats_t *out);
 
+/* The library's default calibration (the figures a new pool starts with). */
+int kv_default_calibration(kv_calib_t *calib);
+
+/* The path selector without a GPU: for a request as kv_backup (direction 0)
+ * or kv_load (1) would get it on a pool of this geometry and calibration,
+ * writes the modelled times of the kernel, copy-engine and staged paths to
+ * times_us[0..2] (microseconds; the staged one may be +infinity where AUTO
+ * leaves that path out) and returns the path AUTO takes (KV_PATH_KERNEL,
+ * KV_PATH_DMA or KV_PATH_STAGED). flags: KV_F_LOAD_OVERLAP as on a pool;
+ * KV_F_DUPLEX stands for the other direction being busy. The request is
+ * validated as kv_validate does without the uniqueness check; an empty
+ * request, a bad argument or calibration: KV_EINVAL (or the validation code). */
+int32_t kv_model_path(const kv_geometry_t *geom, const kv_calib_t *calib, int32_t direction,
+                      const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
+                      int32_t layer_begin, int32_t layer_end, uint32_t flags,
+                      double *times_us);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char *kv_last_error(void);
 
