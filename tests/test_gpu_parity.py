@@ -770,6 +770,32 @@ def test_overlapped_page_major_loads_skip_staged(torch, stream):
             pool.close()
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_auto_takes_the_path_the_model_names(torch, stream, layout):
+    """kv_model_path (host only) and a pool's AUTO choice agree on the same
+    request and calibration, for small and fragmented requests in both
+    directions; the bytes match the oracle."""
+    g = Geometry(6, 2, 1024, 512, 512, 16, layout)
+    bufs = device_buffers(g, seed=22)
+    rng = np.random.default_rng(22 + layout)
+    geom = kvt.geometry(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout)
+    pool = make_pool(g, bufs, kvt.PATH_AUTO)
+    calib = pool.calibration()
+    for kind in ("contiguous", "random", "pages"):
+        d, h = _request(rng, g, kind)
+        for dirn in (kvt.BACKUP, kvt.LOAD):
+            want, _ = kvt.kv_model_path(geom, calib, dirn, d, h, 0, g.L)
+            assert want in (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED)
+            print("model vs auto layout=%d kind=%s dir=%d" % (layout, kind, dirn), flush=True)
+            if dirn == kvt.BACKUP:
+                run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+            else:
+                pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+                run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+            assert pool.last_path(dirn) == want, (kind, dirn)
+    pool.close()
+
+
 # ---- host pages handed out by the free list under churn --------------------------------
 
 @pytest.mark.parametrize("policy", (kvt.FREE_FIFO, kvt.FREE_LIFO), ids=["fifo", "lifo"])
