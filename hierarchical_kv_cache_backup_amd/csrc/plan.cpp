@@ -326,21 +326,31 @@ static int count_common(const kv_geometry_t *geom, const int64_t *dev_idx, const
     set_error(why);
     return rc;
   }
-  int64_t per_lc = 0;
+  int64_t total = 0;
   try {
     std::vector<Run> runs;
     build_runs(g, dev_idx, host_idx, n, &runs);
-    per_lc = (int64_t)runs.size();
+    total = (int64_t)runs.size() * (int64_t)(l1 - l0) * g.C;
     if (merge2d) {
       std::vector<Copy> copies;
       build_copies(g, runs, dev_idx, host_idx, &copies);
-      per_lc = (int64_t)copies.size();
+      // a 2-D copy whose region would leave the host pool or the device
+      // buffer sends its last line as a call of its own (copy_calls)
+      total = 0;
+      for (const Copy &c : copies) {
+        if (c.lines == 1) {
+          total += (int64_t)(l1 - l0) * g.C;
+          continue;
+        }
+        for (int64_t lc = (int64_t)l0 * g.C; lc < (int64_t)l1 * g.C; lc++)
+          total += copy_calls(g, c, lc);
+      }
     }
   } catch (const std::bad_alloc &) {
     set_error("out of host memory while counting segments");
     return KV_ENOMEM;
   }
-  *out = per_lc * (int64_t)(l1 - l0) * g.C;
+  *out = total;
   return KV_OK;
 }
 

@@ -88,6 +88,30 @@ struct Copy {
 void build_copies(const Geom &g, const std::vector<Run> &runs, const int64_t *dev_idx,
                   const int64_t *host_idx, std::vector<Copy> *copies);
 
+// A 2-D copy-engine call names a region of pitch x lines bytes on each side,
+// although its last line is only len rows long. Lines of copy c on (layer,
+// component) buffer lc that can go out as one 2-D call whose whole region lies
+// inside the host pool (L*C*S_host rows) and inside the device buffer (S_dev
+// rows): min(lines, lines that fit on each side). Every line itself lies
+// inside both, so at most the last line is left over; it goes out as a 1-D
+// copy. 1 for a 1-D copy.
+inline int64_t copy_region_lines(const Geom &g, const Copy &c, int64_t lc) {
+  if (c.lines <= 1) return c.lines;
+  const int64_t host_rows = (int64_t)g.L * g.C * g.S_host;
+  const int64_t fit_h = (host_rows - (lc * g.lc_stride + c.key0)) / c.key_pitch;
+  const int64_t fit_d = (g.S_dev - c.dev0) / c.dev_pitch;
+  const int64_t fit = fit_h < fit_d ? fit_h : fit_d;
+  return fit < c.lines ? fit : c.lines;
+}
+
+// Copy-engine calls copy c takes on buffer lc: one 2-D call over the lines
+// copy_region_lines allows (when that is 2 or more) and one 1-D call per line
+// left, else one 1-D call per line.
+inline int64_t copy_calls(const Geom &g, const Copy &c, int64_t lc) {
+  const int64_t fit = copy_region_lines(g, c, lc);
+  return fit >= 2 ? 1 + (c.lines - fit) : c.lines;
+}
+
 // Staged path: the rows (i, l, c), l in [la, lb), are enumerated in the
 // transfer kernels' host-order walk (groups of G request positions, then
 // (pair, position) inside a group; G = n, 1 or page_size for layer_first,

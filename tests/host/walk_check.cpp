@@ -43,6 +43,7 @@ void set_error(const std::string &) {}
 using namespace kvt;
 
 static int failures = 0;
+static int64_t regions_split = 0;  // 2-D copies whose last line went out on its own
 #define CHECK(cond, ...)                                   \
   do {                                                     \
     if (!(cond)) {                                         \
@@ -169,7 +170,8 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
 // per extent piece, as the executor issues them.
 static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int64_t *h, int64_t n,
                           int32_t la, int32_t lb, bool to_host, std::vector<uint8_t> &cover,
-                          int64_t chunk_rows, bool ramp_first, bool ramp_last) {
+                          int64_t chunk_rows, bool ramp_first, bool ramp_last,
+                          uint32_t cap) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -218,20 +220,52 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
   for (int64_t len : chunks) {
     const int64_t r1 = r0 + len;
     set_row_range(&a, (uint32_t)r0, (uint32_t)r1);
-    auto dense = [&](bool gather) {  // the dense kernel, row by row
-      for (int64_t r = a.row_begin; r < a.row_end; r++) {
-        uint32_t i = 0, lc = 0;
-        walk_row(a, (uint32_t)r, i, lc);
-        uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R;
-        uint8_t *sv = stage.data() + (r - a.row_begin) * g.R;
-        CHECK((r - a.row_begin + 1) * g.R <= (int64_t)stage.size(), "stage overrun");
-        if (gather)
-          std::memcpy(sv, dv, g.R);
-        else
-          std::memcpy(dv, sv, g.R);
-        for (int64_t k = 0; k < g.R / kChunkBytes; k++)
-          cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + k]++;
-      }
+    // the device-side pass (stage_rows): waves take tasks of rows_per_task walk
+    // rows, kStageRows rows at a time, stepping the walk position with
+    // walk_next; lanes move 16-byte chunks k0 + j*64 + lane of each row
+    auto dense = [&](bool gather) {
+      const uint32_t rpt = stage_rows_per_task(g.R);
+      const uint32_t blocks = stage_blocks(a, rpt);
+      const uint32_t grid = grid_for(blocks, cap);
+      const uint32_t cpr16 = (uint32_t)(g.R / 16);
+      const uint32_t ntasks = (a.row_end - a.row_begin + rpt - 1) / rpt;
+      CHECK((uint64_t)blocks * kWavesPerBlock >= ntasks, "stage grid too small");
+      for (uint32_t b = 0; b < grid; b++)
+        for (uint32_t wave = 0; wave < kWavesPerBlock; wave++)
+          for (uint32_t t = b * kWavesPerBlock + wave; t < ntasks; t += grid * kWavesPerBlock) {
+            const uint32_t r0 = a.row_begin + t * rpt;
+            const uint32_t r1 = std::min(r0 + rpt, a.row_end);
+            WalkPos w = walk_at(a, r0);
+            for (uint32_t r = r0; r < r1; r += kStageRows) {
+              const uint32_t mrows = std::min((uint32_t)kStageRows, r1 - r);
+              for (uint32_t u = 0; u < mrows; u++) {
+                uint32_t i = 0, lc = 0;
+                walk_row(a, r + u, i, lc);  // the stepped position must be the walk's
+                CHECK(w.r == r + u && w.base + w.pos == i && w.lc == lc,
+                      "stepped walk differs at row %u", r + u);
+                CHECK(i < a.n && lc < a.nlc, "stage walk out of range");
+                if (!(i < a.n && lc < a.nlc)) return;
+                const int64_t srow = (int64_t)(r + u - a.row_begin);
+                CHECK((srow + 1) * g.R <= (int64_t)stage.size(), "stage overrun");
+                uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R;
+                uint8_t *sv = stage.data() + srow * g.R;
+                for (uint32_t k0 = 0; k0 < cpr16; k0 += 64 * kStageChunks)
+                  for (int j = 0; j < kStageChunks; j++)
+                    for (uint32_t lane = 0; lane < 64; lane++) {
+                      const uint32_t k = k0 + j * 64 + lane;
+                      if (k >= cpr16) continue;
+                      if (gather)
+                        std::memcpy(sv + 16 * k, dv + 16 * k, 16);
+                      else
+                        std::memcpy(dv + 16 * k, sv + 16 * k, 16);
+                      for (int h8 = 0; h8 < 2; h8++)
+                        cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) +
+                              2 * k + h8]++;
+                    }
+                walk_next(a, w);
+              }
+            }
+          }
     };
     if (to_host) dense(true);
     while (x < ext.size() && ext[x].walk0 < r1) {
@@ -264,10 +298,28 @@ static void replay_dma(Mirror &m, const int64_t *d, const int64_t *h, int64_t n,
   int64_t total = 0;
   for (const Run &r : runs) total += r.len;
   CHECK(total == n, "runs cover %lld of %lld positions", (long long)total, (long long)n);
+  int64_t calls = 0;
   for (int32_t l = l0; l < l1; l++)
     for (int32_t c = 0; c < g.C; c++)
       for (const Copy &cp : copies) {
         CHECK(cp.lines == 1 || (cp.dev_pitch >= cp.len && cp.key_pitch >= cp.len), "bad pitch");
+        // the region a 2-D call names is pitch x height on each side: it must lie
+        // inside the host pool and the device buffer, not only its lines
+        const int64_t lc = (int64_t)l * g.C + c;
+        const int64_t region = copy_region_lines(g, cp, lc);
+        CHECK(region >= 1 && region <= cp.lines && region >= cp.lines - 1,
+              "2-D region of %lld lines for a copy of %lld", (long long)region,
+              (long long)cp.lines);
+        if (region >= 2) {
+          const int64_t host_end = (lc * g.lc_stride + cp.key0 + region * cp.key_pitch) * g.R;
+          const int64_t dev_end = (cp.dev0 + region * cp.dev_pitch) * g.R;
+          CHECK(host_end <= (int64_t)m.host.size(), "2-D host region ends %lld bytes past the pool",
+                (long long)(host_end - (int64_t)m.host.size()));
+          CHECK(dev_end <= g.S_dev * g.R, "2-D device region ends %lld bytes past the buffer",
+                (long long)(dev_end - g.S_dev * g.R));
+          if (region < cp.lines) regions_split++;
+        }
+        calls += copy_calls(g, cp, lc);
         for (int64_t j = 0; j < cp.lines; j++) {
           const int64_t dev_off = (cp.dev0 + j * cp.dev_pitch) * g.R;
           const int64_t host_off = ((int64_t)(l * g.C + c) * g.lc_stride + cp.key0 + j * cp.key_pitch) * g.R;
@@ -282,7 +334,100 @@ static void replay_dma(Mirror &m, const int64_t *d, const int64_t *h, int64_t n,
             std::memcpy(dp, hp, w);
         }
       }
-  *copies_out = (int64_t)copies.size() * (l1 - l0) * g.C;
+  *copies_out = calls;
+}
+
+// Replays every executor's plan of one request (both directions) on CPU
+// mirrors and compares the bytes with the oracle's.
+static int64_t check_case(const kv_geometry_t &kg, const Geom &g, const std::vector<int64_t> &d,
+                          const std::vector<int64_t> &h, int32_t l0, int32_t l1, int cs,
+                          std::mt19937_64 &rng) {
+  auto uni = [&](int64_t lo, int64_t hi) {  // inclusive
+    return lo + (int64_t)(rng() % (uint64_t)(hi - lo + 1));
+  };
+  const int64_t n = (int64_t)d.size();
+  const int64_t nlc = (int64_t)(l1 - l0) * g.C;
+  int64_t checked = 0;
+  Mirror base;
+  base.g = g;
+  base.dev.resize((size_t)g.L * g.C);
+  for (auto &b : base.dev) {
+    b.resize((size_t)(g.S_dev * g.R));
+    for (auto &x : b) x = (uint8_t)rng();
+  }
+  base.host.resize((size_t)((int64_t)g.L * g.C * g.S_host * g.R));
+  for (auto &x : base.host) x = (uint8_t)rng();
+
+  // expected results from the oracle
+  Mirror want_b = base, want_l = base;
+  {
+    auto p = want_b.ptrs();
+    CHECK(kvo_backup(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, p.data(),
+                     want_b.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle backup");
+    auto q = want_l.ptrs();
+    CHECK(kvo_load(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, q.data(),
+                   want_l.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle load");
+  }
+  int64_t seg = -1;
+  CHECK(kv_count_segments(&kg, d.data(), h.data(), n, l0, l1, &seg) == KV_OK, "count");
+  CHECK(seg == kvo_count_segments(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, d.data(),
+                                  h.data(), n, l0, l1),
+        "segment count differs from the oracle");
+
+  std::vector<int64_t> tok(2 * (size_t)n);
+  for (int64_t i = 0; i < n; i++) {
+    tok[2 * i] = d[i];
+    tok[2 * i + 1] = host_key(g, h[i]);
+  }
+  const int64_t cells = n * g.L * g.C * (g.R / kChunkBytes);
+  for (int dir = 0; dir < 2; dir++) {
+    const bool to_host = dir == 0;
+    const Mirror &want = to_host ? want_b : want_l;
+    for (int variant = 0; variant < 5; variant++) {
+      if (n == 0 || nlc == 0) break;
+      if (variant == 2 && g.R > kMaxLdsRowBytes) continue;
+      Mirror m = base;
+      std::vector<uint8_t> cover((size_t)cells, 0);
+      int64_t copies = 0;
+      const uint32_t cap = (uint32_t)(std::vector<int>{0, 1, 3, 64})[uni(0, 3)];
+      if (variant == 0) {
+        replay_rows(m, tok, n, l0, l1, to_host, cover, cap);
+      } else if (variant == 1) {
+        for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover, cap);
+      } else if (variant == 2) {
+        replay_tiles(m, tok, n, l0, l1, to_host, cover, cap);
+      } else if (variant == 4) {
+        const int64_t walk = n * (int64_t)(l1 - l0) * g.C;
+        const int64_t chunk = std::max<int64_t>(1, (std::vector<int64_t>{1, 7, walk / 3 + 1, walk})[uni(0, 3)]);
+        const int ramp = (int)uni(0, 2);  // none, first, last
+        replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk, ramp == 1, ramp == 2,
+                      cap);
+      } else {
+        replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
+        int64_t counted = -1;
+        CHECK(kv_count_dma_copies(&kg, d.data(), h.data(), n, l0, l1, &counted) == KV_OK &&
+                  counted == copies,
+              "dma copy count");
+        CHECK(copies <= seg, "more copies than segments");
+      }
+      if (variant != 3) {  // every kernel-driven variant moves each chunk exactly once
+        for (int64_t i = 0; i < n; i++)
+          for (int32_t lc = 0; lc < g.L * g.C; lc++)
+            for (int64_t k = 0; k < g.R / kChunkBytes; k++) {
+              const bool inside = lc >= l0 * g.C && lc < l1 * g.C;
+              const uint8_t cnt = cover[(size_t)((i * g.L * g.C + lc) * (g.R / kChunkBytes) + k)];
+              CHECK(cnt == (inside ? 1 : 0), "chunk moved %d times (variant %d)", cnt, variant);
+            }
+      }
+      CHECK(m.host == want.host, "host pool differs from oracle (case %d dir %d variant %d)", cs,
+            dir, variant);
+      for (size_t b = 0; b < m.dev.size(); b++)
+        CHECK(m.dev[b] == want.dev[b], "device buffer %zu differs (case %d dir %d variant %d)", b,
+              cs, dir, variant);
+      checked++;
+    }
+  }
+  return checked;
 }
 
 int main(int argc, char **argv) {
@@ -292,6 +437,39 @@ int main(int argc, char **argv) {
     return lo + (int64_t)(rng() % (uint64_t)(hi - lo + 1));
   };
   int64_t checked = 0;
+  // Directed: uniform-pitch runs that end at the last host slot or device slot,
+  // so a 2-D copy's pitch x height region would run past the host pool or the
+  // device buffer although its last line fits: runs of 16 slots at pitch 32
+  // from slot 16 (layer_first, the region ends past both), and a request on the
+  // last 4 pages of a page_first_direct pool of 78 layers (past the host pool).
+  {
+    struct Directed {
+      int32_t L, C, ps, layout;
+      int64_t R, S_dev, S_host;
+    };
+    const Directed cases_d[] = {{3, 2, 16, 0, 48, 640, 640}, {78, 1, 64, 2, 16, 256, 512}};
+    for (int k = 0; k < 2; k++) {
+      const Directed &x = cases_d[k];
+      const kv_geometry_t kg{x.L, x.C, x.R, x.S_dev, x.S_host, x.ps, x.layout};
+      Geom g;
+      std::string why;
+      CHECK(make_geom(&kg, &g, &why) == KV_OK, "directed geometry: %s", why.c_str());
+      std::vector<int64_t> d, h;
+      if (k == 0) {
+        for (int64_t s0 = 16; s0 + 16 <= 640; s0 += 32)
+          for (int64_t j = 0; j < 16; j++) d.push_back(s0 + j);
+        h = d;
+      } else {
+        for (int64_t j = 0; j < 256; j++) {
+          d.push_back(j);
+          h.push_back(256 + j);
+        }
+      }
+      const int64_t before = regions_split;
+      checked += check_case(kg, g, d, h, 0, x.L, -1 - k, rng);
+      CHECK(regions_split > before, "directed case %d split no 2-D region", k);
+    }
+  }
   for (int cs = 0; cs < cases; cs++) {
     kv_geometry_t kg{};
     kg.num_layers = (int32_t)uni(1, 5);
@@ -330,87 +508,9 @@ int main(int argc, char **argv) {
     }
     std::vector<int64_t> d(dv.begin(), dv.begin() + n), h(hv.begin(), hv.begin() + n);
     const int32_t l0 = (int32_t)uni(0, g.L), l1 = (int32_t)uni(l0, g.L);
-    const int64_t nlc = (int64_t)(l1 - l0) * g.C;
-
-    Mirror base;
-    base.g = g;
-    base.dev.resize((size_t)g.L * g.C);
-    for (auto &b : base.dev) {
-      b.resize((size_t)(g.S_dev * g.R));
-      for (auto &x : b) x = (uint8_t)rng();
-    }
-    base.host.resize((size_t)((int64_t)g.L * g.C * g.S_host * g.R));
-    for (auto &x : base.host) x = (uint8_t)rng();
-
-    // expected results from the oracle
-    Mirror want_b = base, want_l = base;
-    {
-      auto p = want_b.ptrs();
-      CHECK(kvo_backup(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, p.data(),
-                       want_b.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle backup");
-      auto q = want_l.ptrs();
-      CHECK(kvo_load(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, q.data(),
-                     want_l.host.data(), d.data(), h.data(), n, l0, l1, 1) == 0, "oracle load");
-    }
-    int64_t seg = -1;
-    CHECK(kv_count_segments(&kg, d.data(), h.data(), n, l0, l1, &seg) == KV_OK, "count");
-    CHECK(seg == kvo_count_segments(g.L, g.C, g.R, g.S_dev, g.S_host, g.ps, g.layout, d.data(),
-                                    h.data(), n, l0, l1),
-          "segment count differs from the oracle");
-
-    std::vector<int64_t> tok(2 * (size_t)n);
-    for (int64_t i = 0; i < n; i++) {
-      tok[2 * i] = d[i];
-      tok[2 * i + 1] = host_key(g, h[i]);
-    }
-    const int64_t cells = n * g.L * g.C * (g.R / kChunkBytes);
-    for (int dir = 0; dir < 2; dir++) {
-      const bool to_host = dir == 0;
-      const Mirror &want = to_host ? want_b : want_l;
-      for (int variant = 0; variant < 5; variant++) {
-        if (n == 0 || nlc == 0) break;
-        if (variant == 2 && g.R > kMaxLdsRowBytes) continue;
-        Mirror m = base;
-        std::vector<uint8_t> cover((size_t)cells, 0);
-        int64_t copies = 0;
-        const uint32_t cap = (uint32_t)(std::vector<int>{0, 1, 3, 64})[uni(0, 3)];
-        if (variant == 0) {
-          replay_rows(m, tok, n, l0, l1, to_host, cover, cap);
-        } else if (variant == 1) {
-          for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover, cap);
-        } else if (variant == 2) {
-          replay_tiles(m, tok, n, l0, l1, to_host, cover, cap);
-        } else if (variant == 4) {
-          const int64_t walk = n * (int64_t)(l1 - l0) * g.C;
-          const int64_t chunk = std::max<int64_t>(1, (std::vector<int64_t>{1, 7, walk / 3 + 1, walk})[uni(0, 3)]);
-          const int ramp = (int)uni(0, 2);  // none, first, last
-          replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk, ramp == 1, ramp == 2);
-        } else {
-          replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
-          int64_t counted = -1;
-          CHECK(kv_count_dma_copies(&kg, d.data(), h.data(), n, l0, l1, &counted) == KV_OK &&
-                    counted == copies,
-                "dma copy count");
-          CHECK(copies <= seg, "more copies than segments");
-        }
-        if (variant != 3) {  // every kernel-driven variant moves each chunk exactly once
-          for (int64_t i = 0; i < n; i++)
-            for (int32_t lc = 0; lc < g.L * g.C; lc++)
-              for (int64_t k = 0; k < g.R / kChunkBytes; k++) {
-                const bool inside = lc >= l0 * g.C && lc < l1 * g.C;
-                const uint8_t cnt = cover[(size_t)((i * g.L * g.C + lc) * (g.R / kChunkBytes) + k)];
-                CHECK(cnt == (inside ? 1 : 0), "chunk moved %d times (variant %d)", cnt, variant);
-              }
-        }
-        CHECK(m.host == want.host, "host pool differs from oracle (case %d dir %d variant %d)", cs,
-              dir, variant);
-        for (size_t b = 0; b < m.dev.size(); b++)
-          CHECK(m.dev[b] == want.dev[b], "device buffer %zu differs (case %d dir %d variant %d)", b,
-                cs, dir, variant);
-        checked++;
-      }
-    }
+    checked += check_case(kg, g, d, h, l0, l1, cs, rng);
   }
-  std::printf("walk_check: %lld replays, %d failures\n", (long long)checked, failures);
+  std::printf("walk_check: %lld replays, %lld 2-D regions split, %d failures\n",
+              (long long)checked, (long long)regions_split, failures);
   return failures == 0 ? 0 : 1;
 }

@@ -151,7 +151,7 @@ def test_segment_counts_match_oracle(kvt):
         else:  # whole pages in random order on the device
             d = np.arange(n)
             h = np.arange(n)
-            pages = rng.permutation(max(1, n // ps))
+            pages = rng.permutation(max(1, -(-n // ps)))
             d = np.concatenate([np.arange(p * ps, p * ps + ps) for p in pages])[:n] if n else d
         l0 = int(rng.integers(0, g.L + 1))
         l1 = int(rng.integers(l0, g.L + 1))
@@ -164,14 +164,18 @@ def test_segment_counts_match_oracle(kvt):
 def test_pages_example_through_library(kvt):
     """32K tokens, page 64, 78 layers: 39,936 segments page_first_direct, 78 layer_first;
     the copy-engine plan merges page_first_direct's uniform-stride pages into one
-    2-D copy per layer."""
+    2-D copy per layer. The pool holds exactly these 512 pages, so the 2-D region
+    of layer l (512 pitches of 78 x 64 rows from row l x 64) ends l x 64 rows past
+    the pool: every layer but the first sends its last page as a call of its own."""
     n = 32768
     d = np.arange(n) + 8192
     h = np.arange(n)
-    for layout, segs in ((2, 39936), (0, 78)):
+    for layout, segs, copies in ((2, 39936, 1 + 77 * 2), (0, 78, 78)):
         kg = kvt.geometry(78, 1, 1152, 65536, n, 64, layout)
         assert kvt.kv_count_segments(kg, d, h, 0, 78) == (0, segs)
-        assert kvt.kv_count_dma_copies(kg, d, h, 0, 78) == (0, 78)
+        assert kvt.kv_count_dma_copies(kg, d, h, 0, 78) == (0, copies)
+    kg = kvt.geometry(78, 1, 1152, 65536, 2 * n, 64, 2)   # a pool twice the prefix
+    assert kvt.kv_count_dma_copies(kg, d, h, 0, 78) == (0, 78)
 
 
 def test_replay_driver_under_sanitizers(tmp_path):
@@ -252,3 +256,43 @@ def test_allocator_and_ghost_list_threads_under_tsan(tmp_path):
     assert res.returncode == 0, res.stdout + res.stderr
     assert "0 failures" in res.stdout
     assert "ThreadSanitizer" not in res.stderr, res.stderr
+
+
+def test_binding_refuses_index_arrays_it_would_read_past(kvt):
+    """The same-name wrappers check that dev_idx and host_idx are equally long
+    and that n does not exceed them, before the C call reads the arrays."""
+    kg = kvt.geometry(2, 1, 16, 8, 8, 4, 0)
+    with pytest.raises(ValueError):
+        kvt.kv_validate(kg, 0, [1, 2, 3], [1, 2], 0, 1)
+    with pytest.raises(ValueError):
+        kvt.kv_validate(kg, 0, [1, 2], [1, 2], 0, 1, n=3)
+    with pytest.raises(ValueError):
+        kvt.kv_count_segments(kg, [1, 2, 3], [1], 0, 1)
+    with pytest.raises(ValueError):
+        kvt.kv_backup(None, [1, 2], [1], 0, 1)
+    with pytest.raises(ValueError):
+        kvt.kv_load(None, [1], [1], 0, 1, n=2)
+    assert kvt.kv_validate(kg, 0, [1, 2], [1, 2], 0, 1, n=1) == kvt.OK
+    assert kvt.kv_validate(kg, 0, [1], [1], 0, 1, n=-1) == kvt.EINVAL
+
+
+def test_dma_copy_count_splits_regions_past_the_pool(kvt):
+    """A 2-D copy whose pitch x height region would end past the host pool or
+    the device buffer sends its last line on its own: runs of 16 slots at pitch
+    32 from slot 16 of a 640-slot pool are one 2-D copy of 20 lines per buffer
+    whose device region ends 16 rows past the buffer (every buffer splits), and
+    the last 4 pages of a 78-layer page_first_direct pool are one 4-line copy
+    per layer whose host region ends l*64 rows past the pool on layer l (all
+    but layer 0 split)."""
+    d = np.concatenate([np.arange(s, s + 16) for s in range(16, 640, 32)])
+    kg = kvt.geometry(3, 2, 48, 640, 640, 16, 0)
+    assert kvt.kv_count_segments(kg, d, d, 0, 3) == (0, 20 * 6)
+    assert kvt.kv_count_dma_copies(kg, d, d, 0, 3) == (0, 2 * 6)
+    kg = kvt.geometry(3, 2, 48, 656, 640, 16, 0)     # device buffer holds the region
+    assert kvt.kv_count_dma_copies(kg, d, d, 0, 3) == (0, 1 * 5 + 2)
+    kg = kvt.geometry(78, 1, 16, 256, 512, 64, 2)
+    d, h = np.arange(256), np.arange(256, 512)
+    assert kvt.kv_count_segments(kg, d, h, 0, 78) == (0, 4 * 78)
+    assert kvt.kv_count_dma_copies(kg, d, h, 0, 78) == (0, 1 + 77 * 2)
+    assert kvt.kv_count_dma_copies(kg, d, h, 1, 78) == (0, 77 * 2)
+    assert kvt.kv_count_dma_copies(kg, d, h, 0, 1) == (0, 1)
