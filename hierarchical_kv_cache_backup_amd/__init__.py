@@ -195,17 +195,14 @@ def kv_host_row(geom, layer, comp, host_slot):
 
 def kv_validate(geom, direction, dev_idx, host_idx, layer_begin, layer_end, check_unique=True,
                 n=None):
-    d, dp = _idx(dev_idx)
-    h, hp = _idx(host_idx)
-    n = len(d) if n is None else n
+    d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
     return _lib.kv_validate(ctypes.byref(geom), direction, dp, hp, n, layer_begin, layer_end,
                             int(check_unique))
 
 
 def kv_count_segments(geom, dev_idx, host_idx, layer_begin, layer_end):
     """Returns (status, count)."""
-    d, dp = _idx(dev_idx)
-    h, hp = _idx(host_idx)
+    d, dp, h, hp, _ = _pair(dev_idx, host_idx, None)
     out = ctypes.c_int64(-1)
     rc = _lib.kv_count_segments(ctypes.byref(geom), dp, hp, len(d), layer_begin, layer_end,
                                 ctypes.byref(out))
@@ -213,8 +210,7 @@ def kv_count_segments(geom, dev_idx, host_idx, layer_begin, layer_end):
 
 
 def kv_count_dma_copies(geom, dev_idx, host_idx, layer_begin, layer_end):
-    d, dp = _idx(dev_idx)
-    h, hp = _idx(host_idx)
+    d, dp, h, hp, _ = _pair(dev_idx, host_idx, None)
     out = ctypes.c_int64(-1)
     rc = _lib.kv_count_dma_copies(ctypes.byref(geom), dp, hp, len(d), layer_begin, layer_end,
                                   ctypes.byref(out))
@@ -229,8 +225,7 @@ def kv_default_calibration():
 
 def kv_model_path(geom, calib, direction, dev_idx, host_idx, layer_begin, layer_end, flags=0):
     """Returns (path or status, [kernel_us, dma_us, staged_us])."""
-    d, dp = _idx(dev_idx)
-    h, hp = _idx(host_idx)
+    d, dp, h, hp, _ = _pair(dev_idx, host_idx, None)
     t = (ctypes.c_double * 3)()
     rc = _lib.kv_model_path(ctypes.byref(geom), ctypes.byref(calib), direction, dp, hp, len(d),
                             layer_begin, layer_end, flags, t)
@@ -269,17 +264,28 @@ def kv_pool_host_bytes(pool):
     return _lib.kv_pool_host_bytes(pool)
 
 
-def kv_backup(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
+def _pair(dev_idx, host_idx, n):
+    """Both index arrays as int64 with their pointers, and the count the C call
+    gets: the arrays must be equally long and n (default: their length) at most
+    that long, so the library never reads past either numpy buffer. A negative
+    n goes through: the library rejects it (KV_EINVAL) before reading."""
     d, dp = _idx(dev_idx)
     h, hp = _idx(host_idx)
-    n = len(d) if n is None else n
+    if len(d) != len(h):
+        raise ValueError("dev_idx has %d entries, host_idx %d" % (len(d), len(h)))
+    n = len(d) if n is None else int(n)
+    if n > len(d):
+        raise ValueError("n = %d exceeds the %d index pairs given" % (n, len(d)))
+    return d, dp, h, hp, n
+
+
+def kv_backup(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
+    d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
     return _lib.kv_backup(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
 
 
 def kv_load(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
-    d, dp = _idx(dev_idx)
-    h, hp = _idx(host_idx)
-    n = len(d) if n is None else n
+    d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
     return _lib.kv_load(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
 
 
