@@ -39,10 +39,8 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
 }  // namespace
 
 // Direct path: block b moves walk rows [row_begin + b*rows_per_block, ...) of
-// the host-order walk; lanes take consecutive chunks of those rows. kDense
-// (staged path): the host side is a device staging buffer holding walk row r at
-// (r - row_begin) * R instead of the host pool.
-template <bool kToHost, bool kDense>
+// the host-order walk; lanes take consecutive chunks of those rows.
+template <bool kToHost>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
   const uint32_t row0 = a.row_begin + blk * a.rows_per_block;
@@ -61,9 +59,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
         uint32_t i, lc;
         walk_row(a, row0 + rr, i, lc);
         chunk_t *d = reinterpret_cast<chunk_t *>(dev_row(a, i, lc)) + k;
-        chunk_t *h = reinterpret_cast<chunk_t *>(
-                         kDense ? a.host + (int64_t)(row0 + rr - a.row_begin) * a.R
-                                : host_row(a, i, lc)) + k;
+        chunk_t *h = reinterpret_cast<chunk_t *>(host_row(a, i, lc)) + k;
         const chunk_t *src = kToHost ? d : h;
         dst[u] = kToHost ? h : d;
         v[u] = __builtin_nontemporal_load(src);
@@ -72,12 +68,76 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
       if (!dst[u]) continue;
-      if (!kToHost && !kDense)
+      if (!kToHost)
         __builtin_nontemporal_store(v[u], dst[u]);
       else
         *dst[u] = v[u];
     }
   }
+  }
+}
+
+// Staged path, device side (HBM to HBM): kGather packs the walk rows
+// [row_begin, row_end) from the device buffers into a dense staging buffer
+// (a.host: walk row r at (r - row_begin) * R), the scatter unpacks them. Each
+// wave takes tasks of rows_per_task consecutive walk rows and moves
+// kStageRows rows at a time: it steps the walk position row by row (uniform
+// across the wave, so it lives in scalar registers), loads each row's device
+// slot once, and its lanes move the rows' 16-byte chunks, lane-consecutive.
+// Every load and store is a whole-wave 1 KiB access where the row allows.
+typedef uint32_t vec16_t __attribute__((ext_vector_type(4)));
+// The same 16 bytes addressed in the global address space: the device buffers
+// and the staging buffer are device memory, and naming that lets the compiler
+// emit global rather than flat accesses.
+typedef __attribute__((address_space(1))) vec16_t gvec16_t;
+
+template <bool kGather>
+__global__ __launch_bounds__(kXferThreads) void stage_rows(
+    XferArgs a, uint32_t rows_per_task, const int64_t *__restrict__ tok,
+    uint8_t *const *__restrict__ dev_tab) {
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t cpr = (uint32_t)(a.R >> 4);  // 16-byte chunks per row
+  const uint32_t ntasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
+  for (uint32_t t = blockIdx.x * kWavesPerBlock + wave; t < ntasks;
+       t += gridDim.x * kWavesPerBlock) {
+    const uint32_t r0 = a.row_begin + t * rows_per_task;
+    const uint32_t r1 = min(r0 + rows_per_task, a.row_end);
+    WalkPos w = walk_at(a, r0);
+    for (uint32_t r = r0; r < r1; r += kStageRows) {
+      const uint32_t m = min((uint32_t)kStageRows, r1 - r);
+      gvec16_t *dev[kStageRows];
+      gvec16_t *stg[kStageRows];
+#pragma unroll
+      for (int u = 0; u < kStageRows; u++) {
+        dev[u] = stg[u] = nullptr;
+        if ((uint32_t)u < m) {
+          const uint32_t i = w.base + w.pos;
+          dev[u] = (gvec16_t *)(dev_tab[a.lc0 + w.lc] + tok[2 * i] * a.R);
+          stg[u] = (gvec16_t *)(a.host + (int64_t)(r + u - a.row_begin) * a.R);
+          walk_next(a, w);
+        }
+      }
+      for (uint32_t k0 = 0; k0 < cpr; k0 += 64 * kStageChunks) {
+        vec16_t v[kStageRows][kStageChunks];
+#pragma unroll
+        for (int u = 0; u < kStageRows; u++)
+#pragma unroll
+          for (int j = 0; j < kStageChunks; j++) {
+            const uint32_t k = k0 + j * 64 + lane;
+            if ((uint32_t)u < m && k < cpr)
+              v[u][j] = __builtin_nontemporal_load((kGather ? dev[u] : stg[u]) + k);
+          }
+#pragma unroll
+        for (int u = 0; u < kStageRows; u++)
+#pragma unroll
+          for (int j = 0; j < kStageChunks; j++) {
+            const uint32_t k = k0 + j * 64 + lane;
+            if ((uint32_t)u < m && k < cpr)
+              __builtin_nontemporal_store(v[u][j], (kGather ? stg[u] : dev[u]) + k);
+          }
+      }
+    }
   }
 }
 
@@ -138,20 +198,24 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
   }
 }
 
-hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, bool dense,
-                       hipStream_t s) {
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  if (dense) {
-    if (to_host)
-      hipLaunchKernelGGL((xfer_rows<true, true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((xfer_rows<false, true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
-  } else {
-    if (to_host)
-      hipLaunchKernelGGL((xfer_rows<true, false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((xfer_rows<false, false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
-  }
+  if (to_host)
+    hipLaunchKernelGGL((xfer_rows<true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((xfer_rows<false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
+                        hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
+  if (gather)
+    hipLaunchKernelGGL((stage_rows<true>), dim3(blocks), dim3(kXferThreads), 0, s, a,
+                       rows_per_task, a.tok, (uint8_t *const *)a.dev_tab);
+  else
+    hipLaunchKernelGGL((stage_rows<false>), dim3(blocks), dim3(kXferThreads), 0, s, a,
+                       rows_per_task, a.tok, (uint8_t *const *)a.dev_tab);
   return hipGetLastError();
 }
 

@@ -9,9 +9,13 @@ namespace kvt {
 
 // `blocks` is the number of workgroups to launch; the kernels stride over
 // a.nblocks blocks of work (plan_rows / plan_tiles), so blocks may be smaller.
-// dense: the host side of a is a device staging buffer (staged path).
-hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, bool dense,
-                       hipStream_t s);
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s);
+// The staged path's device-side pass over walk rows [a.row_begin, a.row_end):
+// gather packs them from the device buffers into the staging buffer a.host,
+// the scatter unpacks them. The waves stride over the tasks of rows_per_task
+// rows (stage_rows_per_task / stage_blocks), so blocks may be smaller.
+hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
+                        hipStream_t s);
 hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t blocks, bool to_host,
                             hipStream_t s);
 

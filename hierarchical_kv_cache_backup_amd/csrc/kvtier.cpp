@@ -161,11 +161,19 @@ struct kv_pool {
   std::shared_ptr<HostShare> share; // the host pool and the group's write event
   bool reader = false;              // shares another pool's host pool; its backups move nothing
   // Landed events of kv_load. Layers are loaded in groups (one launch or one
-  // batch of copies per group) and one event is recorded per group, on the
-  // group's first layer; layer_src[l] names the event that covers layer l
-  // (-1: no load has covered it yet).
+  // batch of copies per group) and one event is recorded per group;
+  // layer_src[l] names the event that covers layer l in the most recent load
+  // that covered it (-1: none yet). The events form a fixed set of 2L + 16
+  // made at pool creation (kv_load_layer indexes it without a lock); ev_refs
+  // counts the layers naming each, and an event is recorded again only when no
+  // layer names it and its last recording has completed (mark_landed), so a
+  // layer's wait never moves to another load's work. ev_refs, ev_recorded and
+  // ev_next are guarded by the load direction's lock.
   std::vector<hipEvent_t> layer_ev;
   std::vector<std::atomic<int32_t>> layer_src;
+  std::vector<int32_t> ev_refs;
+  std::vector<uint8_t> ev_recorded;
+  size_t ev_next = 0;
   DirState dir[2];
   std::atomic<int32_t> path{KV_PATH_AUTO};
   std::mutex calib_mu;
@@ -444,31 +452,40 @@ int acquire_staging(DirState &d, int64_t n, Staging **out, double *blocked_us) {
 
 // ---- copy-engine executor ------------------------------------------------
 
-hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_t s) {
+// Issues copy c of (layer, component) buffer lc; adds the copy-engine calls
+// made to *calls. A 2-D call goes out only over the lines whose whole
+// pitch x lines region lies inside the host pool and the device buffer
+// (copy_region_lines); a line left over goes out as a 1-D call.
+hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_t s,
+                      int64_t *calls) {
   const Geom &g = p->g;
   uint8_t *dev = p->bufs[lc] + c.dev0 * g.R;
   uint8_t *host = p->host + ((int64_t)lc * g.lc_stride + c.key0) * g.R;
   const size_t width = (size_t)(c.len * g.R);
-  if (c.lines == 1) {
-    return dir == 0 ? hipMemcpyAsync(host, dev, width, hipMemcpyDeviceToHost, s)
-                    : hipMemcpyAsync(dev, host, width, hipMemcpyHostToDevice, s);
-  }
   const size_t dpitch = (size_t)(c.dev_pitch * g.R), hpitch = (size_t)(c.key_pitch * g.R);
-  hipError_t e = dir == 0 ? hipMemcpy2DAsync(host, hpitch, dev, dpitch, width, (size_t)c.lines,
-                                             hipMemcpyDeviceToHost, s)
-                          : hipMemcpy2DAsync(dev, dpitch, host, hpitch, width, (size_t)c.lines,
-                                             hipMemcpyHostToDevice, s);
-  if (e == hipErrorInvalidValue || e == hipErrorInvalidPitchValue) {
-    // Shape the 2-D copy engine path refuses: fall back to one copy per line.
-    (void)hipGetLastError();
-    for (int64_t j = 0; j < c.lines; j++) {
-      Copy line{c.dev0 + j * c.dev_pitch, c.key0 + j * c.key_pitch, c.len, 1, 0, 0};
-      e = issue_copy(p, dir, lc, line, s);
+  auto lines_1d = [&](int64_t j0) {  // lines [j0, lines) one by one
+    for (int64_t j = j0; j < c.lines; j++) {
+      uint8_t *dj = dev + j * dpitch, *hj = host + j * hpitch;
+      hipError_t e = dir == 0 ? hipMemcpyAsync(hj, dj, width, hipMemcpyDeviceToHost, s)
+                              : hipMemcpyAsync(dj, hj, width, hipMemcpyHostToDevice, s);
+      ++*calls;
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
+  };
+  const int64_t region = copy_region_lines(g, c, lc);
+  if (region < 2) return lines_1d(0);
+  hipError_t e = dir == 0 ? hipMemcpy2DAsync(host, hpitch, dev, dpitch, width, (size_t)region,
+                                             hipMemcpyDeviceToHost, s)
+                          : hipMemcpy2DAsync(dev, dpitch, host, hpitch, width, (size_t)region,
+                                             hipMemcpyHostToDevice, s);
+  if (e == hipErrorInvalidValue || e == hipErrorInvalidPitchValue) {
+    (void)hipGetLastError();  // a shape the 2-D path refuses: one copy per line instead
+    return lines_1d(0);
   }
-  return e;
+  ++*calls;
+  if (e != hipSuccess) return e;
+  return lines_1d(region);  // the line the region could not hold, if any
 }
 
 }  // namespace
@@ -476,13 +493,49 @@ hipError_t issue_copy(kv_pool *p, int dir, int32_t lc, const Copy &c, hipStream_
 
 // ---- transfers ----------------------------------------------------------------
 
-// Records the landed event of layers [la, lb) (one event, kept on layer la)
-// after the work enqueued so far on s.
-static hipError_t mark_landed(kv_pool *p, int32_t la, int32_t lb, hipStream_t s) {
-  hipError_t e = hipEventRecord(p->layer_ev[la], s);
-  if (e == hipSuccess)
-    for (int32_t l = la; l < lb; l++) p->layer_src[l].store(la);
-  return e;
+// Records one landed event for layers [la, lb) after the work enqueued so far
+// on s, and points those layers at it. The event is one that no layer names
+// and whose previous recording has completed, taken round-robin from the
+// pool's set (the oldest recording comes first); when every free one is still
+// in flight, the call waits for the oldest (adding the wait to *blocked_us).
+// Caller holds the load direction's lock.
+static hipError_t mark_landed(kv_pool *p, int32_t la, int32_t lb, hipStream_t s,
+                              double *blocked_us) {
+  const size_t E = p->layer_ev.size();
+  size_t pick = E, oldest = E;
+  for (size_t k = 0; k < E && pick == E; k++) {
+    const size_t x = (p->ev_next + k) % E;
+    if (p->ev_refs[x] != 0) continue;
+    if (!p->ev_recorded[x]) {
+      pick = x;
+      break;
+    }
+    const hipError_t q = hipEventQuery(p->layer_ev[x]);
+    if (q == hipSuccess) {
+      pick = x;
+    } else if (q == hipErrorNotReady) {
+      if (oldest == E) oldest = x;
+    } else {
+      return q;
+    }
+  }
+  if (pick == E) {  // 2L + 16 events, at most L named: oldest is set
+    const double t0 = now_us();
+    const hipError_t w = hipEventSynchronize(p->layer_ev[oldest]);
+    *blocked_us += now_us() - t0;
+    if (w != hipSuccess) return w;
+    pick = oldest;
+  }
+  const hipError_t e = hipEventRecord(p->layer_ev[pick], s);
+  if (e != hipSuccess) return e;
+  p->ev_recorded[pick] = 1;
+  p->ev_next = (pick + 1) % E;
+  for (int32_t l = la; l < lb; l++) {
+    const int32_t old = p->layer_src[l].exchange((int32_t)pick);
+    if (old >= 0) p->ev_refs[old]--;
+    p->ev_refs[pick]++;
+  }
+  return hipSuccess;
 }
 
 // A stream with a hardware queue of its own. HIP maps streams onto a few
@@ -610,7 +663,7 @@ static int stage_begin(DirState &d, const Geom &g, int64_t unit_bytes, const kv_
 // b is planned for the group; ramp_first / ramp_last select chunk_plan's ramps.
 static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
                               const int64_t *host_idx, int32_t la, int32_t lb, bool ramp_first,
-                              bool ramp_last, uint32_t cap, hipStream_t s) {
+                              bool ramp_last, uint32_t cap, hipStream_t s, double *blocked_us) {
   const Geom &g = p->g;
   build_extents(g, host_idx, (int64_t)b.n, d.host_run_start, la, lb, &d.extents);
   plan_rows(&b, g.layout, g.ps);
@@ -630,13 +683,15 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
     last = half;
     uint8_t *buf = d.stage + half * d.stage_cap;
     b.host = buf;
-    const uint32_t blocks = set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
+    set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
+    const uint32_t rpt = stage_rows_per_task(g.R);
+    const uint32_t blocks = stage_blocks(b, rpt);
     hipStream_t kern_s = d.aux;
     if (dir == 0) {
       if (d.free_recorded[half]) e = hipStreamWaitEvent(kern_s, d.ev_free[half], 0);
       if (e == hipSuccess) {
         d.launches++;
-        e = launch_rows(b, grid_for(blocks, cap), true, true, kern_s);
+        e = launch_stage(b, rpt, grid_for(blocks, cap), true, kern_s);
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_ready[half], kern_s);
       if (e == hipSuccess) e = hipStreamWaitEvent(s, d.ev_ready[half], 0);
@@ -664,13 +719,14 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
       if (e == hipSuccess) e = hipStreamWaitEvent(kern_s, d.ev_ready[half], 0);
       if (e == hipSuccess) {
         d.launches++;
-        e = launch_rows(b, grid_for(blocks, cap), false, true, kern_s);
+        e = launch_stage(b, rpt, grid_for(blocks, cap), false, kern_s);
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_free[half], kern_s);
     }
     d.free_recorded[half] = true;
   }
-  if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, d.aux);  // after its last scatter
+  if (e == hipSuccess && dir == 1)  // after its last scatter
+    e = mark_landed(p, la, lb, d.aux, blocked_us);
   d.last_half = last;
   return e;
 }
@@ -859,13 +915,12 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       for (int32_t l = la; l < lb && e == hipSuccess; l++)
         for (int32_t comp = 0; comp < g.C && e == hipSuccess; comp++)
           for (const Copy &cp : d.copies) {
-            e = issue_copy(p, dir, l * g.C + comp, cp, s);
+            e = issue_copy(p, dir, l * g.C + comp, cp, s, &d.dma);
             if (e != hipSuccess) break;
           }
-      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
+      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
     }
     if (e != hipSuccess) return hip_fail(e, "enqueueing copy-engine transfers");
-    d.dma += (int64_t)d.copies.size() * nlc_all;
   } else {
     Staging *st = nullptr;
     rc = acquire_staging(d, n, &st, &blocked);
@@ -925,7 +980,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
       if (path == KV_PATH_STAGED) {
         const bool ramp = (double)d.stage_use * kRampMinDiv >= c.staged_chunk_bytes;
         e = staged_unit(p, d, dir, b, host_idx, la, lb, ramp && dir == 0,
-                        ramp && dir == 1 && lb == l1, pass_cap, s);
+                        ramp && dir == 1 && lb == l1, pass_cap, s, &blocked);
         continue;  // staged_unit records the group's landed event itself
       } else if (path == KV_PATH_KERNEL_LDS) {
         plan_rows(&b, g.layout, g.ps);  // fills cpr / total_rows
@@ -938,9 +993,9 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
         const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
         d.launches++;
         d.last_workgroups = grid_for(blocks, cap);
-        e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, false, s);
+        e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
       }
-      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s);
+      if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
     }
     if (e == hipSuccess && path == KV_PATH_STAGED && dir == 1 && d.last_half >= 0)
       e = hipStreamWaitEvent(s, d.ev_free[d.last_half], 0);  // s ends after aux's last scatter
@@ -1181,9 +1236,12 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
     kv_pool_destroy(p);
     return hip_fail(e, "device buffer table");
   }
-  p->layer_ev.assign(g.L, nullptr);
-  for (int l = 0; l < g.L && e == hipSuccess; l++)
-    e = hipEventCreateWithFlags(&p->layer_ev[l], hipEventDisableTiming);
+  const size_t nev = 2 * (size_t)g.L + 16;
+  p->layer_ev.assign(nev, nullptr);
+  p->ev_refs.assign(nev, 0);
+  p->ev_recorded.assign(nev, 0);
+  for (size_t k = 0; k < nev && e == hipSuccess; k++)
+    e = hipEventCreateWithFlags(&p->layer_ev[k], hipEventDisableTiming);
   for (DirState &d : p->dir) {
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.done, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&d.stage_ev, hipEventDisableTiming);

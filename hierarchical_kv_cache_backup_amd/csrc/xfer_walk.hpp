@@ -121,6 +121,71 @@ constexpr void walk_row(const XferArgs &a, uint32_t r, uint32_t &i, uint32_t &lc
   }
 }
 
+// Position of a walk row, kept so that the next row's position follows
+// without a division (the staged path's device-side pass walks its rows in
+// order): request position base + pos, pair lc; gsize positions in the row's
+// group (G, or the ragged last group's).
+struct WalkPos {
+  uint32_t r, base, gsize, pos, lc;
+};
+
+constexpr WalkPos walk_at(const XferArgs &a, uint32_t r) {
+  WalkPos w{r, 0, 0, 0, 0};
+  if (r < a.rows_full) {
+    const uint32_t gsz = a.G * a.nlc;
+    const uint32_t grp = r / gsz;
+    const uint32_t rem = r - grp * gsz;
+    w.lc = rem / a.G;
+    w.pos = rem - w.lc * a.G;
+    w.base = grp * a.G;
+    w.gsize = a.G;
+  } else {  // needs r < total_rows: the ragged group holds n - first >= 1 positions
+    w.base = a.rows_full / a.nlc;
+    w.gsize = a.n - w.base;
+    const uint32_t rem = r - a.rows_full;
+    w.lc = rem / w.gsize;
+    w.pos = rem - w.lc * w.gsize;
+  }
+  return w;
+}
+
+// Advances w to the next walk row (the same position walk_row gives it).
+constexpr void walk_next(const XferArgs &a, WalkPos &w) {
+  w.r++;
+  if (w.r == a.rows_full && w.r < a.total_rows) {  // into the ragged last group
+    w = walk_at(a, w.r);
+    return;
+  }
+  if (++w.pos == w.gsize) {
+    w.pos = 0;
+    if (++w.lc == a.nlc) {
+      w.lc = 0;
+      w.base += w.gsize;
+    }
+  }
+}
+
+// The staged path's device-side pass (stage_rows): a wave moves whole rows
+// with 16-byte lanes, kStageRows rows at a time, each row's index pair loaded
+// once. Its work is cut into tasks of consecutive walk rows, about
+// kStageTaskBytes each, that the waves take in turn.
+constexpr int kStageRows = 4;
+constexpr int kStageChunks = 2;              // 16-byte chunks per lane per row and pass
+constexpr int64_t kStageTaskBytes = 16 * 1024;
+constexpr uint32_t kWavesPerBlock = kXferThreads / 64;
+
+constexpr uint32_t stage_rows_per_task(int64_t R) {
+  const int64_t rows = (kStageTaskBytes + R - 1) / R;
+  const int64_t up = (rows + kStageRows - 1) / kStageRows * kStageRows;
+  return (uint32_t)(up < kStageRows ? kStageRows : up);
+}
+
+// Workgroups of a stage_rows launch over walk rows [row_begin, row_end).
+constexpr uint32_t stage_blocks(const XferArgs &a, uint32_t rows_per_task) {
+  const uint32_t tasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
+  return (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+}
+
 // A tile of the LDS variant: positions [i0, i0+nt), pairs [lcf, lcf+nl).
 struct Tile {
   uint32_t i0, lcf, nt, nl;

@@ -293,6 +293,9 @@ int kv_count_segments(const kv_geometry_t *geom, const int64_t *dev_idx, const i
 
 /* Number of copy-engine calls the DMA path would issue for the request after
  * merging equal-length runs at a uniform device and host stride into 2-D copies.
+ * A 2-D call names pitch x lines bytes on each side; where that region would
+ * end past the host pool or the device buffer (the last line itself always
+ * fits), the last line goes out as a 1-D call of its own, and is counted so.
  * Validates like kv_count_segments. */
 int kv_count_dma_copies(const kv_geometry_t *geom, const int64_t *dev_idx,
                         const int64_t *host_idx, int64_t n, int32_t layer_begin,
@@ -302,7 +305,13 @@ int kv_count_dma_copies(const kv_geometry_t *geom, const int64_t *dev_idx,
 
 /* Allocates the pinned, device-mapped host pool (L*C*S_host*R bytes, contents
  * unspecified), copies the device-buffer table to the device, creates the
- * per-layer load events and the per-direction index staging buffers.
+ * per-layer load events and the per-direction index staging buffers. The
+ * host pool is pinned once, up front, and optionally bound to the GPU's NUMA
+ * node (numa_node) or interleaved (KV_F_HOST_INTERLEAVE): the pages tie
+ * host-link throughput to pinned, registered host memory and to its NUMA
+ * placement ("Tuning SGLang HiCache L2 on Kunlunxin P800/P900", section 2.4
+ * "The physical form of Host memory"; "Baidu's KVCache Overhaul", "Host Memory
+ * & Link Optimization").
  * Not on the timed path. On success *out owns all of it. Errors: KV_EINVAL
  * (bad desc / geometry / null buffer / misaligned buffer), KV_ENOMEM,
  * KV_EHIP. */
@@ -378,14 +387,20 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
 
 /* Makes `compute_stream` wait (on the device, the host does not block) until
  * layer `layer` of the most recent kv_load that covered that layer on this
- * pool has landed in device memory. Call it after that kv_load has returned.
- * The wait is on the landed event of the layer's group (see
- * load_split_min_bytes), so it may also cover the other layers of that group;
- * if a later load re-recorded that group's event, the wait covers the later
- * load too (never less than asked). A layer no kv_load has covered yet: KV_OK,
- * no wait. After a kv_load that returned an error, which of its layers were
- * enqueued is unspecified, and so is this wait for them. Errors: KV_EINVAL
- * (layer out of [0,L)), KV_EHIP. */
+ * pool has landed in device memory: the load stream signals a per-layer ready
+ * event and the compute stream waits on it, so compute, H2D and D2H stay in one
+ * GPU execution domain ordered by events ("Rethinking the SGLang HiCache
+ * Boundary: From L2 Offload to a Cache Runtime", section "Why compute, H2D, and
+ * D2H should stay in one GPU execution domain"). Call it after that kv_load has
+ * returned. The wait is on the landed event of the layer's group in that load
+ * (see load_split_min_bytes), so it may also cover the other layers of that
+ * group. Each group records an event of its own, and an event is recorded
+ * again only once no layer names it and its previous recording has
+ * completed, so the wait never covers less than the layer asked for, whatever
+ * later loads on other streams cover. A layer no kv_load has covered yet:
+ * KV_OK, no wait. After a kv_load that returned an error, which of its layers
+ * were enqueued is unspecified, and so is this wait for them. Errors:
+ * KV_EINVAL (layer out of [0,L)), KV_EHIP. */
 int kv_load_layer(kv_pool_t *pool, int32_t layer, void *compute_stream);
 
 /* ---- streams -------------------------------------------------------------- */
@@ -428,7 +443,9 @@ typedef struct {
   int64_t dma_copies[2];    /* copy-engine calls issued */
   double submit_us[2];      /* host wall time spent inside the calls, minus blocked_us */
   double blocked_us[2];     /* host time spent waiting for an index staging buffer
-                               (only when 16 calls of one direction are in flight) */
+                               (only when 16 calls of one direction are in flight) or,
+                               for loads, for a free landed event (only when more
+                               than L + 16 load groups are in flight) */
   int64_t last_workgroups[2]; /* grid of the latest kernel-path launch (direct or LDS
                                kernel), after any cap; 0 before the first */
 } kv_stats_t;
