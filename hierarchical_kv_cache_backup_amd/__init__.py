@@ -97,6 +97,7 @@ SIGNATURES = {
     "kv_stream_create": (_I32, [_I32, ctypes.POINTER(_VP)]),
     "kv_stream_destroy": (_I32, [_VP]),
     "kv_set_path": (_I32, [_VP, _I32]),
+    "kv_set_direction_path": (_I32, [_VP, _I32, _I32]),
     "kv_last_path": (_I32, [_VP, _I32]),
     "kv_set_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
     "kv_get_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
@@ -327,6 +328,10 @@ class Stream:
 
 def kv_set_path(pool, path):
     return _lib.kv_set_path(pool, path)
+
+
+def kv_set_direction_path(pool, direction, path):
+    return _lib.kv_set_direction_path(pool, direction, path)
 
 
 def kv_last_path(pool, direction):
@@ -562,8 +567,12 @@ class KvPool:
     def load_layer(self, layer, compute_stream=None):
         _check(kv_load_layer(self.handle, layer, compute_stream))
 
-    def set_path(self, path):
-        _check(kv_set_path(self.handle, path))
+    def set_path(self, path, direction=None):
+        """Forces a path for both directions, or for `direction` only."""
+        if direction is None:
+            _check(kv_set_path(self.handle, path))
+        else:
+            _check(kv_set_direction_path(self.handle, direction, path))
 
     def last_path(self, direction):
         return kv_last_path(self.handle, direction)

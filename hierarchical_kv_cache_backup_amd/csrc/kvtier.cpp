@@ -175,7 +175,7 @@ struct kv_pool {
   std::vector<uint8_t> ev_recorded;
   size_t ev_next = 0;
   DirState dir[2];
-  std::atomic<int32_t> path{KV_PATH_AUTO};
+  std::atomic<int32_t> path[2] = {{KV_PATH_AUTO}, {KV_PATH_AUTO}};  // per direction
   std::mutex calib_mu;
   kv_calib_t calib{};
   explicit kv_pool(int L) : layer_src(L) {
@@ -889,7 +889,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   const uint32_t pass_cap = kernel_cap(c, dir, overlap, duplex, false);    // staged passes
 
   // ---- path selection
-  int32_t path = p->path.load();
+  int32_t path = p->path[dir].load();
   bool have_copies = false, have_host_runs = false;
   if (path == KV_PATH_AUTO) {
     double times[3];
@@ -1335,7 +1335,16 @@ int kv_stream_destroy(void *stream) {
 int kv_set_path(kv_pool_t *p, int32_t path) {
   if (!p) return fail(KV_EINVAL, "pool is null");
   if (path < KV_PATH_AUTO || path > KV_PATH_STAGED) return fail(KV_EINVAL, "unknown path");
-  p->path.store(path);
+  p->path[0].store(path);
+  p->path[1].store(path);
+  return KV_OK;
+}
+
+int kv_set_direction_path(kv_pool_t *p, int32_t direction, int32_t path) {
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (direction != 0 && direction != 1) return fail(KV_EINVAL, "direction must be 0 or 1");
+  if (path < KV_PATH_AUTO || path > KV_PATH_STAGED) return fail(KV_EINVAL, "unknown path");
+  p->path[direction].store(path);
   return KV_OK;
 }
 

@@ -422,9 +422,17 @@ int kv_stream_destroy(void *stream);
 
 /* ---- path control, calibration and statistics -------------------------- */
 
-/* Forces a path (kv_path_t) for later calls on this pool; KV_PATH_AUTO
- * restores the selector. */
+/* Forces a path (kv_path_t) for later calls on this pool, both directions;
+ * KV_PATH_AUTO restores the selector. */
 int kv_set_path(kv_pool_t *pool, int32_t path);
+
+/* The same for one direction only (0 = backup, 1 = load), e.g. write-backs on
+ * the staged path while loads stay on the kernel path, the pairing the
+ * bidirectional mixed batch runs with a dedicated thread and stream per
+ * direction ("Tuning SGLang HiCache L2 on Kunlunxin P800/P900", section 2.2;
+ * "Baidu's KVCache Overhaul", "Bidirectional Async Transfer"). Errors:
+ * KV_EINVAL (null pool, bad direction or path). */
+int kv_set_direction_path(kv_pool_t *pool, int32_t direction, int32_t path);
 
 /* Path the most recent call of `direction` (0 = backup, 1 = load) used: one of
  * KV_PATH_KERNEL / KV_PATH_KERNEL_LDS / KV_PATH_DMA / KV_PATH_STAGED (or

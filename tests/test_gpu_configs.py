@@ -16,7 +16,7 @@ import pytest
 import hierarchical_kv_cache_backup_amd as kvt
 from hierarchical_kv_cache_backup_amd import workloads
 import oracle
-from oracle import Geometry
+from oracle import Geometry, np_ref
 
 from gpu_util import SENTINEL, torch_mod
 
@@ -174,8 +174,33 @@ def test_mla32k_load(torch, path):
 
 # ---- mixed batch: H2D of L2 hits concurrent with D2H of new pages ---------------------
 
-@pytest.mark.timeout(400)
+# (write-back path, load path) pairings the mixed batch runs with; AUTO on a
+# pool flagged KV_F_DUPLEX is the pairing bench.py times
+MIXED_PAIRINGS = (("kernel", kvt.PATH_KERNEL, kvt.PATH_KERNEL),
+                  ("auto_duplex", kvt.PATH_AUTO, kvt.PATH_AUTO),
+                  ("staged", kvt.PATH_STAGED, kvt.PATH_STAGED),
+                  ("dma", kvt.PATH_DMA, kvt.PATH_DMA),
+                  ("staged_back_kernel_load", kvt.PATH_STAGED, kvt.PATH_KERNEL))
+
+
+def reset_host_slots(g, pool, host_idx, value):
+    """Sets the host rows of slots host_idx, every layer and component, to value,
+    through the oracle's NumPy view of the host pool in the layout's own
+    dimension order."""
+    view = np_ref.host_view(pool.host_array(), g.layout, g.L, g.C, g.S_host, g.ps, g.R)
+    key, _ = np_ref._host_rows(view, g.layout, host_idx, 0, g.L, g.ps)
+    view[key] = value
+
+
+@pytest.mark.timeout(1100)
 def test_mixed_bidirectional(torch):
+    """The mixed batch at full size (~54 GB each way in all): the L2 hits load
+    while the new pages write back, from two threads on two library streams
+    against one pool flagged KV_F_DUPLEX, on every pairing of MIXED_PAIRINGS,
+    in both of its layouts. Before each pairing the hit rows on the device and
+    the new pages' host rows are reset to the sentinel; afterwards sampled
+    layers are compared with the oracle and every other device row is
+    unchanged."""
     shape = workloads.mixed()
     plan = workloads.mixed_plan(shape, 4)
     S_dev, S_host = plan["device_slots"], plan["host_slots"]
@@ -183,45 +208,56 @@ def test_mixed_bidirectional(torch):
     w_dev, w_host = plan["d2h"]
     print("mixed: %d tokens, %d hits, %d new" % (S_dev, h_dev.size, w_dev.size), flush=True)
     bufs = make_bufs(torch, shape, 4, S_dev)
+    both = np.concatenate([h_dev, w_dev])
+    t_hits = torch.from_numpy(h_dev).cuda()
     for layout in shape.layouts:
         g = Geometry(shape.layers, shape.components, shape.row_bytes, S_dev, S_host,
                      shape.page_size, layout)
-        with kvt.KvPool(kvt.geometry(*g.args()), bufs) as pool:
+        with kvt.KvPool(kvt.geometry(*g.args()), bufs,
+                        flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX) as pool:
             pool.set_path(kvt.PATH_KERNEL)
             s_load, s_back = kvt.Stream(), kvt.Stream()
-            # L2 holds the hit pages: write them back once, then scramble those device rows
+            # L2 holds the hit pages: write them back once
             pool.backup(h_dev, h_host, 0, g.L, s_back)
             s_back.synchronize()
-            t = torch.from_numpy(h_dev).cuda()
-            for b in bufs:
-                b.view(-1, g.R)[t] = SENTINEL
-            torch.cuda.synchronize()
-            untouched = [untouched_sum(torch, b, g.R, np.concatenate([h_dev, w_dev])) for b in bufs]
-            go = threading.Barrier(2)
-            errors = []
+            untouched = [untouched_sum(torch, b, g.R, both) for b in bufs]
+            for name, back_path, load_path in MIXED_PAIRINGS:
+                print("mixed layout=%d pairing=%s" % (layout, name), flush=True)
+                reset_host_slots(g, pool, w_host, SENTINEL)
+                for b in bufs:
+                    b.view(-1, g.R)[t_hits] = SENTINEL
+                torch.cuda.synchronize()
+                pool.set_path(back_path, kvt.BACKUP)
+                pool.set_path(load_path, kvt.LOAD)
+                go = threading.Barrier(2)
+                errors = []
 
-            def run(fn):
-                try:
-                    go.wait()
-                    fn()
-                except Exception as e:  # surfaced below
-                    errors.append(e)
+                def run(fn):
+                    try:
+                        go.wait()
+                        fn()
+                    except Exception as e:  # surfaced below
+                        errors.append(e)
 
-            th = [threading.Thread(target=run, args=(lambda: pool.load(h_dev, h_host, 0, g.L, s_load),)),
-                  threading.Thread(target=run, args=(lambda: pool.backup(w_dev, w_host, 0, g.L, s_back),))]
-            for x in th:
-                x.start()
-            for x in th:
-                x.join()
-            assert not errors, errors
-            s_load.synchronize()
-            s_back.synchronize()
-            print("mixed layout=%d concurrent done" % layout, flush=True)
-            layers = sample_layers(g.L)
-            check_load_layers(torch, g, pool, bufs, h_dev, h_host, layers)
-            check_backup_layers(torch, g, pool, bufs, w_dev, w_host, layers)
-            assert [untouched_sum(torch, b, g.R, np.concatenate([h_dev, w_dev])) for b in bufs] \
-                == untouched
+                th = [threading.Thread(target=run, args=(
+                          lambda: pool.load(h_dev, h_host, 0, g.L, s_load),)),
+                      threading.Thread(target=run, args=(
+                          lambda: pool.backup(w_dev, w_host, 0, g.L, s_back),))]
+                for x in th:
+                    x.start()
+                for x in th:
+                    x.join()
+                assert not errors, errors
+                s_load.synchronize()
+                s_back.synchronize()
+                used = (kvt.PATH_NAMES[pool.last_path(kvt.BACKUP)],
+                        kvt.PATH_NAMES[pool.last_path(kvt.LOAD)])
+                print("mixed layout=%d pairing=%s ran backup=%s load=%s" % ((layout, name) + used),
+                      flush=True)
+                layers = sample_layers(g.L)
+                check_load_layers(torch, g, pool, bufs, h_dev, h_host, layers)
+                check_backup_layers(torch, g, pool, bufs, w_dev, w_host, layers)
+                assert [untouched_sum(torch, b, g.R, both) for b in bufs] == untouched
             s_load.close()
             s_back.close()
     del bufs
