@@ -94,6 +94,7 @@ SIGNATURES = {
     "kv_backup": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_load": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_load_layer": (_I32, [_VP, _I32, _VP]),
+    "kv_stage": (_I32, [_VP, _I32, _P64, _I64, _I32, _I32, _VP, _VP]),
     "kv_stream_create": (_I32, [_I32, ctypes.POINTER(_VP)]),
     "kv_stream_destroy": (_I32, [_VP]),
     "kv_set_path": (_I32, [_VP, _I32]),
@@ -288,6 +289,15 @@ def kv_backup(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=No
 def kv_load(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
     d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
     return _lib.kv_load(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
+
+
+def kv_stage(pool, direction, dev_idx, layer_begin, layer_end, stage_ptr, stream=None, n=None):
+    d, dp = _idx(dev_idx)
+    n = len(d) if n is None else int(n)
+    if n > len(d):
+        raise ValueError("n = %d exceeds the %d device slots given" % (n, len(d)))
+    return _lib.kv_stage(pool, direction, dp, n, layer_begin, layer_end, stage_ptr,
+                         _stream_handle(stream))
 
 
 def kv_load_layer(pool, layer, compute_stream=None):
@@ -563,6 +573,13 @@ class KvPool:
     def load(self, dev_idx, host_idx, layer_begin=0, layer_end=None, stream=None):
         le = self.geom.num_layers if layer_end is None else layer_end
         _check(kv_load(self.handle, dev_idx, host_idx, layer_begin, le, stream))
+
+    def stage(self, direction, dev_idx, stage, layer_begin=0, layer_end=None, stream=None):
+        """Packs (direction 0) or unpacks (1) the rows of dev_idx between the
+        device buffers and `stage` (a torch uint8 device tensor) in host order."""
+        le = self.geom.num_layers if layer_end is None else layer_end
+        _check(kv_stage(self.handle, direction, dev_idx, layer_begin, le, stage.data_ptr(),
+                        stream))
 
     def load_layer(self, layer, compute_stream=None):
         _check(kv_load_layer(self.handle, layer, compute_stream))

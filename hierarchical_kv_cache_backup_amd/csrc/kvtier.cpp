@@ -1031,6 +1031,70 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   return KV_OK;
 }
 
+// The staged path's device-side pass on its own (kv_stage): packs (dir 0) or
+// unpacks (dir 1) the request's rows between the device buffers and the
+// caller's device buffer `stage`, on the caller's stream, in the walk order the
+// staged path uses. Uses the direction's index staging.
+static int stage_call(kv_pool *p, int dir, const int64_t *dev_idx, int64_t n, int32_t l0,
+                      int32_t l1, void *stage, void *stream) {
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (dir != 0 && dir != 1) return fail(KV_EINVAL, "direction must be 0 (pack) or 1 (unpack)");
+  DirState &d = p->dir[dir];
+  std::lock_guard<std::mutex> lock(d.mu);
+  const Geom &g = p->g;
+  std::string why;
+  int rc = validate_stage(g, dir, dev_idx, n, l0, l1, (p->flags & KV_F_CHECK_UNIQUE) != 0,
+                          &d.uniq, &why);
+  if (rc) return fail(rc, why);
+  if (n == 0 || l0 == l1) return KV_OK;
+  const int64_t rows = n * (int64_t)(l1 - l0) * g.C;
+  if (rows >= kMaxRowsPerLaunch)
+    return fail(KV_EINVAL, "request has >= 2^31 rows; split it into several calls");
+  if (!stage || ((uintptr_t)stage & 15u)) return fail(KV_EINVAL, "stage is null or not 16-byte aligned");
+  DeviceGuard dg(p->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, stage);
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (e == hipSuccess && attr.type == hipMemoryTypeDevice && attr.device == p->device)
+    e = hipMemGetAddressRange(&base, &size, stage);
+  if (e != hipSuccess || attr.type != hipMemoryTypeDevice || attr.device != p->device ||
+      (uint8_t *)stage + rows * g.R > (uint8_t *)base + size) {
+    (void)hipGetLastError();
+    return fail(KV_EINVAL, "stage is not device memory of the pool's device holding n*layers*C*R "
+                           "bytes");
+  }
+  double blocked = 0;
+  Staging *st = nullptr;
+  rc = acquire_staging(d, n, &st, &blocked);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  for (int64_t i = 0; i < n; i++) {
+    st->pinned[2 * i] = dev_idx[i];
+    st->pinned[2 * i + 1] = 0;  // the pass reads device slots only
+  }
+  e = hipMemcpyAsync(st->dev, st->pinned, (size_t)n * 16, hipMemcpyHostToDevice, s);
+  XferArgs a{};
+  a.tok = st->dev;
+  a.dev_tab = p->dev_tab;
+  a.host = (uint8_t *)stage;
+  a.R = g.R;
+  a.lc_stride = g.lc_stride;
+  a.n = (uint32_t)n;
+  a.lc0 = (uint32_t)(l0 * g.C);
+  a.nlc = (uint32_t)((l1 - l0) * g.C);
+  plan_rows(&a, g.layout, g.ps);
+  const uint32_t rpt = stage_rows_per_task(g.R);
+  if (e == hipSuccess) e = launch_stage(a, rpt, stage_blocks(a, rpt), dir == 0, s);
+  const hipError_t er = hipEventRecord(st->ev, s);  // the index slot is busy until here
+  if (er == hipSuccess) st->pending = true;
+  if (e != hipSuccess) return hip_fail(e, "enqueueing the staging pass");
+  if (er != hipSuccess) return hip_fail(er, "recording the staging event");
+  d.launches++;
+  return KV_OK;
+}
+
 // ---- C ABI ---------------------------------------------------------------------
 
 // Rejects a calibration with a figure out of range (KV_EINVAL).
@@ -1286,6 +1350,13 @@ int kv_load(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64
             int32_t layer_begin, int32_t layer_end, void *stream) {
   return guarded("kv_load", [&] {
     return transfer(p, 1, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  });
+}
+
+int kv_stage(kv_pool_t *p, int32_t direction, const int64_t *dev_idx, int64_t n,
+             int32_t layer_begin, int32_t layer_end, void *stage, void *stream) {
+  return guarded("kv_stage", [&] {
+    return stage_call(p, direction, dev_idx, n, layer_begin, layer_end, stage, stream);
   });
 }
 

@@ -75,6 +75,42 @@ int make_geom(const kv_geometry_t *in, Geom *g, std::string *why) {
   return KV_OK;
 }
 
+// First position whose slot appeared earlier in dst[0, n) (-1: none), slots in
+// [0, slots). KV_ENOMEM if the check's memory cannot be had.
+static int first_repeat(const int64_t *dst, int64_t n, int64_t slots, UniqueScratch *scratch,
+                        int64_t *dup, std::string *why) {
+  *dup = -1;
+  try {
+    if (slots <= std::max<int64_t>(kStampSlotsMin, 4 * n)) {
+      // one stamp per slot, kept between calls; a generation counter instead
+      // of clearing
+      if ((int64_t)scratch->stamp.size() < slots) scratch->stamp.assign(slots, 0);
+      if (++scratch->gen == 0) {  // wrapped: clear once every 2^32 calls
+        std::fill(scratch->stamp.begin(), scratch->stamp.end(), 0u);
+        scratch->gen = 1;
+      }
+      const uint32_t gen = scratch->gen;
+      uint32_t *st = scratch->stamp.data();
+      for (int64_t i = 0; i < n && *dup < 0; i++) {
+        if (st[dst[i]] == gen) *dup = i;
+        st[dst[i]] = gen;
+      }
+    } else {
+      // far more slots than positions: sort (slot, position) pairs instead of
+      // holding a stamp per slot
+      std::vector<std::pair<int64_t, int64_t>> v((size_t)n);
+      for (int64_t i = 0; i < n; i++) v[(size_t)i] = {dst[i], i};
+      std::sort(v.begin(), v.end());
+      for (size_t k = 1; k < v.size(); k++)
+        if (v[k].first == v[k - 1].first && (*dup < 0 || v[k].second < *dup)) *dup = v[k].second;
+    }
+  } catch (const std::bad_alloc &) {
+    *why = "out of memory in the destination uniqueness check";
+    return KV_ENOMEM;
+  }
+  return KV_OK;
+}
+
 int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t *host_idx,
              int64_t n, int32_t l0, int32_t l1, bool check_unique, UniqueScratch *scratch,
              std::string *why) {
@@ -106,41 +142,48 @@ int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t
   }
   if (check_unique && n > 1) {
     const int64_t *dst = direction == 0 ? host_idx : dev_idx;
-    const int64_t slots = direction == 0 ? g.S_host : g.S_dev;
-    // The first position whose destination appeared earlier in the request.
     int64_t dup = -1;
-    try {
-      if (slots <= std::max<int64_t>(kStampSlotsMin, 4 * n)) {
-        // one stamp per slot, kept between calls; a generation counter instead
-        // of clearing
-        if ((int64_t)scratch->stamp.size() < slots) scratch->stamp.assign(slots, 0);
-        if (++scratch->gen == 0) {  // wrapped: clear once every 2^32 calls
-          std::fill(scratch->stamp.begin(), scratch->stamp.end(), 0u);
-          scratch->gen = 1;
-        }
-        const uint32_t gen = scratch->gen;
-        uint32_t *st = scratch->stamp.data();
-        for (int64_t i = 0; i < n && dup < 0; i++) {
-          if (st[dst[i]] == gen) dup = i;
-          st[dst[i]] = gen;
-        }
-      } else {
-        // far more slots than positions: sort (slot, position) pairs instead of
-        // holding a stamp per slot
-        std::vector<std::pair<int64_t, int64_t>> v((size_t)n);
-        for (int64_t i = 0; i < n; i++) v[(size_t)i] = {dst[i], i};
-        std::sort(v.begin(), v.end());
-        for (size_t k = 1; k < v.size(); k++)
-          if (v[k].first == v[k - 1].first && (dup < 0 || v[k].second < dup)) dup = v[k].second;
-      }
-    } catch (const std::bad_alloc &) {
-      *why = "out of memory in the destination uniqueness check";
-      return KV_ENOMEM;
-    }
+    const int rc = first_repeat(dst, n, direction == 0 ? g.S_host : g.S_dev, scratch, &dup, why);
+    if (rc) return rc;
     if (dup >= 0) {
       *why = fmt(direction == 0 ? "host slot %lld is a destination twice (position %lld)"
                                 : "device slot %lld is a destination twice (position %lld)",
                  dst[dup], dup);
+      return KV_EDUP;
+    }
+  }
+  return KV_OK;
+}
+
+int validate_stage(const Geom &g, int direction, const int64_t *dev_idx, int64_t n, int32_t l0,
+                   int32_t l1, bool check_unique, UniqueScratch *scratch, std::string *why) {
+  if (direction != 0 && direction != 1) {
+    *why = "direction must be 0 (pack) or 1 (unpack)";
+    return KV_EINVAL;
+  }
+  if (n < 0) {
+    *why = fmt("n (%lld) must be >= 0", n);
+    return KV_EINVAL;
+  }
+  if (n > 0 && !dev_idx) {
+    *why = "index array is null";
+    return KV_EINVAL;
+  }
+  if (l0 < 0 || l0 > l1 || l1 > g.L) {
+    *why = fmt("layer range [%lld, %lld) is not inside [0, %lld]", l0, l1, g.L);
+    return KV_EINVAL;
+  }
+  for (int64_t i = 0; i < n; i++)
+    if ((uint64_t)dev_idx[i] >= (uint64_t)g.S_dev) {
+      *why = fmt("dev_idx[%lld] = %lld is outside [0, %lld)", i, dev_idx[i], g.S_dev);
+      return KV_ERANGE;
+    }
+  if (check_unique && direction == 1 && n > 1) {
+    int64_t dup = -1;
+    const int rc = first_repeat(dev_idx, n, g.S_dev, scratch, &dup, why);
+    if (rc) return rc;
+    if (dup >= 0) {
+      *why = fmt("device slot %lld is a destination twice (position %lld)", dev_idx[dup], dup);
       return KV_EDUP;
     }
   }

@@ -66,6 +66,12 @@ int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t
              int64_t n, int32_t l0, int32_t l1, bool check_unique, UniqueScratch *scratch,
              std::string *why);
 
+// Validation of kv_stage (the staged path's device-side pass on its own): the
+// rules of validate without the host side. Only an unpack (direction 1) writes
+// device slots, so only it checks them for repeats.
+int validate_stage(const Geom &g, int direction, const int64_t *dev_idx, int64_t n, int32_t l0,
+                   int32_t l1, bool check_unique, UniqueScratch *scratch, std::string *why);
+
 // A maximal group of request positions [i0, i0+len) whose device slots and
 // host rows both advance by one row per position.
 struct Run {

@@ -385,6 +385,35 @@ int kv_backup(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, 
 int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
             int32_t layer_begin, int32_t layer_end, void *stream);
 
+/* The staged path's device-side pass on its own: the batched gather/scatter
+ * that packs a request's scattered device rows into one contiguous,
+ * host-ordered buffer in HBM, so that a single large copy moves it ("Baidu's
+ * KVCache Overhaul", "DMA Segment Explosion & Batched Gather/Scatter").
+ * direction 0 packs the rows of positions [0, n), layers [layer_begin,
+ * layer_end), from the device buffers into `stage`; direction 1 unpacks them
+ * from `stage` into the device buffers. Row order in `stage` is the host
+ * address order of the pool's layout, as if the request's positions were host
+ * slots 0..n-1 of a pool holding layers [layer_begin, layer_end) only:
+ *   layer_first        (layer, comp, position)
+ *   page_first         (position, layer, comp)
+ *   page_first_direct  (page of ps positions, layer, comp, position in page);
+ *                      the last page holds the n % ps positions left, if any.
+ * So a request on whole, consecutive host pages packs into exactly the bytes
+ * the host pool holds for those pages, and one copy moves them to L2 or to an
+ * L3 store. `stage`: device memory of the pool's device, 16-byte aligned,
+ * n * (layer_end - layer_begin) * C * R bytes, BORROWED until the stream has
+ * passed the call. dev_idx: host array of n int64, read during the call.
+ * Enqueued on `stream`; the caller orders it after the work that produced the
+ * rows (pack) or the stage's bytes (unpack). Errors as kv_backup (KV_EDUP only
+ * for an unpack, with KV_F_CHECK_UNIQUE); KV_EINVAL also for a direction other
+ * than 0 or 1 and for a stage that is null, misaligned, not device memory of
+ * the pool's device, or whose rows would run past the end of the device
+ * allocation holding it (a buffer carved out of a larger allocation, as a
+ * caching allocator hands out, is checked against that allocation only).
+ * n == 0 or an empty layer range: KV_OK, nothing enqueued. */
+int kv_stage(kv_pool_t *pool, int32_t direction, const int64_t *dev_idx, int64_t n,
+             int32_t layer_begin, int32_t layer_end, void *stage, void *stream);
+
 /* Makes `compute_stream` wait (on the device, the host does not block) until
  * layer `layer` of the most recent kv_load that covered that layer on this
  * pool has landed in device memory: the load stream signals a per-layer ready
