@@ -79,23 +79,27 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
 
 // Staged path, device side (HBM to HBM): kGather packs the walk rows
 // [row_begin, row_end) from the device buffers into a dense staging buffer
-// (a.host: walk row r at (r - row_begin) * R), the scatter unpacks them. Each
-// wave takes tasks of rows_per_task consecutive walk rows and moves
-// kStageRows rows at a time: it steps the walk position row by row (uniform
-// across the wave, so it lives in scalar registers), loads each row's device
-// slot once, and its lanes move the rows' 16-byte chunks, lane-consecutive.
-// Every load and store is a whole-wave 1 KiB access where the row allows.
+// (a.host: walk row r at (r - row_begin) * R), the scatter unpacks them. A wave
+// is K lane groups of 64/K lanes; its task is K batches of K consecutive walk
+// rows. The wave steps the walk position row by row (uniform across the wave,
+// so it lives in scalar registers), loads each row's device slot once, and
+// hands the row's two addresses to its lane group, whose lanes move the row's
+// 16-byte chunks, lane-consecutive, in passes of 64/K chunks. Each wave takes
+// one task of a large grid: many small tasks keep more of HBM busy than a few
+// long ones.
 typedef uint32_t vec16_t __attribute__((ext_vector_type(4)));
 // The same 16 bytes addressed in the global address space: the device buffers
 // and the staging buffer are device memory, and naming that lets the compiler
 // emit global rather than flat accesses.
 typedef __attribute__((address_space(1))) vec16_t gvec16_t;
 
-template <bool kGather>
+template <bool kGather, uint32_t K>
 __global__ __launch_bounds__(kXferThreads) void stage_rows(
     XferArgs a, uint32_t rows_per_task, const int64_t *__restrict__ tok,
     uint8_t *const *__restrict__ dev_tab) {
+  constexpr uint32_t kLanes = 64 / K;  // lanes per row
   const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t grp = lane / kLanes, sub = lane % kLanes;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t cpr = (uint32_t)(a.R >> 4);  // 16-byte chunks per row
   const uint32_t ntasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
@@ -104,39 +108,34 @@ __global__ __launch_bounds__(kXferThreads) void stage_rows(
     const uint32_t r0 = a.row_begin + t * rows_per_task;
     const uint32_t r1 = min(r0 + rows_per_task, a.row_end);
     WalkPos w = walk_at(a, r0);
-    for (uint32_t r = r0; r < r1; r += kStageRows) {
-      const uint32_t m = min((uint32_t)kStageRows, r1 - r);
-      gvec16_t *dev[kStageRows];
-      gvec16_t *stg[kStageRows];
+    gvec16_t *dev[K];
+    gvec16_t *stg[K];
 #pragma unroll
-      for (int u = 0; u < kStageRows; u++) {
-        dev[u] = stg[u] = nullptr;
-        if ((uint32_t)u < m) {
-          const uint32_t i = w.base + w.pos;
-          dev[u] = (gvec16_t *)(dev_tab[a.lc0 + w.lc] + tok[2 * i] * a.R);
-          stg[u] = (gvec16_t *)(a.host + (int64_t)(r + u - a.row_begin) * a.R);
+    for (uint32_t u = 0; u < K; u++) {  // batch u: rows r0 + u*K + g for group g
+      dev[u] = stg[u] = nullptr;
+#pragma unroll
+      for (uint32_t g = 0; g < K; g++) {
+        const uint32_t r = r0 + u * K + g;
+        if (r < r1) {
+          gvec16_t *d = (gvec16_t *)(dev_tab[a.lc0 + w.lc] + tok[2 * (w.base + w.pos)] * a.R);
+          gvec16_t *st = (gvec16_t *)(a.host + (int64_t)(r - a.row_begin) * a.R);
+          if (grp == g) {
+            dev[u] = d;
+            stg[u] = st;
+          }
           walk_next(a, w);
         }
       }
-      for (uint32_t k0 = 0; k0 < cpr; k0 += 64 * kStageChunks) {
-        vec16_t v[kStageRows][kStageChunks];
+    }
+    for (uint32_t k0 = 0; k0 < cpr; k0 += kLanes) {
+      const uint32_t k = k0 + sub;
+      vec16_t v[K];
 #pragma unroll
-        for (int u = 0; u < kStageRows; u++)
+      for (uint32_t u = 0; u < K; u++)
+        if (dev[u] && k < cpr) v[u] = __builtin_nontemporal_load((kGather ? dev[u] : stg[u]) + k);
 #pragma unroll
-          for (int j = 0; j < kStageChunks; j++) {
-            const uint32_t k = k0 + j * 64 + lane;
-            if ((uint32_t)u < m && k < cpr)
-              v[u][j] = __builtin_nontemporal_load((kGather ? dev[u] : stg[u]) + k);
-          }
-#pragma unroll
-        for (int u = 0; u < kStageRows; u++)
-#pragma unroll
-          for (int j = 0; j < kStageChunks; j++) {
-            const uint32_t k = k0 + j * 64 + lane;
-            if ((uint32_t)u < m && k < cpr)
-              __builtin_nontemporal_store(v[u][j], (kGather ? stg[u] : dev[u]) + k);
-          }
-      }
+      for (uint32_t u = 0; u < K; u++)
+        if (dev[u] && k < cpr) __builtin_nontemporal_store(v[u], (kGather ? stg[u] : dev[u]) + k);
     }
   }
 }
@@ -210,12 +209,17 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
 hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
                         hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  if (gather)
-    hipLaunchKernelGGL((stage_rows<true>), dim3(blocks), dim3(kXferThreads), 0, s, a,
-                       rows_per_task, a.tok, (uint8_t *const *)a.dev_tab);
-  else
-    hipLaunchKernelGGL((stage_rows<false>), dim3(blocks), dim3(kXferThreads), 0, s, a,
-                       rows_per_task, a.tok, (uint8_t *const *)a.dev_tab);
+  const int64_t *tok = a.tok;
+  uint8_t *const *tab = (uint8_t *const *)a.dev_tab;
+  const dim3 grid(blocks), block(kXferThreads);
+  switch (stage_lane_groups(a.R) * 2 + (gather ? 1 : 0)) {
+    case 9: hipLaunchKernelGGL((stage_rows<true, 4>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+    case 8: hipLaunchKernelGGL((stage_rows<false, 4>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+    case 5: hipLaunchKernelGGL((stage_rows<true, 2>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+    case 4: hipLaunchKernelGGL((stage_rows<false, 2>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+    case 3: hipLaunchKernelGGL((stage_rows<true, 1>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+    default: hipLaunchKernelGGL((stage_rows<false, 1>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+  }
   return hipGetLastError();
 }
 

@@ -269,9 +269,10 @@ void default_calibration(kv_calib_t *c) {
   c->duplex_kernel_max_workgroups[0] = 24;
   c->duplex_kernel_max_workgroups[1] = 128;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
-  // the device-side gather / scatter of a staged chunk (HBM to HBM, full
-  // grid): 256 MiB of 1152-byte rows in 330 us, 37.7 MB in 45 us (kernel trace)
-  c->staged_gather_gbps = 800.0;
+  // the device-side gather / scatter of a staged chunk (stage_rows, HBM to
+  // HBM, full grid), payload rate: the 2.94 GB prefix of 1152-byte rows packs
+  // in ~1.0 ms (5.9 TB/s of HBM traffic), so a 256 MiB half in ~92 us
+  c->staged_gather_gbps = 2900.0;
   // Reading the index pairs from mapped pinned memory instead of copying them
   // first measured +0.6..1.6% at 64 tokens, even at 256, and down to -2% for
   // loads of 1K tokens and more (the reads share the link and lengthen each

@@ -165,22 +165,25 @@ constexpr void walk_next(const XferArgs &a, WalkPos &w) {
   }
 }
 
-// The staged path's device-side pass (stage_rows): a wave moves whole rows
-// with 16-byte lanes, kStageRows rows at a time, each row's index pair loaded
-// once. Its work is cut into tasks of consecutive walk rows, about
-// kStageTaskBytes each, that the waves take in turn.
-constexpr int kStageRows = 4;
-constexpr int kStageChunks = 2;              // 16-byte chunks per lane per row and pass
-constexpr int64_t kStageTaskBytes = 16 * 1024;
+// The staged path's device-side pass (stage_rows), HBM to HBM. A wave splits
+// into K lane groups of 64/K lanes, one row per group and pass, so that a row of
+// R/16 16-byte chunks fills its group in one pass where it can: K = 4 for rows of
+// at most 16 chunks (256 B), 2 for at most 32, else 1 (longer rows take several
+// passes of 64 lanes). A wave's task is K batches of K consecutive walk rows
+// (K*K rows); each row's walk position and index pair are taken once, in
+// scalar registers, and handed to its lane group.
 constexpr uint32_t kWavesPerBlock = kXferThreads / 64;
 
-constexpr uint32_t stage_rows_per_task(int64_t R) {
-  const int64_t rows = (kStageTaskBytes + R - 1) / R;
-  const int64_t up = (rows + kStageRows - 1) / kStageRows * kStageRows;
-  return (uint32_t)(up < kStageRows ? kStageRows : up);
+constexpr uint32_t stage_lane_groups(int64_t R) {
+  return R / 16 <= 16 ? 4u : R / 16 <= 32 ? 2u : 1u;
 }
 
-// Workgroups of a stage_rows launch over walk rows [row_begin, row_end).
+constexpr uint32_t stage_rows_per_task(int64_t R) {
+  return stage_lane_groups(R) * stage_lane_groups(R);
+}
+
+// Workgroups of a stage_rows launch over walk rows [row_begin, row_end): one
+// task per wave.
 constexpr uint32_t stage_blocks(const XferArgs &a, uint32_t rows_per_task) {
   const uint32_t tasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
   return (tasks + kWavesPerBlock - 1) / kWavesPerBlock;

@@ -220,11 +220,14 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
   for (int64_t len : chunks) {
     const int64_t r1 = r0 + len;
     set_row_range(&a, (uint32_t)r0, (uint32_t)r1);
-    // the device-side pass (stage_rows): waves take tasks of rows_per_task walk
-    // rows, kStageRows rows at a time, stepping the walk position with
-    // walk_next; lanes move 16-byte chunks k0 + j*64 + lane of each row
+    // the device-side pass (stage_rows): each wave takes tasks of K*K walk rows
+    // (K lane groups of 64/K lanes), batch u's row r0 + u*K + g going to lane
+    // group g, the walk position stepped with walk_next in that order; lane sub
+    // of a group moves 16-byte chunks k0 + sub of its row, in passes of 64/K
     auto dense = [&](bool gather) {
+      const uint32_t K = stage_lane_groups(g.R), lanes = 64 / K;
       const uint32_t rpt = stage_rows_per_task(g.R);
+      CHECK(rpt == K * K, "rows per task");
       const uint32_t blocks = stage_blocks(a, rpt);
       const uint32_t grid = grid_for(blocks, cap);
       const uint32_t cpr16 = (uint32_t)(g.R / 16);
@@ -236,35 +239,34 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
             const uint32_t r0 = a.row_begin + t * rpt;
             const uint32_t r1 = std::min(r0 + rpt, a.row_end);
             WalkPos w = walk_at(a, r0);
-            for (uint32_t r = r0; r < r1; r += kStageRows) {
-              const uint32_t mrows = std::min((uint32_t)kStageRows, r1 - r);
-              for (uint32_t u = 0; u < mrows; u++) {
+            for (uint32_t u = 0; u < K; u++)
+              for (uint32_t gr = 0; gr < K; gr++) {
+                const uint32_t r = r0 + u * K + gr;
+                if (r >= r1) continue;
                 uint32_t i = 0, lc = 0;
-                walk_row(a, r + u, i, lc);  // the stepped position must be the walk's
-                CHECK(w.r == r + u && w.base + w.pos == i && w.lc == lc,
-                      "stepped walk differs at row %u", r + u);
+                walk_row(a, r, i, lc);  // the stepped position must be the walk's
+                CHECK(w.r == r && w.base + w.pos == i && w.lc == lc,
+                      "stepped walk differs at row %u", r);
                 CHECK(i < a.n && lc < a.nlc, "stage walk out of range");
                 if (!(i < a.n && lc < a.nlc)) return;
-                const int64_t srow = (int64_t)(r + u - a.row_begin);
+                const int64_t srow = (int64_t)(r - a.row_begin);
                 CHECK((srow + 1) * g.R <= (int64_t)stage.size(), "stage overrun");
                 uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R;
                 uint8_t *sv = stage.data() + srow * g.R;
-                for (uint32_t k0 = 0; k0 < cpr16; k0 += 64 * kStageChunks)
-                  for (int j = 0; j < kStageChunks; j++)
-                    for (uint32_t lane = 0; lane < 64; lane++) {
-                      const uint32_t k = k0 + j * 64 + lane;
-                      if (k >= cpr16) continue;
-                      if (gather)
-                        std::memcpy(sv + 16 * k, dv + 16 * k, 16);
-                      else
-                        std::memcpy(dv + 16 * k, sv + 16 * k, 16);
-                      for (int h8 = 0; h8 < 2; h8++)
-                        cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) +
-                              2 * k + h8]++;
-                    }
+                for (uint32_t k0 = 0; k0 < cpr16; k0 += lanes)
+                  for (uint32_t sub = 0; sub < lanes; sub++) {
+                    const uint32_t k = k0 + sub;
+                    if (k >= cpr16) continue;
+                    if (gather)
+                      std::memcpy(sv + 16 * k, dv + 16 * k, 16);
+                    else
+                      std::memcpy(dv + 16 * k, sv + 16 * k, 16);
+                    for (int h8 = 0; h8 < 2; h8++)
+                      cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + 2 * k +
+                            h8]++;
+                  }
                 walk_next(a, w);
               }
-            }
           }
     };
     if (to_host) dense(true);
@@ -474,8 +476,9 @@ int main(int argc, char **argv) {
     kv_geometry_t kg{};
     kg.num_layers = (int32_t)uni(1, 5);
     kg.num_components = (int32_t)uni(1, 2);
-    const int64_t rsel = uni(0, 5);
-    kg.row_bytes = rsel == 0 ? 16 : rsel == 1 ? 48 : rsel == 2 ? 272 : rsel == 3 ? 1152 : rsel == 4 ? 2048 : 36864;
+    // row sizes on both sides of the staged pass's lane-group bounds (256, 512 B)
+    const int64_t sizes[] = {16, 48, 256, 272, 512, 528, 1152, 2048, 36864};
+    kg.row_bytes = sizes[uni(0, 8)];
     kg.page_size = (int32_t)(std::vector<int>{1, 2, 3, 4, 16, 64})[uni(0, 5)];
     kg.host_slots = kg.page_size * uni(1, 300 / kg.page_size + 1);
     kg.device_slots = uni(1, 400);
