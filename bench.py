@@ -73,6 +73,9 @@ def parse():
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn two rocprofv3 --pmc output directories (FETCH_SIZE, WRITE_SIZE) "
                         "into profiles/counters.json and exit")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="print the per-kernel, per-grid launch durations of a rocprofv3 "
+                        "--kernel-trace output directory as a markdown table and exit")
     p.add_argument("--summarize-link-counters", nargs=2, metavar=("WRREQ_DIR", "RDREQ_DIR"),
                    help="add the host-link bytes of two rocprofv3 --pmc output directories "
                         "(TCC_EA0_WRREQ*_sum, TCC_EA0_RDREQ*_sum) to profiles/counters.json "
@@ -87,6 +90,9 @@ def main():
         return
     if args.summarize_link_counters:
         summarize_link_counters(*args.summarize_link_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -645,8 +651,8 @@ def _kernel_key(name):
     return ("copy" if "elementwise_kernel" in name and "copy" in name else
             "xfer_rows_d2h" if "xfer_rows<true>" in name else
             "xfer_rows_h2d" if "xfer_rows<false>" in name else
-            "stage_gather" if "stage_rows<true>" in name else
-            "stage_scatter" if "stage_rows<false>" in name else None)
+            "stage_gather" if "stage_rows<true" in name else
+            "stage_scatter" if "stage_rows<false" in name else None)
 
 
 def summarize_link_counters(wr_dir, rd_dir):
@@ -706,6 +712,28 @@ def summarize_link_counters(wr_dir, rd_dir):
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
+
+
+def summarize_trace(trace_dir):
+    """Launch durations (End - Start) of the library's kernels in a rocprofv3
+    kernel trace, grouped by kernel and grid size: dispatches, mean, min, max."""
+    import csv
+    import glob
+    groups = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if "kvt::" not in name:
+                    continue
+                grid = int(r.get("Grid_Size_X") or r.get("Grid_Size") or 0)
+                dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                groups.setdefault((name.split("(")[0].replace("void ", ""), grid), []).append(dur)
+    print("| kernel | grid (threads) | dispatches | mean ns | min ns | max ns |")
+    print("|---|---|---|---|---|---|")
+    for (name, grid), d in sorted(groups.items()):
+        print("| %s | %d | %d | %.1f | %d | %d |" % (name, grid, len(d), statistics.mean(d),
+                                                    min(d), max(d)))
 
 
 def summarize_counters(fetch_dir, write_dir):
