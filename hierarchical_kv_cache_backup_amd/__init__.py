@@ -95,6 +95,7 @@ SIGNATURES = {
     "kv_load": (_I32, [_VP, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_load_layer": (_I32, [_VP, _I32, _VP]),
     "kv_stage": (_I32, [_VP, _I32, _P64, _I64, _I32, _I32, _VP, _VP]),
+    "kv_transfer_noalloc": (_I32, [_VP, _I32, _P64, _P64, _I64, _I32, _I32, _VP]),
     "kv_stream_create": (_I32, [_I32, ctypes.POINTER(_VP)]),
     "kv_stream_destroy": (_I32, [_VP]),
     "kv_set_path": (_I32, [_VP, _I32]),
@@ -289,6 +290,13 @@ def kv_backup(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=No
 def kv_load(pool, dev_idx, host_idx, layer_begin, layer_end, stream=None, n=None):
     d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
     return _lib.kv_load(pool, dp, hp, n, layer_begin, layer_end, _stream_handle(stream))
+
+
+def kv_transfer_noalloc(pool, direction, dev_idx, host_idx, layer_begin, layer_end, stream=None,
+                        n=None):
+    d, dp, h, hp, n = _pair(dev_idx, host_idx, n)
+    return _lib.kv_transfer_noalloc(pool, direction, dp, hp, n, layer_begin, layer_end,
+                                    _stream_handle(stream))
 
 
 def kv_stage(pool, direction, dev_idx, layer_begin, layer_end, stage_ptr, stream=None, n=None):

@@ -197,6 +197,36 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
   }
 }
 
+// Index pairs of a request from its raw index arrays, on the device:
+// tok[2i] = dev_idx[i], tok[2i+1] = the host key of host_idx[i] in the pool's
+// layout (layer_first h; page_first h*L*C; page_first_direct
+// (h/ps)*L*C*ps + h%ps), as the host-side staging writes them.
+__global__ __launch_bounds__(kXferThreads) void pack_pairs(const int64_t *__restrict__ dev_idx,
+                                                           const int64_t *__restrict__ host_idx,
+                                                           int64_t *__restrict__ tok, uint32_t n,
+                                                           int32_t layout, int64_t lc, int32_t ps) {
+  const uint32_t i = blockIdx.x * kXferThreads + threadIdx.x;
+  if (i >= n) return;
+  const int64_t h = host_idx[i];
+  int64_t key = h;
+  if (layout == kLayoutPageFirst) {
+    key = h * lc;
+  } else if (layout == kLayoutPageFirstDirect) {
+    const int64_t q = h / ps;
+    key = q * lc * ps + (h - q * ps);
+  }
+  tok[2 * i] = dev_idx[i];
+  tok[2 * i + 1] = key;
+}
+
+hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, int64_t *tok,
+                             uint32_t n, int32_t layout, int64_t lc, int32_t ps, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_pairs, dim3((n + kXferThreads - 1) / kXferThreads), dim3(kXferThreads),
+                     0, s, dev_idx, host_idx, tok, n, layout, lc, ps);
+  return hipGetLastError();
+}
+
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (to_host)

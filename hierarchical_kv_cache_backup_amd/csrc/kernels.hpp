@@ -16,6 +16,10 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
 // rows (stage_rows_per_task / stage_blocks), so blocks may be smaller.
 hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
                         hipStream_t s);
+// The index pairs {device slot, host key} of n positions from the raw index
+// arrays (all three device pointers): lc = L*C of the pool.
+hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, int64_t *tok,
+                             uint32_t n, int32_t layout, int64_t lc, int32_t ps, hipStream_t s);
 hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t blocks, bool to_host,
                             hipStream_t s);
 

@@ -1032,6 +1032,124 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
   return KV_OK;
 }
 
+// ---- the entry point that allocates nothing (kv_transfer_noalloc) -----------
+
+// A kv_transfer_noalloc call's request lives in a file-scope device array:
+// positions [0, n) of its raw device slots, of its raw host slots, and its
+// index pairs {device slot, host key} (16 bytes each): 8 MiB, 262,144 positions
+// at most. Each GPU holds its own copy until the process ends.
+constexpr int64_t kNoAllocMaxPositions = int64_t(1) << 18;
+static __device__ __align__(256) int64_t scratch[4 * kNoAllocMaxPositions];
+
+// The array's device address on each device, looked up once per device with
+// that device current (each GPU holds the array at its own address). Host code
+// uses these addresses, never the array's name, for kernel arguments and copies.
+constexpr int kNoAllocMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static int64_t *g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+static int scratch_of(int device, int64_t **out) {
+  if (device < 0 || device >= kNoAllocMaxDevices)
+    return fail(KV_EINVAL, "device ordinal beyond the no-allocation scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the no-allocation scratch");
+    if (!ptr) return fail(KV_EHIP, "hipGetSymbolAddress gave no address for the scratch");
+    g_scratch_ptr[device] = static_cast<int64_t *>(ptr);
+  }
+  *out = g_scratch_ptr[device];
+  return KV_OK;
+}
+
+// kv_backup (dir 0) / kv_load (dir 1) on the zero-copy kernel path, with the
+// request's index arrays copied straight from the caller's arrays into the
+// scratch array and paired on the device (pack_pairs), instead of through the
+// pool's pinned and device index staging: nothing is allocated on success.
+static int transfer_noalloc(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *host_idx,
+                            int64_t n, int32_t l0, int32_t l1, void *stream) {
+  const double t0 = now_us();
+  double blocked = 0;
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (dir != 0 && dir != 1) return fail(KV_EINVAL, "direction must be 0 (backup) or 1 (load)");
+  DirState &d = p->dir[dir];
+  std::lock_guard<std::mutex> lock(d.mu);
+  const Geom &g = p->g;
+  std::string why;
+  int rc = validate(g, dir, dev_idx, host_idx, n, l0, l1, (p->flags & KV_F_CHECK_UNIQUE) != 0,
+                    &d.uniq, &why, false);
+  if (rc) return fail(rc, why);
+  if (n > kNoAllocMaxPositions)
+    return fail(KV_EINVAL, "n = " + std::to_string(n) +
+                               " exceeds the no-allocation call's maximum of 262144 positions");
+  if (n == 0 || l0 == l1) return KV_OK;
+  const int64_t nlc_all = (int64_t)(l1 - l0) * g.C;
+  if (n * nlc_all >= kMaxRowsPerLaunch)
+    return fail(KV_EINVAL, "request has >= 2^31 rows; split it into several calls");
+  DeviceGuard dg(p->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipStream_t s = (hipStream_t)stream;
+  if (dir == 0 && p->reader) return shared_backup(p, d, host_idx, n, l0, l1, s, t0);
+  int64_t *sc = nullptr;
+  rc = scratch_of(p->device, &sc);
+  if (rc) return rc;
+  int64_t *raw_dev = sc, *raw_host = sc + kNoAllocMaxPositions, *tok = sc + 2 * kNoAllocMaxPositions;
+  kv_calib_t c;
+  {
+    std::lock_guard<std::mutex> cl(p->calib_mu);
+    c = p->calib;
+  }
+  const int32_t group = load_group(g, c, dir, n, l0, l1);
+  const bool overlap = dir == 1 && (p->flags & KV_F_LOAD_OVERLAP) != 0;
+  const bool duplex = (p->flags & KV_F_DUPLEX) != 0 || other_direction_busy(p, dir, s);
+  const uint32_t cap = kernel_cap(c, dir, overlap, duplex, true);
+  hipError_t e = hipMemcpyAsync(raw_dev, dev_idx, (size_t)n * 8, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(raw_host, host_idx, (size_t)n * 8, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = launch_pack_pairs(raw_dev, raw_host, tok, (uint32_t)n, g.layout, (int64_t)g.L * g.C, g.ps,
+                          s);
+  XferArgs a{};
+  a.tok = tok;
+  a.dev_tab = p->dev_tab;
+  a.host = p->host_dev;
+  a.R = g.R;
+  a.lc_stride = g.lc_stride;
+  a.n = (uint32_t)n;
+  for (int32_t la = l0; la < l1 && e == hipSuccess; la += group) {
+    const int32_t lb = std::min(l1, la + group);
+    XferArgs b = a;
+    b.lc0 = (uint32_t)(la * g.C);
+    b.nlc = (uint32_t)((lb - la) * g.C);
+    const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
+    d.launches++;
+    d.last_workgroups = grid_for(blocks, cap);
+    e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
+    if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
+  }
+  if (e != hipSuccess) return hip_fail(e, "enqueueing the no-allocation transfer");
+  e = hipEventRecord(d.done, s);
+  if (e != hipSuccess) return hip_fail(e, "recording the completion event");
+  d.done_pending = true;
+  d.done_stream.store(s);
+  d.done_recorded.store(true);
+  if (dir == 0) {  // the writer of the host pool: sharing pools' backups wait for this
+    HostShare &sh = *p->share;
+    std::lock_guard<std::mutex> sl(sh.mu);
+    e = hipEventRecord(sh.written, s);
+    if (e != hipSuccess) return hip_fail(e, "recording the host pool's write event");
+    sh.recorded = true;
+    if (sh.check) sh.digest = request_digest(host_idx, n, l0, l1);
+  }
+  d.last_path.store(KV_PATH_KERNEL);
+  d.calls++;
+  d.bytes += n * nlc_all * g.R;
+  d.blocked_us += blocked;
+  d.submit_us += now_us() - t0 - blocked;
+  return KV_OK;
+}
+
 // The staged path's device-side pass on its own (kv_stage): packs (dir 0) or
 // unpacks (dir 1) the request's rows between the device buffers and the
 // caller's device buffer `stage`, on the caller's stream, in the walk order the
@@ -1232,6 +1350,15 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
     p->bufs[k] = b;
   }
 
+  if (desc->flags & KV_F_CHECK_UNIQUE) {  // tables kv_transfer_noalloc checks with
+    try {
+      p->dir[0].uniq.stamp.assign((size_t)std::min(g.S_host, kStampSlotsPresize), 0u);
+      p->dir[1].uniq.stamp.assign((size_t)std::min(g.S_dev, kStampSlotsPresize), 0u);
+    } catch (const std::bad_alloc &) {
+      delete p;
+      return fail(KV_ENOMEM, "allocating the uniqueness tables");
+    }
+  }
   if (group) {  // the group's host pool
     p->share = group->share;
     p->reader = true;
@@ -1351,6 +1478,14 @@ int kv_load(kv_pool_t *p, const int64_t *dev_idx, const int64_t *host_idx, int64
             int32_t layer_begin, int32_t layer_end, void *stream) {
   return guarded("kv_load", [&] {
     return transfer(p, 1, dev_idx, host_idx, n, layer_begin, layer_end, stream);
+  });
+}
+
+int kv_transfer_noalloc(kv_pool_t *p, int32_t direction, const int64_t *dev_idx,
+                        const int64_t *host_idx, int64_t n, int32_t layer_begin,
+                        int32_t layer_end, void *stream) {
+  return guarded("kv_transfer_noalloc", [&] {
+    return transfer_noalloc(p, direction, dev_idx, host_idx, n, layer_begin, layer_end, stream);
   });
 }
 

@@ -76,15 +76,23 @@ int make_geom(const kv_geometry_t *in, Geom *g, std::string *why) {
 }
 
 // First position whose slot appeared earlier in dst[0, n) (-1: none), slots in
-// [0, slots). KV_ENOMEM if the check's memory cannot be had.
+// [0, slots). KV_ENOMEM if the check's memory cannot be had. Without
+// may_allocate only a stamp table already covering the slots can be used, else
+// KV_EINVAL.
 static int first_repeat(const int64_t *dst, int64_t n, int64_t slots, UniqueScratch *scratch,
-                        int64_t *dup, std::string *why) {
+                        int64_t *dup, std::string *why, bool may_allocate) {
   *dup = -1;
+  const bool table = (int64_t)scratch->stamp.size() >= slots;
+  if (!table && !may_allocate) {
+    *why = "the pool's uniqueness table does not cover its destination slots (more than "
+           "2^26), so the check cannot run without allocating";
+    return KV_EINVAL;
+  }
   try {
-    if (slots <= std::max<int64_t>(kStampSlotsMin, 4 * n)) {
+    if (table || slots <= std::max<int64_t>(kStampSlotsMin, 4 * n)) {
       // one stamp per slot, kept between calls; a generation counter instead
       // of clearing
-      if ((int64_t)scratch->stamp.size() < slots) scratch->stamp.assign(slots, 0);
+      if (!table) scratch->stamp.assign(slots, 0);
       if (++scratch->gen == 0) {  // wrapped: clear once every 2^32 calls
         std::fill(scratch->stamp.begin(), scratch->stamp.end(), 0u);
         scratch->gen = 1;
@@ -113,7 +121,7 @@ static int first_repeat(const int64_t *dst, int64_t n, int64_t slots, UniqueScra
 
 int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t *host_idx,
              int64_t n, int32_t l0, int32_t l1, bool check_unique, UniqueScratch *scratch,
-             std::string *why) {
+             std::string *why, bool may_allocate) {
   if (direction != 0 && direction != 1) {
     *why = "direction must be 0 (backup) or 1 (load)";
     return KV_EINVAL;
@@ -143,7 +151,8 @@ int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t
   if (check_unique && n > 1) {
     const int64_t *dst = direction == 0 ? host_idx : dev_idx;
     int64_t dup = -1;
-    const int rc = first_repeat(dst, n, direction == 0 ? g.S_host : g.S_dev, scratch, &dup, why);
+    const int rc = first_repeat(dst, n, direction == 0 ? g.S_host : g.S_dev, scratch, &dup, why,
+                                may_allocate);
     if (rc) return rc;
     if (dup >= 0) {
       *why = fmt(direction == 0 ? "host slot %lld is a destination twice (position %lld)"
@@ -180,7 +189,7 @@ int validate_stage(const Geom &g, int direction, const int64_t *dev_idx, int64_t
     }
   if (check_unique && direction == 1 && n > 1) {
     int64_t dup = -1;
-    const int rc = first_repeat(dev_idx, n, g.S_dev, scratch, &dup, why);
+    const int rc = first_repeat(dev_idx, n, g.S_dev, scratch, &dup, why, true);
     if (rc) return rc;
     if (dup >= 0) {
       *why = fmt("device slot %lld is a destination twice (position %lld)", dev_idx[dup], dup);

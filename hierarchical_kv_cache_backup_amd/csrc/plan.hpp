@@ -54,17 +54,24 @@ inline int64_t host_row(const Geom &g, int32_t l, int32_t c, int64_t h) {
 // slot and a generation counter, so no clearing between calls. Used while the
 // pool has at most max(kStampSlotsMin, 4 n) destination slots; beyond that the
 // check sorts a copy of the request instead (O(n log n), no per-slot memory).
+// A table that already covers the pool's slots is always used. A pool made
+// with the uniqueness check sizes its tables at creation for up to
+// kStampSlotsPresize slots, so that kv_transfer_noalloc can check without
+// allocating.
 constexpr int64_t kStampSlotsMin = int64_t(1) << 22;
+constexpr int64_t kStampSlotsPresize = int64_t(1) << 26;
 struct UniqueScratch {
   std::vector<uint32_t> stamp;
   uint32_t gen = 0;
 };
 
 // Request validation (rules and their order are those documented for
-// kv_validate). `scratch` may be null when check_unique is false.
+// kv_validate). `scratch` may be null when check_unique is false. Without
+// may_allocate the uniqueness check uses only a table that already covers the
+// destination slots (else KV_EINVAL): on success nothing is allocated.
 int validate(const Geom &g, int direction, const int64_t *dev_idx, const int64_t *host_idx,
              int64_t n, int32_t l0, int32_t l1, bool check_unique, UniqueScratch *scratch,
-             std::string *why);
+             std::string *why, bool may_allocate = true);
 
 // Validation of kv_stage (the staged path's device-side pass on its own): the
 // rules of validate without the host side. Only an unpack (direction 1) writes

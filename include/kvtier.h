@@ -385,6 +385,27 @@ int kv_backup(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, 
 int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, int64_t n,
             int32_t layer_begin, int32_t layer_end, void *stream);
 
+/* kv_backup (direction 0) or kv_load (direction 1) that allocates nothing, for
+ * callers that cannot allocate device or pinned memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. It always
+ * takes the zero-copy kernel path (KV_PATH_KERNEL; kv_last_path reports it),
+ * with that path's grid caps, load groups and landed events, so kv_load_layer
+ * works after it as after kv_load. Instead of the pool's index staging, the
+ * request's index arrays are copied from the caller's host arrays (read during
+ * the call only) into a device array the library holds for each GPU from its
+ * first such call until the process ends: 8 MiB, n <= 262144 positions
+ * (a larger n: KV_EINVAL, nothing enqueued). The index pairs are formed there
+ * on the device. Every call on one GPU shares that GPU's array: calls issued on
+ * one stream are ordered, but calls that overlap on one GPU (other streams,
+ * or other threads without ordering) race and may move the wrong rows. With
+ * KV_F_CHECK_UNIQUE the destination check uses the table kv_pool_create sized
+ * for the pool (pools of more than 2^26 destination slots: KV_EINVAL). On
+ * success the call allocates nothing; a failure's message may. Errors as
+ * kv_backup / kv_load, and KV_EINVAL for a direction other than 0 or 1. */
+int kv_transfer_noalloc(kv_pool_t *pool, int32_t direction, const int64_t *dev_idx,
+                        const int64_t *host_idx, int64_t n, int32_t layer_begin,
+                        int32_t layer_end, void *stream);
+
 /* The staged path's device-side pass on its own: the batched gather/scatter
  * that packs a request's scattered device rows into one contiguous,
  * host-ordered buffer in HBM, so that a single large copy moves it ("Baidu's
