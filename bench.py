@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--size-sweep", action="store_true",
                    help="only time write-backs and loads of 64..32768 tokens on every path "
                         "and layout (one JSON line per size on stderr), then exit")
+    p.add_argument("--overlap-study", action="store_true",
+                   help="only sweep the kernel path's grid for loads beside compute "
+                        "(KV_F_LOAD_OVERLAP) and for write-backs beside compute, on the "
+                        "streamed workload, then exit")
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -114,6 +118,9 @@ def main():
         return
     if args.size_sweep:
         print(json.dumps(size_sweep(torch, kvt, workloads)))
+        return
+    if args.overlap_study:
+        print(json.dumps(overlap_study(torch, kvt, workloads)))
         return
     if args.tp_shared_study:
         print(json.dumps(tp_shared_study(torch, kvt, workloads, args.tp_shared_study)))
@@ -1246,6 +1253,128 @@ def leg_streamed(torch, kvt, workloads, args):
                             "its pass over layer 0 60 times; slowdown against the consumer "
                             "alone", "consumer_alone_ms": round(t_alone * 1e3, 3),
                 "paths": writeback}}
+
+
+def overlap_study(torch, kvt, workloads, layers=24):
+    """The kernel path's grid beside an HBM-bound consumer, on the streamed
+    workload's first `layers` layers (256 MiB each, K and V): (1) a per-layer
+    load flagged KV_F_LOAD_OVERLAP, overlapped layer by layer with the consumer
+    (as in the streamed leg), for overlap grid caps of 32 to 256 workgroups and
+    the full grid; (2) a write-back of layers 1.. beside the consumer's repeated
+    pass over layer 0, for write-back caps of 8 to 64 and the full grid; and the
+    copy path for both, as reference."""
+    shape = workloads.streamed()
+    L, C, R, ps = layers, shape.components, shape.row_bytes, shape.page_size
+    S, n = shape.device_slots, shape.extra["tokens"]
+    dev_idx, host_idx = workloads.prefix_indices(shape, 5, n, fragmented=False)
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, 5, l, c, torch)
+            bufs.append(b)
+    s_load, s_comp = kvt.Stream(), torch.cuda.Stream()
+    acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+    torch.cuda.synchronize()
+    layer_bytes = n * C * R
+
+    def consume(l, k):
+        for _ in range(k):
+            for c in range(C):
+                acc.add_(bufs[l * C + c].view(torch.int64).sum())
+
+    def timed_consume(l, k):
+        with torch.cuda.stream(s_comp):
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s_comp)
+            consume(l, k)
+            e1.record(s_comp)
+            e1.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    timed_consume(0, 2)
+    t_pass = timed_consume(0, 10) / 10
+    geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
+    loads, backs = {}, {}
+    with kvt.KvPool(geom, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP) as pool:
+        pool.set_path(kvt.PATH_KERNEL)
+        pool.backup(dev_idx, host_idx, 0, L, s_load)
+        s_load.synchronize()
+        for cap in (32, 64, 96, 128, 256, 0, "dma"):
+            cal = pool.calibration()
+            if cap == "dma":
+                pool.set_path(kvt.PATH_DMA)
+            else:
+                cal.overlap_kernel_max_workgroups = cap
+                pool.set_calibration(cal)
+            pool.load(dev_idx, host_idx, 0, L, s_load)
+            s_load.synchronize()
+            e0, e1 = _ev(torch), _ev(torch)
+            e0.record(s_load.torch)
+            pool.load(dev_idx, host_idx, 0, L, s_load)
+            e1.record(s_load.torch)
+            e1.synchronize()
+            t_h2d = e0.elapsed_time(e1) / 1e3
+            k = max(1, round(t_h2d / L / t_pass))
+            t_comp = sum(timed_consume(l, k) for l in range(L))
+            walls, rates, comp = [], [], []
+            for rep in range(3):
+                torch.cuda.synchronize()
+                ev = [_ev(torch) for _ in range(3)]
+                lev = [(_ev(torch), _ev(torch)) for _ in range(L)]
+                ev[0].record(s_load.torch)
+                s_comp.wait_event(ev[0])
+                pool.load(dev_idx, host_idx, 0, L, s_load)
+                ev[1].record(s_load.torch)
+                with torch.cuda.stream(s_comp):
+                    for l in range(L):
+                        pool.load_layer(l, s_comp)
+                        lev[l][0].record(s_comp)
+                        consume(l, k)
+                        lev[l][1].record(s_comp)
+                    ev[2].record(s_comp)
+                ev[2].synchronize()
+                s_load.synchronize()
+                walls.append(ev[0].elapsed_time(ev[2]) / 1e3)
+                rates.append(L * layer_bytes / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
+                comp.append(sum(a.elapsed_time(b) for a, b in lev) / 1e3)
+            wall = statistics.median(walls)
+            key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
+            loads[key] = {"h2d_alone_gbps": round(L * layer_bytes / t_h2d / 1e9, 2),
+                          "h2d_overlapped_gbps": round(statistics.median(rates), 2),
+                          "compute_slowdown": round(statistics.median(comp) / t_comp, 3),
+                          "overlap_efficiency": round((t_h2d + t_comp - wall) / min(t_h2d, t_comp), 3)}
+            log("overlap study load %s %s" % (key, json.dumps(loads[key])))
+        pool.set_path(kvt.PATH_KERNEL)
+        t_alone = statistics.median([timed_consume(0, 40) for _ in range(3)])
+        wb_bytes = n * (L - 1) * C * R
+        for cap in (8, 16, 24, 32, 48, 64, 0, "dma"):
+            cal = pool.calibration()
+            if cap == "dma":
+                pool.set_path(kvt.PATH_DMA)
+            else:
+                cal.kernel_max_workgroups[0] = cap
+                pool.set_calibration(cal)
+            slow, rates = [], []
+            for rep in range(3):
+                torch.cuda.synchronize()
+                e0, e1 = _ev(torch), _ev(torch)
+                e0.record(s_load.torch)
+                pool.backup(dev_idx, host_idx, 1, L, s_load)
+                e1.record(s_load.torch)
+                slow.append(timed_consume(0, 40) / t_alone)
+                e1.synchronize()
+                rates.append(wb_bytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
+            key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
+            backs[key] = {"d2h_gbps_beside_compute": round(statistics.median(rates), 2),
+                          "compute_slowdown": round(statistics.median(slow), 3)}
+            log("overlap study write-back %s %s" % (key, json.dumps(backs[key])))
+    s_load.close()
+    return {"study": "kernel-path grid beside an HBM-bound consumer (torch int64 sums of "
+                     "each layer's K and V)",
+            "workload": "%d layers x K/V x 1024 B fp8, 131072-token prefix, layer_first" % L,
+            "consumer_pass_ms": round(t_pass * 1e3, 3),
+            "load_overlap_caps": loads, "write_back_caps": backs}
 
 
 def leg_ghost_list(kvt, workloads):

@@ -242,12 +242,15 @@ void default_calibration(kv_calib_t *c) {
   // load beside compute is KV_F_LOAD_OVERLAP's case).
   c->kernel_max_workgroups[0] = 24;
   c->kernel_max_workgroups[1] = 0;
-  // Measured on MI355X with a 61-layer streamed load and an HBM-bound consumer:
-  // the consumer ran ~1.65x longer beside the kernel path (128-workgroup grid)
-  // and ~1.15x longer beside the copy engines.
-  c->overlap_kernel_penalty = 0.65;
+  // Measured on MI355X with a streamed 24-layer load (256 MiB per layer) and an
+  // HBM-bound consumer (torch int64 sums) overlapped layer by layer: the
+  // consumer's slowdown beside the kernel path grows with the load's grid (32
+  // workgroups 1.39x at 24 GB/s, 64 1.43x at 47, 96 1.52x at 55.7, 128 1.61x,
+  // full grid 1.87x), beside the copy path it is 1.15x at 56.8 GB/s. 96
+  // workgroups is the smallest grid that still keeps the link near full.
+  c->overlap_kernel_penalty = 0.52;
   c->overlap_dma_penalty = 0.15;
-  c->overlap_kernel_max_workgroups = 128;
+  c->overlap_kernel_max_workgroups = 96;
   // Concurrent 1 GiB H2D + D2H (GB/s, H2D / D2H): copy engines both ways
   // 56.4 / 48.5; H2D kernel beside D2H copy engines 56.4 / 31.0; H2D copy
   // engines beside a D2H kernel 42.3 / 51.3; kernels both ways 37.8 / 38.1.

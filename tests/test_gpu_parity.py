@@ -285,7 +285,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
     (default 24); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
     on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load), at most
-    overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP, and the
+    overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP (default 96), and the
     smallest cap that applies; without a cap a launch has one workgroup per
     block of work. The bytes match the oracle under every cap."""
     g = Geometry(4, 2, 2048, 4096, 4096, 64, 0)
@@ -333,7 +333,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
     got = grids(overlap, kvt.PATH_KERNEL)
-    assert got == (24, 128), got                    # the overlap cap is a load's only
+    assert got == (24, 96), got                     # the overlap cap is a load's only
     overlap.close()
 
 
@@ -532,7 +532,7 @@ def test_overlap_flag_steers_selector(torch, stream):
         pool = make_pool(g, bufs, kvt.PATH_AUTO, flags=flags)
         c = pool.calibration()
         # two 1-D copies at 10 us each against one launch at 15 us: the kernel wins
-        # alone; charged the default overlap penalties (x1.65 vs x1.15) the copy
+        # alone; charged overlap penalties of x1.65 vs x1.15 the copy
         # engines win
         c.kernel_launch_us[1], c.dma_copy_us[1] = 15.0, 10.0
         c.kernel_gbps[1] = c.dma_gbps[1] = 1e6
