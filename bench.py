@@ -602,8 +602,9 @@ def staged_pass_roofline(torch, kvt, pool, s, dev_b, dev_l, L, C, R, n, args, sr
     for key, t, cnt, what in (("stage_gather", tg, ng, "pack (gather)"),
                               ("stage_scatter", ts, ns, "unpack (scatter)")):
         achieved = 2 * payload / t / 1e9
-        out[key] = {"kernel": "kvt::stage_rows<%s> (staged pass, %s of the whole prefix in one "
-                              "launch)" % ("true" if key == "stage_gather" else "false", what),
+        out[key] = {"kernel": "kvt::stage_rows<%s, 1u> (staged pass, %s of the whole prefix in "
+                              "one launch; one lane group per wave for 1152-byte rows)"
+                              % ("true" if key == "stage_gather" else "false", what),
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                     "traffic": counter_traffic(key, src_hash),
