@@ -1349,7 +1349,7 @@ def overlap_study(torch, kvt, workloads, layers=24):
         pool.set_path(kvt.PATH_KERNEL)
         t_alone = statistics.median([timed_consume(0, 40) for _ in range(3)])
         wb_bytes = n * (L - 1) * C * R
-        for cap in (8, 16, 24, 32, 48, 64, 0, "dma"):
+        for cap in (8, 16, 20, 22, 24, 25, 26, 27, 28, 30, 32, 48, 64, 0, "dma"):
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
