@@ -85,7 +85,7 @@ static int first_repeat(const int64_t *dst, int64_t n, int64_t slots, UniqueScra
   const bool table = (int64_t)scratch->stamp.size() >= slots;
   if (!table && !may_allocate) {
     *why = "the pool's uniqueness table does not cover its destination slots (more than "
-           "2^26), so the check cannot run without allocating";
+           "2^24 and no earlier call sized it), so the check cannot run without allocating";
     return KV_EINVAL;
   }
   try {

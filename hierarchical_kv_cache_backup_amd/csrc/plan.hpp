@@ -59,7 +59,7 @@ inline int64_t host_row(const Geom &g, int32_t l, int32_t c, int64_t h) {
 // kStampSlotsPresize slots, so that kv_transfer_noalloc can check without
 // allocating.
 constexpr int64_t kStampSlotsMin = int64_t(1) << 22;
-constexpr int64_t kStampSlotsPresize = int64_t(1) << 26;
+constexpr int64_t kStampSlotsPresize = int64_t(1) << 24;  // 64 MiB per direction at most
 struct UniqueScratch {
   std::vector<uint32_t> stamp;
   uint32_t gen = 0;

@@ -398,8 +398,10 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
  * on the device. Every call on one GPU shares that GPU's array: calls issued on
  * one stream are ordered, but calls that overlap on one GPU (other streams,
  * or other threads without ordering) race and may move the wrong rows. With
- * KV_F_CHECK_UNIQUE the destination check uses the table kv_pool_create sized
- * for the pool (pools of more than 2^26 destination slots: KV_EINVAL). On
+ * KV_F_CHECK_UNIQUE the destination check uses the per-slot table kv_pool_create
+ * sizes for pools of up to 2^24 destination slots (4 bytes per slot); a larger
+ * pool's table exists only once a kv_backup / kv_load of that direction has
+ * sized it, else the call returns KV_EINVAL. On
  * success the call allocates nothing; a failure's message may. Errors as
  * kv_backup / kv_load, and KV_EINVAL for a direction other than 0 or 1. */
 int kv_transfer_noalloc(kv_pool_t *pool, int32_t direction, const int64_t *dev_idx,

@@ -125,3 +125,21 @@ def test_noalloc_refuses_oversized_and_bad_requests(torch):
     assert kvt.kv_transfer_noalloc(None, kvt.LOAD, [3], [2], 0, 1, s) == kvt.EINVAL
     assert kvt.kv_transfer_noalloc(pool.handle, kvt.LOAD, [], [], 0, 1, s) == kvt.OK
     pool.close()
+
+
+def test_noalloc_uniqueness_table_bound(torch):
+    """A pool flagged KV_F_CHECK_UNIQUE sizes its uniqueness tables at creation
+    for up to 2^24 destination slots. Past that, a no-allocation write-back is
+    refused (its destinations are host slots); a load into the small device
+    pool still runs."""
+    S_host = (1 << 24) + 16
+    g = Geometry(1, 1, 16, 4096, S_host, 16, oracle.LAYER_FIRST)
+    bufs = device_buffers(g, seed=13, fill=9)
+    pool = kvt.KvPool(kv_geom(g), bufs)
+    s = torch.cuda.Stream()
+    idx = np.arange(4, dtype=np.int64)
+    assert kvt.kv_transfer_noalloc(pool.handle, kvt.BACKUP, idx, idx, 0, 1, s) == kvt.EINVAL
+    assert "2^24" in kvt.kv_last_error()
+    assert kvt.kv_transfer_noalloc(pool.handle, kvt.LOAD, idx, idx + S_host - 4, 0, 1, s) == kvt.OK
+    s.synchronize()
+    pool.close()
