@@ -332,6 +332,7 @@ def main():
     # ---- layout x path matrix at the same geometry
     matrix = []
     if not args.no_matrix:
+        settle(torch, SETTLE_BYTES)       # the roofline's staging tensors were freed
         for spec in matrix_specs(torch, kvt, workloads, shape, bufs, dev_b, dev_l, host_idx):
             matrix += transfer_matrix(torch, kvt, spec, s, link_peak, calib, args)
             del spec
@@ -846,7 +847,24 @@ def transfer_matrix(torch, kvt, spec, s, link_peak, calib, args):
                     " ".join("%s %.1f" % (k, cell[k]["gbps"]) for k, _ in MATRIX_PATHS
                              if k in cell)))
                 rows.append(cell)
+        settle(torch, L * C * spec["S_host"] * R)     # the pool's host memory was freed
     return rows
+
+
+# After the process frees gigabytes of device or pinned host memory, the
+# runtime's copies between device and host run slower for about a second
+# (driver-side work after the free): write-back copies of the next cell then
+# measured up to ~45% below their rate, while the library's kernels ran at
+# theirs. A matrix cell measures a path, not the previous cell's teardown, so
+# after such a free the matrix waits before it times anything.
+SETTLE_BYTES = 1 << 30
+SETTLE_S = 1.5
+
+
+def settle(torch, freed_bytes):
+    if freed_bytes >= SETTLE_BYTES:
+        torch.cuda.synchronize()
+        time.sleep(SETTLE_S)
 
 
 def matrix_specs(torch, kvt, workloads, shape, bufs, dev_b, dev_l, host_idx):
@@ -898,9 +916,11 @@ def matrix_specs(torch, kvt, workloads, shape, bufs, dev_b, dev_l, host_idx):
                "dev_b": workloads.page_indices(pb, sh.page_size),
                "dev_l": workloads.page_indices(pl, sh.page_size),
                "host_idx": np.arange(tokens, dtype=np.int64), "paths": no_lds}
+        freed = sum(b.numel() for b in b2)
         del b2
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+        settle(torch, freed)
 
 
 def _ev(torch):
