@@ -583,18 +583,21 @@ def staged_pass_roofline(torch, kvt, pool, s, dev_b, dev_l, L, C, R, n, args, sr
     stage = torch.empty(payload, dtype=torch.uint8, device="cuda:0")
 
     def measure(direction, idx):
+        # calls back to back, an event after each: once the GPU runs behind the
+        # host, the interval between two events is one call's GPU time (its
+        # index copy and its launch); the first interval, which also holds the
+        # host's submission of the first call, is dropped
         for _ in range(2):
             pool.stage(direction, idx, stage, 0, L, s)
         s.synchronize()
-        durs = []
-        for _ in range(max(5, args.steps)):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(s)
+        calls = max(5, args.steps) + 1
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+        evs[0].record(s)
+        for k in range(calls):
             pool.stage(direction, idx, stage, 0, L, s)
-            e1.record(s)
-            e1.synchronize()
-            durs.append(e0.elapsed_time(e1) / 1e3)
+            evs[k + 1].record(s)
+        evs[-1].synchronize()
+        durs = [evs[k].elapsed_time(evs[k + 1]) / 1e3 for k in range(1, calls)]
         return statistics.mean(durs), len(durs)
 
     (tg, ng), (ts, ns) = measure(0, dev_b), measure(1, dev_l)
@@ -603,8 +606,8 @@ def staged_pass_roofline(torch, kvt, pool, s, dev_b, dev_l, L, C, R, n, args, sr
     for key, t, cnt, what in (("stage_gather", tg, ng, "pack (gather)"),
                               ("stage_scatter", ts, ns, "unpack (scatter)")):
         achieved = 2 * payload / t / 1e9
-        out[key] = {"kernel": "kvt::stage_rows<%s, 1u> (staged pass, %s of the whole prefix in "
-                              "one launch; one lane group per wave for 1152-byte rows)"
+        out[key] = {"kernel": "kvt::stage_windows<%s, true> (staged pass, %s of the whole prefix "
+                              "in one launch; one 1 KiB window of the staging buffer per wave)"
                               % ("true" if key == "stage_gather" else "false", what),
                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -660,8 +663,8 @@ def _kernel_key(name):
     return ("copy" if "elementwise_kernel" in name and "copy" in name else
             "xfer_rows_d2h" if "xfer_rows<true>" in name else
             "xfer_rows_h2d" if "xfer_rows<false>" in name else
-            "stage_gather" if "stage_rows<true" in name else
-            "stage_scatter" if "stage_rows<false" in name else None)
+            "stage_gather" if "stage_windows<true" in name else
+            "stage_scatter" if "stage_windows<false" in name else None)
 
 
 def summarize_link_counters(wr_dir, rd_dir):

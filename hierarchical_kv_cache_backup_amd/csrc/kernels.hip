@@ -79,63 +79,78 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
 
 // Staged path, device side (HBM to HBM): kGather packs the walk rows
 // [row_begin, row_end) from the device buffers into a dense staging buffer
-// (a.host: walk row r at (r - row_begin) * R), the scatter unpacks them. A wave
-// is K lane groups of 64/K lanes; its task is K batches of K consecutive walk
-// rows. The wave steps the walk position row by row (uniform across the wave,
-// so it lives in scalar registers), loads each row's device slot once, and
-// hands the row's two addresses to its lane group, whose lanes move the row's
-// 16-byte chunks, lane-consecutive, in passes of 64/K chunks. Each wave takes
-// one task of a large grid: many small tasks keep more of HBM busy than a few
-// long ones.
+// (a.host: walk row r at (r - row_begin) * R), the scatter unpacks them. Each
+// wave moves one 1 KiB window of the staging buffer's chunk stream per
+// iteration (stage_window / stage_lane): one 16-byte chunk per lane, so every
+// pass is full whatever the row size, and each wave's work is short, which
+// keeps more of HBM busy than long per-wave tasks do. Wide rows take their
+// two possible device addresses in scalar registers (the window's position is
+// uniform across the wave); narrow rows resolve one row per lane and pass the
+// addresses across the wave.
 typedef uint32_t vec16_t __attribute__((ext_vector_type(4)));
 // The same 16 bytes addressed in the global address space: the device buffers
 // and the staging buffer are device memory, and naming that lets the compiler
 // emit global rather than flat accesses.
 typedef __attribute__((address_space(1))) vec16_t gvec16_t;
 
-template <bool kGather, uint32_t K>
-__global__ __launch_bounds__(kXferThreads) void stage_rows(
-    XferArgs a, uint32_t rows_per_task, const int64_t *__restrict__ tok,
+namespace {
+
+__device__ __forceinline__ gvec16_t *stage_row(const XferArgs &a, const WalkPos &w,
+                                               const int64_t *__restrict__ tok,
+                                               uint8_t *const *__restrict__ dev_tab) {
+  return (gvec16_t *)(dev_tab[a.lc0 + w.lc] + tok[2 * (w.base + w.pos)] * a.R);
+}
+
+// The value `v` of lane `src` (ds_bpermute addresses lanes in bytes).
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src << 2), (int)v);
+}
+
+}  // namespace
+
+template <bool kGather, bool kWide>
+__global__ __launch_bounds__(kXferThreads) void stage_windows(
+    XferArgs a, uint32_t recip, const int64_t *__restrict__ tok,
     uint8_t *const *__restrict__ dev_tab) {
-  constexpr uint32_t kLanes = 64 / K;  // lanes per row
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t grp = lane / kLanes, sub = lane % kLanes;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t cpr = (uint32_t)(a.R >> 4);  // 16-byte chunks per row
-  const uint32_t ntasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
-  for (uint32_t t = blockIdx.x * kWavesPerBlock + wave; t < ntasks;
-       t += gridDim.x * kWavesPerBlock) {
-    const uint32_t r0 = a.row_begin + t * rows_per_task;
-    const uint32_t r1 = min(r0 + rows_per_task, a.row_end);
-    WalkPos w = walk_at(a, r0);
-    gvec16_t *dev[K];
-    gvec16_t *stg[K];
-#pragma unroll
-    for (uint32_t u = 0; u < K; u++) {  // batch u: rows r0 + u*K + g for group g
-      dev[u] = stg[u] = nullptr;
-#pragma unroll
-      for (uint32_t g = 0; g < K; g++) {
-        const uint32_t r = r0 + u * K + g;
-        if (r < r1) {
-          gvec16_t *d = (gvec16_t *)(dev_tab[a.lc0 + w.lc] + tok[2 * (w.base + w.pos)] * a.R);
-          gvec16_t *st = (gvec16_t *)(a.host + (int64_t)(r - a.row_begin) * a.R);
-          if (grp == g) {
-            dev[u] = d;
-            stg[u] = st;
-          }
-          walk_next(a, w);
-        }
+  const uint32_t cpr = stage_cpr(a.R);
+  const uint32_t total = stage_chunks(a);
+  const uint32_t nwin = stage_windows(a);
+  gvec16_t *const stg = (gvec16_t *)a.host;
+  for (uint32_t w = blockIdx.x * kWavesPerBlock + wave; w < nwin;
+       w += gridDim.x * kWavesPerBlock) {
+    const StageWindow s = stage_window(a, w, recip);
+    gvec16_t *d = nullptr;
+    if (kWide) {
+      // stage_lane's mapping with the per-lane part reduced to a compare: the
+      // lanes below split = cpr - ka move chunk ka + lane of the first row,
+      // the others chunk lane - split of the second
+      WalkPos wp = walk_at(a, a.row_begin + s.ra);
+      gvec16_t *const first = stage_row(a, wp, tok, dev_tab);
+      gvec16_t *second = first;
+      if (s.rows > 1) {
+        walk_next(a, wp);
+        second = stage_row(a, wp, tok, dev_tab);
       }
+      const uint32_t split = cpr - s.ka;
+      d = (lane < split ? first + s.ka : second - split) + lane;
+    } else {
+      uint32_t j = 0, k = 0;
+      stage_lane(s, cpr, recip, lane, j, k);
+      uint64_t mine = 0;
+      if (lane < s.rows) {
+        const WalkPos wp = walk_at(a, a.row_begin + s.ra + lane);
+        mine = (uint64_t)stage_row(a, wp, tok, dev_tab);
+      }
+      d = (gvec16_t *)((uint64_t)lane_value((uint32_t)mine, j) |
+                       ((uint64_t)lane_value((uint32_t)(mine >> 32), j) << 32)) + k;
     }
-    for (uint32_t k0 = 0; k0 < cpr; k0 += kLanes) {
-      const uint32_t k = k0 + sub;
-      vec16_t v[K];
-#pragma unroll
-      for (uint32_t u = 0; u < K; u++)
-        if (dev[u] && k < cpr) v[u] = __builtin_nontemporal_load((kGather ? dev[u] : stg[u]) + k);
-#pragma unroll
-      for (uint32_t u = 0; u < K; u++)
-        if (dev[u] && k < cpr) __builtin_nontemporal_store(v[u], (kGather ? stg[u] : dev[u]) + k);
+    const uint32_t c = s.c0 + lane;
+    if (c < total) {
+      gvec16_t *const st = stg + c;
+      const vec16_t v = __builtin_nontemporal_load(kGather ? d : st);
+      __builtin_nontemporal_store(v, kGather ? st : d);
     }
   }
 }
@@ -236,21 +251,31 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
-                        hipStream_t s) {
-  if (blocks == 0) return hipSuccess;
+hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_t s,
+                        uint32_t *launches) {
   const int64_t *tok = a.tok;
   uint8_t *const *tab = (uint8_t *const *)a.dev_tab;
-  const dim3 grid(blocks), block(kXferThreads);
-  switch (stage_lane_groups(a.R) * 2 + (gather ? 1 : 0)) {
-    case 9: hipLaunchKernelGGL((stage_rows<true, 4>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
-    case 8: hipLaunchKernelGGL((stage_rows<false, 4>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
-    case 5: hipLaunchKernelGGL((stage_rows<true, 2>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
-    case 4: hipLaunchKernelGGL((stage_rows<false, 2>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
-    case 3: hipLaunchKernelGGL((stage_rows<true, 1>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
-    default: hipLaunchKernelGGL((stage_rows<false, 1>), grid, block, 0, s, a, rows_per_task, tok, tab); break;
+  const uint32_t cpr = stage_cpr(a.R);
+  const uint32_t recip = stage_wide(a.R) ? 0u : stage_recip(cpr);
+  const uint32_t step = stage_max_rows(a.R);
+  const dim3 block(kXferThreads);
+  for (uint32_t r = a.row_begin; r < a.row_end; r += step) {
+    XferArgs p = a;
+    p.row_begin = r;
+    p.row_end = a.row_end - r > step ? r + step : a.row_end;
+    p.host = a.host + (int64_t)(r - a.row_begin) * a.R;
+    const dim3 grid(grid_for(stage_blocks(p), cap));
+    switch ((stage_wide(a.R) ? 2 : 0) + (gather ? 1 : 0)) {
+      case 3: hipLaunchKernelGGL((stage_windows<true, true>), grid, block, 0, s, p, recip, tok, tab); break;
+      case 2: hipLaunchKernelGGL((stage_windows<false, true>), grid, block, 0, s, p, recip, tok, tab); break;
+      case 1: hipLaunchKernelGGL((stage_windows<true, false>), grid, block, 0, s, p, recip, tok, tab); break;
+      default: hipLaunchKernelGGL((stage_windows<false, false>), grid, block, 0, s, p, recip, tok, tab); break;
+    }
+    if (launches) (*launches)++;
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t blocks, bool to_host,

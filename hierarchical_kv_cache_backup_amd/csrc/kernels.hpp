@@ -12,10 +12,12 @@ namespace kvt {
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s);
 // The staged path's device-side pass over walk rows [a.row_begin, a.row_end):
 // gather packs them from the device buffers into the staging buffer a.host,
-// the scatter unpacks them. The waves stride over the tasks of rows_per_task
-// rows (stage_rows_per_task / stage_blocks), so blocks may be smaller.
-hipError_t launch_stage(const XferArgs &a, uint32_t rows_per_task, uint32_t blocks, bool gather,
-                        hipStream_t s);
+// the scatter unpacks them. One launch per stage_max_rows(R) rows (one for any
+// staging chunk of 32 GiB or less), each on at most `cap` workgroups (0 = one
+// per kWavesPerBlock windows): the waves stride over the windows. Adds the
+// launches made to *launches (may be null). An empty range launches nothing.
+hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_t s,
+                        uint32_t *launches);
 // The index pairs {device slot, host key} of n positions from the raw index
 // arrays (all three device pointers): lc = L*C of the pool.
 hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, int64_t *tok,

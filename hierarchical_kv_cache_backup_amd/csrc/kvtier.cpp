@@ -272,10 +272,11 @@ void default_calibration(kv_calib_t *c) {
   c->duplex_kernel_max_workgroups[0] = 24;
   c->duplex_kernel_max_workgroups[1] = 128;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
-  // the device-side gather / scatter of a staged chunk (stage_rows, HBM to
+  // the device-side gather / scatter of a staged chunk (stage_windows, HBM to
   // HBM, full grid), payload rate: the 2.94 GB prefix of 1152-byte rows packs
-  // in ~1.0 ms (5.9 TB/s of HBM traffic), so a 256 MiB half in ~92 us
-  c->staged_gather_gbps = 2900.0;
+  // in ~0.97 ms and unpacks in ~0.94 ms (6.1-6.3 TB/s of HBM traffic), so a
+  // 256 MiB half takes ~88 us
+  c->staged_gather_gbps = 3000.0;
   // Reading the index pairs from mapped pinned memory instead of copying them
   // first measured +0.6..1.6% at 64 tokens, even at 256, and down to -2% for
   // loads of 1K tokens and more (the reads share the link and lengthen each
@@ -688,14 +689,13 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
     uint8_t *buf = d.stage + half * d.stage_cap;
     b.host = buf;
     set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
-    const uint32_t rpt = stage_rows_per_task(g.R);
-    const uint32_t blocks = stage_blocks(b, rpt);
     hipStream_t kern_s = d.aux;
+    uint32_t launched = 0;
     if (dir == 0) {
       if (d.free_recorded[half]) e = hipStreamWaitEvent(kern_s, d.ev_free[half], 0);
       if (e == hipSuccess) {
-        d.launches++;
-        e = launch_stage(b, rpt, grid_for(blocks, cap), true, kern_s);
+        e = launch_stage(b, cap, true, kern_s, &launched);
+        d.launches += launched;
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_ready[half], kern_s);
       if (e == hipSuccess) e = hipStreamWaitEvent(s, d.ev_ready[half], 0);
@@ -722,8 +722,8 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
       e = hipEventRecord(d.ev_ready[half], s);
       if (e == hipSuccess) e = hipStreamWaitEvent(kern_s, d.ev_ready[half], 0);
       if (e == hipSuccess) {
-        d.launches++;
-        e = launch_stage(b, rpt, grid_for(blocks, cap), false, kern_s);
+        e = launch_stage(b, cap, false, kern_s, &launched);
+        d.launches += launched;
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_free[half], kern_s);
     }
@@ -1207,13 +1207,13 @@ static int stage_call(kv_pool *p, int dir, const int64_t *dev_idx, int64_t n, in
   a.lc0 = (uint32_t)(l0 * g.C);
   a.nlc = (uint32_t)((l1 - l0) * g.C);
   plan_rows(&a, g.layout, g.ps);
-  const uint32_t rpt = stage_rows_per_task(g.R);
-  if (e == hipSuccess) e = launch_stage(a, rpt, stage_blocks(a, rpt), dir == 0, s);
+  uint32_t launched = 0;
+  if (e == hipSuccess) e = launch_stage(a, 0, dir == 0, s, &launched);
+  d.launches += launched;
   const hipError_t er = hipEventRecord(st->ev, s);  // the index slot is busy until here
   if (er == hipSuccess) st->pending = true;
   if (e != hipSuccess) return hip_fail(e, "enqueueing the staging pass");
   if (er != hipSuccess) return hip_fail(er, "recording the staging event");
-  d.launches++;
   return KV_OK;
 }
 

@@ -165,28 +165,77 @@ constexpr void walk_next(const XferArgs &a, WalkPos &w) {
   }
 }
 
-// The staged path's device-side pass (stage_rows), HBM to HBM. A wave splits
-// into K lane groups of 64/K lanes, one row per group and pass, so that a row of
-// R/16 16-byte chunks fills its group in one pass where it can: K = 4 for rows of
-// at most 16 chunks (256 B), 2 for at most 32, else 1 (longer rows take several
-// passes of 64 lanes). A wave's task is K batches of K consecutive walk rows
-// (K*K rows); each row's walk position and index pair are taken once, in
-// scalar registers, and handed to its lane group.
+// The staged path's device-side pass (stage_windows), HBM to HBM. The staging
+// buffer holds the walk rows [row_begin, row_end) back to back, so it is one
+// stream of 16-byte chunks: chunk c is chunk c % cpr of walk row
+// row_begin + c / cpr (cpr = R / 16). A wave moves one window of kStageWindow
+// consecutive chunks (1 KiB: one pass of its 64 lanes), each chunk to or from
+// its offset in its device row. Windows are cut on the staging side, not at
+// row boundaries, so every pass is full and every wave's staging bytes are one
+// aligned KiB whatever the row size. Wide rows (at least kStageWindow chunks):
+// a window spans at most two rows, whose device addresses the wave takes once,
+// in scalar registers. Narrow rows: a window spans up to kStageWindow rows;
+// lane j resolves the window's row j, and each lane reads its row's address
+// from that lane.
+constexpr uint32_t kStageWindow = 64;                     // chunks per window
 constexpr uint32_t kWavesPerBlock = kXferThreads / 64;
+constexpr uint32_t kStageMaxChunks = uint32_t(1) << 31;   // per launch: chunk numbers fit 32 bits
 
-constexpr uint32_t stage_lane_groups(int64_t R) {
-  return R / 16 <= 16 ? 4u : R / 16 <= 32 ? 2u : 1u;
+constexpr uint32_t stage_cpr(int64_t R) { return (uint32_t)(R / 16); }
+constexpr bool stage_wide(int64_t R) { return R / 16 >= kStageWindow; }
+
+// (x * stage_recip(cpr)) >> 16 == x / cpr for every x < 2 * kStageWindow and
+// 1 <= cpr < kStageWindow: the error of the scaled reciprocal stays below
+// x / 65536 < 1 / cpr, too small to cross an integer.
+constexpr uint32_t stage_recip(uint32_t cpr) { return 65536u / cpr + 1u; }
+constexpr bool stage_recip_exact() {
+  for (uint32_t cpr = 1; cpr < kStageWindow; cpr++)
+    for (uint32_t x = 0; x < 2 * kStageWindow; x++)
+      if (((x * stage_recip(cpr)) >> 16) != x / cpr) return false;
+  return true;
+}
+static_assert(stage_recip_exact(), "reciprocal division of the narrow windows");
+
+// Chunks and windows of a launch over walk rows [row_begin, row_end); the
+// launcher keeps a launch at kStageMaxChunks chunks or fewer (stage_max_rows).
+constexpr uint32_t stage_chunks(const XferArgs &a) {
+  return (a.row_end - a.row_begin) * stage_cpr(a.R);
+}
+constexpr uint32_t stage_windows(const XferArgs &a) {
+  return (uint32_t)(((uint64_t)stage_chunks(a) + kStageWindow - 1) / kStageWindow);
+}
+constexpr uint32_t stage_blocks(const XferArgs &a) {
+  return (stage_windows(a) + kWavesPerBlock - 1) / kWavesPerBlock;
+}
+constexpr uint32_t stage_max_rows(int64_t R) { return kStageMaxChunks / stage_cpr(R); }
+
+// Window w of a launch: its first chunk c0, the row ra (relative to
+// row_begin) and chunk ka of that chunk, and the rows it touches; recip =
+// stage_recip(cpr) for narrow rows. One division per window: the window's
+// last row follows from ka + 63 < 2 * max(cpr, kStageWindow) by a comparison
+// (wide) or the reciprocal (narrow).
+struct StageWindow {
+  uint32_t c0, ra, ka, rows;
+};
+
+constexpr StageWindow stage_window(const XferArgs &a, uint32_t w, uint32_t recip) {
+  const uint32_t cpr = stage_cpr(a.R);
+  StageWindow s{w * kStageWindow, 0, 0, 0};
+  s.ra = s.c0 / cpr;
+  s.ka = s.c0 - s.ra * cpr;
+  const uint32_t x = s.ka + kStageWindow - 1;
+  const uint32_t last = cpr >= kStageWindow ? (x >= cpr ? 1u : 0u) : (x * recip) >> 16;
+  s.rows = umin(last + 1, (a.row_end - a.row_begin) - s.ra);
+  return s;
 }
 
-constexpr uint32_t stage_rows_per_task(int64_t R) {
-  return stage_lane_groups(R) * stage_lane_groups(R);
-}
-
-// Workgroups of a stage_rows launch over walk rows [row_begin, row_end): one
-// task per wave.
-constexpr uint32_t stage_blocks(const XferArgs &a, uint32_t rows_per_task) {
-  const uint32_t tasks = (a.row_end - a.row_begin + rows_per_task - 1) / rows_per_task;
-  return (tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+// Lane `lane` of window s moves chunk k of the window's row j (row ra + j);
+// recip = stage_recip(cpr) for narrow rows.
+constexpr void stage_lane(const StageWindow &s, uint32_t cpr, uint32_t recip, uint32_t lane,
+                          uint32_t &j, uint32_t &k) {
+  const uint32_t x = s.ka + lane;
+  j = cpr >= kStageWindow ? (x >= cpr ? 1u : 0u) : (x * recip) >> 16;
+  k = x - j * cpr;
 }
 
 // A tile of the LDS variant: positions [i0, i0+nt), pairs [lcf, lcf+nl).

@@ -220,53 +220,77 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
   for (int64_t len : chunks) {
     const int64_t r1 = r0 + len;
     set_row_range(&a, (uint32_t)r0, (uint32_t)r1);
-    // the device-side pass (stage_rows): each wave takes tasks of K*K walk rows
-    // (K lane groups of 64/K lanes), batch u's row r0 + u*K + g going to lane
-    // group g, the walk position stepped with walk_next in that order; lane sub
-    // of a group moves 16-byte chunks k0 + sub of its row, in passes of 64/K
+    // the device-side pass (stage_windows): wave w of the grid-stride loop
+    // moves window w of the staging chunk stream; lane `lane` moves chunk k of
+    // the window's row j (stage_lane). Wide rows: the wave resolves the
+    // window's first row with walk_at and the second with walk_next. Narrow
+    // rows: lane j resolves row ra + j with walk_at, for j < rows.
     auto dense = [&](bool gather) {
-      const uint32_t K = stage_lane_groups(g.R), lanes = 64 / K;
-      const uint32_t rpt = stage_rows_per_task(g.R);
-      CHECK(rpt == K * K, "rows per task");
-      const uint32_t blocks = stage_blocks(a, rpt);
-      const uint32_t grid = grid_for(blocks, cap);
-      const uint32_t cpr16 = (uint32_t)(g.R / 16);
-      const uint32_t ntasks = (a.row_end - a.row_begin + rpt - 1) / rpt;
-      CHECK((uint64_t)blocks * kWavesPerBlock >= ntasks, "stage grid too small");
+      const uint32_t cpr16 = stage_cpr(g.R);
+      const bool wide = stage_wide(g.R);
+      const uint32_t recip = wide ? 0u : stage_recip(cpr16);
+      CHECK(stage_chunks(a) == (uint64_t)(a.row_end - a.row_begin) * cpr16 &&
+                (uint64_t)(a.row_end - a.row_begin) * cpr16 <= kStageMaxChunks,
+            "stage chunk count");
+      const uint32_t nwin = stage_windows(a);
+      const uint32_t grid = grid_for(stage_blocks(a), cap);
+      CHECK((uint64_t)stage_blocks(a) * kWavesPerBlock >= nwin, "stage grid too small");
+      const uint32_t total = stage_chunks(a);
       for (uint32_t b = 0; b < grid; b++)
         for (uint32_t wave = 0; wave < kWavesPerBlock; wave++)
-          for (uint32_t t = b * kWavesPerBlock + wave; t < ntasks; t += grid * kWavesPerBlock) {
-            const uint32_t r0 = a.row_begin + t * rpt;
-            const uint32_t r1 = std::min(r0 + rpt, a.row_end);
-            WalkPos w = walk_at(a, r0);
-            for (uint32_t u = 0; u < K; u++)
-              for (uint32_t gr = 0; gr < K; gr++) {
-                const uint32_t r = r0 + u * K + gr;
-                if (r >= r1) continue;
-                uint32_t i = 0, lc = 0;
-                walk_row(a, r, i, lc);  // the stepped position must be the walk's
-                CHECK(w.r == r && w.base + w.pos == i && w.lc == lc,
-                      "stepped walk differs at row %u", r);
-                CHECK(i < a.n && lc < a.nlc, "stage walk out of range");
-                if (!(i < a.n && lc < a.nlc)) return;
-                const int64_t srow = (int64_t)(r - a.row_begin);
-                CHECK((srow + 1) * g.R <= (int64_t)stage.size(), "stage overrun");
-                uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R;
-                uint8_t *sv = stage.data() + srow * g.R;
-                for (uint32_t k0 = 0; k0 < cpr16; k0 += lanes)
-                  for (uint32_t sub = 0; sub < lanes; sub++) {
-                    const uint32_t k = k0 + sub;
-                    if (k >= cpr16) continue;
-                    if (gather)
-                      std::memcpy(sv + 16 * k, dv + 16 * k, 16);
-                    else
-                      std::memcpy(dv + 16 * k, sv + 16 * k, 16);
-                    for (int h8 = 0; h8 < 2; h8++)
-                      cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + 2 * k +
-                            h8]++;
-                  }
-                walk_next(a, w);
+          for (uint32_t w = b * kWavesPerBlock + wave; w < nwin; w += grid * kWavesPerBlock) {
+            const StageWindow s = stage_window(a, w, recip);
+            CHECK(s.rows >= 1 && s.rows <= (wide ? 2u : 64u), "window of %u rows", s.rows);
+            if (s.rows < 1 || s.rows > 64) return;
+            // the rows' (position, pair) as the kernel resolves them
+            uint32_t ri[64], rl[64];
+            if (wide) {
+              WalkPos wp = walk_at(a, a.row_begin + s.ra);
+              ri[0] = wp.base + wp.pos;
+              rl[0] = wp.lc;
+              if (s.rows > 1) {
+                walk_next(a, wp);
+                ri[1] = wp.base + wp.pos;
+                rl[1] = wp.lc;
               }
+            } else {
+              for (uint32_t jj = 0; jj < s.rows; jj++) {
+                const WalkPos wp = walk_at(a, a.row_begin + s.ra + jj);
+                ri[jj] = wp.base + wp.pos;
+                rl[jj] = wp.lc;
+              }
+            }
+            for (uint32_t jj = 0; jj < s.rows; jj++) {
+              uint32_t i = 0, lc = 0;
+              walk_row(a, a.row_begin + s.ra + jj, i, lc);
+              CHECK(ri[jj] == i && rl[jj] == lc, "window row %u of window %u differs", jj, w);
+              CHECK(i < a.n && lc < a.nlc, "stage walk out of range");
+              if (!(i < a.n && lc < a.nlc)) return;
+            }
+            for (uint32_t lane = 0; lane < 64; lane++) {
+              const uint32_t c = s.c0 + lane;
+              if (c >= total) continue;
+              uint32_t jj = 0, k = 0;
+              stage_lane(s, cpr16, recip, lane, jj, k);
+              if (wide) {  // the kernel's form of the same mapping
+                const uint32_t split = cpr16 - s.ka;
+                CHECK(lane < split ? (jj == 0 && k == s.ka + lane) : (jj == 1 && k == lane - split),
+                      "wide lane %u of window %u: compare form differs", lane, w);
+              }
+              CHECK(jj < s.rows && k < cpr16 && (s.ra + jj) * cpr16 + k == c,
+                    "lane %u of window %u maps to row %u chunk %u", lane, w, jj, k);
+              if (!(jj < s.rows && k < cpr16)) return;
+              const uint32_t i = ri[jj], lc = rl[jj];
+              CHECK((int64_t)(c + 1) * 16 <= (int64_t)stage.size(), "stage overrun");
+              uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R + 16 * (int64_t)k;
+              uint8_t *sv = stage.data() + 16 * (int64_t)c;
+              if (gather)
+                std::memcpy(sv, dv, 16);
+              else
+                std::memcpy(dv, sv, 16);
+              for (int h8 = 0; h8 < 2; h8++)
+                cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + 2 * k + h8]++;
+            }
           }
     };
     if (to_host) dense(true);
@@ -476,9 +500,13 @@ int main(int argc, char **argv) {
     kv_geometry_t kg{};
     kg.num_layers = (int32_t)uni(1, 5);
     kg.num_components = (int32_t)uni(1, 2);
-    // row sizes on both sides of the staged pass's lane-group bounds (256, 512 B)
-    const int64_t sizes[] = {16, 48, 256, 272, 512, 528, 1152, 2048, 36864};
-    kg.row_bytes = sizes[uni(0, 8)];
+    // row sizes on both sides of the staged pass's window (64 chunks, 1 KiB):
+    // narrow rows that do and do not divide it, the widest narrow row (1008),
+    // a row of exactly one window (1024), wide rows that straddle windows;
+    // the first cases take each size once, the others draw
+    const int64_t sizes[] = {16, 48, 256, 272, 512, 528, 1008, 1024, 1040, 1152, 2048, 36864};
+    const int nsizes = (int)(sizeof(sizes) / sizeof(sizes[0]));
+    kg.row_bytes = cs < nsizes ? sizes[cs] : sizes[uni(0, nsizes - 1)];
     kg.page_size = (int32_t)(std::vector<int>{1, 2, 3, 4, 16, 64})[uni(0, 5)];
     kg.host_slots = kg.page_size * uni(1, 300 / kg.page_size + 1);
     kg.device_slots = uni(1, 400);

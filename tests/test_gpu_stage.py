@@ -32,7 +32,7 @@ def torch():
     return t
 
 
-def stage_rows(g, n, l0, l1):
+def stage_order(g, n, l0, l1):
     """(position, layer, comp) of each row of the staging buffer, in order."""
     Lp, C, ps = l1 - l0, g.C, g.ps
     S = -(-n // ps) * ps
@@ -42,7 +42,7 @@ def stage_rows(g, n, l0, l1):
 
 
 def expected_pack(g, dev_m, dev_idx, l0, l1):
-    i, l, c = stage_rows(g, len(dev_idx), l0, l1)
+    i, l, c = stage_order(g, len(dev_idx), l0, l1)
     out = np.empty((i.size, g.R), np.uint8)
     for k in range(i.size):
         d = int(dev_idx[i[k]])
@@ -92,7 +92,7 @@ def test_stage_pack_and_unpack_match_oracle(torch, layout, case):
     torch.cuda.synchronize()
     pool.stage(1, dev_idx, stage, l0, l1, s)
     s.synchronize()
-    i, l, c = stage_rows(g, n, l0, l1)
+    i, l, c = stage_order(g, n, l0, l1)
     for k in range(i.size):
         d = int(dev_idx[i[k]])
         dev_m[l[k] * C + c[k]][d * R:(d + 1) * R] = src[k * R:(k + 1) * R]
@@ -154,7 +154,7 @@ def test_stage_full_prefix(torch, layout):
     print("stage full prefix layout=%d" % layout, flush=True)
     pool.stage(0, dev_idx, stage, 0, L, s)
     s.synchronize()
-    i, l, _ = stage_rows(g, n, 0, L)
+    i, l, _ = stage_order(g, n, 0, L)
     pick = np.random.default_rng(7).choice(i.size, 4096, replace=False)
     st = stage.view(-1, R)
     for k in pick:
