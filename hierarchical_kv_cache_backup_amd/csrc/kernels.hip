@@ -260,10 +260,7 @@ hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_
   const uint32_t step = stage_max_rows(a.R);
   const dim3 block(kXferThreads);
   for (uint32_t r = a.row_begin; r < a.row_end; r += step) {
-    XferArgs p = a;
-    p.row_begin = r;
-    p.row_end = a.row_end - r > step ? r + step : a.row_end;
-    p.host = a.host + (int64_t)(r - a.row_begin) * a.R;
+    const XferArgs p = stage_piece(a, r, step);
     const dim3 grid(grid_for(stage_blocks(p), cap));
     switch ((stage_wide(a.R) ? 2 : 0) + (gather ? 1 : 0)) {
       case 3: hipLaunchKernelGGL((stage_windows<true, true>), grid, block, 0, s, p, recip, tok, tab); break;

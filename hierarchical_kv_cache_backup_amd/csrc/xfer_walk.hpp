@@ -209,6 +209,17 @@ constexpr uint32_t stage_blocks(const XferArgs &a) {
 }
 constexpr uint32_t stage_max_rows(int64_t R) { return kStageMaxChunks / stage_cpr(R); }
 
+// The piece of a launch over walk rows [a.row_begin, a.row_end) that starts at
+// walk row r and holds at most `step` rows; its staging rows start where row r
+// sits in the whole launch's staging buffer.
+constexpr XferArgs stage_piece(const XferArgs &a, uint32_t r, uint32_t step) {
+  XferArgs p = a;
+  p.row_begin = r;
+  p.row_end = a.row_end - r > step ? r + step : a.row_end;
+  p.host = a.host + (int64_t)(r - a.row_begin) * a.R;
+  return p;
+}
+
 // Window w of a launch: its first chunk c0, the row ra (relative to
 // row_begin) and chunk ka of that chunk, and the rows it touches; recip =
 // stage_recip(cpr) for narrow rows. One division per window: the window's

@@ -171,7 +171,7 @@ static void replay_tiles(Mirror &m, const std::vector<int64_t> &tok, int64_t n, 
 static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int64_t *h, int64_t n,
                           int32_t la, int32_t lb, bool to_host, std::vector<uint8_t> &cover,
                           int64_t chunk_rows, bool ramp_first, bool ramp_last,
-                          uint32_t cap) {
+                          uint32_t cap, uint32_t step) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -225,47 +225,47 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
     // the window's row j (stage_lane). Wide rows: the wave resolves the
     // window's first row with walk_at and the second with walk_next. Narrow
     // rows: lane j resolves row ra + j with walk_at, for j < rows.
-    auto dense = [&](bool gather) {
+    auto window_pass = [&](const XferArgs &piece, bool gather) {
       const uint32_t cpr16 = stage_cpr(g.R);
       const bool wide = stage_wide(g.R);
       const uint32_t recip = wide ? 0u : stage_recip(cpr16);
-      CHECK(stage_chunks(a) == (uint64_t)(a.row_end - a.row_begin) * cpr16 &&
-                (uint64_t)(a.row_end - a.row_begin) * cpr16 <= kStageMaxChunks,
+      CHECK(stage_chunks(piece) == (uint64_t)(piece.row_end - piece.row_begin) * cpr16 &&
+                (uint64_t)(piece.row_end - piece.row_begin) * cpr16 <= kStageMaxChunks,
             "stage chunk count");
-      const uint32_t nwin = stage_windows(a);
-      const uint32_t grid = grid_for(stage_blocks(a), cap);
-      CHECK((uint64_t)stage_blocks(a) * kWavesPerBlock >= nwin, "stage grid too small");
-      const uint32_t total = stage_chunks(a);
+      const uint32_t nwin = stage_windows(piece);
+      const uint32_t grid = grid_for(stage_blocks(piece), cap);
+      CHECK((uint64_t)stage_blocks(piece) * kWavesPerBlock >= nwin, "stage grid too small");
+      const uint32_t total = stage_chunks(piece);
       for (uint32_t b = 0; b < grid; b++)
         for (uint32_t wave = 0; wave < kWavesPerBlock; wave++)
           for (uint32_t w = b * kWavesPerBlock + wave; w < nwin; w += grid * kWavesPerBlock) {
-            const StageWindow s = stage_window(a, w, recip);
+            const StageWindow s = stage_window(piece, w, recip);
             CHECK(s.rows >= 1 && s.rows <= (wide ? 2u : 64u), "window of %u rows", s.rows);
             if (s.rows < 1 || s.rows > 64) return;
             // the rows' (position, pair) as the kernel resolves them
             uint32_t ri[64], rl[64];
             if (wide) {
-              WalkPos wp = walk_at(a, a.row_begin + s.ra);
+              WalkPos wp = walk_at(piece, piece.row_begin + s.ra);
               ri[0] = wp.base + wp.pos;
               rl[0] = wp.lc;
               if (s.rows > 1) {
-                walk_next(a, wp);
+                walk_next(piece, wp);
                 ri[1] = wp.base + wp.pos;
                 rl[1] = wp.lc;
               }
             } else {
               for (uint32_t jj = 0; jj < s.rows; jj++) {
-                const WalkPos wp = walk_at(a, a.row_begin + s.ra + jj);
+                const WalkPos wp = walk_at(piece, piece.row_begin + s.ra + jj);
                 ri[jj] = wp.base + wp.pos;
                 rl[jj] = wp.lc;
               }
             }
             for (uint32_t jj = 0; jj < s.rows; jj++) {
               uint32_t i = 0, lc = 0;
-              walk_row(a, a.row_begin + s.ra + jj, i, lc);
+              walk_row(piece, piece.row_begin + s.ra + jj, i, lc);
               CHECK(ri[jj] == i && rl[jj] == lc, "window row %u of window %u differs", jj, w);
-              CHECK(i < a.n && lc < a.nlc, "stage walk out of range");
-              if (!(i < a.n && lc < a.nlc)) return;
+              CHECK(i < piece.n && lc < piece.nlc, "stage walk out of range");
+              if (!(i < piece.n && lc < piece.nlc)) return;
             }
             for (uint32_t lane = 0; lane < 64; lane++) {
               const uint32_t c = s.c0 + lane;
@@ -281,17 +281,34 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
                     "lane %u of window %u maps to row %u chunk %u", lane, w, jj, k);
               if (!(jj < s.rows && k < cpr16)) return;
               const uint32_t i = ri[jj], lc = rl[jj];
-              CHECK((int64_t)(c + 1) * 16 <= (int64_t)stage.size(), "stage overrun");
-              uint8_t *dv = m.dev[a.lc0 + lc].data() + tok[2 * i] * g.R + 16 * (int64_t)k;
-              uint8_t *sv = stage.data() + 16 * (int64_t)c;
+              const bool inside = piece.host >= stage.data() &&
+                                  piece.host - stage.data() + (int64_t)(c + 1) * 16 <=
+                                      (int64_t)stage.size();
+              CHECK(inside, "stage overrun");
+              if (!inside) return;
+              uint8_t *dv = m.dev[piece.lc0 + lc].data() + tok[2 * i] * g.R + 16 * (int64_t)k;
+              uint8_t *sv = piece.host + 16 * (int64_t)c;
               if (gather)
                 std::memcpy(sv, dv, 16);
               else
                 std::memcpy(dv, sv, 16);
               for (int h8 = 0; h8 < 2; h8++)
-                cover[((int64_t)i * g.L * g.C + a.lc0 + lc) * (g.R / kChunkBytes) + 2 * k + h8]++;
+                cover[((int64_t)i * g.L * g.C + piece.lc0 + lc) * (g.R / kChunkBytes) + 2 * k + h8]++;
             }
           }
+    };
+    // launch_stage splits the pass into pieces of at most `step` rows
+    // (stage_piece; stage_max_rows(R) in the library, small steps here too)
+    auto dense = [&](bool gather) {
+      XferArgs whole = a;
+      whole.host = stage.data();
+      for (uint32_t r = whole.row_begin; r < whole.row_end; r += step) {
+        const XferArgs p = stage_piece(whole, r, step);
+        const bool ok = p.row_begin == r && p.row_end > r && p.row_end <= whole.row_end &&
+                        p.host == stage.data() + (int64_t)(r - whole.row_begin) * g.R;
+        CHECK(ok, "stage piece at row %u", r);
+        if (ok) window_pass(p, gather);
+      }
     };
     if (to_host) dense(true);
     while (x < ext.size() && ext[x].walk0 < r1) {
@@ -426,8 +443,10 @@ static int64_t check_case(const kv_geometry_t &kg, const Geom &g, const std::vec
         const int64_t walk = n * (int64_t)(l1 - l0) * g.C;
         const int64_t chunk = std::max<int64_t>(1, (std::vector<int64_t>{1, 7, walk / 3 + 1, walk})[uni(0, 3)]);
         const int ramp = (int)uni(0, 2);  // none, first, last
+        // pieces of the library's size, or small ones that split every chunk
+        const uint32_t step = uni(0, 1) ? stage_max_rows(g.R) : (uint32_t)uni(1, 40);
         replay_staged(m, tok, h.data(), n, l0, l1, to_host, cover, chunk, ramp == 1, ramp == 2,
-                      cap);
+                      cap, step);
       } else {
         replay_dma(m, d.data(), h.data(), n, l0, l1, to_host, &copies);
         int64_t counted = -1;
