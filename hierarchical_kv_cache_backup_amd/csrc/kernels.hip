@@ -255,8 +255,7 @@ hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_
                         uint32_t *launches) {
   const int64_t *tok = a.tok;
   uint8_t *const *tab = (uint8_t *const *)a.dev_tab;
-  const uint32_t cpr = stage_cpr(a.R);
-  const uint32_t recip = stage_wide(a.R) ? 0u : stage_recip(cpr);
+  const uint32_t recip = stage_recip_of(a.R);
   const uint32_t step = stage_max_rows(a.R);
   const dim3 block(kXferThreads);
   for (uint32_t r = a.row_begin; r < a.row_end; r += step) {

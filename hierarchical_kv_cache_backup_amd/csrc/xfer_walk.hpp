@@ -174,7 +174,8 @@ constexpr void walk_next(const XferArgs &a, WalkPos &w) {
 // row boundaries, so every pass is full and every wave's staging bytes are one
 // aligned KiB whatever the row size. Wide rows (at least kStageWindow chunks):
 // a window spans at most two rows, whose device addresses the wave takes once,
-// in scalar registers. Narrow rows: a window spans up to kStageWindow rows;
+// in scalar registers (also rows of exactly half a window, which it holds
+// two of). Narrow rows: a window spans up to kStageWindow rows;
 // lane j resolves the window's row j, and each lane reads its row's address
 // from that lane.
 constexpr uint32_t kStageWindow = 64;                     // chunks per window
@@ -182,7 +183,12 @@ constexpr uint32_t kWavesPerBlock = kXferThreads / 64;
 constexpr uint32_t kStageMaxChunks = uint32_t(1) << 31;   // per launch: chunk numbers fit 32 bits
 
 constexpr uint32_t stage_cpr(int64_t R) { return (uint32_t)(R / 16); }
-constexpr bool stage_wide(int64_t R) { return R / 16 >= kStageWindow; }
+// Rows whose windows span at most two rows, which the wave resolves in scalar
+// registers: rows of a window or more, and rows of exactly half a window (a
+// window then holds two whole rows).
+constexpr bool stage_wide(int64_t R) {
+  return R / 16 >= kStageWindow || R / 16 == kStageWindow / 2;
+}
 
 // (x * stage_recip(cpr)) >> 16 == x / cpr for every x < 2 * kStageWindow and
 // 1 <= cpr < kStageWindow: the error of the scaled reciprocal stays below
@@ -195,6 +201,11 @@ constexpr bool stage_recip_exact() {
   return true;
 }
 static_assert(stage_recip_exact(), "reciprocal division of the narrow windows");
+// stage_window / stage_lane's multiplier for rows of R bytes (rows shorter
+// than a window need it).
+constexpr uint32_t stage_recip_of(int64_t R) {
+  return stage_cpr(R) < kStageWindow ? stage_recip(stage_cpr(R)) : 0u;
+}
 
 // Chunks and windows of a launch over walk rows [row_begin, row_end); the
 // launcher keeps a launch at kStageMaxChunks chunks or fewer (stage_max_rows).
@@ -222,7 +233,7 @@ constexpr XferArgs stage_piece(const XferArgs &a, uint32_t r, uint32_t step) {
 
 // Window w of a launch: its first chunk c0, the row ra (relative to
 // row_begin) and chunk ka of that chunk, and the rows it touches; recip =
-// stage_recip(cpr) for narrow rows. One division per window: the window's
+// stage_recip_of(R). One division per window: the window's
 // last row follows from ka + 63 < 2 * max(cpr, kStageWindow) by a comparison
 // (wide) or the reciprocal (narrow).
 struct StageWindow {
@@ -241,7 +252,7 @@ constexpr StageWindow stage_window(const XferArgs &a, uint32_t w, uint32_t recip
 }
 
 // Lane `lane` of window s moves chunk k of the window's row j (row ra + j);
-// recip = stage_recip(cpr) for narrow rows.
+// recip = stage_recip_of(R).
 constexpr void stage_lane(const StageWindow &s, uint32_t cpr, uint32_t recip, uint32_t lane,
                           uint32_t &j, uint32_t &k) {
   const uint32_t x = s.ka + lane;

@@ -228,7 +228,7 @@ static void replay_staged(Mirror &m, const std::vector<int64_t> &tok, const int6
     auto window_pass = [&](const XferArgs &piece, bool gather) {
       const uint32_t cpr16 = stage_cpr(g.R);
       const bool wide = stage_wide(g.R);
-      const uint32_t recip = wide ? 0u : stage_recip(cpr16);
+      const uint32_t recip = stage_recip_of(g.R);
       CHECK(stage_chunks(piece) == (uint64_t)(piece.row_end - piece.row_begin) * cpr16 &&
                 (uint64_t)(piece.row_end - piece.row_begin) * cpr16 <= kStageMaxChunks,
             "stage chunk count");

@@ -57,6 +57,10 @@ CASES = [  # (L, C, R, S_dev, ps, n, l0, l1)
     (2, 2, 48, 900, 1, 777, 0, 2),
     (5, 1, 16, 2000, 4, 1999, 2, 5),
     (2, 2, 4096, 64, 8, 40, 0, 2),       # rows larger than a wave's pass
+    (3, 2, 512, 600, 16, 333, 0, 3),     # half a window: two whole rows per window
+    (2, 1, 1024, 500, 8, 257, 0, 2),     # exactly one window per row
+    (2, 2, 1040, 300, 4, 123, 1, 2),     # the narrowest rows that straddle windows
+    (2, 1, 1008, 300, 4, 201, 0, 2),     # the widest rows shorter than a window
 ]
 
 
