@@ -42,6 +42,10 @@ int make_geom(const kv_geometry_t *in, Geom *g, std::string *why) {
     *why = fmt("row_bytes (%lld) must be a positive multiple of 16", in->row_bytes);
     return KV_EINVAL;
   }
+  if (in->row_bytes > kRowBytesLimit) {
+    *why = fmt("row_bytes (%lld) exceeds the library's limit of 2^30", in->row_bytes);
+    return KV_EINVAL;
+  }
   if (in->device_slots < 1 || in->host_slots < 1) {
     *why = "device_slots and host_slots must be >= 1";
     return KV_EINVAL;

@@ -22,6 +22,11 @@
 
 namespace kvt {
 
+// Largest row the library takes: the kernels count a row's chunks in 32 bits
+// (8-byte chunks on the direct path), and a staged launch holds at least
+// stage_max_rows(R) >= 32 rows.
+constexpr int64_t kRowBytesLimit = int64_t(1) << 30;
+
 struct Geom {
   int32_t L = 0, C = 0;
   int64_t R = 0, S_dev = 0, S_host = 0;

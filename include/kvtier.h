@@ -145,7 +145,8 @@ typedef enum {
 typedef struct {
   int32_t num_layers;     /* L  >= 1 */
   int32_t num_components; /* C  >= 1 (2 = K,V; 1 = MLA latent) */
-  int64_t row_bytes;      /* R  >= 16, R % 16 == 0 */
+  int64_t row_bytes;      /* R  >= 16, R % 16 == 0, R <= 2^30 (the kernels count a
+                             row's chunks in 32 bits) */
   int64_t device_slots;   /* S_dev >= 1 */
   int64_t host_slots;     /* S_host >= 1, S_host % page_size == 0 */
   int32_t page_size;      /* ps >= 1 */

@@ -90,6 +90,10 @@ def test_geometry_and_validation_codes_match_oracle(kvt):
                 got = kvt.kv_validate(kg, direction, d, h, l0, l1, uniq)
                 assert got == want, (direction, uniq, d, h, l0, l1)
     assert kvt.kv_validate(kg, 0, [1], [1], 0, 1, True, n=-1) == kvt.EINVAL
+    # the library's own ceiling on a row (the kernels count a row's chunks in
+    # 32 bits); the pages set none, so the oracle takes both
+    assert kvt.kv_geometry_check(_geom(kvt, base.replace(R=1 << 30))) == kvt.OK
+    assert kvt.kv_geometry_check(_geom(kvt, base.replace(R=(1 << 30) + 16))) == kvt.EINVAL
     rng = np.random.default_rng(1)
     for _ in range(200):
         g = Geometry(int(rng.integers(1, 4)), int(rng.integers(1, 3)), 16, int(rng.integers(1, 9)),
