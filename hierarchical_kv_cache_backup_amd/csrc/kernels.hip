@@ -252,7 +252,7 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
 }
 
 hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_t s,
-                        uint32_t *launches) {
+                        uint32_t *launches, uint32_t *last_grid) {
   const int64_t *tok = a.tok;
   uint8_t *const *tab = (uint8_t *const *)a.dev_tab;
   const uint32_t recip = stage_recip_of(a.R);
@@ -268,6 +268,7 @@ hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_
       default: hipLaunchKernelGGL((stage_windows<false, false>), grid, block, 0, s, p, recip, tok, tab); break;
     }
     if (launches) (*launches)++;
+    if (last_grid) *last_grid = grid.x;
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -15,9 +15,10 @@ hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStre
 // the scatter unpacks them. One launch per stage_max_rows(R) rows (one for any
 // staging chunk of 32 GiB or less), each on at most `cap` workgroups (0 = one
 // per kWavesPerBlock windows): the waves stride over the windows. Adds the
-// launches made to *launches (may be null). An empty range launches nothing.
+// launches made to *launches and sets *last_grid to the last launch's grid
+// (either may be null). An empty range launches nothing.
 hipError_t launch_stage(const XferArgs &a, uint32_t cap, bool gather, hipStream_t s,
-                        uint32_t *launches);
+                        uint32_t *launches, uint32_t *last_grid);
 // The index pairs {device slot, host key} of n positions from the raw index
 // arrays (all three device pointers): lc = L*C of the pool.
 hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, int64_t *tok,

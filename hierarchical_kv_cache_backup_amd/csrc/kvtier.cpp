@@ -690,12 +690,13 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
     b.host = buf;
     set_row_range(&b, (uint32_t)r0, (uint32_t)r1);
     hipStream_t kern_s = d.aux;
-    uint32_t launched = 0;
+    uint32_t launched = 0, grid = 0;
     if (dir == 0) {
       if (d.free_recorded[half]) e = hipStreamWaitEvent(kern_s, d.ev_free[half], 0);
       if (e == hipSuccess) {
-        e = launch_stage(b, cap, true, kern_s, &launched);
+        e = launch_stage(b, cap, true, kern_s, &launched, &grid);
         d.launches += launched;
+        d.last_workgroups = grid;
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_ready[half], kern_s);
       if (e == hipSuccess) e = hipStreamWaitEvent(s, d.ev_ready[half], 0);
@@ -722,8 +723,9 @@ static hipError_t staged_unit(kv_pool *p, DirState &d, int dir, XferArgs b,
       e = hipEventRecord(d.ev_ready[half], s);
       if (e == hipSuccess) e = hipStreamWaitEvent(kern_s, d.ev_ready[half], 0);
       if (e == hipSuccess) {
-        e = launch_stage(b, cap, false, kern_s, &launched);
+        e = launch_stage(b, cap, false, kern_s, &launched, &grid);
         d.launches += launched;
+        d.last_workgroups = grid;
       }
       if (e == hipSuccess) e = hipEventRecord(d.ev_free[half], kern_s);
     }
@@ -1207,9 +1209,10 @@ static int stage_call(kv_pool *p, int dir, const int64_t *dev_idx, int64_t n, in
   a.lc0 = (uint32_t)(l0 * g.C);
   a.nlc = (uint32_t)((l1 - l0) * g.C);
   plan_rows(&a, g.layout, g.ps);
-  uint32_t launched = 0;
-  if (e == hipSuccess) e = launch_stage(a, 0, dir == 0, s, &launched);
+  uint32_t launched = 0, grid = 0;
+  if (e == hipSuccess) e = launch_stage(a, 0, dir == 0, s, &launched, &grid);
   d.launches += launched;
+  if (launched) d.last_workgroups = grid;
   const hipError_t er = hipEventRecord(st->ev, s);  // the index slot is busy until here
   if (er == hipSuccess) st->pending = true;
   if (e != hipSuccess) return hip_fail(e, "enqueueing the staging pass");

@@ -507,8 +507,10 @@ typedef struct {
                                (only when 16 calls of one direction are in flight) or,
                                for loads, for a free landed event (only when more
                                than L + 16 load groups are in flight) */
-  int64_t last_workgroups[2]; /* grid of the latest kernel-path launch (direct or LDS
-                               kernel), after any cap; 0 before the first */
+  int64_t last_workgroups[2]; /* grid of the latest launch of a kernel that moves rows
+                               (direct or LDS kernel, or the staged path's device-side
+                               pass, kv_stage's included), after any cap; 0 before
+                               the first */
 } kv_stats_t;
 
 int kv_get_stats(const kv_pool_t *pool, kv_stats_t *out);

@@ -337,6 +337,37 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     overlap.close()
 
 
+@pytest.mark.parametrize("R", (256, 512, 1152))
+def test_staged_pass_on_a_capped_grid(torch, stream, R):
+    """A load flagged KV_F_LOAD_OVERLAP runs the staged path's device-side
+    pass on at most overlap_kernel_max_workgroups workgroups, whose waves then
+    stride over the 1 KiB windows. With caps of 1, 3 and 96 workgroups, for
+    narrow, half-window and wide rows in every layout, the loaded device pool
+    matches the oracle, and the last pass launched no more workgroups than the
+    cap."""
+    for layout in LAYOUTS:
+        g = Geometry(3, 2, R, 640, 512, 16, layout)
+        bufs = device_buffers(g, seed=40 + layout)
+        rng = np.random.default_rng(40 + layout)
+        d = rng.permutation(g.S_dev)[:400].astype(np.int64)
+        h = rng.permutation(g.S_host)[:400].astype(np.int64)
+        pool = make_pool(g, bufs, path=kvt.PATH_STAGED,
+                         flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP, host_fill=None)
+        pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+        c = pool.calibration()
+        for cap in (1, 3, 96):
+            print("staged capped R=%d layout=%d cap=%d" % (R, layout, cap), flush=True)
+            c.overlap_kernel_max_workgroups = cap
+            c.staged_chunk_bytes = 64 * 1024      # several chunks, ramped
+            pool.set_calibration(c)
+            run_load_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+            assert pool.last_path(kvt.LOAD) == kvt.PATH_STAGED
+            assert 1 <= pool.stats().last_workgroups[1] <= cap
+            run_load_and_compare(g, pool, bufs, d[:123], h[:123], 1, 3, stream)
+            assert 1 <= pool.stats().last_workgroups[1] <= cap
+        pool.close()
+
+
 def _hold_stream(torch, st, gate):
     """Enqueues on `st` a host function that returns once `gate` is set (or after
     10 s): work queued behind it stays in flight until then."""
