@@ -1015,15 +1015,16 @@ def leg_bidirectional(torch, kvt, workloads, args, link_peak, duplex_fresh):
     wall_min = max(hb / link_peak["h2d"], wb / link_peak["d2h"], (hb + wb) / peak) / 1e9
     bound = (hb + wb) / wall_min / 1e9
     results = {}
-    # "full_grids": the duplex grid caps switched off (every kernel launch one
-    # workgroup per block of work), to show what the caps buy
+    # "no_duplex_caps": the duplex grid caps switched off (the load then runs
+    # on a full grid; the write-back keeps its own default cap), to show what
+    # the caps buy
     variants = (("layer_first", 0, "kernel", kvt.PATH_KERNEL, True),
-                ("layer_first", 0, "kernel_full_grids", kvt.PATH_KERNEL, False),
+                ("layer_first", 0, "kernel_no_duplex_caps", kvt.PATH_KERNEL, False),
                 ("layer_first", 0, "auto", kvt.PATH_AUTO, True),
                 ("page_first_direct", 2, "kernel", kvt.PATH_KERNEL, True),
                 ("page_first_direct", 2, "staged", kvt.PATH_STAGED, True),
                 ("page_first_direct", 2, "auto", kvt.PATH_AUTO, True),
-                ("page_first_direct", 2, "auto_full_grids", kvt.PATH_AUTO, False))
+                ("page_first_direct", 2, "auto_no_duplex_caps", kvt.PATH_AUTO, False))
     for lname, lay, pname, p, caps in variants:
         pool = kvt.KvPool(kvt.geometry(L, C, R, S, plan["host_slots"], ps, lay), bufs,
                           flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
