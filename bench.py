@@ -1697,6 +1697,7 @@ def size_sweep(torch, kvt, workloads):
                     pool.set_calibration(base)
                 log("size sweep", json.dumps(row))
                 rows.append(row)
+        settle(torch, L * C * S_host * R)            # the pool's host memory was freed
     del bufs
     torch.cuda.synchronize()
     return {"size_sweep": rows}
