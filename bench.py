@@ -37,6 +37,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV transfer GB/s H2D & D2H (32K-token prefix) as % of host-link peak"
 PCIE_GEN5_X16_GBPS = 64.0   # PCIe 5.0 x16, per direction, 32 GT/s x 16 lanes (raw)
 HBM_PEAK_GBPS = 8000.0
+# the paced write-back grid's rate as a fraction of the measured D2H link peak
+PACE_OF_LINK = 0.98
 LAYOUTS = {"layer_first": 0, "page_first": 1, "page_first_direct": 2}
 
 
@@ -68,10 +70,11 @@ def parse():
     p.add_argument("--size-sweep", action="store_true",
                    help="only time write-backs and loads of 64..32768 tokens on every path "
                         "and layout (one JSON line per size on stderr), then exit")
-    p.add_argument("--overlap-study", action="store_true",
+    p.add_argument("--overlap-study", nargs="?", const="all", choices=["all", "write-back"],
                    help="only sweep the kernel path's grid for loads beside compute "
-                        "(KV_F_LOAD_OVERLAP) and for write-backs beside compute, on the "
-                        "streamed workload, then exit")
+                        "(KV_F_LOAD_OVERLAP) and for write-backs beside compute (plain and "
+                        "paced grids), on the streamed workload, then exit; 'write-back': "
+                        "the write-backs only")
     p.add_argument("--profile-counters", action="store_true",
                    help="only run the kernels a rocprofv3 --pmc pass needs, then exit")
     p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -120,7 +123,8 @@ def main():
         print(json.dumps(size_sweep(torch, kvt, workloads)))
         return
     if args.overlap_study:
-        print(json.dumps(overlap_study(torch, kvt, workloads)))
+        print(json.dumps(overlap_study(torch, kvt, workloads,
+                                       with_loads=args.overlap_study == "all")))
         return
     if args.tp_shared_study:
         print(json.dumps(tp_shared_study(torch, kvt, workloads, args.tp_shared_study)))
@@ -209,6 +213,7 @@ def main():
     kernel_peak = {"h2d": GiB / k_h2d / 1e9, "d2h": GiB / k_d2h / 1e9}
     peak_pool.close()
     del dbuf, peak_pool
+    settle(torch, 3 * GiB)      # 1 GiB device and 2 GiB pinned memory were freed
     log("1 GiB contiguous: copy engines H2D %.2f / D2H %.2f GB/s, kernel H2D %.2f / D2H %.2f"
         % (memcpy_peak["h2d"], memcpy_peak["d2h"], kernel_peak["h2d"], kernel_peak["d2h"]))
 
@@ -262,16 +267,18 @@ def main():
     # one small ramp chunk's device-side pass (the others overlap the copies);
     # that pass rate (staged_gather_gbps) keeps the library's value, as a few
     # microseconds of a 50 ms call cannot be fitted from it.
-    pool.set_calibration(calib)
-    pool.set_path(path)
-    best_rate = {dd: max(bytes_dir / meas[(dd, p)] / 1e9 for p in
-                         (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
-                 for dd in (kvt.BACKUP, kvt.LOAD)}
     # the measured peak is the better of the two contiguous 1 GiB copies per
     # direction; the workload's own best path rate is reported beside it, never
     # inside it
     link_peak = {"h2d": max(memcpy_peak["h2d"], kernel_peak["h2d"]),
                  "d2h": max(memcpy_peak["d2h"], kernel_peak["d2h"])}
+    # a paced write-back grid must not issue more than this link drains
+    calib.kernel_pace_gbps[0] = round(PACE_OF_LINK * link_peak["d2h"], 2)
+    pool.set_calibration(calib)
+    pool.set_path(path)
+    best_rate = {dd: max(bytes_dir / meas[(dd, p)] / 1e9 for p in
+                         (kvt.PATH_KERNEL, kvt.PATH_DMA, kvt.PATH_STAGED))
+                 for dd in (kvt.BACKUP, kvt.LOAD)}
     workload_best = {"h2d": best_rate[kvt.LOAD], "d2h": best_rate[kvt.BACKUP]}
 
     # ---- the timed steps
@@ -345,7 +352,8 @@ def main():
         extra["bidirectional_mixed"] = leg_bidirectional(torch, kvt, workloads, args,
                                                          link_peak, duplex_fresh)
         torch.cuda.empty_cache()
-        extra["streamed_per_layer"] = leg_streamed(torch, kvt, workloads, args)
+        extra["streamed_per_layer"] = leg_streamed(torch, kvt, workloads, args,
+                                                   d2h_pace=calib.kernel_pace_gbps[0])
         torch.cuda.empty_cache()
         extra["ghost_list"] = leg_ghost_list(kvt, workloads)
     cpu = None
@@ -366,6 +374,8 @@ def main():
         "selector_calibration": {
             "kernel_gbps": list(calib.kernel_gbps), "dma_gbps": list(calib.dma_gbps),
             "staged_gather_gbps": calib.staged_gather_gbps,
+            "kernel_max_workgroups": list(calib.kernel_max_workgroups),
+            "kernel_pace_gbps": list(calib.kernel_pace_gbps),
             "launches_copies_per_call": {"%s/%s" % ("d2h" if d == 0 else "h2d",
                                                     kvt.PATH_NAMES[p]): list(v)
                                          for (d, p), v in ops.items()}},
@@ -486,9 +496,9 @@ def counter_link_bytes(kernel_name, src_hash):
     return link.get("host_link_bytes_per_launch")
 
 
-KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true> (D2H gather, whole prefix in one launch, "
-                       "on the default write-back grid)",
-                "h2d": "kvt::xfer_rows<false> (H2D scatter, one launch per layer: each "
+KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true, true> (D2H gather, whole prefix in one launch, "
+                       "on the default write-back grid, paced under the measured D2H link rate)",
+                "h2d": "kvt::xfer_rows<false, false> (H2D scatter, one launch per layer: each "
                        "layer holds more than the 16 MiB load group threshold)"}
 
 
@@ -661,8 +671,8 @@ def _counter_rows(d):
 
 def _kernel_key(name):
     return ("copy" if "elementwise_kernel" in name and "copy" in name else
-            "xfer_rows_d2h" if "xfer_rows<true>" in name else
-            "xfer_rows_h2d" if "xfer_rows<false>" in name else
+            "xfer_rows_d2h" if "xfer_rows<true, true>" in name else
+            "xfer_rows_h2d" if "xfer_rows<false, false>" in name else
             "stage_gather" if "stage_windows<true" in name else
             "stage_scatter" if "stage_windows<false" in name else None)
 
@@ -1119,12 +1129,14 @@ def leg_bidirectional(torch, kvt, workloads, args, link_peak, duplex_fresh):
             "variants": results}
 
 
-def leg_streamed(torch, kvt, workloads, args):
+def leg_streamed(torch, kvt, workloads, args, d2h_pace=0.0):
     """Per-layer streamed load: 61 layers x K/V x 1024 B fp8 rows, 131072-token
     prefix (256 MiB per layer). Layer l+1 loads on a side stream while a
     synthetic HBM-bound consumer reads layer l's whole K and V buffers on the
     compute stream, after kv_load_layer(l). The consumer repeats its pass k times
-    so that its time per layer matches the transfer's."""
+    so that its time per layer matches the transfer's. Then write-backs beside
+    the consumer, the kernel's on the library's default grid paced to d2h_pace
+    GB/s (the run's measured pace; 0 keeps the library's)."""
     shape = workloads.streamed()
     L, C, R, ps = shape.layers, shape.components, shape.row_bytes, shape.page_size
     S, n = shape.device_slots, shape.extra["tokens"]
@@ -1240,12 +1252,15 @@ def leg_streamed(torch, kvt, workloads, args):
 
     t_alone = statistics.median([consume_timed(60) for _ in range(3)])
     wb_bytes = n * (L - 1) * C * R
-    for wname, p, cap in (("kernel_default_grid", kvt.PATH_KERNEL, 24),
+    for wname, p, cap in (("kernel_default_grid", kvt.PATH_KERNEL, None),
                           ("kernel_full_grid", kvt.PATH_KERNEL, 0),
-                          ("dma", kvt.PATH_DMA, 24), ("staged", kvt.PATH_STAGED, 24)):
+                          ("dma", kvt.PATH_DMA, None), ("staged", kvt.PATH_STAGED, None)):
         pool.set_path(p)
         cal = pool.calibration()
-        cal.kernel_max_workgroups[0] = cap
+        if cap is not None:
+            cal.kernel_max_workgroups[0] = cap
+        if d2h_pace:
+            cal.kernel_pace_gbps[0] = d2h_pace
         pool.set_calibration(cal)
         slow, rates = [], []
         for rep in range(3):
@@ -1280,14 +1295,15 @@ def leg_streamed(torch, kvt, workloads, args):
                 "paths": writeback}}
 
 
-def overlap_study(torch, kvt, workloads, layers=24):
+def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
     """The kernel path's grid beside an HBM-bound consumer, on the streamed
     workload's first `layers` layers (256 MiB each, K and V): (1) a per-layer
     load flagged KV_F_LOAD_OVERLAP, overlapped layer by layer with the consumer
     (as in the streamed leg), for overlap grid caps of 32 to 256 workgroups and
     the full grid; (2) a write-back of layers 1.. beside the consumer's repeated
-    pass over layer 0, for write-back caps of 8 to 64 and the full grid; and the
-    copy path for both, as reference."""
+    pass over layer 0, for write-back caps of 8 to 64 and the full grid, and
+    for capped grids paced to a set rate (kernel_pace_gbps); and the copy path
+    for both, as reference. with_loads=False skips (1)."""
     shape = workloads.streamed()
     L, C, R, ps = layers, shape.components, shape.row_bytes, shape.page_size
     S, n = shape.device_slots, shape.extra["tokens"]
@@ -1325,7 +1341,7 @@ def overlap_study(torch, kvt, workloads, layers=24):
         pool.set_path(kvt.PATH_KERNEL)
         pool.backup(dev_idx, host_idx, 0, L, s_load)
         s_load.synchronize()
-        for cap in (32, 64, 96, 128, 256, 0, "dma"):
+        for cap in (32, 64, 96, 128, 256, 0, "dma") if with_loads else ():
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
@@ -1373,12 +1389,17 @@ def overlap_study(torch, kvt, workloads, layers=24):
         pool.set_path(kvt.PATH_KERNEL)
         t_alone = statistics.median([timed_consume(0, 40) for _ in range(3)])
         wb_bytes = n * (L - 1) * C * R
-        for cap in (8, 16, 20, 22, 24, 25, 26, 27, 28, 30, 32, 48, 64, 0, "dma"):
+        plain = [(cap, 0.0, 0) for cap in (8, 16, 20, 22, 24, 25, 26, 27, 28, 30, 32, 48, 64, 0)]
+        paced = ([(cap, gbps, 32) for cap in (26, 28, 32, 48) for gbps in (55.0, 56.0, 57.0)]
+                 + [(26, 56.0, 0)])
+        for cap, pace, burst in plain + paced + [("dma", 0.0, 0)]:
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
             else:
                 cal.kernel_max_workgroups[0] = cap
+                cal.kernel_pace_gbps[0] = pace
+                cal.kernel_pace_burst_blocks[0] = burst
                 pool.set_calibration(cal)
             slow, rates = [], []
             for rep in range(3):
@@ -1391,6 +1412,8 @@ def overlap_study(torch, kvt, workloads, layers=24):
                 e1.synchronize()
                 rates.append(wb_bytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
             key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
+            if pace:
+                key += " paced %g burst %d" % (pace, burst)
             backs[key] = {"d2h_gbps_beside_compute": round(statistics.median(rates), 2),
                           "compute_slowdown": round(statistics.median(slow), 3)}
             log("overlap study write-back %s %s" % (key, json.dumps(backs[key])))

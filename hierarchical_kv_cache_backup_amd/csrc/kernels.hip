@@ -36,13 +36,40 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
   return a.host + ((int64_t)(a.lc0 + lc) * a.lc_stride + a.tok[2 * i + 1]) * a.R;
 }
 
+// Paced kernels: a workgroup's first max(1, a.pace_burst) blocks go out at
+// once (the start of a call is latency-bound); from then on each block waits
+// until the device's constant-rate wall clock reaches `next`, the earliest
+// start of the workgroup's next block, which then moves one interval on. A
+// workgroup that fell behind keeps at most one interval of credit, so it
+// cannot burst to catch up.
+__device__ __forceinline__ void pace_block(uint64_t &next, uint32_t &done, const XferArgs &a) {
+  if (done < a.pace_burst) {  // the last burst block starts the schedule
+    if (++done == a.pace_burst) next = (uint64_t)wall_clock64() + a.pace_ticks;
+    return;
+  }
+  const uint32_t ticks = a.pace_ticks;
+  uint64_t now = (uint64_t)wall_clock64();
+  while (now < next) {
+    __builtin_amdgcn_s_sleep(4);
+    now = (uint64_t)wall_clock64();
+  }
+  next = (now - next > ticks ? now - ticks : next) + ticks;
+}
+
 }  // namespace
 
 // Direct path: block b moves walk rows [row_begin + b*rows_per_block, ...) of
 // the host-order walk; lanes take consecutive chunks of those rows.
-template <bool kToHost>
+// kPaced: each workgroup starts its blocks at least a.pace_ticks apart on the
+// device's constant-rate wall clock, so that the grid as a whole produces host
+// traffic at a set rate instead of at what its workgroups can issue; a
+// workgroup that fell behind may catch up by one block, no more.
+template <bool kToHost, bool kPaced>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
+  uint64_t next = kPaced ? (uint64_t)wall_clock64() : 0;
+  uint32_t done = 0;
   for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
+  if (kPaced) pace_block(next, done, a);
   const uint32_t row0 = a.row_begin + blk * a.rows_per_block;
   const uint32_t nrows = min(a.rows_per_block, a.row_end - row0);
   const uint32_t nchunks = nrows * a.cpr;
@@ -159,10 +186,14 @@ __global__ __launch_bounds__(kXferThreads) void stage_windows(
 // the tile in source-address order into LDS (slot (pair, position)), then
 // writes it out in destination-address order. Device order is pair-major;
 // host order is position-major for page_first and pair-major otherwise.
-template <bool kToHost>
+// kPaced: as xfer_rows, one interval per tile.
+template <bool kToHost, bool kPaced>
 __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileArgs ta) {
   extern __shared__ chunk_t lds[];
+  uint64_t next = kPaced ? (uint64_t)wall_clock64() : 0;
+  uint32_t done = 0;
   for (uint32_t blk = blockIdx.x; blk < a.nblocks; blk += gridDim.x) {
+  if (kPaced) pace_block(next, done, a);
   const Tile t = tile_of(a, ta, blk);
   const uint32_t cpr = a.cpr;
   const uint32_t nchunks = t.nt * t.nl * cpr;
@@ -244,10 +275,13 @@ hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, in
 
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
-  if (to_host)
-    hipLaunchKernelGGL((xfer_rows<true>), dim3(blocks), dim3(kXferThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((xfer_rows<false>), dim3(blocks), dim3(kXferThreads), 0, s, a);
+  const dim3 grid(blocks), block(kXferThreads);
+  switch ((a.pace_ticks ? 2 : 0) + (to_host ? 1 : 0)) {
+    case 3: hipLaunchKernelGGL((xfer_rows<true, true>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((xfer_rows<false, true>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((xfer_rows<true, false>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((xfer_rows<false, false>), grid, block, 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -279,10 +313,13 @@ hipError_t launch_tiles_lds(const XferArgs &a, const TileArgs &t, uint32_t block
                             hipStream_t s) {
   const size_t lds = (size_t)t.tile_t * t.tile_lc * a.R;
   if (blocks == 0) return hipSuccess;
-  if (to_host)
-    hipLaunchKernelGGL(xfer_tiles_lds<true>, dim3(blocks), dim3(kXferThreads), lds, s, a, t);
-  else
-    hipLaunchKernelGGL(xfer_tiles_lds<false>, dim3(blocks), dim3(kXferThreads), lds, s, a, t);
+  const dim3 grid(blocks), block(kXferThreads);
+  switch ((a.pace_ticks ? 2 : 0) + (to_host ? 1 : 0)) {
+    case 3: hipLaunchKernelGGL((xfer_tiles_lds<true, true>), grid, block, lds, s, a, t); break;
+    case 2: hipLaunchKernelGGL((xfer_tiles_lds<false, true>), grid, block, lds, s, a, t); break;
+    case 1: hipLaunchKernelGGL((xfer_tiles_lds<true, false>), grid, block, lds, s, a, t); break;
+    default: hipLaunchKernelGGL((xfer_tiles_lds<false, false>), grid, block, lds, s, a, t); break;
+  }
   return hipGetLastError();
 }
 

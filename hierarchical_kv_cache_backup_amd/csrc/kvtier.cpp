@@ -41,6 +41,10 @@ constexpr double kExtentPlanLimit = 4.0 * 1024 * 1024;  // staged extents AUTO l
 // staged_chunk_bytes / kRampMinDiv; below that the pass the ramp shortens is
 // shorter than the launches and copies it adds.
 constexpr double kRampMinDiv = 16.0;
+// A paced kernel grid delivers slightly less than its pace: 99.2% alone (2.9 GB
+// write-back paced to 55.9 GB/s), 97.9-98.1% beside an HBM-bound kernel
+// (paced to 55-57 GB/s); the model takes 99%.
+constexpr double kPaceYield = 0.99;
 
 int fail(int code, const std::string &msg) {
   set_error(msg);
@@ -178,6 +182,7 @@ struct kv_pool {
   std::atomic<int32_t> path[2] = {{KV_PATH_AUTO}, {KV_PATH_AUTO}};  // per direction
   std::mutex calib_mu;
   kv_calib_t calib{};
+  int wall_khz = 0;  // the device's constant wall-clock rate (paced kernels)
   explicit kv_pool(int L) : layer_src(L) {
     for (auto &x : layer_src) x.store(-1);
   }
@@ -215,13 +220,19 @@ void default_calibration(kv_calib_t *c) {
   // workgroup, and a slow start: the first ~27 MB of a call move at ~35 GB/s
   // instead of ~52, 242 us more (64-token calls run at 31 GB/s, 32K-token ones
   // at 51.9). With the start modelled, no per-row cost remains between 256-
-  // and 1152-byte rows; the fit is within 5% from 64 tokens up. A load's
-  // workgroup moves ~0.78 GB/s (link-rate sweep of 4-64 workgroups); loads
-  // run capped only beside other work.
+  // and 1152-byte rows; the fit is within 5% from 64 tokens up. Those rows
+  // were contiguous on the device. Where the walk jumps between device rows
+  // (random device slots; page_first, whose walk changes layer every row) a
+  // workgroup moved 2.04-2.09 GB/s instead of 2.17 (16-24 workgroups, 4096
+  // and 32768 tokens): ~30 ns per jump, 14 rows a block. A load's workgroup
+  // moves ~0.78 GB/s (link-rate sweep of 4-64 workgroups); loads run capped
+  // only beside other work.
   c->kernel_wg_gbps[0] = 2.17;
   c->kernel_wg_gbps[1] = 0.78;
   c->kernel_wg_row_ns[0] = 0.0;
   c->kernel_wg_row_ns[1] = 0.0;
+  c->kernel_wg_jump_ns[0] = 30.0;
+  c->kernel_wg_jump_ns[1] = 0.0;
   c->kernel_wg_start_bytes[0] = 27e6;
   c->kernel_wg_start_us[0] = 242.0;
   c->kernel_wg_start_bytes[1] = 0.0;
@@ -232,16 +243,33 @@ void default_calibration(kv_calib_t *c) {
   c->load_split_min_bytes = 16.0 * 1024 * 1024;
   // A write-back kernel on a full grid keeps the link full with posted host
   // writes, and an HBM-bound kernel running beside it (the model's next
-  // prefill or decode) then ran 35-41x longer (61-layer fp8 write-back beside
-  // a stream of 2 x 256 MiB reductions); on 24 workgroups it ran 1.15x longer
-  // (the copy engines: 1.12x) while the write-back still moved 51.6-53.6 GB/s
-  // against 55.9-56.5 on a full grid. Per workgroup the write-back moves
-  // ~2.15 GB/s up to 24 workgroups; 28-48 workgroups moved less in total
-  // (38-48 GB/s), 64 moved 52 but slowed the other kernel 6x. Loads keep the
-  // full grid: a load's host reads slow a neighbour 1.65-1.9x at any grid (a
-  // load beside compute is KV_F_LOAD_OVERLAP's case).
-  c->kernel_max_workgroups[0] = 24;
+  // prefill or decode) then ran 25-41x longer (fp8 write-backs beside a stream
+  // of 2 x 256 MiB reductions). Each workgroup issues ~2.2 GB/s of posted
+  // writes; up to 25 workgroups the neighbour ran 1.14-1.15x longer (the copy
+  // engines: 1.11x) and the write-back moved 52.7 (24) to 54.5-54.8 GB/s
+  // (25). From 26 unpaced workgroups the writes outran what the link drains
+  // (~56-57 GB/s): they queued, and the write-back fell to 38-47 GB/s (on one
+  // host even alone). Paced (kernel_pace_gbps) the grid cannot outrun the
+  // link: 26 workgroups paced to 56 GB/s moved 54.9 GB/s at 1.16x on two hosts;
+  // paced to 57 they moved 55.8 on one and collapsed to 51.6 on the other,
+  // whose link drains less. The neighbour's cost follows the workgroup count,
+  // not the pace (28: 1.18x, 32: 1.23x, 48: 1.75x at any pace), hence the
+  // smallest grid that can reach the link. On the host whose link drained
+  // least (1 GiB D2H copy 56.2 GB/s, full-grid kernel 55.0), a pace of 56 sagged
+  // to 52.2-52.9 GB/s on 8K-32K-token write-backs and one of 55.1 held 54.6:
+  // the default pace, 54, stays ~2% under that. A caller that measures its
+  // link paces at ~0.98 of its D2H copy rate. The start of a call is latency-bound: pacing it
+  // from the first block cost calls of 64-128 tokens (5.8-11.5 MB) 15-20%,
+  // while 32 blocks of burst per workgroup (13 MB for the grid) left them at
+  // the unpaced rate and changed nothing beside compute. Loads keep the full
+  // grid: a load's host reads slow a neighbour 1.65-1.9x at any grid (a load
+  // beside compute is KV_F_LOAD_OVERLAP's case).
+  c->kernel_max_workgroups[0] = 26;
   c->kernel_max_workgroups[1] = 0;
+  c->kernel_pace_gbps[0] = 54.0;
+  c->kernel_pace_gbps[1] = 0.0;
+  c->kernel_pace_burst_blocks[0] = 32.0;
+  c->kernel_pace_burst_blocks[1] = 0.0;
   // Measured on MI355X with a streamed 24-layer load (256 MiB per layer) and an
   // HBM-bound consumer (torch int64 sums) overlapped layer by layer: the
   // consumer's slowdown beside the kernel path grows with the load's grid (32
@@ -618,6 +646,17 @@ static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool dupl
   return cap;
 }
 
+// Wall-clock ticks each of `grid` workgroups spends at least per block (of
+// block_bytes) of a direct launch over `blocks` blocks, so that the grid moves
+// at most `gbps` GB/s in all (0: unpaced). A grid of one workgroup per block
+// has nothing to pace and runs unpaced.
+static uint32_t pace_ticks(double block_bytes, uint32_t blocks, uint32_t grid, double gbps,
+                           int wall_khz) {
+  if (!(gbps > 0) || grid == 0 || grid >= blocks || wall_khz <= 0) return 0;
+  const double ticks = std::ceil(block_bytes * grid * wall_khz / (gbps * 1e6));
+  return (uint32_t)std::min(std::max(ticks, 1.0), 4294967295.0);
+}
+
 // Staged path: makes the direction's staging buffer ready for a call on s that
 // moves at most unit_bytes per layer group: the call fills halves of
 // min(staged_chunk_bytes, unit_bytes) rounded down to whole rows (stage_use);
@@ -813,15 +852,30 @@ static int32_t model_path(const Geom &g, const kv_calib_t &c, int dir, const int
   const double blocks = std::ceil(launch_rows / (double)rows_per_block);
   const double wgs = cap > 0 ? std::min<double>(cap, blocks) : blocks;
   const double rows_all = (double)n * nlc_all;
-  double t_wg = (rows_all * c.kernel_wg_row_ns[dir] * 1e-3 +
+  // walk rows whose device row does not follow the previous walk row's: each
+  // (layer, component) pair starts a run of consecutive device slots inside
+  // each group of G positions of the host-order walk
+  const int64_t G = g.layout == KV_LAYER_FIRST ? n : (g.layout == KV_PAGE_FIRST ? 1 : g.ps);
+  int64_t dev_runs = 0;
+  for (int64_t i = 0; i < n; i++)
+    if (i % G == 0 || dev_idx[i] != dev_idx[i - 1] + 1) dev_runs++;
+  const double jumps = (double)dev_runs * nlc_all;
+  double t_wg = ((rows_all * c.kernel_wg_row_ns[dir] + jumps * c.kernel_wg_jump_ns[dir]) * 1e-3 +
                  mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
   if (cap > 0 && blocks > cap)  // a capped grid's slow start
     t_wg += c.kernel_wg_start_us[dir] *
             (c.kernel_wg_start_bytes[dir] > 0 ? std::min(1.0, mb / c.kernel_wg_start_bytes[dir])
                                               : 1.0);
+  double t_move = std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
+  if (c.kernel_pace_gbps[dir] > 0 && cap > 0 && blocks > cap) {  // a paced grid: past each
+    // workgroup's burst, the bytes move at most at the pace
+    const double burst = wgs * c.kernel_pace_burst_blocks[dir] * (double)rows_per_block * g.R;
+    t_move = std::max(t_move, std::max(0.0, mb - burst) /
+                                  (kPaceYield * c.kernel_pace_gbps[dir] * 1e3));
+  }
   double t_kernel = c.kernel_launch_us[dir] +
                     (ngroups - 1) * (c.kernel_group_us[dir] + c.kernel_link_gap_us[dir]) +
-                    std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
+                    t_move;
   double t_dma = (double)copies->size() * nlc_all * c.dma_copy_us[dir] +
                  mb / (c.dma_gbps[dir] * 1e3);
   // the staged path moves page-major layouts in one unit (see transfer); its
@@ -994,11 +1048,19 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
         b.nblocks = plan_tiles(b, g.layout, &t);
         d.launches++;
         d.last_workgroups = grid_for(b.nblocks, cap);
+        b.pace_ticks = pace_ticks((double)t.tile_t * t.tile_lc * g.R, b.nblocks,
+                                  (uint32_t)d.last_workgroups,
+                                  c.kernel_pace_gbps[dir], p->wall_khz);
+        b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
         e = launch_tiles_lds(b, t, (uint32_t)d.last_workgroups, dir == 0, s);
       } else {
         const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
         d.launches++;
         d.last_workgroups = grid_for(blocks, cap);
+        b.pace_ticks = pace_ticks((double)b.rows_per_block * g.R, blocks,
+                                  (uint32_t)d.last_workgroups, c.kernel_pace_gbps[dir],
+                                  p->wall_khz);
+        b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
         e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
       }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
@@ -1130,6 +1192,9 @@ static int transfer_noalloc(kv_pool *p, int dir, const int64_t *dev_idx, const i
     const uint32_t blocks = plan_rows(&b, g.layout, g.ps);
     d.launches++;
     d.last_workgroups = grid_for(blocks, cap);
+    b.pace_ticks = pace_ticks((double)b.rows_per_block * g.R, blocks,
+                              (uint32_t)d.last_workgroups, c.kernel_pace_gbps[dir], p->wall_khz);
+    b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
     e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
     if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
   }
@@ -1244,10 +1309,17 @@ static int check_calibration(const kv_calib_t *c) {
       return fail(KV_EINVAL, "duplex_kernel_max_workgroups must be in [0, 2^32)");
   for (int d = 0; d < 2; d++)
     if (!(c->kernel_wg_gbps[d] > 0) || !(c->kernel_wg_row_ns[d] >= 0) ||
+        !(c->kernel_wg_jump_ns[d] >= 0) ||
         !(c->kernel_wg_start_bytes[d] >= 0) || !(c->kernel_wg_start_us[d] >= 0) ||
         !(c->kernel_link_gap_us[d] >= 0))
-      return fail(KV_EINVAL, "kernel_wg_gbps must be > 0, kernel_wg_row_ns, kernel_wg_start_* "
-                             "and kernel_link_gap_us >= 0");
+      return fail(KV_EINVAL, "kernel_wg_gbps must be > 0, kernel_wg_row_ns, kernel_wg_jump_ns, "
+                             "kernel_wg_start_* and kernel_link_gap_us >= 0");
+  for (int d = 0; d < 2; d++)
+    if (!(c->kernel_pace_gbps[d] == 0 || c->kernel_pace_gbps[d] >= 1) ||
+        !(c->kernel_pace_burst_blocks[d] >= 0 && c->kernel_pace_burst_blocks[d] <= 65536) ||
+        c->kernel_pace_burst_blocks[d] != std::floor(c->kernel_pace_burst_blocks[d]))
+      return fail(KV_EINVAL, "kernel_pace_gbps must be 0 (unpaced) or >= 1, "
+                             "kernel_pace_burst_blocks a whole number in [0, 65536]");
   if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
       !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
@@ -1425,6 +1497,12 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
     return hip_fail(e, "hipHostGetDevicePointer");
   }
   p->host_dev = (uint8_t *)hd;
+  e = hipDeviceGetAttribute(&p->wall_khz, hipDeviceAttributeWallClockRate, p->device);
+  if (e != hipSuccess || p->wall_khz <= 0) {
+    kv_pool_destroy(p);
+    return e != hipSuccess ? hip_fail(e, "reading the device's wall-clock rate")
+                           : fail(KV_EHIP, "the device reports no wall-clock rate");
+  }
 
   e = hipMalloc((void **)&p->dev_tab, (size_t)nbuf * sizeof(uint8_t *));
   if (e == hipSuccess)

@@ -32,6 +32,9 @@ struct XferArgs {
   uint32_t row_begin;       // this launch moves walk rows [row_begin, row_end)
   uint32_t row_end;
   uint32_t nblocks;         // row blocks (or LDS tiles); workgroups stride over them
+  uint32_t pace_ticks;      // direct kernel: device wall-clock ticks each workgroup takes at
+                            // least per block (0 = unpaced)
+  uint32_t pace_burst;      // paced: blocks each workgroup moves unpaced before the pacing starts
 };
 
 // Tiling of the LDS-staged variant: a workgroup owns tile_t request positions x

@@ -174,11 +174,17 @@ typedef struct {
  * staging, ramp), kernel_group_us the gap each further launch of the same
  * call adds, and kernel_link_gap_us the time the host link then also stands
  * idle while one launch drains and the next ramps up (the staged path's
- * launches overlap its copies, so it pays kernel_group_us alone). On a capped grid of W workgroups the kernel is limited by what W
- * workgroups move: bytes / kernel_gbps is replaced by the larger of itself and
- * (rows * kernel_wg_row_ns * 1e-3 + bytes / (kernel_wg_gbps * 1e3)) / W
+ * launches overlap its copies, so it pays kernel_group_us alone). On a
+ * capped grid of W workgroups the kernel is limited by what W workgroups
+ * move: bytes / kernel_gbps is replaced by the larger of itself and
+ * ((rows * kernel_wg_row_ns + jumps * kernel_wg_jump_ns) * 1e-3
+ *  + bytes / (kernel_wg_gbps * 1e3)) / W
  * + kernel_wg_start_us * min(1, bytes / kernel_wg_start_bytes)
- * (microseconds), rows being the call's n * layers * C rows: a capped grid
+ * (microseconds), rows being the call's n * layers * C rows and jumps those
+ * rows of the host-order walk whose device row does not follow the previous
+ * walk row's (layers * C times the runs of consecutive device slots within
+ * the walk's groups of positions: the whole request in layer_first, each
+ * position in page_first, each page in page_first_direct): a capped grid
  * moves the first kernel_wg_start_bytes of a call more slowly, which costs up
  * to kernel_wg_start_us more (a capped grid has W < the launch's blocks).
  * The rates are fitted per direction on the target machine to the time a
@@ -190,14 +196,32 @@ typedef struct {
  * launches and events, large ones signal every layer as soon as it lands.
  * kernel_max_workgroups: cap on the workgroups one direct transfer kernel
  * (kernel and LDS paths) launches (0 = one per block of work; the staged
- * path's device-side passes, HBM to HBM, are not capped by it). The kernels stride over their work, so a cap
- * moves the same bytes while leaving compute units free for kernels on other
- * streams (e.g. the layer that was just loaded). Default: 24 for a backup, none
- * for a load. A write-back kernel on a large grid keeps so many posted host
- * writes queued that HBM-bound kernels running beside it slow by up to ~40x;
- * with 24 workgroups it still moves 92-96% of its full-grid rate and they slow
- * by ~1.15x, as beside the copy engines. Set [0] to 0 for the full grid when
- * nothing else runs during backups.
+ * path's device-side passes, HBM to HBM, are not capped by it). The kernels
+ * stride over their work, so a cap moves the same bytes while leaving compute
+ * units free for kernels on other streams (e.g. the layer that was just
+ * loaded). Default: 26 for a backup, none for a load. A write-back kernel on a
+ * large grid keeps so many posted host writes queued that HBM-bound kernels
+ * running beside it slow by up to ~40x; the slowdown follows the workgroup
+ * count, and 26 workgroups, paced, move 96-98% of the full grid's rate while
+ * they slow by ~1.16x (the copy engines: ~1.11x). Set [0] to 0 for the full
+ * grid when nothing else runs during backups.
+ * kernel_pace_gbps: on the kernel and LDS paths, > 0 holds a launch's
+ * workgroups to this total rate: each starts its blocks of work (tiles on the
+ * LDS path) at least grid * block bytes / rate apart on the device's
+ * constant-rate wall clock, with one block of catch-up after a stall. Each
+ * write-back workgroup issues ~2.2 GB/s of posted host writes; a grid that
+ * issues more than the host link drains queues them in the memory system and
+ * falls to ~40 GB/s, so the pace must stay under the link's D2H rate.
+ * Default: 54 for a backup (~2% under the lowest D2H drain rate measured on
+ * an MI355X's PCIe Gen5 x16 link; a caller that measures its own link's D2H
+ * copy rate can pace at ~0.98 of it), 0 (unpaced) for a load.
+ * kernel_pace_burst_blocks: a paced workgroup's first max(1, this) blocks go
+ * out at once and its pacing starts from the last of them: the start of a call
+ * is latency-bound, and pacing it from the first block slows small calls.
+ * Default: 32 for a backup. On a capped grid of W workgroups the model's
+ * kernel time is at least (bytes - W * burst blocks * block bytes) /
+ * (0.99 * kernel_pace_gbps), a block being the rows of 16 KiB or one row if
+ * longer (a paced grid delivered 98-99% of its pace).
  * With KV_F_LOAD_OVERLAP, a load's modelled time on each path is multiplied
  * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
  * fractions of the transfer time by which a concurrent HBM-bound kernel is
@@ -251,6 +275,13 @@ typedef struct {
                                       that move more slowly (0 = none) */
   double kernel_wg_start_us[2]; /* capped kernel grid: what those bytes cost in full (us) */
   double kernel_link_gap_us[2]; /* kernel path: link idle time per further launch (us) */
+  double kernel_pace_gbps[2];   /* kernel and LDS paths: > 0 paces a capped launch's
+                                   workgroups to this total rate (GB/s, >= 1) on the
+                                   device's wall clock; 0 = unpaced */
+  double kernel_pace_burst_blocks[2]; /* paced launches: blocks each workgroup moves at
+                                   once before its pacing starts (whole number, 0..2^16) */
+  double kernel_wg_jump_ns[2];  /* kernel path: a workgroup's extra time per walk row whose
+                                   device row does not follow the previous one's (ns) */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */
@@ -392,9 +423,12 @@ int kv_load(kv_pool_t *pool, const int64_t *dev_idx, const int64_t *host_idx, in
  * takes the zero-copy kernel path (KV_PATH_KERNEL; kv_last_path reports it),
  * with that path's grid caps, load groups and landed events, so kv_load_layer
  * works after it as after kv_load. Instead of the pool's index staging, the
- * request's index arrays are copied from the caller's host arrays (read during
- * the call only) into a device array the library holds for each GPU from its
- * first such call until the process ends: 8 MiB, n <= 262144 positions
+ * request's index arrays are copied from the caller's host arrays into a
+ * device array the library holds for each GPU from its first such call until
+ * the process ends. A pageable array is read before the call returns (the
+ * runtime stages it); a page-locked one is read by the copy on `stream`, so
+ * the caller keeps it unchanged until the stream has passed the call. The
+ * device array holds 8 MiB: n <= 262144 positions
  * (a larger n: KV_EINVAL, nothing enqueued). The index pairs are formed there
  * on the device. Every call on one GPU shares that GPU's array: calls issued on
  * one stream are ordered, but calls that overlap on one GPU (other streams,

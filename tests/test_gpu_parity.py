@@ -281,9 +281,79 @@ def test_capped_grid_matches_oracle(torch, stream, layout):
         pool.close()
 
 
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_paced_grid_matches_oracle(torch, stream, layout):
+    """kernel_pace_gbps holds a capped kernel grid to a set rate: the bytes of a
+    paced backup and load (kv_backup / kv_load and kv_transfer_noalloc) match
+    the oracle, and each call takes at least what the pace allows: after its
+    first max(1, burst) blocks a workgroup starts its blocks of rows_per_block
+    rows at least grid * block bytes / rate apart, with one block of catch-up,
+    so the busiest workgroup's m blocks take at least m - max(1, burst) - 1
+    such intervals."""
+    L, C, R, S_dev, S_host, ps = GEOMS[1]
+    g = Geometry(L, C, R, S_dev, S_host, ps, layout)
+    bufs = device_buffers(g, seed=12)
+    rng = np.random.default_rng(12 + layout)
+    pool = make_pool(g, bufs, kvt.PATH_KERNEL)
+    cap, gbps, burst = 3, 1.0, 4
+    c = pool.calibration()
+    assert list(c.kernel_pace_gbps) == [54.0, 0.0]     # defaults: backups paced, loads not
+    assert list(c.kernel_pace_burst_blocks) == [32.0, 0.0]
+    c.kernel_max_workgroups[:] = [cap, cap]
+    c.kernel_pace_gbps[:] = [gbps, gbps]
+    c.kernel_pace_burst_blocks[:] = [burst, burst]
+    pool.set_calibration(c)
+    rows_per_block = 2048 // (R // 8)            # 16 KiB of 8-byte chunks per block
+    interval_s = cap * rows_per_block * R / (gbps * 1e9)
+    launches = list(pool.stats().kernel_launches)
+    for noalloc in (False, True):
+        d, h = _request(rng, g, "random")
+        n = len(d)
+        print("paced layout=%d noalloc=%d n=%d" % (layout, noalloc, n), flush=True)
+        # one launch each way: a backup is one group, and a load this small too
+        blocks = -(-n * L * C // rows_per_block)
+        floor_s = max(0, -(-blocks // cap) - max(1, burst) - 1) * interval_s
+        for direction in (kvt.BACKUP, kvt.LOAD):
+            want_host = pool.host_array().copy()
+            dev_m = mirrors(bufs)
+            if direction == kvt.BACKUP:
+                assert oracle.backup(g, dev_m, want_host, d, h, 0, L) == 0
+            else:
+                pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+                want_host = pool.host_array().copy()
+                assert oracle.load(g, dev_m, want_host, d, h, 0, L) == 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if noalloc:
+                rc = kvt.kv_transfer_noalloc(pool.handle, direction, d, h, 0, L, stream)
+                assert rc == kvt.OK, kvt.kv_last_error()
+            elif direction == kvt.BACKUP:
+                pool.backup(d, h, 0, L, stream)
+            else:
+                pool.load(d, h, 0, L, stream)
+            e1.record(stream)
+            stream.synchronize()
+            torch.cuda.synchronize()
+            assert pool.stats().last_workgroups[direction] == cap
+            assert np.array_equal(pool.host_array(), want_host)
+            for k, b in enumerate(bufs):
+                assert np.array_equal(b.cpu().numpy(), dev_m[k]), k
+            took = e0.elapsed_time(e1) / 1e3
+            assert pool.stats().kernel_launches[direction] == launches[direction] + 1
+            launches[direction] += 1
+            assert took >= floor_s, (took, floor_s)
+    for field, bad in (("kernel_pace_gbps", 0.5), ("kernel_pace_burst_blocks", 1.5),
+                       ("kernel_pace_burst_blocks", -1.0), ("kernel_pace_burst_blocks", 65537.0)):
+        c = pool.calibration()
+        getattr(c, field)[0] = bad
+        with pytest.raises(kvt.KvError):
+            pool.set_calibration(c)
+    pool.close()
+
+
 def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
-    (default 24); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
+    (default 26); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
     on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load), at most
     overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP (default 96), and the
     smallest cap that applies; without a cap a launch has one workgroup per
@@ -304,14 +374,14 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     plain = make_pool(g, bufs)
     c = plain.calibration()
     assert list(c.duplex_kernel_max_workgroups) == [24.0, 128.0]
-    assert list(c.kernel_max_workgroups) == [24.0, 0.0]
+    assert list(c.kernel_max_workgroups) == [26.0, 0.0]
     assert tuple(plain.stats().last_workgroups) == (0, 0)
     default = grids(plain, kvt.PATH_KERNEL)
     c.kernel_max_workgroups[0] = 0
     plain.set_calibration(c)
     free = grids(plain, kvt.PATH_KERNEL)
     assert free[0] > 1000 and free[1] > 1000, free     # one workgroup per 16 KiB block
-    assert default == (24, free[1]), default
+    assert default == (26, free[1]), default
     c.duplex_kernel_max_workgroups[0] = -1
     with pytest.raises(kvt.KvError):
         plain.set_calibration(c)
@@ -333,7 +403,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
     got = grids(overlap, kvt.PATH_KERNEL)
-    assert got == (24, 96), got                     # the overlap cap is a load's only
+    assert got == (26, 96), got                     # the overlap cap is a load's only
     overlap.close()
 
 
@@ -512,9 +582,9 @@ def test_destroy_waits_for_work_in_flight(torch, path):
 
 def test_selector_models_capped_grids_per_workgroup(torch, stream):
     """AUTO prices a capped kernel by what its workgroups move: a backup of 512
-    blocks on the default 24-workgroup grid, at 10 GB/s per workgroup, loses to
-    two copy-engine copies; on a full grid (512 workgroups) it wins. Bytes match
-    the oracle on both paths."""
+    blocks on a 24-workgroup grid, at 10 GB/s per workgroup, loses to two
+    copy-engine copies; on a full grid (512 workgroups) it wins. Bytes match
+    the oracle on both paths. Unpaced: the per-workgroup terms are priced."""
     g = Geometry(2, 1, 4096, 1024, 1024, 8, 0)
     bufs = device_buffers(g, seed=20)
     pool = make_pool(g, bufs, kvt.PATH_AUTO)
@@ -524,6 +594,8 @@ def test_selector_models_capped_grids_per_workgroup(torch, stream):
     c.kernel_launch_us[0], c.dma_copy_us[0] = 15.0, 10.0        # kernel 15 us, copies 2 x 10 us
     c.kernel_gbps[0] = c.dma_gbps[0] = 1e6                       # link terms negligible
     c.kernel_wg_gbps[0], c.kernel_wg_row_ns[0] = 10.0, 0.0      # 8 MiB / (24 x 10 GB/s) = 35 us
+    c.kernel_max_workgroups[0] = 24
+    c.kernel_pace_gbps[0] = 0.0
     pool.set_calibration(c)
     run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
     assert pool.last_path(kvt.BACKUP) == kvt.PATH_DMA

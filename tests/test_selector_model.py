@@ -47,6 +47,7 @@ def test_closed_form_uncapped_and_capped_kernel():
     c.dma_gbps[:] = [25.0, 20.0]
     c.load_split_min_bytes = 1.0              # one group per layer
     c.kernel_max_workgroups[:] = [0, 0]
+    c.kernel_wg_jump_ns[:] = [0.0, 0.0]
     d, h = _req(1024)
     nbytes = 1024 * 4 * 2 * 4096
     rc, t = kvt.kv_model_path(g, c, 1, d, h, 0, 4)
@@ -70,6 +71,53 @@ def test_closed_form_uncapped_and_capped_kernel():
     c.kernel_max_workgroups[:] = [4096, 0]
     rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
     assert t[0] == pytest.approx(20 + max(nbytes / 50e3, (rows * 100e-3 + nbytes / 2e3) / 2048))
+    # a paced capped grid moves no faster than its pace past each workgroup's
+    # burst (24 x 16 blocks of 4 rows of 4 KiB); the pace does not apply to a
+    # grid of one workgroup per block, and 0 is unpaced
+    c.kernel_max_workgroups[:] = [24, 0]
+    burst_bytes = 24 * 16 * 4 * 4096
+    yld = 0.99                                          # what a paced grid delivers
+    for pace, burst, want in ((10.0, 0, nbytes / (yld * 10e3)),
+                              (10.0, 16, (nbytes - burst_bytes) / (yld * 10e3)),
+                              (1000.0, 0, t_wg), (0.0, 16, t_wg)):
+        c.kernel_pace_gbps[:] = [pace, 0.0]
+        c.kernel_pace_burst_blocks[:] = [burst, 0.0]
+        rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
+        assert t[0] == pytest.approx(20 + max(nbytes / 50e3, want)), (pace, burst)
+    c.kernel_pace_burst_blocks[:] = [10 ** 4, 0.0]     # a burst past the call: unpaced
+    c.kernel_pace_gbps[:] = [10.0, 0.0]
+    rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
+    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg))
+    # jumps: walk rows whose device row does not follow the previous walk row's,
+    # (layers x C) x the runs of consecutive device slots in each walk group:
+    # contiguous slots make one run in layer_first, one per position in
+    # page_first and one per 16-token page in page_first_direct; reversed
+    # slots make one per position everywhere
+    c.kernel_pace_gbps[:] = [0.0, 0.0]
+    c.kernel_wg_row_ns[:] = [0.0, 0.0]
+    c.kernel_wg_jump_ns[:] = [50.0, 0.0]
+    for layout, slots, runs in ((0, d, 1), (1, d, 1024), (2, d, 1024 // 16),
+                                (0, d[::-1].copy(), 1024), (2, d[::-1].copy(), 1024)):
+        g2 = kvt.geometry(4, 2, 4096, 4096, 4096, 16, layout)
+        rc, t = kvt.kv_model_path(g2, c, 0, slots, h, 0, 4)
+        want_wg = (runs * 8 * 50e-3 + nbytes / 2e3) / 24 + 50.0
+        assert t[0] == pytest.approx(20 + max(nbytes / 50e3, want_wg)), (layout, runs)
+    c.kernel_max_workgroups[:] = [4096, 0]
+    c.kernel_pace_gbps[:] = [10.0, 0.0]
+    rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
+    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, (rows * 100e-3 + nbytes / 2e3) / 2048))
+    for bad in (0.5, -1.0, float("nan")):
+        c.kernel_pace_gbps[:] = [bad, 0.0]
+        rc, _ = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
+        assert rc == kvt.EINVAL, bad
+    c.kernel_pace_gbps[:] = [10.0, 0.0]
+    for bad in (0.5, -1.0, 65537.0, float("nan")):
+        c.kernel_pace_burst_blocks[:] = [bad, 0.0]
+        rc, _ = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
+        assert rc == kvt.EINVAL, bad
+    c.kernel_pace_burst_blocks[:] = [0.0, 0.0]
+    c.kernel_wg_jump_ns[:] = [-1.0, 0.0]
+    assert kvt.kv_model_path(g, c, 0, d, h, 0, 4)[0] == kvt.EINVAL
 
 
 def test_staged_closed_form_with_and_without_ramp():
@@ -108,10 +156,16 @@ def test_flags_overlap_and_duplex():
             assert t1[2] == pytest.approx(t0[2] * (1 + c.overlap_dma_penalty))
         else:   # one unit: every layer would land at the end of the load
             assert math.isinf(t1[2]) and p1 != kvt.PATH_STAGED
-        # duplex: the kernel path is charged its penalty and runs capped
+        # duplex: the kernel path is charged its penalty and runs on the
+        # smaller of the two grid caps (the duplex cap, 24, below the default 26)
         p2, t2 = kvt.kv_model_path(g, c, 0, d, h, 0, 78, kvt.F_DUPLEX)
         p3, t3 = kvt.kv_model_path(g, c, 0, d, h, 0, 78)
-        assert t2[0] == pytest.approx(t3[0] * (1 + c.duplex_kernel_penalty[0]))
+        c24 = _default()
+        assert c.duplex_kernel_max_workgroups[0] < c.kernel_max_workgroups[0]
+        c24.kernel_max_workgroups[0] = c.duplex_kernel_max_workgroups[0]
+        p5, t5 = kvt.kv_model_path(g, c24, 0, d, h, 0, 78)
+        assert t2[0] == pytest.approx(t5[0] * (1 + c.duplex_kernel_penalty[0]))
+        assert t2[0] > t3[0] * (1 + c.duplex_kernel_penalty[0])
         assert t2[1] == t3[1] and t2[2] == t3[2]
         # backups never take the overlap charge
         p4, t4 = kvt.kv_model_path(g, c, 0, d, h, 0, 78, kvt.F_LOAD_OVERLAP)
@@ -122,18 +176,18 @@ def test_flags_overlap_and_duplex():
 # calibration; in brackets the GB/s measured per path (kernel / copy engines /
 # staged) by bench.py --size-sweep on an MI355X.
 MEASURED = [
-    ("layer_first", 256, 0, kvt.PATH_KERNEL),          # 32.5 / 19.8 / 19.4
-    ("layer_first", 2048, 0, kvt.PATH_KERNEL),         # 48.1 / 46.1 / 45.8
-    ("layer_first", 4096, 0, kvt.PATH_DMA),            # 50.2 / 50.9 / 50.5
-    ("layer_first", 8192, 0, kvt.PATH_DMA),            # 51.5 / 53.8 / 53.4
-    ("page_first", 64, 0, kvt.PATH_STAGED),            # 30.7 / 6.7 / 32.0
-    ("page_first", 1024, 0, kvt.PATH_STAGED),          # 42.4 / 38.1 / 53.1
-    ("page_first_direct", 256, 0, kvt.PATH_STAGED),    # 32.1 / 19.6 / 43.9
-    ("page_first_direct", 8192, 0, kvt.PATH_STAGED),   # 50.9 / 53.6 / 56.1
-    ("layer_first", 1024, 1, kvt.PATH_KERNEL),         # 53.4 / 38.3 / 36.6
-    ("layer_first", 8192, 1, kvt.PATH_KERNEL),         # 54.2 / 52.9 / 51.7
-    ("page_first", 256, 1, kvt.PATH_KERNEL),           # 50.6 / 20.0 / 45.2
-    ("page_first_direct", 4096, 1, kvt.PATH_STAGED),   # 54.5 / 50.0 / 55.8
+    ("layer_first", 256, 0, kvt.PATH_KERNEL),          # 33.2 / 19.6 / 19.0
+    ("layer_first", 2048, 0, kvt.PATH_KERNEL),         # 50.9 / 46.1 / 45.5
+    ("layer_first", 4096, 0, kvt.PATH_KERNEL),         # 53.3 / 51.0 / 50.3
+    ("page_first", 64, 0, kvt.PATH_STAGED),            # 31.2 / 6.7 / 32.5
+    ("page_first", 1024, 0, kvt.PATH_STAGED),          # 44.9 / 38.1 / 53.0
+    ("page_first", 16384, 0, kvt.PATH_STAGED),         # 51.8 / 54.7 / 56.3
+    ("page_first_direct", 256, 0, kvt.PATH_STAGED),    # 32.7 / 19.5 / 44.0
+    ("page_first_direct", 8192, 0, kvt.PATH_STAGED),   # 54.5 / 53.5 / 56.0
+    ("layer_first", 1024, 1, kvt.PATH_KERNEL),         # 53.4 / 37.1 / 36.7
+    ("layer_first", 8192, 1, kvt.PATH_KERNEL),         # 54.7 / 53.3 / 51.8
+    ("page_first", 256, 1, kvt.PATH_KERNEL),           # 50.6 / 20.1 / 45.4
+    ("page_first_direct", 4096, 1, kvt.PATH_STAGED),   # 54.5 / 50.0 / 55.7
 ]
 
 
