@@ -108,6 +108,8 @@ SIGNATURES = {
     "kv_get_calibration": (_I32, [_VP, ctypes.POINTER(kv_calib_t)]),
     "kv_get_stats": (_I32, [_VP, ctypes.POINTER(kv_stats_t)]),
     "kv_default_calibration": (_I32, [ctypes.POINTER(kv_calib_t)]),
+    "kv_calibrate_write_pace": (_I32, [_VP, ctypes.c_double, _VP,
+                                       ctypes.POINTER(ctypes.c_double)]),
     "kv_model_path": (_I32, [ctypes.POINTER(kv_geometry_t), ctypes.POINTER(kv_calib_t), _I32,
                              _P64, _P64, _I64, _I32, _I32, ctypes.c_uint32,
                              ctypes.POINTER(ctypes.c_double)]),
@@ -369,6 +371,14 @@ def kv_get_calibration(pool):
     return rc, c
 
 
+def kv_calibrate_write_pace(pool, fraction=0.98, stream=None):
+    """Returns (status, measured D2H GB/s)."""
+    g = ctypes.c_double(0.0)
+    rc = _lib.kv_calibrate_write_pace(pool, float(fraction), _stream_handle(stream),
+                                      ctypes.byref(g))
+    return rc, g.value
+
+
 def kv_get_stats(pool):
     s = kv_stats_t()
     rc = _lib.kv_get_stats(pool, ctypes.byref(s))
@@ -612,6 +622,13 @@ class KvPool:
 
     def set_calibration(self, c):
         _check(kv_set_calibration(self.handle, c))
+
+    def calibrate_write_pace(self, fraction=0.98, stream=None):
+        """Measures the D2H link into this pool's host pool (overwriting its
+        start) and paces kernel write-backs at `fraction` of it; returns GB/s."""
+        rc, gbps = kv_calibrate_write_pace(self.handle, fraction, stream)
+        _check(rc)
+        return gbps
 
     def stats(self):
         rc, s = kv_get_stats(self.handle)

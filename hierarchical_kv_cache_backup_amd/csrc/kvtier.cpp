@@ -1285,6 +1285,64 @@ static int stage_call(kv_pool *p, int dir, const int64_t *dev_idx, int64_t n, in
   return KV_OK;
 }
 
+// kv_calibrate_write_pace: the pool's D2H link rate from timed copy-engine
+// copies of its first device buffer into its host pool, and the write-back
+// pace set to `fraction` of it. The pool's transfers wait for the measurement
+// (both directions' locks, their work in flight drained first).
+constexpr int64_t kPaceProbeBytes = int64_t(256) << 20;
+constexpr int64_t kPaceProbeMinBytes = int64_t(16) << 20;
+constexpr int kPaceProbeCopies = 5;
+
+static int calibrate_write_pace(kv_pool *p, double fraction, void *stream, double *gbps_out) {
+  if (!p) return fail(KV_EINVAL, "pool is null");
+  if (!(fraction > 0 && fraction <= 1)) return fail(KV_EINVAL, "fraction must be in (0, 1]");
+  if (p->reader)
+    return fail(KV_EINVAL, "a pool sharing another pool's host pool cannot write into it to "
+                           "measure the link; calibrate the group's writer");
+  const int64_t buf_bytes = p->g.S_dev * p->g.R;
+  const int64_t bytes = std::min({kPaceProbeBytes, p->host_bytes, buf_bytes}) & ~int64_t(4095);
+  if (bytes < kPaceProbeMinBytes)
+    return fail(KV_EINVAL, "the pool's host pool and first device buffer must each hold 16 MiB "
+                           "to measure the link");
+  std::lock_guard<std::mutex> l0(p->dir[0].mu);
+  std::lock_guard<std::mutex> l1(p->dir[1].mu);
+  DeviceGuard dg(p->device);
+  if (dg.err != hipSuccess) return hip_fail(dg.err, "hipSetDevice");
+  hipError_t e = drain_direction(p->dir[0]);
+  if (e == hipSuccess) e = drain_direction(p->dir[1]);
+  if (e != hipSuccess) return hip_fail(e, "pending transfer failed");
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t ev[2] = {nullptr, nullptr};
+  for (hipEvent_t &x : ev)
+    if (e == hipSuccess) e = hipEventCreate(&x);
+  std::vector<double> rates;
+  for (int k = 0; k <= kPaceProbeCopies && e == hipSuccess; k++) {  // the first warms up
+    e = hipEventRecord(ev[0], s);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(p->host, p->bufs[0], (size_t)bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipEventRecord(ev[1], s);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[1]);
+    float ms = 0;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+    if (e == hipSuccess && k > 0 && ms > 0) rates.push_back((double)bytes / (ms * 1e6));
+  }
+  for (hipEvent_t x : ev)
+    if (x) (void)hipEventDestroy(x);
+  if (e != hipSuccess) return hip_fail(e, "timing the link");
+  if (rates.empty()) return fail(KV_EHIP, "the link measurement timed no copy");
+  std::sort(rates.begin(), rates.end());
+  const double gbps = rates[rates.size() / 2];
+  if (!(fraction * gbps >= 1))
+    return fail(KV_EINVAL, "measured D2H rate " + std::to_string(gbps) +
+                               " GB/s gives a pace below 1 GB/s");
+  {
+    std::lock_guard<std::mutex> cl(p->calib_mu);
+    p->calib.kernel_pace_gbps[0] = fraction * gbps;
+  }
+  if (gbps_out) *gbps_out = gbps;
+  return KV_OK;
+}
+
 // ---- C ABI ---------------------------------------------------------------------
 
 // Rejects a calibration with a figure out of range (KV_EINVAL).
@@ -1674,6 +1732,11 @@ int kv_get_stats(const kv_pool_t *p, kv_stats_t *out) {
     out->last_workgroups[d] = s.last_workgroups;
   }
   return KV_OK;
+}
+
+int kv_calibrate_write_pace(kv_pool_t *p, double fraction, void *stream, double *d2h_gbps) {
+  return guarded("kv_calibrate_write_pace",
+                 [&] { return calibrate_write_pace(p, fraction, stream, d2h_gbps); });
 }
 
 int kv_default_calibration(kv_calib_t *c) {

@@ -531,6 +531,27 @@ int32_t kv_last_path(const kv_pool_t *pool, int32_t direction);
 int kv_set_calibration(kv_pool_t *pool, const kv_calib_t *calib);
 int kv_get_calibration(const kv_pool_t *pool, kv_calib_t *calib);
 
+/* Measures the pool's D2H host-link rate and paces the kernel path's
+ * write-backs under it: kernel_pace_gbps[0] = fraction * the measured rate.
+ * For callers that write back on the GPU-assisted kernel path (the zero-copy
+ * kernels of the HiCache system design page, "data transfer optimisation")
+ * beside compute, on a host whose link rate they do not know: the paced grid
+ * must stay under what the link drains, which differs by host (see
+ * kernel_pace_gbps). The rate is the median of 5 timed copy-engine copies (after
+ * one untimed) of min(256 MiB, host pool, one device buffer) bytes from device
+ * buffer 0 into the start of the host pool, on `stream`; the call blocks
+ * until they finish (~30 ms). It OVERWRITES those host-pool bytes, so call it
+ * before the pool holds data, and not within a second of the process freeing
+ * gigabytes (the runtime's copies run slow then, which only lowers the pace).
+ * The pool's transfers already in flight are waited for first, and its other
+ * calls wait for the measurement. fraction in (0, 1]; 0.98 keeps the grid
+ * under the link on the hosts measured. *d2h_gbps (may be null) receives the
+ * measured rate. KV_EINVAL: null pool, fraction out of range, a pool that
+ * shares another pool's host pool (calibrate the group's writer), a host pool
+ * or first device buffer under 16 MiB, or a pace below 1 GB/s; KV_EHIP on a
+ * runtime error (the calibration is then unchanged). */
+int kv_calibrate_write_pace(kv_pool_t *pool, double fraction, void *stream, double *d2h_gbps);
+
 typedef struct {
   int64_t calls[2];         /* per direction (0 backup, 1 load) */
   int64_t bytes[2];         /* algorithmic bytes enqueued */

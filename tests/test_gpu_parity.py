@@ -351,6 +351,47 @@ def test_paced_grid_matches_oracle(torch, stream, layout):
     pool.close()
 
 
+def test_calibrate_write_pace(torch, stream):
+    """kv_calibrate_write_pace times copies of device buffer 0 into the host
+    pool and sets kernel_pace_gbps[0] to the given fraction of the median rate,
+    leaving the rest of the calibration alone; the pool still moves bytes that
+    match the oracle afterwards. It refuses fractions outside (0, 1], pools
+    whose host pool or first buffer is under 16 MiB, and a pool that shares
+    another pool's host pool."""
+    g = Geometry(2, 1, 4096, 8192, 8192, 64, 0)     # 32 MiB buffers, 64 MiB host pool
+    bufs = device_buffers(g, seed=23)
+    pool = make_pool(g, bufs, kvt.PATH_KERNEL)
+    before = pool.calibration()
+    print("calibrate write pace", flush=True)
+    gbps = pool.calibrate_write_pace(0.9, stream)
+    assert 1.0 < gbps < 200.0, gbps
+    c = pool.calibration()
+    assert c.kernel_pace_gbps[0] == pytest.approx(0.9 * gbps)
+    assert c.kernel_pace_gbps[1] == before.kernel_pace_gbps[1]
+    assert list(c.kernel_max_workgroups) == list(before.kernel_max_workgroups)
+    assert list(c.dma_gbps) == list(before.dma_gbps)
+    # the measurement wrote the start of the host pool; transfers stay exact
+    rng = np.random.default_rng(23)
+    pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
+    d = rng.permutation(g.S_dev)[:6000].astype(np.int64)
+    h = rng.permutation(g.S_host)[:6000].astype(np.int64)
+    run_backup_and_compare(g, pool, bufs, d, h, 0, g.L, stream)
+    for bad in (0.0, -0.5, 1.5, float("nan")):
+        rc, _ = kvt.kv_calibrate_write_pace(pool.handle, bad, stream)
+        assert rc == kvt.EINVAL, bad
+    assert pool.calibration().kernel_pace_gbps[0] == pytest.approx(0.9 * gbps)
+    gs = Geometry(2, 1, 4096, 1024, 1024, 64, 0)    # 4 MiB buffers
+    small = make_pool(gs, device_buffers(gs, seed=24))
+    rc, _ = kvt.kv_calibrate_write_pace(small.handle, 0.98, stream)
+    assert rc == kvt.EINVAL and "16 MiB" in kvt.kv_last_error()
+    small.close()
+    reader = kvt.KvPool(kv_geom(g), device_buffers(g, seed=25), share_with=pool)
+    rc, _ = kvt.kv_calibrate_write_pace(reader.handle, 0.98, stream)
+    assert rc == kvt.EINVAL and "writer" in kvt.kv_last_error()
+    reader.close()
+    pool.close()
+
+
 def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
     (default 26); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
