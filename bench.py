@@ -20,6 +20,8 @@ compute, the write filter and the oracle as CPU baseline. Studies that print the
     python bench.py --free-list-study           # FIFO vs LIFO host free list under churn
     python bench.py --tp-shared-study 8         # tensor-parallel group sharing one host pool
     python bench.py --profile-counters          # the kernels a rocprofv3 --pmc pass needs
+    python bench.py --interference-loader DIR & # a load beside the consumer below, which
+    rocprofv3 --pmc ... -- python bench.py --interference-consumer DIR   # runs under the profiler
 """
 import argparse
 import hashlib
@@ -87,6 +89,19 @@ def parse():
                    help="add the host-link bytes of two rocprofv3 --pmc output directories "
                         "(TCC_EA0_WRREQ*_sum, TCC_EA0_RDREQ*_sum) to profiles/counters.json "
                         "and exit")
+    p.add_argument("--interference-loader", metavar="DIR",
+                   help="one half of the interference counter study: in this process, keep "
+                        "per-layer loads running on each transfer path in turn while the "
+                        "consumer process (--interference-consumer DIR, the one under "
+                        "rocprofv3 --pmc) asks for it through files in DIR, then exit")
+    p.add_argument("--interference-consumer", metavar="DIR",
+                   help="the other half: run an HBM-bound consumer alone, then beside each of "
+                        "the loader's paths, then alone again, writing its phases to "
+                        "DIR/consumer.json, then exit")
+    p.add_argument("--summarize-interference", nargs="+", metavar="DIR",
+                   help="per-phase medians of the consumer's counters and launch durations "
+                        "from --interference-consumer runs under rocprofv3 (one DIR per "
+                        "counter pass), as a markdown table, and exit")
     return p.parse_args()
 
 
@@ -100,6 +115,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_interference:
+        summarize_interference(args.summarize_interference)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -128,6 +146,12 @@ def main():
         return
     if args.tp_shared_study:
         print(json.dumps(tp_shared_study(torch, kvt, workloads, args.tp_shared_study)))
+        return
+    if args.interference_loader:
+        interference_loader(torch, kvt, workloads, args.interference_loader)
+        return
+    if args.interference_consumer:
+        print(json.dumps(interference_consumer(torch, args.interference_consumer)))
         return
     dev = torch.device("cuda:0")
     shape = workloads.mla32k()
@@ -1423,6 +1447,210 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
             "workload": "%d layers x K/V x 1024 B fp8, 131072-token prefix, layer_first" % L,
             "consumer_pass_ms": round(t_pass * 1e3, 3),
             "load_overlap_caps": loads, "write_back_caps": backs}
+
+
+# ---- interference counters: a transfer in one process, the consumer in another
+
+# The loader's variants, in the order the consumer asks for them: the load path,
+# the grid cap of a load flagged KV_F_LOAD_OVERLAP (None: the pool's default
+# overlap grid; 0: full grid) and a label.
+INTERFERENCE_VARIANTS = (("kernel_overlap_grid", "PATH_KERNEL", None),
+                         ("kernel_full_grid", "PATH_KERNEL", 0),
+                         ("dma", "PATH_DMA", None))
+INTERFERENCE_WAIT_S = 120.0
+INTERFERENCE_LAYERS = 8
+
+
+def _await_file(path, deadline_s=INTERFERENCE_WAIT_S):
+    t0 = time.monotonic()
+    while not os.path.exists(path):
+        if time.monotonic() - t0 > deadline_s:
+            raise TimeoutError("no %s after %.0f s" % (path, deadline_s))
+        time.sleep(0.002)
+    with open(path) as f:
+        return f.read()
+
+
+def _put_file(path, text=""):
+    tmp = path + ".tmp"
+    with open(tmp, "w") as f:
+        f.write(text)
+    os.replace(tmp, path)
+
+
+def interference_loader(torch, kvt, workloads, d):
+    """The transfer side of the interference counter study, in a process of its
+    own so that the profiler's per-dispatch counter collection in the consumer's
+    process does not serialize it. On the streamed workload's first
+    INTERFERENCE_LAYERS layers (256 MiB each, K and V, 1024 B rows, 131072-token
+    prefix, layer_first): for each variant, wait for DIR/go.<name>, then issue
+    per-layer loads of the whole range back to back on a queue of its own until
+    DIR/stop.<name> appears; write DIR/running.<name> once the first load has
+    landed and DIR/stopped.<name> (the loads' GB/s) at the end. Every wait ends
+    after INTERFERENCE_WAIT_S seconds."""
+    shape = workloads.streamed()
+    L, C, R, ps = INTERFERENCE_LAYERS, shape.components, shape.row_bytes, shape.page_size
+    S, n = shape.device_slots, shape.extra["tokens"]
+    dev_idx, host_idx = workloads.prefix_indices(shape, 5, n, fragmented=False)
+    bufs = []
+    for l in range(L):
+        for c in range(C):
+            b = torch.empty(S * R, dtype=torch.uint8, device="cuda:0")
+            workloads.fill_device_buffer(b, shape, 5, l, c, torch)
+            bufs.append(b)
+    torch.cuda.synchronize()
+    s = kvt.Stream()
+    geom = kvt.geometry(L, C, R, S, shape.host_slots, ps, 0)
+    load_bytes = n * L * C * R
+    with kvt.KvPool(geom, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP) as pool:
+        pool.set_path(kvt.PATH_KERNEL)
+        pool.backup(dev_idx, host_idx, 0, L, s)
+        s.synchronize()
+        default_cal = pool.calibration()
+        _put_file(os.path.join(d, "loader_ready"))
+        for name, path, cap in INTERFERENCE_VARIANTS:
+            _await_file(os.path.join(d, "go." + name))
+            cal = pool.calibration()
+            cal.overlap_kernel_max_workgroups = (default_cal.overlap_kernel_max_workgroups
+                                                 if cap is None else cap)
+            pool.set_calibration(cal)
+            pool.set_path(getattr(kvt, path))
+            pool.load(dev_idx, host_idx, 0, L, s)
+            s.synchronize()
+            _put_file(os.path.join(d, "running." + name))
+            stop = os.path.join(d, "stop." + name)
+            t0, loads = time.perf_counter(), 0
+            while not os.path.exists(stop):
+                pool.load(dev_idx, host_idx, 0, L, s)
+                s.synchronize()
+                loads += 1
+                if time.perf_counter() - t0 > INTERFERENCE_WAIT_S:
+                    raise TimeoutError("no %s" % stop)
+            dt = time.perf_counter() - t0
+            st = pool.stats()
+            rec = {"variant": name, "path_used": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
+                   "workgroups": int(st.last_workgroups[1]) if path == "PATH_KERNEL" else None,
+                   "loads": loads, "h2d_gbps": round(loads * load_bytes / dt / 1e9, 3)}
+            log("interference loader %s" % json.dumps(rec))
+            _put_file(os.path.join(d, "stopped." + name), json.dumps(rec))
+    s.close()
+
+
+def interference_consumer(torch, d, reps=40):
+    """The compute side, run under rocprofv3 --pmc: an HBM-bound consumer (torch
+    int64 sums over two 256 MiB buffers, one reduction kernel each) runs `reps`
+    passes alone, then beside each of the loader's variants (asked for and
+    released through files in DIR), then alone again. DIR/consumer.json lists
+    the phases in order with their reduction dispatches, so that the counter
+    rows can be split by phase (the profiler serializes this process's
+    dispatches, not the loader's)."""
+    bufs = [torch.randint(0, 1 << 30, (32 << 20,), dtype=torch.int64, device="cuda:0")
+            for _ in range(2)]
+    acc = torch.zeros(1, dtype=torch.int64, device="cuda:0")
+
+    def passes(k):
+        for _ in range(k):
+            for b in bufs:
+                acc.add_(b.sum())
+        torch.cuda.synchronize()
+
+    phases = []
+
+    def phase(name, k):
+        t0 = time.perf_counter()
+        passes(k)
+        phases.append({"phase": name, "reduce_dispatches": k * len(bufs),
+                       "wall_s": round(time.perf_counter() - t0, 4)})
+
+    phase("warmup", 4)
+    _await_file(os.path.join(d, "loader_ready"))
+    phase("alone_before", reps)
+    loader = {}
+    for name, _, _ in INTERFERENCE_VARIANTS:
+        _put_file(os.path.join(d, "go." + name))
+        _await_file(os.path.join(d, "running." + name))
+        phase(name, reps)
+        _put_file(os.path.join(d, "stop." + name))
+        loader[name] = json.loads(_await_file(os.path.join(d, "stopped." + name)))
+    phase("alone_after", reps)
+    out = {"consumer": "torch int64 sum over 2 x 256 MiB, %d passes per phase" % reps,
+           "phases": phases, "loader": loader}
+    _put_file(os.path.join(d, "consumer.json"), json.dumps(out, indent=1))
+    return out
+
+
+# per-dispatch ratios the summary derives: name -> (numerator, denominator)
+INTERFERENCE_RATIOS = {
+    "ea_read_latency_cycles": ("TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum"),
+    "tcp_tcc_read_latency_cycles": ("TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum"),
+}
+
+
+def summarize_interference(dirs):
+    """Per-phase medians of the consumer's reduction dispatches over one or
+    more --interference-consumer directories (one rocprofv3 --pmc pass each,
+    with --kernel-trace): every counter, the launch duration, and the derived
+    ratios (EA read latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ; L1-to-L2 read
+    latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ). The reduction
+    kernel is the one named in most rows; its dispatches, in dispatch order,
+    are cut into the phases DIR/consumer.json lists."""
+    import csv
+    import glob
+    table = {}
+    order = []
+    loader = {}
+    for d in dirs:
+        with open(os.path.join(d, "consumer.json")) as f:
+            meta = json.load(f)
+        loader.update(meta["loader"])
+        per_dispatch = {}
+        names = {}
+        for r in _counter_rows(d):
+            did = int(r.get("Dispatch_Id") or r["Correlation_Id"])
+            per_dispatch.setdefault(did, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+            names[did] = r["Kernel_Name"]
+        durations = {}
+        for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    did = int(r.get("Dispatch_Id") or r["Correlation_Id"])
+                    durations[did] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        counts = {}
+        for did, name in names.items():
+            counts[name] = counts.get(name, 0) + 1
+        reduce_name = max(counts, key=lambda k: (counts[k], "reduce" in k))
+        ids = sorted(did for did, name in names.items() if name == reduce_name)
+        want = sum(p["reduce_dispatches"] for p in meta["phases"])
+        if len(ids) != want:
+            raise SystemExit("%s: %d dispatches of %s, consumer.json lists %d"
+                             % (d, len(ids), reduce_name[:60], want))
+        pos = 0
+        for p in meta["phases"]:
+            chunk = ids[pos:pos + p["reduce_dispatches"]]
+            pos += p["reduce_dispatches"]
+            if p["phase"] not in order:
+                order.append(p["phase"])
+            row = table.setdefault(p["phase"], {})
+            for did in chunk:
+                vals = dict(per_dispatch[did])
+                for ratio, (num, den) in INTERFERENCE_RATIOS.items():
+                    if vals.get(den):
+                        vals[ratio] = vals[num] / vals[den]
+                for c, v in vals.items():
+                    row.setdefault(c, []).append(v)
+                if did in durations:
+                    row.setdefault("duration_us", []).append(durations[did] / 1e3)
+    med = {ph: {c: statistics.median(v) for c, v in row.items()} for ph, row in table.items()}
+    cols = sorted({c for row in med.values() for c in row})
+    cols.remove("duration_us") if "duration_us" in cols else None
+    cols = ["duration_us"] + cols
+    print("| phase | " + " | ".join(cols) + " |")
+    print("|---|" + "---|" * len(cols))
+    for ph in order:
+        print("| %s | " % ph + " | ".join(
+            ("%.6g" % med[ph][c]) if c in med[ph] else "" for c in cols) + " |")
+    print()
+    print("loader: " + json.dumps(loader))
 
 
 def leg_ghost_list(kvt, workloads):
