@@ -1591,9 +1591,11 @@ def summarize_interference(dirs):
     more --interference-consumer directories (one rocprofv3 --pmc pass each,
     with --kernel-trace): every counter, the launch duration, and the derived
     ratios (EA read latency = TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ; L1-to-L2 read
-    latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ). The reduction
-    kernel is the one named in most rows; its dispatches, in dispatch order,
-    are cut into the phases DIR/consumer.json lists."""
+    latency = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ), each taken per
+    dispatch. The reduction kernel is torch's reduce_kernel (the most frequent
+    one, if several); its dispatches, in dispatch order, are cut into the phases
+    DIR/consumer.json lists, and a count that differs from the list's is
+    refused."""
     import csv
     import glob
     table = {}
@@ -1618,7 +1620,7 @@ def summarize_interference(dirs):
         counts = {}
         for did, name in names.items():
             counts[name] = counts.get(name, 0) + 1
-        reduce_name = max(counts, key=lambda k: (counts[k], "reduce" in k))
+        reduce_name = max(counts, key=lambda k: ("reduce_kernel" in k, counts[k]))
         ids = sorted(did for did, name in names.items() if name == reduce_name)
         want = sum(p["reduce_dispatches"] for p in meta["phases"])
         if len(ids) != want:
