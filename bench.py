@@ -1365,12 +1365,15 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
         pool.set_path(kvt.PATH_KERNEL)
         pool.backup(dev_idx, host_idx, 0, L, s_load)
         s_load.synchronize()
-        for cap in (32, 64, 96, 128, 256, 0, "dma") if with_loads else ():
+        load_cells = [(cap, ex) for ex in (1, 0) for cap in (8, 16, 24, 32, 48, 96)]
+        load_cells += [(0, 0), ("dma", 0)]
+        for cap, ex in load_cells if with_loads else ():
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
             else:
                 cal.overlap_kernel_max_workgroups = cap
+                cal.kernel_cu_exclusive[1] = ex
                 pool.set_calibration(cal)
             pool.load(dev_idx, host_idx, 0, L, s_load)
             s_load.synchronize()
@@ -1404,7 +1407,8 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
                 rates.append(L * layer_bytes / (ev[0].elapsed_time(ev[1]) / 1e3) / 1e9)
                 comp.append(sum(a.elapsed_time(b) for a, b in lev) / 1e3)
             wall = statistics.median(walls)
-            key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
+            key = "dma" if cap == "dma" else ("full" if cap == 0 else
+                                               str(cap) + (" cu-exclusive" if ex else ""))
             loads[key] = {"h2d_alone_gbps": round(L * layer_bytes / t_h2d / 1e9, 2),
                           "h2d_overlapped_gbps": round(statistics.median(rates), 2),
                           "compute_slowdown": round(statistics.median(comp) / t_comp, 3),
@@ -1413,10 +1417,12 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
         pool.set_path(kvt.PATH_KERNEL)
         t_alone = statistics.median([timed_consume(0, 40) for _ in range(3)])
         wb_bytes = n * (L - 1) * C * R
-        plain = [(cap, 0.0, 0) for cap in (8, 16, 20, 22, 24, 25, 26, 27, 28, 30, 32, 48, 64, 0)]
-        paced = ([(cap, gbps, 32) for cap in (26, 28, 32, 48) for gbps in (55.0, 56.0, 57.0)]
-                 + [(26, 56.0, 0)])
-        for cap, pace, burst in plain + paced + [("dma", 0.0, 0)]:
+        plain = [(cap, 0.0, 0, ex) for ex in (1, 0) for cap in (4, 6, 8, 10, 12, 16, 26)]
+        plain += [(0, 0.0, 0, 0)]
+        paced = [(cap, gbps, 32, 0) for cap in (7, 8, 9, 10, 12, 16, 26)
+                 for gbps in (50.0, 54.0, 56.0)]
+        paced += [(cap, 54.0, 32, 1) for cap in (8, 12, 26)]
+        for cap, pace, burst, ex in plain + paced + [("dma", 0.0, 0, 0)]:
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
@@ -1424,6 +1430,7 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
                 cal.kernel_max_workgroups[0] = cap
                 cal.kernel_pace_gbps[0] = pace
                 cal.kernel_pace_burst_blocks[0] = burst
+                cal.kernel_cu_exclusive[0] = ex
                 pool.set_calibration(cal)
             slow, rates = [], []
             for rep in range(3):
@@ -1438,6 +1445,8 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
             key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
             if pace:
                 key += " paced %g burst %d" % (pace, burst)
+            if cap not in ("dma", 0) and ex:
+                key += " cu-exclusive"
             backs[key] = {"d2h_gbps_beside_compute": round(statistics.median(rates), 2),
                           "compute_slowdown": round(statistics.median(slow), 3)}
             log("overlap study write-back %s %s" % (key, json.dumps(backs[key])))

@@ -25,6 +25,15 @@ namespace kvt {
 
 typedef uint32_t chunk_t __attribute__((ext_vector_type(2)));
 static_assert(sizeof(chunk_t) == kChunkBytes, "chunk size");
+// The same 8 bytes addressed in the global address space (device buffers and
+// the mapped host pool both are), so that the direct kernel's accesses are
+// global rather than flat ones.
+typedef __attribute__((address_space(1))) chunk_t gchunk_t;
+
+// Where the direct kernel's slots past a block's last chunk read and write:
+// one 8-byte chunk per lane of a wave, never read back by anyone.
+constexpr int kSinkChunks = 64;
+__device__ chunk_t g_sink[kSinkChunks];
 
 namespace {
 
@@ -74,27 +83,37 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   const uint32_t nrows = min(a.rows_per_block, a.row_end - row0);
   const uint32_t nchunks = nrows * a.cpr;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
-    chunk_t v[kXferUnroll];
-    chunk_t *dst[kXferUnroll];
+    // Branch-free slots: a slot past the block's chunks reads and writes the
+    // sink instead (its index arithmetic takes the block's last chunk, so its
+    // index loads stay in bounds). Then every slot's index-pair and
+    // buffer-table loads issue together under one wait, the payload loads all
+    // go out before any is waited for, and each store waits only for its own
+    // load. Under a per-slot branch the compiler waits for every outstanding
+    // access at each slot (it cannot count accesses across divergent
+    // branches); loads and stores complete in issue order, so the slots' host
+    // accesses would go out one at a time.
+    gchunk_t *src[kXferUnroll];
+    gchunk_t *dst[kXferUnroll];
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
-      const uint32_t f = base + u * kXferThreads + threadIdx.x;
-      dst[u] = nullptr;
-      if (f < nchunks) {
-        const uint32_t rr = f / a.cpr;
-        const uint32_t k = f - rr * a.cpr;
-        uint32_t i, lc;
-        walk_row(a, row0 + rr, i, lc);
-        chunk_t *d = reinterpret_cast<chunk_t *>(dev_row(a, i, lc)) + k;
-        chunk_t *h = reinterpret_cast<chunk_t *>(host_row(a, i, lc)) + k;
-        const chunk_t *src = kToHost ? d : h;
-        dst[u] = kToHost ? h : d;
-        v[u] = __builtin_nontemporal_load(src);
-      }
+      const uint32_t f0 = base + u * kXferThreads + threadIdx.x;
+      const bool live = f0 < nchunks;
+      const uint32_t f = live ? f0 : nchunks - 1;
+      const uint32_t rr = f / a.cpr;
+      const uint32_t k = f - rr * a.cpr;
+      uint32_t i, lc;
+      walk_row(a, row0 + rr, i, lc);
+      gchunk_t *d = (gchunk_t *)dev_row(a, i, lc) + k;
+      gchunk_t *h = (gchunk_t *)host_row(a, i, lc) + k;
+      gchunk_t *const sink = (gchunk_t *)(g_sink + (threadIdx.x & (kSinkChunks - 1)));
+      src[u] = live ? (kToHost ? d : h) : sink;
+      dst[u] = live ? (kToHost ? h : d) : sink;
     }
+    chunk_t v[kXferUnroll];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) v[u] = __builtin_nontemporal_load(src[u]);
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
-      if (!dst[u]) continue;
       if (!kToHost)
         __builtin_nontemporal_store(v[u], dst[u]);
       else
@@ -273,14 +292,15 @@ hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, in
   return hipGetLastError();
 }
 
-hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, hipStream_t s) {
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, size_t lds_bytes,
+                       hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid(blocks), block(kXferThreads);
   switch ((a.pace_ticks ? 2 : 0) + (to_host ? 1 : 0)) {
-    case 3: hipLaunchKernelGGL((xfer_rows<true, true>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((xfer_rows<false, true>), grid, block, 0, s, a); break;
-    case 1: hipLaunchKernelGGL((xfer_rows<true, false>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((xfer_rows<false, false>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((xfer_rows<true, true>), grid, block, lds_bytes, s, a); break;
+    case 2: hipLaunchKernelGGL((xfer_rows<false, true>), grid, block, lds_bytes, s, a); break;
+    case 1: hipLaunchKernelGGL((xfer_rows<true, false>), grid, block, lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL((xfer_rows<false, false>), grid, block, lds_bytes, s, a); break;
   }
   return hipGetLastError();
 }

@@ -183,6 +183,7 @@ struct kv_pool {
   std::mutex calib_mu;
   kv_calib_t calib{};
   int wall_khz = 0;  // the device's constant wall-clock rate (paced kernels)
+  int lds_max = 0;   // LDS bytes one workgroup may ask for (a compute unit's whole LDS)
   explicit kv_pool(int L) : layer_src(L) {
     for (auto &x : layer_src) x.store(-1);
   }
@@ -198,43 +199,41 @@ namespace {
 // against event time); sustained rates at 2.9 GB per call. bench.py re-fits
 // the rates live.
 void default_calibration(kv_calib_t *c) {
-  c->kernel_launch_us[0] = c->kernel_launch_us[1] = 30.0;
+  // A load's launches: 25 us for the first, 8.9 us for each further layer
+  // group (the 7 us gap between launches and 1.9 us of the link draining and
+  // ramping), at 57.3 GB/s: least squares on relative error over full-grid
+  // loads of 64 to 32768 tokens x 78 layers of 1152 bytes in the three
+  // layouts (1 to 78 launches), all within 2%. Backups are one launch.
+  c->kernel_launch_us[0] = 30.0;
+  c->kernel_launch_us[1] = 25.0;
   c->kernel_group_us[0] = c->kernel_group_us[1] = 7.0;
-  // A load's per-group launches cost 17.4 us each in all: the 7 us gap and
-  // 10.4 us of the link draining and ramping (least squares over loads of 64 to
-  // 32768 tokens in the three layouts, 1 to 78 launches, all within 1.7%,
-  // with kernel_gbps[1] = 57.3). Backups are one launch.
   c->kernel_link_gap_us[0] = 0.0;
-  c->kernel_link_gap_us[1] = 10.4;
+  c->kernel_link_gap_us[1] = 1.9;
   // The staged path also takes HBM bandwidth, compute units and a second
-  // stream: beside an HBM-bound kernel a staged write-back slowed it 1.17x,
-  // the copy engines 1.13-1.14x. Its time model is within ~1% of measured
+  // stream: beside an HBM-bound kernel a staged write-back slowed it 1.16x,
+  // the copy engines 1.10-1.12x. Its time model is within ~1% of measured
   // calls (4096-32768 tokens), so a 2% margin keeps it off ties and still
   // takes it where it is 3-6% faster (page-major write-backs of 8K+ tokens).
   c->staged_min_gain = 0.02;
   c->kernel_gbps[0] = 55.9;  // full grid; a capped grid is modelled per workgroup below
   c->kernel_gbps[1] = 57.3;
-  // What W workgroups move on a capped grid, fitted on 24-workgroup
-  // write-backs of the 78 x 1152-byte MLA latent from 64 to 32768 tokens (5.8
-  // MB to 2.9 GB) and of 32 x 2 x 256-byte rows (134 MB): 2.17 GB/s per
-  // workgroup, and a slow start: the first ~27 MB of a call move at ~35 GB/s
-  // instead of ~52, 242 us more (64-token calls run at 31 GB/s, 32K-token ones
-  // at 51.9). With the start modelled, no per-row cost remains between 256-
-  // and 1152-byte rows; the fit is within 5% from 64 tokens up. Those rows
-  // were contiguous on the device. Where the walk jumps between device rows
-  // (random device slots; page_first, whose walk changes layer every row) a
-  // workgroup moved 2.04-2.09 GB/s instead of 2.17 (16-24 workgroups, 4096
-  // and 32768 tokens): ~30 ns per jump, 14 rows a block. A load's workgroup
-  // moves ~0.78 GB/s (link-rate sweep of 4-64 workgroups); loads run capped
-  // only beside other work.
-  c->kernel_wg_gbps[0] = 2.17;
-  c->kernel_wg_gbps[1] = 0.78;
+  // What W workgroups move on a capped grid. A workgroup keeps 8 chunks of
+  // 8 bytes in flight per lane (16 KiB): a write-back workgroup moves 6.56
+  // GB/s, a load's 3.6-4.0 (4-16 workgroups). Write-backs on 8 workgroups, 64
+  // to 32768 tokens of the 78 x 1152-byte MLA latent (5.8 MB to 2.9 GB), fit
+  // 6.56 GB/s per workgroup with a slow start: the first ~17 MB of a call
+  // cost up to 267 us more than the launch (64-token calls run at 27 GB/s,
+  // 32K-token ones at 52.3); within 1.4%. Where the walk jumps between device
+  // rows (page_first, whose walk changes layer every row) a write-back
+  // workgroup pays ~4 ns more per jump.
+  c->kernel_wg_gbps[0] = 6.56;
+  c->kernel_wg_gbps[1] = 3.8;
   c->kernel_wg_row_ns[0] = 0.0;
   c->kernel_wg_row_ns[1] = 0.0;
-  c->kernel_wg_jump_ns[0] = 30.0;
+  c->kernel_wg_jump_ns[0] = 4.0;
   c->kernel_wg_jump_ns[1] = 0.0;
-  c->kernel_wg_start_bytes[0] = 27e6;
-  c->kernel_wg_start_us[0] = 242.0;
+  c->kernel_wg_start_bytes[0] = 17e6;
+  c->kernel_wg_start_us[0] = 267.0;
   c->kernel_wg_start_bytes[1] = 0.0;
   c->kernel_wg_start_us[1] = 0.0;
   c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
@@ -243,62 +242,56 @@ void default_calibration(kv_calib_t *c) {
   c->load_split_min_bytes = 16.0 * 1024 * 1024;
   // A write-back kernel on a full grid keeps the link full with posted host
   // writes, and an HBM-bound kernel running beside it (the model's next
-  // prefill or decode) then ran 25-41x longer (fp8 write-backs beside a stream
-  // of 2 x 256 MiB reductions). Each workgroup issues ~2.2 GB/s of posted
-  // writes; up to 25 workgroups the neighbour ran 1.14-1.15x longer (the copy
-  // engines: 1.11x) and the write-back moved 52.7 (24) to 54.5-54.8 GB/s
-  // (25). From 26 unpaced workgroups the writes outran what the link drains
-  // (~56-57 GB/s): they queued, and the write-back fell to 38-47 GB/s (on one
-  // host even alone). Paced (kernel_pace_gbps) the grid cannot outrun the
-  // link: 26 workgroups paced to 56 GB/s moved 54.9 GB/s at 1.16x on two hosts;
-  // paced to 57 they moved 55.8 on one and collapsed to 51.6 on the other,
-  // whose link drains less. The neighbour's cost follows the workgroup count,
-  // not the pace (28: 1.18x, 32: 1.23x, 48: 1.75x at any pace), hence the
-  // smallest grid that can reach the link. On the host whose link drained
-  // least (1 GiB D2H copy 56.2 GB/s, full-grid kernel 55.0), a pace of 56 sagged
-  // to 52.2-52.9 GB/s on 8K-32K-token write-backs and one of 55.1 held 54.6:
-  // the default pace, 54, stays ~2% under that. A caller that measures its
-  // link paces at ~0.98 of its D2H copy rate. The start of a call is latency-bound: pacing it
-  // from the first block cost calls of 64-128 tokens (5.8-11.5 MB) 15-20%,
-  // while 32 blocks of burst per workgroup (13 MB for the grid) left them at
-  // the unpaced rate and changed nothing beside compute. Loads keep the full
-  // grid: a load's host reads slow a neighbour 1.65-1.9x at any grid (a load
-  // beside compute is KV_F_LOAD_OVERLAP's case).
-  c->kernel_max_workgroups[0] = 26;
+  // prefill or decode) then ran ~26-45x longer (fp8 write-backs beside a
+  // stream of 2 x 256 MiB reductions). Unpaced, 8 workgroups (~54 GB/s of
+  // writes) moved 54.5-54.8 GB/s beside it for 1.21x; from 10 the writes
+  // outran what the link drains (~56-57 GB/s), queued in the memory system,
+  // and the write-back fell to 39-49 GB/s while the neighbour slowed 1.3-5x.
+  // Paced (kernel_pace_gbps) a grid cannot outrun the link, and the
+  // neighbour's cost follows the workgroup count (paced to 54-56 GB/s: 8
+  // 1.19-1.21x, 9 1.22x, 10 1.28x, 12 1.42-1.47x, 16 1.9-2x, 26 2.6-3x; the
+  // copy engines 1.12x): 9 is the smallest grid that produces more than the
+  // pace, and moved 53.0 GB/s paced to 54 and 54.9 paced to 56 beside the
+  // neighbour. On the host whose link drained least (1 GiB D2H copy 56.2
+  // GB/s) a pace of 56 sagged to 52.2-52.9 GB/s on 8K-32K-token write-backs
+  // and one of 55.1 held 54.6: the default pace, 54, stays ~2% under that. A
+  // caller that measures its link paces at ~0.98 of its D2H copy rate. The
+  // start of a call is latency-bound: 32 blocks of burst per workgroup before
+  // the pacing starts keep small calls at the unpaced rate. Loads keep the
+  // full grid: a load beside compute is KV_F_LOAD_OVERLAP's case.
+  c->kernel_max_workgroups[0] = 9;
   c->kernel_max_workgroups[1] = 0;
   c->kernel_pace_gbps[0] = 54.0;
   c->kernel_pace_gbps[1] = 0.0;
   c->kernel_pace_burst_blocks[0] = 32.0;
   c->kernel_pace_burst_blocks[1] = 0.0;
+  // A capped load's workgroups each take a compute unit of their own: beside
+  // the reductions below, 16 load workgroups slowed them 1.23x that way and
+  // 1.43x sharing compute units with them (24: 1.28x against 1.56x). A
+  // write-back's did not gain (8 workgroups: 1.33x alone on their compute
+  // units, 1.21x sharing them).
+  c->kernel_cu_exclusive[0] = 0.0;
+  c->kernel_cu_exclusive[1] = 1.0;
   // Measured on MI355X with a streamed 24-layer load (256 MiB per layer) and an
   // HBM-bound consumer (torch int64 sums) overlapped layer by layer: the
-  // consumer's slowdown beside the kernel path grows with the load's grid (32
-  // workgroups 1.39x at 24 GB/s, 64 1.43x at 47, 96 1.52x at 55.7, 128 1.61x,
-  // full grid 1.87x), beside the copy path it is 1.15x at 56.8 GB/s. 96
-  // workgroups is the smallest grid that still keeps the link near full.
-  c->overlap_kernel_penalty = 0.52;
+  // consumer's slowdown beside the kernel path grows with the load's grid
+  // (workgroups on compute units of their own: 8 1.17x at 29 GB/s, 16 1.23x
+  // at 52.9, 24 1.28x at 56.5, 32 1.32x, 48 1.40x; a full grid 1.93x); beside
+  // the copy path it is 1.14x at 56.8 GB/s. 24 workgroups is the smallest grid
+  // that keeps the link full.
+  c->overlap_kernel_penalty = 0.28;
   c->overlap_dma_penalty = 0.15;
-  c->overlap_kernel_max_workgroups = 96;
-  // Concurrent 1 GiB H2D + D2H (GB/s, H2D / D2H): copy engines both ways
-  // 56.4 / 48.5; H2D kernel beside D2H copy engines 56.4 / 31.0; H2D copy
-  // engines beside a D2H kernel 42.3 / 51.3; kernels both ways 37.8 / 38.1.
-  // A load's kernel keeps the link whatever the write-back runs on, unless the
-  // write-back is a full-grid kernel too. With the duplex caps below (load 128
-  // workgroups, backup 24) the mixed batch measured H2D 56.5 beside a D2H
-  // kernel of 33 GB/s (52 alone): the backup's kernel runs at ~0.6 of its
-  // uncapped rate, charged here as ~0.4 more time.
-  c->duplex_kernel_penalty[0] = 0.4;
+  c->overlap_kernel_max_workgroups = 24;
+  // On the mixed batch (load 51.2 GB || write-back 11.6 GB) with the duplex
+  // caps below, the load's kernel held 56.8 GB/s (57.3 alone) beside a
+  // write-back kernel of 24.4 GB/s (26.8 alone on its duplex cap of 4
+  // workgroups): 99.2% of the duplex bound, against 79.8% with the caps off
+  // (the load on a full grid). The write-back's cap already sets its rate;
+  // what the load's traffic costs it on top is charged here.
+  c->duplex_kernel_penalty[0] = 0.1;
   c->duplex_kernel_penalty[1] = 0.0;
-  // Full-grid transfer kernels occupy every compute unit with workgroups that
-  // wait microseconds on the host link; kernels of the other direction (and the
-  // staged path's gathers) that land beside them stall. On the mixed batch
-  // (load 51.2 GB || write-back 11.6 GB) a load kernel of 128 workgroups and a
-  // write-back kernel of 16-24 kept the load at 56.5 GB/s with the write-back
-  // at 22-34 (98.6% of the duplex bound, against 86% with full grids); at 48
-  // write-back workgroups the load fell to 50, at 8 the write-back became the
-  // longer of the two.
-  c->duplex_kernel_max_workgroups[0] = 24;
-  c->duplex_kernel_max_workgroups[1] = 128;
+  c->duplex_kernel_max_workgroups[0] = 4;
+  c->duplex_kernel_max_workgroups[1] = 32;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
   // the device-side gather / scatter of a staged chunk (stage_windows, HBM to
   // HBM, full grid), payload rate: the 2.94 GB prefix of 1152-byte rows packs
@@ -644,6 +637,16 @@ static uint32_t kernel_cap(const kv_calib_t &c, int dir, bool overlap, bool dupl
   if (overlap) tighten(c.overlap_kernel_max_workgroups);
   if (duplex && direct) tighten(c.duplex_kernel_max_workgroups[dir]);
   return cap;
+}
+
+// Dynamic LDS a direct kernel launch asks for per workgroup: a compute unit's
+// whole LDS when the launch runs under a grid cap and the direction's
+// kernel_cu_exclusive is set, so that its few workgroups each hold a compute
+// unit of their own; else none. A workgroup of a capped grid keeps host
+// accesses in flight for microseconds, and another kernel's waves on the same
+// compute unit then issue their own memory accesses more slowly.
+static size_t exclusive_lds(const kv_pool *p, const kv_calib_t &c, int dir, uint32_t cap) {
+  return cap != 0 && c.kernel_cu_exclusive[dir] > 0 ? (size_t)p->lds_max : 0;
 }
 
 // Wall-clock ticks each of `grid` workgroups spends at least per block (of
@@ -1061,7 +1064,8 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
                                   (uint32_t)d.last_workgroups, c.kernel_pace_gbps[dir],
                                   p->wall_khz);
         b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
-        e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
+        e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, exclusive_lds(p, c, dir, cap),
+                        s);
       }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
     }
@@ -1195,7 +1199,7 @@ static int transfer_noalloc(kv_pool *p, int dir, const int64_t *dev_idx, const i
     b.pace_ticks = pace_ticks((double)b.rows_per_block * g.R, blocks,
                               (uint32_t)d.last_workgroups, c.kernel_pace_gbps[dir], p->wall_khz);
     b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
-    e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, s);
+    e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, exclusive_lds(p, c, dir, cap), s);
     if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
   }
   if (e != hipSuccess) return hip_fail(e, "enqueueing the no-allocation transfer");
@@ -1378,6 +1382,9 @@ static int check_calibration(const kv_calib_t *c) {
         c->kernel_pace_burst_blocks[d] != std::floor(c->kernel_pace_burst_blocks[d]))
       return fail(KV_EINVAL, "kernel_pace_gbps must be 0 (unpaced) or >= 1, "
                              "kernel_pace_burst_blocks a whole number in [0, 65536]");
+  for (int d = 0; d < 2; d++)
+    if (c->kernel_cu_exclusive[d] != 0 && c->kernel_cu_exclusive[d] != 1)
+      return fail(KV_EINVAL, "kernel_cu_exclusive must be 0 or 1");
   if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
       !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))
@@ -1560,6 +1567,12 @@ static int create_pool(const kv_pool_desc_t *desc, kv_pool *group, kv_pool_t **o
     kv_pool_destroy(p);
     return e != hipSuccess ? hip_fail(e, "reading the device's wall-clock rate")
                            : fail(KV_EHIP, "the device reports no wall-clock rate");
+  }
+  e = hipDeviceGetAttribute(&p->lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, p->device);
+  if (e != hipSuccess || p->lds_max < 0) {
+    kv_pool_destroy(p);
+    return e != hipSuccess ? hip_fail(e, "reading the device's LDS per workgroup")
+                           : fail(KV_EHIP, "the device reports a negative LDS size");
   }
 
   e = hipMalloc((void **)&p->dev_tab, (size_t)nbuf * sizeof(uint8_t *));

@@ -199,19 +199,19 @@ typedef struct {
  * path's device-side passes, HBM to HBM, are not capped by it). The kernels
  * stride over their work, so a cap moves the same bytes while leaving compute
  * units free for kernels on other streams (e.g. the layer that was just
- * loaded). Default: 26 for a backup, none for a load. A write-back kernel on a
+ * loaded). Default: 9 for a backup, none for a load. A write-back kernel on a
  * large grid keeps so many posted host writes queued that HBM-bound kernels
- * running beside it slow by up to ~40x; the slowdown follows the workgroup
- * count, and 26 workgroups, paced, move 96-98% of the full grid's rate while
- * they slow by ~1.16x (the copy engines: ~1.11x). Set [0] to 0 for the full
+ * running beside it slow by up to ~45x; the slowdown follows the workgroup
+ * count, and 9 workgroups, paced, move ~95-98% of the full grid's rate while
+ * they slow by ~1.22x (the copy engines: ~1.12x). Set [0] to 0 for the full
  * grid when nothing else runs during backups.
  * kernel_pace_gbps: on the kernel and LDS paths, > 0 holds a launch's
  * workgroups to this total rate: each starts its blocks of work (tiles on the
  * LDS path) at least grid * block bytes / rate apart on the device's
  * constant-rate wall clock, with one block of catch-up after a stall. Each
- * write-back workgroup issues ~2.2 GB/s of posted host writes; a grid that
- * issues more than the host link drains queues them in the memory system and
- * falls to ~40 GB/s, so the pace must stay under the link's D2H rate.
+ * write-back workgroup issues up to ~6.6 GB/s of posted host writes; a grid
+ * that issues more than the host link drains queues them in the memory system
+ * and falls to ~40 GB/s, so the pace must stay under the link's D2H rate.
  * Default: 54 for a backup (~2% under the lowest D2H drain rate measured on
  * an MI355X's PCIe Gen5 x16 link; a caller that measures its own link's D2H
  * copy rate can pace at ~0.98 of it), 0 (unpaced) for a load.
@@ -226,15 +226,16 @@ typedef struct {
  * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
  * fractions of the transfer time by which a concurrent HBM-bound kernel is
  * slowed, measured per path; and the kernel path launches at most
- * overlap_kernel_max_workgroups workgroups.
+ * overlap_kernel_max_workgroups workgroups (default 24, which keep the link
+ * full; their workgroups take compute units of their own, kernel_cu_exclusive).
  * duplex_kernel_max_workgroups: cap on the workgroups of a kernel-path
  * transfer while the other direction is busy (KV_F_DUPLEX, or a transfer of
  * the other direction in flight at submission on another stream); [0] for a
- * backup, [1] for a load, 0 = no cap. A load's kernel holds the link with 128
- * workgroups; a write-back kernel with a small grid leaves the load most of the
- * link and, together with the load's cap, leaves compute units free for the
- * other direction's kernels. The staged path's device-side passes are not
- * capped by it.
+ * backup, [1] for a load, 0 = no cap; defaults 4 and 32. A load's kernel holds
+ * the link with 32 workgroups; a write-back kernel with a small grid leaves the
+ * load most of the link and, together with the load's cap, leaves compute
+ * units free for the other direction's kernels. The staged path's device-side
+ * passes are not capped by it.
  * The staged path moves a unit (all layers, or one load group in layer_first)
  * through two staging halves of min(staged_chunk_bytes, unit bytes) each, in
  * chunks that fill a half, except where a device-side pass cannot overlap a
@@ -282,6 +283,10 @@ typedef struct {
                                    once before its pacing starts (whole number, 0..2^16) */
   double kernel_wg_jump_ns[2];  /* kernel path: a workgroup's extra time per walk row whose
                                    device row does not follow the previous one's (ns) */
+  double kernel_cu_exclusive[2]; /* kernel path, a launch under a grid cap (a write-back's,
+                                   an overlapped load's, a duplex one): 1 = each workgroup
+                                   asks for a compute unit's whole LDS, so that no other
+                                   kernel's workgroups share its compute units; 0 = off */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

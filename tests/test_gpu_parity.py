@@ -269,12 +269,16 @@ def test_capped_grid_matches_oracle(torch, stream, layout):
     rng = np.random.default_rng(11 + layout)
     for path in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS):
         pool = make_pool(g, bufs, path)
-        for cap in (1, 3, 7):
+        # capped grids with and without a compute unit per workgroup
+        # (kernel_cu_exclusive), each way
+        for cap, excl in ((1, 1), (3, 0), (7, 1), (7, 0)):
             c = pool.calibration()
             c.kernel_max_workgroups[0] = c.kernel_max_workgroups[1] = cap
+            c.kernel_cu_exclusive[0] = c.kernel_cu_exclusive[1] = excl
             pool.set_calibration(c)
             d, h = _request(rng, g, "random")
-            print("capped layout=%d path=%d cap=%d" % (layout, path, cap), flush=True)
+            print("capped layout=%d path=%d cap=%d exclusive=%d" % (layout, path, cap, excl),
+                  flush=True)
             run_backup_and_compare(g, pool, bufs, d, h, 0, L, stream)
             pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
             run_load_and_compare(g, pool, bufs, d, h, 0, L, stream)
@@ -394,9 +398,9 @@ def test_calibrate_write_pace(torch, stream):
 
 def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
-    (default 26); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
-    on a KV_F_DUPLEX pool (defaults: 24 for a backup, 128 for a load), at most
-    overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP (default 96), and the
+    (default 9); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
+    on a KV_F_DUPLEX pool (defaults: 4 for a backup, 32 for a load), at most
+    overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP (default 24), and the
     smallest cap that applies; without a cap a launch has one workgroup per
     block of work. The bytes match the oracle under every cap."""
     g = Geometry(4, 2, 2048, 4096, 4096, 64, 0)
@@ -414,28 +418,33 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     plain = make_pool(g, bufs)
     c = plain.calibration()
-    assert list(c.duplex_kernel_max_workgroups) == [24.0, 128.0]
-    assert list(c.kernel_max_workgroups) == [26.0, 0.0]
+    assert list(c.duplex_kernel_max_workgroups) == [4.0, 32.0]
+    assert list(c.kernel_max_workgroups) == [9.0, 0.0]
+    assert list(c.kernel_cu_exclusive) == [0.0, 1.0]
     assert tuple(plain.stats().last_workgroups) == (0, 0)
     default = grids(plain, kvt.PATH_KERNEL)
     c.kernel_max_workgroups[0] = 0
     plain.set_calibration(c)
     free = grids(plain, kvt.PATH_KERNEL)
     assert free[0] > 1000 and free[1] > 1000, free     # one workgroup per 16 KiB block
-    assert default == (26, free[1]), default
+    assert default == (9, free[1]), default
     c.duplex_kernel_max_workgroups[0] = -1
+    with pytest.raises(kvt.KvError):
+        plain.set_calibration(c)
+    c = plain.calibration()
+    c.kernel_cu_exclusive[1] = 0.5               # 0 or 1 only
     with pytest.raises(kvt.KvError):
         plain.set_calibration(c)
     plain.close()
 
     duplex = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
-    assert grids(duplex, kvt.PATH_KERNEL) == (24, 128)
+    assert grids(duplex, kvt.PATH_KERNEL) == (4, 32)
     lds = grids(duplex, kvt.PATH_KERNEL_LDS)
-    assert 0 < lds[0] <= 24 and 0 < lds[1] <= 128, lds
+    assert 0 < lds[0] <= 4 and 0 < lds[1] <= 32, lds
     c = duplex.calibration()
-    c.kernel_max_workgroups[:] = [0, 64]             # the tighter cap wins
+    c.kernel_max_workgroups[:] = [0, 16]             # the tighter cap wins
     duplex.set_calibration(c)
-    assert grids(duplex, kvt.PATH_KERNEL) == (24, 64)
+    assert grids(duplex, kvt.PATH_KERNEL) == (4, 16)
     c.kernel_max_workgroups[:] = [0, 0]
     c.duplex_kernel_max_workgroups[:] = [0, 0]       # duplex caps off
     duplex.set_calibration(c)
@@ -444,7 +453,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
     got = grids(overlap, kvt.PATH_KERNEL)
-    assert got == (26, 96), got                     # the overlap cap is a load's only
+    assert got == (9, 24), got                      # the overlap cap is a load's only
     overlap.close()
 
 
@@ -494,8 +503,8 @@ def _hold_stream(torch, st, gate):
 def test_duplex_caps_follow_the_other_direction(torch):
     """Without KV_F_DUPLEX the duplex grid caps apply while the other direction
     has a transfer in flight on another stream at submission: a backup issued
-    while a load is held in flight gets 24 workgroups and a load issued while a
-    backup is held gets 128; issued alone, each gets the full grid. Both
+    while a load is held in flight gets 4 workgroups and a load issued while a
+    backup is held gets 32; issued alone, each gets the full grid. Both
     directions' bytes match the oracle."""
     import threading
     g = Geometry(4, 2, 2048, 8192, 8192, 64, 0)
@@ -527,13 +536,13 @@ def test_duplex_caps_follow_the_other_direction(torch):
             pool.load(d_load, h_load, 0, g.L, s_load)
             pool.backup(d_back, h_back, 0, g.L, s_back)
             grids = tuple(pool.stats().last_workgroups)
-            assert grids == (24, full_load), grids
+            assert grids == (4, full_load), grids
         else:
             cb = _hold_stream(torch, s_back, gate)
             pool.backup(d_back, h_back, 0, g.L, s_back)
             pool.load(d_load, h_load, 0, g.L, s_load)
             grids = tuple(pool.stats().last_workgroups)
-            assert grids == (full_backup, 128), grids
+            assert grids == (full_backup, 32), grids
         gate.set()
         s_load.synchronize()
         s_back.synchronize()
