@@ -50,10 +50,15 @@ __device__ __forceinline__ uint8_t *host_row(const XferArgs &a, uint32_t i, uint
 // until the device's constant-rate wall clock reaches `next`, the earliest
 // start of the workgroup's next block, which then moves one interval on. A
 // workgroup that fell behind keeps at most one interval of credit, so it
-// cannot burst to catch up.
+// cannot burst to catch up. The workgroups end their bursts together, so each
+// starts its schedule at its own fraction of an interval: their blocks then
+// go out evenly spread instead of all at once every interval.
 __device__ __forceinline__ void pace_block(uint64_t &next, uint32_t &done, const XferArgs &a) {
-  if (done < a.pace_burst) {  // the last burst block starts the schedule
-    if (++done == a.pace_burst) next = (uint64_t)wall_clock64() + a.pace_ticks;
+  const uint32_t burst = max(1u, a.pace_burst);
+  if (done < burst) {  // the last burst block starts the schedule
+    if (++done == burst)
+      next = (uint64_t)wall_clock64() + a.pace_ticks +
+             (uint64_t)a.pace_ticks * blockIdx.x / gridDim.x;
     return;
   }
   const uint32_t ticks = a.pace_ticks;
@@ -218,45 +223,55 @@ __global__ __launch_bounds__(kXferThreads) void xfer_tiles_lds(XferArgs a, TileA
   const uint32_t nchunks = t.nt * t.nl * cpr;
   const bool host_pos_major = ta.token_major != 0;
 
-  // phase 1: source -> LDS, in source order
+  // phase 1: source -> LDS, in source order. As in xfer_rows the slots are
+  // branch-free up to the LDS writes (a slot past the tile's chunks loads the
+  // sink), so the source loads are all in flight at once.
   const bool src_pos_major = kToHost ? false : host_pos_major;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
-    chunk_t v[kXferUnroll];
+    gchunk_t *src[kXferUnroll];
     uint32_t slot[kXferUnroll];
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
-      const uint32_t f = base + u * kXferThreads + threadIdx.x;
-      slot[u] = 0xffffffffu;
-      if (f < nchunks) {
-        uint32_t lc_t, p_t, k;
-        tile_walk(t, cpr, src_pos_major, f, lc_t, p_t, k);
-        const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
-        const chunk_t *src = reinterpret_cast<const chunk_t *>(kToHost ? dev_row(a, i, lc)
-                                                                    : host_row(a, i, lc)) + k;
-        v[u] = __builtin_nontemporal_load(src);
-        slot[u] = tile_slot(t, cpr, lc_t, p_t, k);
-      }
+      const uint32_t f0 = base + u * kXferThreads + threadIdx.x;
+      const bool live = f0 < nchunks;
+      uint32_t lc_t, p_t, k;
+      tile_walk(t, cpr, src_pos_major, live ? f0 : nchunks - 1, lc_t, p_t, k);
+      const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
+      gchunk_t *const s0 = (gchunk_t *)(kToHost ? dev_row(a, i, lc) : host_row(a, i, lc)) + k;
+      src[u] = live ? s0 : (gchunk_t *)(g_sink + (threadIdx.x & (kSinkChunks - 1)));
+      slot[u] = live ? tile_slot(t, cpr, lc_t, p_t, k) : 0xffffffffu;
     }
+    chunk_t v[kXferUnroll];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) v[u] = __builtin_nontemporal_load(src[u]);
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++)
       if (slot[u] != 0xffffffffu) lds[slot[u]] = v[u];
   }
   __syncthreads();
 
-  // phase 2: LDS -> destination, in destination order
+  // phase 2: LDS -> destination, in destination order; a slot past the
+  // tile's chunks reads the tile's last chunk and writes it to the sink.
   const bool dst_pos_major = kToHost ? host_pos_major : false;
   for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
+    gchunk_t *dst[kXferUnroll];
+    uint32_t slot[kXferUnroll];
 #pragma unroll
     for (int u = 0; u < kXferUnroll; u++) {
-      const uint32_t f = base + u * kXferThreads + threadIdx.x;
-      if (f < nchunks) {
-        uint32_t lc_t, p_t, k;
-        tile_walk(t, cpr, dst_pos_major, f, lc_t, p_t, k);
-        const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
-        chunk_t *dst = reinterpret_cast<chunk_t *>(kToHost ? host_row(a, i, lc) : dev_row(a, i, lc)) + k;
-        *dst = lds[tile_slot(t, cpr, lc_t, p_t, k)];
-      }
+      const uint32_t f0 = base + u * kXferThreads + threadIdx.x;
+      const bool live = f0 < nchunks;
+      uint32_t lc_t, p_t, k;
+      tile_walk(t, cpr, dst_pos_major, live ? f0 : nchunks - 1, lc_t, p_t, k);
+      const uint32_t i = t.i0 + p_t, lc = t.lcf + lc_t;
+      gchunk_t *const d0 = (gchunk_t *)(kToHost ? host_row(a, i, lc) : dev_row(a, i, lc)) + k;
+      dst[u] = live ? d0 : (gchunk_t *)(g_sink + (threadIdx.x & (kSinkChunks - 1)));
+      slot[u] = tile_slot(t, cpr, lc_t, p_t, k);
     }
+    chunk_t v[kXferUnroll];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) v[u] = lds[slot[u]];
+#pragma unroll
+    for (int u = 0; u < kXferUnroll; u++) *dst[u] = v[u];
   }
   __syncthreads();  // the next tile reuses the LDS
   }
