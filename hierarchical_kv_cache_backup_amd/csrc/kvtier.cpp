@@ -863,12 +863,9 @@ static int32_t model_path(const Geom &g, const kv_calib_t &c, int dir, const int
   for (int64_t i = 0; i < n; i++)
     if (i % G == 0 || dev_idx[i] != dev_idx[i - 1] + 1) dev_runs++;
   const double jumps = (double)dev_runs * nlc_all;
-  double t_wg = ((rows_all * c.kernel_wg_row_ns[dir] + jumps * c.kernel_wg_jump_ns[dir]) * 1e-3 +
-                 mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
-  if (cap > 0 && blocks > cap)  // a capped grid's slow start
-    t_wg += c.kernel_wg_start_us[dir] *
-            (c.kernel_wg_start_bytes[dir] > 0 ? std::min(1.0, mb / c.kernel_wg_start_bytes[dir])
-                                              : 1.0);
+  const double t_wg =
+      ((rows_all * c.kernel_wg_row_ns[dir] + jumps * c.kernel_wg_jump_ns[dir]) * 1e-3 +
+       mb / (c.kernel_wg_gbps[dir] * 1e3)) / std::max(wgs, 1.0);
   double t_move = std::max(mb / (c.kernel_gbps[dir] * 1e3), t_wg);
   if (c.kernel_pace_gbps[dir] > 0 && cap > 0 && blocks > cap) {  // a paced grid: past each
     // workgroup's burst, the bytes move at most at the pace
@@ -876,6 +873,10 @@ static int32_t model_path(const Geom &g, const kv_calib_t &c, int dir, const int
     t_move = std::max(t_move, std::max(0.0, mb - burst) /
                                   (kPaceYield * c.kernel_pace_gbps[dir] * 1e3));
   }
+  if (cap > 0 && blocks > cap)  // a capped grid's slow start, whichever bound holds after it
+    t_move += c.kernel_wg_start_us[dir] *
+              (c.kernel_wg_start_bytes[dir] > 0 ? std::min(1.0, mb / c.kernel_wg_start_bytes[dir])
+                                                : 1.0);
   double t_kernel = c.kernel_launch_us[dir] +
                     (ngroups - 1) * (c.kernel_group_us[dir] + c.kernel_link_gap_us[dir]) +
                     t_move;

@@ -176,17 +176,19 @@ typedef struct {
  * idle while one launch drains and the next ramps up (the staged path's
  * launches overlap its copies, so it pays kernel_group_us alone). On a
  * capped grid of W workgroups the kernel is limited by what W workgroups
- * move: bytes / kernel_gbps is replaced by the larger of itself and
+ * move: bytes / kernel_gbps is replaced by the larger of itself,
  * ((rows * kernel_wg_row_ns + jumps * kernel_wg_jump_ns) * 1e-3
  *  + bytes / (kernel_wg_gbps * 1e3)) / W
- * + kernel_wg_start_us * min(1, bytes / kernel_wg_start_bytes)
+ * and, when paced, the pace term under kernel_pace_burst_blocks below, plus
+ * kernel_wg_start_us * min(1, bytes / kernel_wg_start_bytes)
  * (microseconds), rows being the call's n * layers * C rows and jumps those
  * rows of the host-order walk whose device row does not follow the previous
  * walk row's (layers * C times the runs of consecutive device slots within
  * the walk's groups of positions: the whole request in layer_first, each
  * position in page_first, each page in page_first_direct): a capped grid
  * moves the first kernel_wg_start_bytes of a call more slowly, which costs up
- * to kernel_wg_start_us more (a capped grid has W < the launch's blocks).
+ * to kernel_wg_start_us more whichever bound holds (a capped grid has W < the
+ * launch's blocks).
  * The rates are fitted per direction on the target machine to the time a
  * call takes less its modelled fixed costs.
  * load_split_min_bytes: kv_load goes out in groups of consecutive layers, one
@@ -219,9 +221,10 @@ typedef struct {
  * out at once and its pacing starts from the last of them: the start of a call
  * is latency-bound, and pacing it from the first block slows small calls.
  * Default: 32 for a backup. On a capped grid of W workgroups the model's
- * kernel time is at least (bytes - W * burst blocks * block bytes) /
- * (0.99 * kernel_pace_gbps), a block being the rows of 16 KiB or one row if
- * longer (a paced grid delivered 98-99% of its pace).
+ * kernel time before the slow start is at least (bytes - W * burst blocks *
+ * block bytes) / (0.99 * kernel_pace_gbps), a block being the rows of 16 KiB
+ * or one row if longer (a paced grid delivered 98-99% of its pace past its
+ * start).
  * With KV_F_LOAD_OVERLAP, a load's modelled time on each path is multiplied
  * by (1 + penalty): overlap_kernel_penalty / overlap_dma_penalty are the
  * fractions of the transfer time by which a concurrent HBM-bound kernel is

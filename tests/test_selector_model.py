@@ -64,16 +64,17 @@ def test_closed_form_uncapped_and_capped_kernel():
     c.kernel_wg_start_us[:] = [50.0, 0.0]
     rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
     rows = 1024 * 8
-    t_wg = (rows * 100e-3 + nbytes / 2e3) / 24 + 50.0
-    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg))
+    t_wg = (rows * 100e-3 + nbytes / 2e3) / 24          # before the slow start
+    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg) + 50.0)
     # a cap above the block count leaves the grid whole (4 rows of 4 KiB per
     # 16 KiB block: 2048 blocks) and takes no slow start
     c.kernel_max_workgroups[:] = [4096, 0]
     rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
     assert t[0] == pytest.approx(20 + max(nbytes / 50e3, (rows * 100e-3 + nbytes / 2e3) / 2048))
     # a paced capped grid moves no faster than its pace past each workgroup's
-    # burst (24 x 16 blocks of 4 rows of 4 KiB); the pace does not apply to a
-    # grid of one workgroup per block, and 0 is unpaced
+    # burst (24 x 16 blocks of 4 rows of 4 KiB), and the slow start comes on
+    # top of whichever bound holds; the pace does not apply to a grid of one
+    # workgroup per block, and 0 is unpaced
     c.kernel_max_workgroups[:] = [24, 0]
     burst_bytes = 24 * 16 * 4 * 4096
     yld = 0.99                                          # what a paced grid delivers
@@ -83,11 +84,11 @@ def test_closed_form_uncapped_and_capped_kernel():
         c.kernel_pace_gbps[:] = [pace, 0.0]
         c.kernel_pace_burst_blocks[:] = [burst, 0.0]
         rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
-        assert t[0] == pytest.approx(20 + max(nbytes / 50e3, want)), (pace, burst)
+        assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg, want) + 50.0), (pace, burst)
     c.kernel_pace_burst_blocks[:] = [10 ** 4, 0.0]     # a burst past the call: unpaced
     c.kernel_pace_gbps[:] = [10.0, 0.0]
     rc, t = kvt.kv_model_path(g, c, 0, d, h, 0, 4)
-    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg))
+    assert t[0] == pytest.approx(20 + max(nbytes / 50e3, t_wg) + 50.0)
     # jumps: walk rows whose device row does not follow the previous walk row's,
     # (layers x C) x the runs of consecutive device slots in each walk group:
     # contiguous slots make one run in layer_first, one per position in
