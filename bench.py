@@ -1460,12 +1460,14 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
 
 # ---- interference counters: a transfer in one process, the consumer in another
 
-# The loader's variants, in the order the consumer asks for them: the load path,
-# the grid cap of a load flagged KV_F_LOAD_OVERLAP (None: the pool's default
-# overlap grid; 0: full grid) and a label.
-INTERFERENCE_VARIANTS = (("kernel_overlap_grid", "PATH_KERNEL", None),
-                         ("kernel_full_grid", "PATH_KERNEL", 0),
-                         ("dma", "PATH_DMA", None))
+# The loader's variants, in the order the consumer asks for them: a label, the
+# load path, the grid cap of a load flagged KV_F_LOAD_OVERLAP (None: the pool's
+# default overlap grid; 0: full grid) and whether a capped load's workgroups
+# take compute units of their own (kernel_cu_exclusive[1]; None: the default).
+INTERFERENCE_VARIANTS = (("kernel_overlap_grid", "PATH_KERNEL", None, None),
+                         ("kernel_overlap_grid_shared_cus", "PATH_KERNEL", None, 0),
+                         ("kernel_full_grid", "PATH_KERNEL", 0, None),
+                         ("dma", "PATH_DMA", None, None))
 INTERFERENCE_WAIT_S = 120.0
 INTERFERENCE_LAYERS = 8
 
@@ -1517,11 +1519,13 @@ def interference_loader(torch, kvt, workloads, d):
         s.synchronize()
         default_cal = pool.calibration()
         _put_file(os.path.join(d, "loader_ready"))
-        for name, path, cap in INTERFERENCE_VARIANTS:
+        for name, path, cap, exclusive in INTERFERENCE_VARIANTS:
             _await_file(os.path.join(d, "go." + name))
             cal = pool.calibration()
             cal.overlap_kernel_max_workgroups = (default_cal.overlap_kernel_max_workgroups
                                                  if cap is None else cap)
+            cal.kernel_cu_exclusive[1] = (default_cal.kernel_cu_exclusive[1]
+                                          if exclusive is None else exclusive)
             pool.set_calibration(cal)
             pool.set_path(getattr(kvt, path))
             pool.load(dev_idx, host_idx, 0, L, s)
@@ -1539,6 +1543,9 @@ def interference_loader(torch, kvt, workloads, d):
             st = pool.stats()
             rec = {"variant": name, "path_used": kvt.PATH_NAMES[pool.last_path(kvt.LOAD)],
                    "workgroups": int(st.last_workgroups[1]) if path == "PATH_KERNEL" else None,
+                   "cu_exclusive": (bool(cal.kernel_cu_exclusive[1])
+                                    if path == "PATH_KERNEL" and cal.overlap_kernel_max_workgroups > 0
+                                    else None),
                    "loads": loads, "h2d_gbps": round(loads * load_bytes / dt / 1e9, 3)}
             log("interference loader %s" % json.dumps(rec))
             _put_file(os.path.join(d, "stopped." + name), json.dumps(rec))
@@ -1575,7 +1582,7 @@ def interference_consumer(torch, d, reps=40):
     _await_file(os.path.join(d, "loader_ready"))
     phase("alone_before", reps)
     loader = {}
-    for name, _, _ in INTERFERENCE_VARIANTS:
+    for name, _, _, _ in INTERFERENCE_VARIANTS:
         _put_file(os.path.join(d, "go." + name))
         _await_file(os.path.join(d, "running." + name))
         phase(name, reps)
