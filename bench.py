@@ -1417,12 +1417,15 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
         pool.set_path(kvt.PATH_KERNEL)
         t_alone = statistics.median([timed_consume(0, 40) for _ in range(3)])
         wb_bytes = n * (L - 1) * C * R
-        plain = [(cap, 0.0, 0, ex) for ex in (1, 0) for cap in (4, 6, 8, 10, 12, 16, 26)]
-        plain += [(0, 0.0, 0, 0)]
-        paced = [(cap, gbps, 32, 0) for cap in (7, 8, 9, 10, 12, 16, 26)
-                 for gbps in (50.0, 54.0, 56.0)]
-        paced += [(cap, 54.0, 32, 1) for cap in (8, 12, 26)]
-        for cap, pace, burst, ex in plain + paced + [("dma", 0.0, 0, 0)]:
+        # (grid cap, pace, burst blocks, a compute unit per workgroup, lane depth)
+        plain = [(cap, 0.0, 0, 0, 2) for cap in (8, 12, 16, 18, 20, 24, 32)]
+        plain += [(cap, 0.0, 0, 0, 8) for cap in (4, 6, 8, 10, 12)]
+        plain += [(0, 0.0, 0, 0, 2)]
+        paced = [(cap, gbps, 32, 0, 2) for cap in (14, 16, 18, 20, 24, 28)
+                 for gbps in (54.0, 56.0)]
+        paced += [(cap, gbps, 32, 0, 8) for cap in (8, 9, 10, 12) for gbps in (54.0, 56.0)]
+        paced += [(18, 54.0, 32, 1, 2), (9, 54.0, 32, 1, 8)]
+        for cap, pace, burst, ex, depth in plain + paced + [("dma", 0.0, 0, 0, 2)]:
             cal = pool.calibration()
             if cap == "dma":
                 pool.set_path(kvt.PATH_DMA)
@@ -1431,6 +1434,7 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
                 cal.kernel_pace_gbps[0] = pace
                 cal.kernel_pace_burst_blocks[0] = burst
                 cal.kernel_cu_exclusive[0] = ex
+                cal.kernel_lane_depth[0] = depth
                 pool.set_calibration(cal)
             slow, rates = [], []
             for rep in range(3):
@@ -1443,6 +1447,8 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
                 e1.synchronize()
                 rates.append(wb_bytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
             key = "dma" if cap == "dma" else ("full" if cap == 0 else str(cap))
+            if cap != "dma":
+                key += " depth %d" % depth
             if pace:
                 key += " paced %g burst %d" % (pace, burst)
             if cap not in ("dma", 0) and ex:

@@ -68,7 +68,8 @@ class kv_calib_t(ctypes.Structure):
                 ("kernel_pace_gbps", ctypes.c_double * 2),
                 ("kernel_pace_burst_blocks", ctypes.c_double * 2),
                 ("kernel_wg_jump_ns", ctypes.c_double * 2),
-                ("kernel_cu_exclusive", ctypes.c_double * 2)]
+                ("kernel_cu_exclusive", ctypes.c_double * 2),
+                ("kernel_lane_depth", ctypes.c_double * 2)]
 
 
 class kv_stats_t(ctypes.Structure):

@@ -78,7 +78,9 @@ __device__ __forceinline__ void pace_block(uint64_t &next, uint32_t &done, const
 // device's constant-rate wall clock, so that the grid as a whole produces host
 // traffic at a set rate instead of at what its workgroups can issue; a
 // workgroup that fell behind may catch up by one block, no more.
-template <bool kToHost, bool kPaced>
+// kDepth: chunks each lane keeps in flight (the slots of one pass); a block of
+// rows_per_block rows takes ceil(its chunks / (256 * kDepth)) passes.
+template <bool kToHost, bool kPaced, int kDepth>
 __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   uint64_t next = kPaced ? (uint64_t)wall_clock64() : 0;
   uint32_t done = 0;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
   const uint32_t row0 = a.row_begin + blk * a.rows_per_block;
   const uint32_t nrows = min(a.rows_per_block, a.row_end - row0);
   const uint32_t nchunks = nrows * a.cpr;
-  for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock) {
+  for (uint32_t base = 0; base < nchunks; base += kXferThreads * kDepth) {
     // Branch-free slots: a slot past the block's chunks reads and writes the
     // sink instead (its index arithmetic takes the block's last chunk, so its
     // index loads stay in bounds). Then every slot's index-pair and
@@ -97,10 +99,10 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
     // access at each slot (it cannot count accesses across divergent
     // branches); loads and stores complete in issue order, so the slots' host
     // accesses would go out one at a time.
-    gchunk_t *src[kXferUnroll];
-    gchunk_t *dst[kXferUnroll];
+    gchunk_t *src[kDepth];
+    gchunk_t *dst[kDepth];
 #pragma unroll
-    for (int u = 0; u < kXferUnroll; u++) {
+    for (int u = 0; u < kDepth; u++) {
       const uint32_t f0 = base + u * kXferThreads + threadIdx.x;
       const bool live = f0 < nchunks;
       const uint32_t f = live ? f0 : nchunks - 1;
@@ -114,11 +116,11 @@ __global__ __launch_bounds__(kXferThreads) void xfer_rows(XferArgs a) {
       src[u] = live ? (kToHost ? d : h) : sink;
       dst[u] = live ? (kToHost ? h : d) : sink;
     }
-    chunk_t v[kXferUnroll];
+    chunk_t v[kDepth];
 #pragma unroll
-    for (int u = 0; u < kXferUnroll; u++) v[u] = __builtin_nontemporal_load(src[u]);
+    for (int u = 0; u < kDepth; u++) v[u] = __builtin_nontemporal_load(src[u]);
 #pragma unroll
-    for (int u = 0; u < kXferUnroll; u++) {
+    for (int u = 0; u < kDepth; u++) {
       if (!kToHost)
         __builtin_nontemporal_store(v[u], dst[u]);
       else
@@ -307,15 +309,32 @@ hipError_t launch_pack_pairs(const int64_t *dev_idx, const int64_t *host_idx, in
   return hipGetLastError();
 }
 
-hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, size_t lds_bytes,
+namespace {
+
+template <int kDepth>
+void launch_rows_depth(const XferArgs &a, dim3 grid, bool to_host, size_t lds_bytes,
                        hipStream_t s) {
-  if (blocks == 0) return hipSuccess;
-  const dim3 grid(blocks), block(kXferThreads);
+  const dim3 block(kXferThreads);
   switch ((a.pace_ticks ? 2 : 0) + (to_host ? 1 : 0)) {
-    case 3: hipLaunchKernelGGL((xfer_rows<true, true>), grid, block, lds_bytes, s, a); break;
-    case 2: hipLaunchKernelGGL((xfer_rows<false, true>), grid, block, lds_bytes, s, a); break;
-    case 1: hipLaunchKernelGGL((xfer_rows<true, false>), grid, block, lds_bytes, s, a); break;
-    default: hipLaunchKernelGGL((xfer_rows<false, false>), grid, block, lds_bytes, s, a); break;
+    case 3: hipLaunchKernelGGL((xfer_rows<true, true, kDepth>), grid, block, lds_bytes, s, a); break;
+    case 2: hipLaunchKernelGGL((xfer_rows<false, true, kDepth>), grid, block, lds_bytes, s, a); break;
+    case 1: hipLaunchKernelGGL((xfer_rows<true, false, kDepth>), grid, block, lds_bytes, s, a); break;
+    default: hipLaunchKernelGGL((xfer_rows<false, false, kDepth>), grid, block, lds_bytes, s, a); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, size_t lds_bytes,
+                       int depth, hipStream_t s) {
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid(blocks);
+  switch (depth) {
+    case 1: launch_rows_depth<1>(a, grid, to_host, lds_bytes, s); break;
+    case 2: launch_rows_depth<2>(a, grid, to_host, lds_bytes, s); break;
+    case 4: launch_rows_depth<4>(a, grid, to_host, lds_bytes, s); break;
+    case 8: launch_rows_depth<8>(a, grid, to_host, lds_bytes, s); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

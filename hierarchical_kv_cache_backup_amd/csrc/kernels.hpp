@@ -11,8 +11,9 @@ namespace kvt {
 // a.nblocks blocks of work (plan_rows / plan_tiles), so blocks may be smaller.
 // lds_bytes: dynamic LDS asked for per workgroup (the kernel uses none; a
 // compute unit's whole LDS keeps other kernels' workgroups off its compute unit).
+// depth: chunks each lane keeps in flight, 1, 2, 4 or 8 (else hipErrorInvalidValue).
 hipError_t launch_rows(const XferArgs &a, uint32_t blocks, bool to_host, size_t lds_bytes,
-                       hipStream_t s);
+                       int depth, hipStream_t s);
 // The staged path's device-side pass over walk rows [a.row_begin, a.row_end):
 // gather packs them from the device buffers into the staging buffer a.host,
 // the scatter unpacks them. One launch per stage_max_rows(R) rows (one for any

@@ -217,23 +217,24 @@ void default_calibration(kv_calib_t *c) {
   c->staged_min_gain = 0.02;
   c->kernel_gbps[0] = 55.9;  // full grid; a capped grid is modelled per workgroup below
   c->kernel_gbps[1] = 57.3;
-  // What W workgroups move on a capped grid. A workgroup keeps 8 chunks of
-  // 8 bytes in flight per lane (16 KiB): a write-back workgroup moves 6.56
-  // GB/s, a load's 3.6-4.0 (4-16 workgroups). Write-backs on 8 workgroups, 64
-  // to 32768 tokens of the 78 x 1152-byte MLA latent (5.8 MB to 2.9 GB), fit
-  // 6.56 GB/s per workgroup with a slow start: the first ~17 MB of a call
-  // cost up to 267 us more than the launch (64-token calls run at 27 GB/s,
-  // 32K-token ones at 52.3); within 1.4%. Where the walk jumps between device
-  // rows (page_first, whose walk changes layer every row) a write-back
-  // workgroup pays ~4 ns more per jump.
-  c->kernel_wg_gbps[0] = 6.56;
+  // What W workgroups move on a capped grid. A workgroup keeps
+  // kernel_lane_depth chunks of 8 bytes in flight per lane: a write-back
+  // workgroup moves ~3.3 GB/s at the default depth of 2 (6.6 at 8), a load's
+  // 3.6-4.0 at 8 (4-16 workgroups). Write-backs on the default grid (18
+  // workgroups, depth 2, paced to 54 GB/s), 64 to 32768 tokens of the 78 x
+  // 1152-byte MLA latent (5.8 MB to 2.9 GB) in the three layouts, fit a slow
+  // start: the first ~30 MB of a call cost up to 275 us more (64-token calls
+  // run at 34 GB/s, 32K-token ones at 53.6); within 4% from 512 tokens up and
+  // 9.5% below (the paths there are far apart). At depth 2 the walk's jumps
+  // between device rows (page_first) cost nothing measurable.
+  c->kernel_wg_gbps[0] = 3.3;
   c->kernel_wg_gbps[1] = 3.8;
   c->kernel_wg_row_ns[0] = 0.0;
   c->kernel_wg_row_ns[1] = 0.0;
-  c->kernel_wg_jump_ns[0] = 4.0;
+  c->kernel_wg_jump_ns[0] = 0.0;
   c->kernel_wg_jump_ns[1] = 0.0;
-  c->kernel_wg_start_bytes[0] = 17e6;
-  c->kernel_wg_start_us[0] = 267.0;
+  c->kernel_wg_start_bytes[0] = 30e6;
+  c->kernel_wg_start_us[0] = 275.0;
   c->kernel_wg_start_bytes[1] = 0.0;
   c->kernel_wg_start_us[1] = 0.0;
   c->dma_copy_us[0] = c->dma_copy_us[1] = 9.5;
@@ -242,24 +243,25 @@ void default_calibration(kv_calib_t *c) {
   c->load_split_min_bytes = 16.0 * 1024 * 1024;
   // A write-back kernel on a full grid keeps the link full with posted host
   // writes, and an HBM-bound kernel running beside it (the model's next
-  // prefill or decode) then ran ~26-45x longer (fp8 write-backs beside a
-  // stream of 2 x 256 MiB reductions). Unpaced, 8 workgroups (~54 GB/s of
-  // writes) moved 54.5-54.8 GB/s beside it for 1.21x; from 10 the writes
-  // outran what the link drains (~56-57 GB/s), queued in the memory system,
-  // and the write-back fell to 39-49 GB/s while the neighbour slowed 1.3-5x.
-  // Paced (kernel_pace_gbps) a grid cannot outrun the link, and the
-  // neighbour's cost follows the workgroup count (paced to 54-56 GB/s: 8
-  // 1.19-1.21x, 9 1.22x, 10 1.28x, 12 1.42-1.47x, 16 1.9-2x, 26 2.6-3x; the
-  // copy engines 1.12x): 9 is the smallest grid that produces more than the
-  // pace, and moved 53.0 GB/s paced to 54 and 54.9 paced to 56 beside the
-  // neighbour. On the host whose link drained least (1 GiB D2H copy 56.2
-  // GB/s) a pace of 56 sagged to 52.2-52.9 GB/s on 8K-32K-token write-backs
-  // and one of 55.1 held 54.6: the default pace, 54, stays ~2% under that. A
-  // caller that measures its link paces at ~0.98 of its D2H copy rate. The
-  // start of a call is latency-bound: 32 blocks of burst per workgroup before
-  // the pacing starts keep small calls at the unpaced rate. Loads keep the
-  // full grid: a load beside compute is KV_F_LOAD_OVERLAP's case.
-  c->kernel_max_workgroups[0] = 9;
+  // prefill or decode) then ran ~26-46x longer (fp8 write-backs beside a
+  // stream of 2 x 256 MiB reductions). Unpaced, a grid whose writes outrun
+  // what the link drains (~56-57 GB/s) backs up in the memory system and the
+  // write-back falls to ~39-44 GB/s (depth 2: from 18 workgroups; depth 8:
+  // from 10). Paced (kernel_pace_gbps) a grid cannot outrun the link, and the
+  // neighbour's cost follows the workgroups and the accesses each keeps in
+  // flight (paced to 54-56 GB/s, depth 2: 16 workgroups 1.13x, 18 1.16x, 20
+  // 1.19x, 24 1.28-1.30x; depth 8: 8 1.19-1.20x, 9 1.22x, 10 1.27-1.28x, 12
+  // 1.43-1.48x; the copy engines 1.11x). 18 workgroups at depth 2 are the
+  // smallest grid that produces more than its pace: 53.0 GB/s beside the
+  // neighbour paced to 54, 54.9 paced to 56. On the host whose link drained
+  // least (1 GiB D2H copy 56.2 GB/s) a pace of 56 sagged to 52.2-52.9 GB/s on
+  // 8K-32K-token write-backs and one of 55.1 held 54.6: the default pace, 54,
+  // stays ~2% under that. A caller that measures its link paces at ~0.98 of
+  // its D2H copy rate. The start of a call is latency-bound: 32 blocks of
+  // burst per workgroup before the pacing starts keep small calls at the
+  // unpaced rate. Loads keep the full grid: a load beside compute is
+  // KV_F_LOAD_OVERLAP's case.
+  c->kernel_max_workgroups[0] = 18;
   c->kernel_max_workgroups[1] = 0;
   c->kernel_pace_gbps[0] = 54.0;
   c->kernel_pace_gbps[1] = 0.0;
@@ -268,10 +270,12 @@ void default_calibration(kv_calib_t *c) {
   // A capped load's workgroups each take a compute unit of their own: beside
   // the reductions below, 16 load workgroups slowed them 1.23x that way and
   // 1.43x sharing compute units with them (24: 1.28x against 1.56x). A
-  // write-back's did not gain (8 workgroups: 1.33x alone on their compute
-  // units, 1.21x sharing them).
+  // write-back's did not gain (18 workgroups at depth 2, paced: 1.34x alone on
+  // their compute units, 1.17x sharing them).
   c->kernel_cu_exclusive[0] = 0.0;
   c->kernel_cu_exclusive[1] = 1.0;
+  c->kernel_lane_depth[0] = 2.0;
+  c->kernel_lane_depth[1] = 8.0;
   // Measured on MI355X with a streamed 24-layer load (256 MiB per layer) and an
   // HBM-bound consumer (torch int64 sums) overlapped layer by layer: the
   // consumer's slowdown beside the kernel path grows with the load's grid
@@ -283,14 +287,14 @@ void default_calibration(kv_calib_t *c) {
   c->overlap_dma_penalty = 0.15;
   c->overlap_kernel_max_workgroups = 24;
   // On the mixed batch (load 51.2 GB || write-back 11.6 GB) with the duplex
-  // caps below, the load's kernel held 56.8 GB/s (57.3 alone) beside a
-  // write-back kernel of 24.4 GB/s (26.8 alone on its duplex cap of 4
-  // workgroups): 99.2% of the duplex bound, against 79.8% with the caps off
-  // (the load on a full grid). The write-back's cap already sets its rate;
-  // what the load's traffic costs it on top is charged here.
+  // caps below, the load's kernel held 56.5-56.8 GB/s (57.3 alone) beside a
+  // write-back kernel of 23-24 GB/s (26.6-26.8 alone on its duplex cap of 8
+  // workgroups at depth 2): 98.6-99.2% of the duplex bound, against 80% with
+  // the caps off (the load on a full grid). The write-back's cap already sets
+  // its rate; what the load's traffic costs it on top is charged here.
   c->duplex_kernel_penalty[0] = 0.1;
   c->duplex_kernel_penalty[1] = 0.0;
-  c->duplex_kernel_max_workgroups[0] = 4;
+  c->duplex_kernel_max_workgroups[0] = 8;
   c->duplex_kernel_max_workgroups[1] = 32;
   c->staged_chunk_bytes = 256.0 * 1024 * 1024;
   // the device-side gather / scatter of a staged chunk (stage_windows, HBM to
@@ -1066,7 +1070,7 @@ static int transfer(kv_pool *p, int dir, const int64_t *dev_idx, const int64_t *
                                   p->wall_khz);
         b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
         e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, exclusive_lds(p, c, dir, cap),
-                        s);
+                        (int)c.kernel_lane_depth[dir], s);
       }
       if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
     }
@@ -1200,7 +1204,8 @@ static int transfer_noalloc(kv_pool *p, int dir, const int64_t *dev_idx, const i
     b.pace_ticks = pace_ticks((double)b.rows_per_block * g.R, blocks,
                               (uint32_t)d.last_workgroups, c.kernel_pace_gbps[dir], p->wall_khz);
     b.pace_burst = (uint32_t)c.kernel_pace_burst_blocks[dir];
-    e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, exclusive_lds(p, c, dir, cap), s);
+    e = launch_rows(b, (uint32_t)d.last_workgroups, dir == 0, exclusive_lds(p, c, dir, cap),
+                    (int)c.kernel_lane_depth[dir], s);
     if (e == hipSuccess && dir == 1) e = mark_landed(p, la, lb, s, &blocked);
   }
   if (e != hipSuccess) return hip_fail(e, "enqueueing the no-allocation transfer");
@@ -1386,6 +1391,10 @@ static int check_calibration(const kv_calib_t *c) {
   for (int d = 0; d < 2; d++)
     if (c->kernel_cu_exclusive[d] != 0 && c->kernel_cu_exclusive[d] != 1)
       return fail(KV_EINVAL, "kernel_cu_exclusive must be 0 or 1");
+  for (int d = 0; d < 2; d++)
+    if (c->kernel_lane_depth[d] != 1 && c->kernel_lane_depth[d] != 2 &&
+        c->kernel_lane_depth[d] != 4 && c->kernel_lane_depth[d] != 8)
+      return fail(KV_EINVAL, "kernel_lane_depth must be 1, 2, 4 or 8");
   if (!(c->duplex_kernel_penalty[0] >= 0) || !(c->duplex_kernel_penalty[1] >= 0) ||
       !(c->staged_chunk_bytes >= 16) ||
       !(c->staged_gather_gbps > 0) || !(c->staged_min_gain >= 0 && c->staged_min_gain < 1))

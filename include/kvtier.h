@@ -290,6 +290,13 @@ typedef struct {
                                    an overlapped load's, a duplex one): 1 = each workgroup
                                    asks for a compute unit's whole LDS, so that no other
                                    kernel's workgroups share its compute units; 0 = off */
+  double kernel_lane_depth[2];  /* kernel path: 8-byte chunks each lane keeps in flight,
+                                   1, 2, 4 or 8. A workgroup's rate grows with it (a
+                                   write-back workgroup ~3.3 GB/s at 2, ~6.6 at 8); at a
+                                   given rate, more workgroups with fewer accesses in flight
+                                   each cost a kernel beside them less. Defaults 2 for a
+                                   backup, 8 for a load; kernel_wg_gbps and the slow start
+                                   are fitted at the default */
 } kv_calib_t;
 
 typedef struct kv_pool kv_pool_t; /* opaque */

@@ -67,9 +67,13 @@ struct Mirror {
   }
 };
 
-// Replays one launch of xfer_rows on the mirrors. tok holds {dev slot, host key}.
+// Replays one launch of xfer_rows on the mirrors, `depth` chunks in flight per
+// lane. tok holds {dev slot, host key}. Like the kernel, a slot past the
+// block's chunks resolves the block's last chunk (its index loads must stay in
+// bounds) and moves nothing (the kernel sends it to its sink).
 static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, int32_t la,
-                        int32_t lb, bool to_host, std::vector<uint8_t> &cover, uint32_t cap) {
+                        int32_t lb, bool to_host, std::vector<uint8_t> &cover, uint32_t cap,
+                        int depth) {
   const Geom &g = m.g;
   XferArgs a{};
   a.R = g.R;
@@ -88,11 +92,12 @@ static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, i
     const uint32_t row0 = b * a.rows_per_block;
     const uint32_t nrows = umin(a.rows_per_block, a.total_rows - row0);
     const uint32_t nchunks = nrows * a.cpr;
-    for (uint32_t base = 0; base < nchunks; base += kChunksPerBlock)
-      for (int u = 0; u < kXferUnroll; u++)
+    for (uint32_t base = 0; base < nchunks; base += (uint32_t)kXferThreads * depth)
+      for (int u = 0; u < depth; u++)
         for (uint32_t tid = 0; tid < (uint32_t)kXferThreads; tid++) {
-          const uint32_t f = base + u * kXferThreads + tid;
-          if (f >= nchunks) continue;
+          const uint32_t f0 = base + u * kXferThreads + tid;
+          const bool live = f0 < nchunks;
+          const uint32_t f = live ? f0 : nchunks - 1;
           const uint32_t rr = f / a.cpr, k = f - rr * a.cpr;
           uint32_t i = 0, lc = 0;
           walk_row(a, row0 + rr, i, lc);
@@ -103,6 +108,7 @@ static void replay_rows(Mirror &m, const std::vector<int64_t> &tok, int64_t n, i
           const int64_t host_off = ((int64_t)(a.lc0 + lc) * a.lc_stride + key) * g.R + kChunkBytes * (int64_t)k;
           CHECK(dev_off >= 0 && dev_off + kChunkBytes <= g.S_dev * g.R, "device offset out of bounds");
           CHECK(host_off >= 0 && host_off + kChunkBytes <= (int64_t)m.host.size(), "host offset out of bounds");
+          if (!live) continue;
           uint8_t *d = m.dev[a.lc0 + lc].data() + dev_off;
           uint8_t *h = m.host.data() + host_off;
           if (to_host)
@@ -433,10 +439,12 @@ static int64_t check_case(const kv_geometry_t &kg, const Geom &g, const std::vec
       std::vector<uint8_t> cover((size_t)cells, 0);
       int64_t copies = 0;
       const uint32_t cap = (uint32_t)(std::vector<int>{0, 1, 3, 64})[uni(0, 3)];
+      const int depth = (std::vector<int>{1, 2, 4, 8})[uni(0, 3)];
       if (variant == 0) {
-        replay_rows(m, tok, n, l0, l1, to_host, cover, cap);
+        replay_rows(m, tok, n, l0, l1, to_host, cover, cap, depth);
       } else if (variant == 1) {
-        for (int32_t l = l0; l < l1; l++) replay_rows(m, tok, n, l, l + 1, to_host, cover, cap);
+        for (int32_t l = l0; l < l1; l++)
+          replay_rows(m, tok, n, l, l + 1, to_host, cover, cap, depth);
       } else if (variant == 2) {
         replay_tiles(m, tok, n, l0, l1, to_host, cover, cap);
       } else if (variant == 4) {

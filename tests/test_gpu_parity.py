@@ -270,15 +270,18 @@ def test_capped_grid_matches_oracle(torch, stream, layout):
     for path in (kvt.PATH_KERNEL, kvt.PATH_KERNEL_LDS):
         pool = make_pool(g, bufs, path)
         # capped grids with and without a compute unit per workgroup
-        # (kernel_cu_exclusive), each way
-        for cap, excl in ((1, 1), (3, 0), (7, 1), (7, 0)):
+        # (kernel_cu_exclusive), each way, at every lane depth; and full grids
+        # (cap 0) at the shallow depths
+        for cap, excl, depth in ((1, 1, 8), (3, 0, 2), (7, 1, 4), (7, 0, 1), (0, 0, 1),
+                                 (0, 0, 2)):
             c = pool.calibration()
             c.kernel_max_workgroups[0] = c.kernel_max_workgroups[1] = cap
             c.kernel_cu_exclusive[0] = c.kernel_cu_exclusive[1] = excl
+            c.kernel_lane_depth[0] = c.kernel_lane_depth[1] = depth
             pool.set_calibration(c)
             d, h = _request(rng, g, "random")
-            print("capped layout=%d path=%d cap=%d exclusive=%d" % (layout, path, cap, excl),
-                  flush=True)
+            print("capped layout=%d path=%d cap=%d exclusive=%d depth=%d"
+                  % (layout, path, cap, excl, depth), flush=True)
             run_backup_and_compare(g, pool, bufs, d, h, 0, L, stream)
             pool.host_array()[:] = rng.integers(0, 256, size=g.host_bytes(), dtype=np.uint8)
             run_load_and_compare(g, pool, bufs, d, h, 0, L, stream)
@@ -398,8 +401,8 @@ def test_calibrate_write_pace(torch, stream):
 
 def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     """A backup's kernel launches at most kernel_max_workgroups[0] workgroups
-    (default 9); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
-    on a KV_F_DUPLEX pool (defaults: 4 for a backup, 32 for a load), at most
+    (default 18); the kernel paths launch at most duplex_kernel_max_workgroups[dir]
+    on a KV_F_DUPLEX pool (defaults: 8 for a backup, 32 for a load), at most
     overlap_kernel_max_workgroups for a load flagged KV_F_LOAD_OVERLAP (default 24), and the
     smallest cap that applies; without a cap a launch has one workgroup per
     block of work. The bytes match the oracle under every cap."""
@@ -418,16 +421,17 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     plain = make_pool(g, bufs)
     c = plain.calibration()
-    assert list(c.duplex_kernel_max_workgroups) == [4.0, 32.0]
-    assert list(c.kernel_max_workgroups) == [9.0, 0.0]
+    assert list(c.duplex_kernel_max_workgroups) == [8.0, 32.0]
+    assert list(c.kernel_max_workgroups) == [18.0, 0.0]
     assert list(c.kernel_cu_exclusive) == [0.0, 1.0]
+    assert list(c.kernel_lane_depth) == [2.0, 8.0]
     assert tuple(plain.stats().last_workgroups) == (0, 0)
     default = grids(plain, kvt.PATH_KERNEL)
     c.kernel_max_workgroups[0] = 0
     plain.set_calibration(c)
     free = grids(plain, kvt.PATH_KERNEL)
     assert free[0] > 1000 and free[1] > 1000, free     # one workgroup per 16 KiB block
-    assert default == (9, free[1]), default
+    assert default == (18, free[1]), default
     c.duplex_kernel_max_workgroups[0] = -1
     with pytest.raises(kvt.KvError):
         plain.set_calibration(c)
@@ -435,16 +439,21 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
     c.kernel_cu_exclusive[1] = 0.5               # 0 or 1 only
     with pytest.raises(kvt.KvError):
         plain.set_calibration(c)
+    for bad in (0.0, 3.0, 16.0):                 # 1, 2, 4 or 8 only
+        c = plain.calibration()
+        c.kernel_lane_depth[0] = bad
+        with pytest.raises(kvt.KvError):
+            plain.set_calibration(c)
     plain.close()
 
     duplex = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_DUPLEX)
-    assert grids(duplex, kvt.PATH_KERNEL) == (4, 32)
+    assert grids(duplex, kvt.PATH_KERNEL) == (8, 32)
     lds = grids(duplex, kvt.PATH_KERNEL_LDS)
-    assert 0 < lds[0] <= 4 and 0 < lds[1] <= 32, lds
+    assert 0 < lds[0] <= 8 and 0 < lds[1] <= 32, lds
     c = duplex.calibration()
     c.kernel_max_workgroups[:] = [0, 16]             # the tighter cap wins
     duplex.set_calibration(c)
-    assert grids(duplex, kvt.PATH_KERNEL) == (4, 16)
+    assert grids(duplex, kvt.PATH_KERNEL) == (8, 16)
     c.kernel_max_workgroups[:] = [0, 0]
     c.duplex_kernel_max_workgroups[:] = [0, 0]       # duplex caps off
     duplex.set_calibration(c)
@@ -453,7 +462,7 @@ def test_duplex_and_overlap_caps_bound_the_grid(torch, stream):
 
     overlap = make_pool(g, bufs, flags=kvt.F_CHECK_UNIQUE | kvt.F_LOAD_OVERLAP)
     got = grids(overlap, kvt.PATH_KERNEL)
-    assert got == (9, 24), got                      # the overlap cap is a load's only
+    assert got == (18, 24), got                     # the overlap cap is a load's only
     overlap.close()
 
 
@@ -503,7 +512,7 @@ def _hold_stream(torch, st, gate):
 def test_duplex_caps_follow_the_other_direction(torch):
     """Without KV_F_DUPLEX the duplex grid caps apply while the other direction
     has a transfer in flight on another stream at submission: a backup issued
-    while a load is held in flight gets 4 workgroups and a load issued while a
+    while a load is held in flight gets 8 workgroups and a load issued while a
     backup is held gets 32; issued alone, each gets the full grid. Both
     directions' bytes match the oracle."""
     import threading
@@ -536,7 +545,7 @@ def test_duplex_caps_follow_the_other_direction(torch):
             pool.load(d_load, h_load, 0, g.L, s_load)
             pool.backup(d_back, h_back, 0, g.L, s_back)
             grids = tuple(pool.stats().last_workgroups)
-            assert grids == (4, full_load), grids
+            assert grids == (8, full_load), grids
         else:
             cb = _hold_stream(torch, s_back, gate)
             pool.backup(d_back, h_back, 0, g.L, s_back)

@@ -177,18 +177,18 @@ def test_flags_overlap_and_duplex():
 # calibration; in brackets the GB/s measured per path (kernel / copy engines /
 # staged) by bench.py --size-sweep on an MI355X.
 MEASURED = [
-    ("layer_first", 256, 0, kvt.PATH_KERNEL),          # 31.0 / 19.8 / 19.2
-    ("layer_first", 2048, 0, kvt.PATH_KERNEL),         # 48.7 / 46.2 / 45.6
-    ("page_first", 64, 0, kvt.PATH_STAGED),            # 26.9 / 6.7 / 34.1
-    ("page_first", 1024, 0, kvt.PATH_STAGED),          # 43.7 / 38.1 / 53.2
-    ("page_first", 8192, 0, kvt.PATH_STAGED),          # 50.4 / 53.1 / 56.0
-    ("page_first", 16384, 0, kvt.PATH_STAGED),         # 50.7 / 54.7 / 56.4
-    ("page_first_direct", 256, 0, kvt.PATH_STAGED),    # 31.3 / 19.6 / 44.3
-    ("page_first_direct", 4096, 0, kvt.PATH_STAGED),   # 50.4 / 50.5 / 55.5
-    ("layer_first", 1024, 1, kvt.PATH_KERNEL),         # 55.2 / 38.4 / 36.6
-    ("layer_first", 8192, 1, kvt.PATH_KERNEL),         # 55.8 / 53.1 / 51.3
-    ("page_first", 256, 1, kvt.PATH_KERNEL),           # 51.8 / 20.1 / 45.8
-    ("page_first_direct", 512, 1, kvt.PATH_KERNEL),    # 54.4 / 29.6 / 50.5
+    ("layer_first", 256, 0, kvt.PATH_KERNEL),          # 33.1 / 19.8 / 19.0
+    ("layer_first", 2048, 0, kvt.PATH_KERNEL),         # 49.4 / 46.1 / 45.5
+    ("page_first", 256, 0, kvt.PATH_STAGED),           # 31.9 / 19.8 / 44.5
+    ("page_first", 1024, 0, kvt.PATH_STAGED),          # 45.4 / 38.1 / 53.1
+    ("page_first", 8192, 0, kvt.PATH_STAGED),          # 52.7 / 53.1 / 56.2
+    ("page_first", 16384, 0, kvt.PATH_STAGED),         # 53.2 / 54.8 / 56.3
+    ("page_first_direct", 256, 0, kvt.PATH_STAGED),    # 32.7 / 19.6 / 44.8
+    ("page_first_direct", 4096, 0, kvt.PATH_STAGED),   # 51.5 / 50.5 / 55.6
+    ("layer_first", 1024, 1, kvt.PATH_KERNEL),         # 55.1 / 38.3 / 36.5
+    ("layer_first", 8192, 1, kvt.PATH_KERNEL),         # 56.0 / 53.2 / 50.4
+    ("page_first", 256, 1, kvt.PATH_KERNEL),           # 51.9 / 20.0 / 45.4
+    ("page_first_direct", 512, 1, kvt.PATH_KERNEL),    # 54.5 / 29.6 / 50.6
 ]
 
 
