@@ -520,9 +520,9 @@ def counter_link_bytes(kernel_name, src_hash):
     return link.get("host_link_bytes_per_launch")
 
 
-KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true, true> (D2H gather, whole prefix in one launch, "
+KERNEL_NAMES = {"d2h": "kvt::xfer_rows<true, true, 2> (D2H gather, whole prefix in one launch, "
                        "on the default write-back grid, paced under the measured D2H link rate)",
-                "h2d": "kvt::xfer_rows<false, false> (H2D scatter, one launch per layer: each "
+                "h2d": "kvt::xfer_rows<false, false, 8> (H2D scatter, one launch per layer: each "
                        "layer holds more than the 16 MiB load group threshold)"}
 
 
@@ -695,8 +695,8 @@ def _counter_rows(d):
 
 def _kernel_key(name):
     return ("copy" if "elementwise_kernel" in name and "copy" in name else
-            "xfer_rows_d2h" if "xfer_rows<true, true>" in name else
-            "xfer_rows_h2d" if "xfer_rows<false, false>" in name else
+            "xfer_rows_d2h" if "xfer_rows<true, true" in name else
+            "xfer_rows_h2d" if "xfer_rows<false, false" in name else
             "stage_gather" if "stage_windows<true" in name else
             "stage_scatter" if "stage_windows<false" in name else None)
 
