@@ -201,17 +201,20 @@ typedef struct {
  * path's device-side passes, HBM to HBM, are not capped by it). The kernels
  * stride over their work, so a cap moves the same bytes while leaving compute
  * units free for kernels on other streams (e.g. the layer that was just
- * loaded). Default: 9 for a backup, none for a load. A write-back kernel on a
+ * loaded). Default: 18 for a backup, none for a load. A write-back kernel on a
  * large grid keeps so many posted host writes queued that HBM-bound kernels
- * running beside it slow by up to ~45x; the slowdown follows the workgroup
- * count, and 9 workgroups, paced, move ~95-98% of the full grid's rate while
- * they slow by ~1.22x (the copy engines: ~1.12x). Set [0] to 0 for the full
- * grid when nothing else runs during backups.
+ * running beside it slow by up to ~46x; the slowdown follows the writes in
+ * flight, and 18 workgroups of two chunks per lane (kernel_lane_depth), paced,
+ * move ~96-98% of the full grid's rate while they slow by ~1.16x (the copy
+ * engines: ~1.12-1.15x). Set [0] to 0 for the full grid when nothing else runs
+ * during backups.
  * kernel_pace_gbps: on the kernel and LDS paths, > 0 holds a launch's
  * workgroups to this total rate: each starts its blocks of work (tiles on the
  * LDS path) at least grid * block bytes / rate apart on the device's
- * constant-rate wall clock, with one block of catch-up after a stall. Each
- * write-back workgroup issues up to ~6.6 GB/s of posted host writes; a grid
+ * constant-rate wall clock, with one block of catch-up after a stall; each
+ * workgroup's first interval is offset by its share of one, so the grid's
+ * blocks go out spread over it. Each write-back workgroup issues up to ~3.3
+ * GB/s of posted host writes at two chunks per lane (~6.6 at eight); a grid
  * that issues more than the host link drains queues them in the memory system
  * and falls to ~40 GB/s, so the pace must stay under the link's D2H rate.
  * Default: 54 for a backup (~2% under the lowest D2H drain rate measured on
@@ -234,7 +237,7 @@ typedef struct {
  * duplex_kernel_max_workgroups: cap on the workgroups of a kernel-path
  * transfer while the other direction is busy (KV_F_DUPLEX, or a transfer of
  * the other direction in flight at submission on another stream); [0] for a
- * backup, [1] for a load, 0 = no cap; defaults 4 and 32. A load's kernel holds
+ * backup, [1] for a load, 0 = no cap; defaults 8 and 32. A load's kernel holds
  * the link with 32 workgroups; a write-back kernel with a small grid leaves the
  * load most of the link and, together with the load's cap, leaves compute
  * units free for the other direction's kernels. The staged path's device-side
