@@ -1420,10 +1420,13 @@ def overlap_study(torch, kvt, workloads, layers=24, with_loads=True):
         # (grid cap, pace, burst blocks, a compute unit per workgroup, lane depth)
         plain = [(cap, 0.0, 0, 0, 2) for cap in (8, 12, 16, 18, 20, 24, 32)]
         plain += [(cap, 0.0, 0, 0, 8) for cap in (4, 6, 8, 10, 12)]
+        plain += [(cap, 0.0, 0, 0, 1) for cap in (16, 32)]
         plain += [(0, 0.0, 0, 0, 2)]
         paced = [(cap, gbps, 32, 0, 2) for cap in (14, 16, 18, 20, 24, 28)
                  for gbps in (54.0, 56.0)]
         paced += [(cap, gbps, 32, 0, 8) for cap in (8, 9, 10, 12) for gbps in (54.0, 56.0)]
+        paced += [(cap, gbps, 32, 0, 1) for cap in (32, 36, 40, 48) for gbps in (54.0, 56.0)]
+        paced += [(cap, 56.0, 32, 0, 4) for cap in (10, 12, 14)]
         paced += [(18, 54.0, 32, 1, 2), (9, 54.0, 32, 1, 8)]
         for cap, pace, burst, ex, depth in plain + paced + [("dma", 0.0, 0, 0, 2)]:
             cal = pool.calibration()
