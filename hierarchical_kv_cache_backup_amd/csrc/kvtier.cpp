@@ -251,7 +251,8 @@ void default_calibration(kv_calib_t *c) {
   // neighbour's cost follows the workgroups and the accesses each keeps in
   // flight (paced to 54-56 GB/s, depth 2: 16 workgroups 1.13x, 18 1.16x, 20
   // 1.19x, 24 1.28-1.30x; depth 8: 8 1.19-1.20x, 9 1.22x, 10 1.27-1.28x, 12
-  // 1.43-1.48x; the copy engines 1.11x). 18 workgroups at depth 2 are the
+  // 1.43-1.48x; depth 1: 32 1.25-1.28x, 36 1.33-1.35x; depth 4: 10 1.18x;
+  // the copy engines 1.11x). 18 workgroups at depth 2 are the
   // smallest grid that produces more than its pace: 53.0 GB/s beside the
   // neighbour paced to 54, 54.9 paced to 56. On the host whose link drained
   // least (1 GiB D2H copy 56.2 GB/s) a pace of 56 sagged to 52.2-52.9 GB/s on
